@@ -1,0 +1,209 @@
+"""CPU oracle for key-only gated linear attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP
+implementation in ``recurrent_vision_backbone_key_amd`` and never imports it.
+
+Two independent references of the same definition ("GTR: Gated Token
+Recurrence for Efficient Dense Prediction", paper Section 2.1):
+
+* :func:`fwd` -- the token-by-token fp64 recurrence in plain C
+  (``gla_oracle.c``), OpenMP over the (batch, head) units;
+* :func:`closed_form_fwd` -- the O(L^2) unrolled sum
+  ``o_t = scale * sum_{s<=t} (q_t (.) prod_{j=s+1..t} gamma_j (.) k_s) v_s``
+  in numpy fp64 with explicit per-pair gate sums, for tiny inputs.  Its scan
+  orders are built from array flips and grid transposes, not from the C
+  code's index formula.
+
+Every function's pins (closed forms, special cases, invariants) are the
+``tests/test_oracle*.py`` tests.  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_BUILD_DIR = os.path.join(_HERE, "_build")
+LIB_PATH = os.path.join(_BUILD_DIR, "libgla_oracle.so")
+SOURCE = os.path.join(_HERE, "gla_oracle.c")
+
+L2R, R2L, T2B, B2T = 0, 1, 2, 3
+DIRS = (L2R, R2L, T2B, B2T)
+DIR_NAMES = {L2R: "L2R", R2L: "R2L", T2B: "T2B", B2T: "B2T"}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gla_oracle.c with gcc (fp64, no fast-math, no FMA contraction)."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    os.makedirs(_BUILD_DIR, exist_ok=True)
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-o", tmp, SOURCE, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gla_oracle_fwd.restype = ctypes.c_int
+    lib.gla_oracle_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int,
+        ctypes.c_double, ctypes.c_double, ctypes.c_double,
+        ctypes.c_long, ctypes.c_long, ctypes.c_void_p]
+    lib.gla_oracle_half_to_double.restype = ctypes.c_double
+    lib.gla_oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.gla_oracle_scan_token.restype = ctypes.c_long
+    lib.gla_oracle_scan_token.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_long,
+                                          ctypes.c_long]
+    _lib = lib
+    return lib
+
+
+def half_to_double(bits: int) -> float:
+    return _load().gla_oracle_half_to_double(bits)
+
+
+def scan_token(direction: int, i: int, H: int, W: int) -> int:
+    return _load().gla_oracle_scan_token(direction, i, H, W)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def fwd(q, k, v, z, direction, H, W, r=None, w=None, tau=16.0, scale=None,
+        eps=1e-6, units=None, threads=None):
+    """fp64 recurrence.  q, k: [B, L, NH, dk]; v, r: [B, L, NH, dv] (float16 or
+    float32 arrays, read exactly as stored); z: [B, L, NH, dk] float32;
+    w: [dv] float32 or None.  Returns float64 [B, L, NH, dv].
+
+    ``units=(u0, u1)`` restricts the work to (batch*NH + head) units in
+    [u0, u1); other rows of the result are NaN.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    if q.dtype == np.float16:
+        dtype = 0
+    elif q.dtype == np.float32:
+        dtype = 1
+    else:
+        raise TypeError("q must be float16 or float32")
+    for name, a in (("k", k), ("v", v)) + ((("r", r),) if r is not None else ()):
+        if a.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    B, L, NH, dk = q.shape
+    dv = v.shape[3]
+    if L != H * W or k.shape != q.shape or z.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("shape mismatch")
+    if r is not None:
+        r = np.ascontiguousarray(r)
+        if r.shape != v.shape:
+            raise ValueError("r shape mismatch")
+    if w is not None:
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        if w.shape != (dv,):
+            raise ValueError("w must have shape [dv]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    u0, u1 = (0, B * NH) if units is None else units
+    out = np.full((B, L, NH, dv), np.nan, dtype=np.float64)
+    old = os.environ.get("OMP_NUM_THREADS")
+    if threads is not None:
+        os.environ["OMP_NUM_THREADS"] = str(threads)
+    try:
+        rc = lib.gla_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(r), _ptr(w), dtype,
+                                B, NH, H, W, dk, dv, direction, float(tau), float(scale),
+                                float(eps), u0, u1, _ptr(out))
+    finally:
+        if threads is not None:
+            if old is None:
+                os.environ.pop("OMP_NUM_THREADS", None)
+            else:
+                os.environ["OMP_NUM_THREADS"] = old
+    if rc != 0:
+        raise RuntimeError(f"gla_oracle_fwd failed with status {rc}")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Independent O(L^2) closed form (numpy fp64), tiny inputs only.
+# ---------------------------------------------------------------------------
+
+def to_scan_order(x, direction, H, W):
+    """Token-ordered [L, ...] -> scan-ordered [L, ...] by flips and transposes."""
+    rest = x.shape[1:]
+    if direction == L2R:
+        return x
+    if direction == R2L:
+        return x[::-1]
+    cols = x.reshape((H, W) + rest).swapaxes(0, 1).reshape((H * W,) + rest)
+    return cols if direction == T2B else cols[::-1]
+
+
+def from_scan_order(y, direction, H, W):
+    """Inverse of :func:`to_scan_order`."""
+    rest = y.shape[1:]
+    if direction == L2R:
+        return y
+    if direction == R2L:
+        return y[::-1]
+    if direction == B2T:
+        y = y[::-1]
+    return y.reshape((W, H) + rest).swapaxes(0, 1).reshape((H * W,) + rest)
+
+
+def closed_form_fwd(q, k, v, z, direction, H, W, r=None, w=None, tau=16.0, scale=None,
+                    eps=1e-6):
+    """Unrolled sum over s <= t with gamma products formed per pair.
+
+    log gamma_j = log(sigmoid(z_j)) / tau = -logaddexp(0, -z_j) / tau, and the
+    decay between key s and query t is exp(sum_{j=s+1..t} log gamma_j).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    B, L, NH, dk = q.shape
+    dv = v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    out = np.empty((B, L, NH, dv))
+    for b in range(B):
+        for h in range(NH):
+            Qs = to_scan_order(q[b, :, h, :], direction, H, W)
+            Ks = to_scan_order(k[b, :, h, :], direction, H, W)
+            Vs = to_scan_order(v[b, :, h, :], direction, H, W)
+            lg = -np.logaddexp(0.0, -to_scan_order(z[b, :, h, :], direction, H, W)) / tau
+            Os = np.zeros((L, dv))
+            for t in range(L):
+                for s in range(t + 1):
+                    decay = np.exp(lg[s + 1:t + 1].sum(axis=0)) if t > s else np.ones(dk)
+                    Os[t] += np.dot(Qs[t] * decay, Ks[s]) * Vs[s]
+            Os *= scale
+            if r is not None:
+                Rs = to_scan_order(np.asarray(r, dtype=np.float64)[b, :, h, :], direction, H, W)
+                wv = np.ones(dv) if w is None else np.asarray(w, dtype=np.float64)
+                rms = np.sqrt((Os * Os).mean(axis=1, keepdims=True) + eps)
+                Os = (Rs / (1.0 + np.exp(-Rs))) * wv * Os / rms
+            out[b, :, h, :] = from_scan_order(Os, direction, H, W)
+    return out

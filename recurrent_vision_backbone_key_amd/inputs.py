@@ -1,0 +1,74 @@
+"""Seeded synthetic inputs and the workload table.
+
+This module holds no arithmetic of the method: it only draws random arrays
+with the shapes and distributions of the workloads and casts them to the
+storage dtype.  Both the oracle side and the HIP side of every parity test
+consume exactly the arrays produced here.
+
+Workloads (shapes follow the GTR pages: a 640 px frame at stride 16 is a
+40x40 patch grid of 1.6K tokens, 1280 px is 80x80, and the long-sequence
+kernel point is 16.4K tokens; head dim 64 and 6 heads as in the GTR-L/X
+backbone table).  No dataset or trained weight is involved.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+L2R, R2L, T2B, B2T = 0, 1, 2, 3
+
+# name -> spec.  z = (mean, std) of the gate logits.  dirs: the direction of
+# each call in order.  gated: whether the fused output gate (r, w) is used.
+WORKLOADS = {
+    "tiny": dict(index=1, B=1, NH=1, H=8, W=8, dk=16, dv=16, dtype="f32", z=(0.0, 1.0),
+                 chunk=16, dirs=(L2R,), gated=False),
+    "frame640": dict(index=2, B=1, NH=6, H=40, W=40, dk=64, dv=64, dtype="f16", z=(0.0, 1.0),
+                     chunk=64, dirs=(L2R, R2L, T2B, B2T), gated=False),
+    "batch640_gated": dict(index=3, B=8, NH=6, H=40, W=40, dk=64, dv=64, dtype="f16",
+                           z=(0.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T), gated=True),
+    "frame1280_gated": dict(index=4, B=1, NH=12, H=80, W=80, dk=64, dv=64, dtype="f16",
+                            z=(0.0, 1.5), chunk=64, dirs=(L2R, R2L, T2B, B2T), gated=True),
+    "stack16k_gated": dict(index=5, B=2, NH=12, H=128, W=128, dk=128, dv=128, dtype="f16",
+                           z=(2.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T) * 3, gated=True),
+}
+
+EPS = 1e-6
+TAU = 16.0
+
+
+def np_dtype(name: str):
+    return {"f16": np.float16, "f32": np.float32}[name]
+
+
+def tokens_per_call(spec) -> int:
+    return spec["B"] * spec["NH"] * spec["H"] * spec["W"]
+
+
+def make_inputs(B, NH, H, W, dk, dv, dtype="f16", z=(0.0, 1.0), gated=False, seed=0,
+                q_std=1.0):
+    """Draw q, k, v, z, r, w in that fixed order from PCG64(seed).
+
+    q, k, v, r ~ N(0, 1) drawn in float64 and rounded to ``dtype`` (numpy's
+    cast rounds to nearest even); z ~ N(z_mean, z_std) kept in float32;
+    w ~ U(0.5, 1.5) float32.  r and w are None unless ``gated``.
+    """
+    rng = np.random.default_rng(seed)
+    L = H * W
+    dt = np_dtype(dtype)
+    q = (rng.standard_normal((B, L, NH, dk)) * q_std).astype(dt)
+    k = rng.standard_normal((B, L, NH, dk)).astype(dt)
+    v = rng.standard_normal((B, L, NH, dv)).astype(dt)
+    zz = (z[0] + z[1] * rng.standard_normal((B, L, NH, dk))).astype(np.float32)
+    r = w = None
+    if gated:
+        r = rng.standard_normal((B, L, NH, dv)).astype(dt)
+        w = rng.uniform(0.5, 1.5, size=(dv,)).astype(np.float32)
+    return dict(q=q, k=k, v=v, z=zz, r=r, w=w)
+
+
+def workload_inputs(name: str, call: int = 0, **overrides):
+    """Inputs of call ``call`` of a named workload; seed = 1000*index + call."""
+    spec = dict(WORKLOADS[name])
+    spec.update(overrides)
+    return make_inputs(spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"], spec["dv"],
+                       spec["dtype"], spec["z"], spec["gated"],
+                       seed=1000 * spec["index"] + call)
