@@ -1,0 +1,126 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) chunkwise forward of key-only gated
+ * linear attention (GLA), the token mixer of GTR ("GTR: Gated Token
+ * Recurrence for Efficient Dense Prediction", paper Section 2.1).
+ *
+ * Operation (paper Section 2.1, key-only GLA paragraph and output-gate
+ * paragraph).  For every batch b and head h, along the scan order of the
+ * H x W patch grid:
+ *     gamma_t = sigmoid(z_t)^(1/tau)            elementwise, 1 x d_k
+ *     S_t     = Diag(gamma_t) S_{t-1} + k_t^T v_t,   S_0 = 0   (d_k x d_v)
+ *     o_t     = scale * q_t S_t                 (scale = d_k^-1/2 by default)
+ * and, when the output gate is requested (r != NULL),
+ *     u_t     = SiLU(r_t) (.) w (.) o_t / sqrt(mean_{d_v}(o_t^2) + eps).
+ * The value-side decay is fixed to one (no right-hand diagonal on S).
+ *
+ * Scan directions (paper Section 2.1, scan-direction paragraph; Figure 2 is
+ * not available, so the orders below are this library's reading): token
+ * index t = h*W + w on the row-major grid;
+ *     GLA_L2R: raster order t = i;   GLA_R2L: raster order reversed;
+ *     GLA_T2B: column-major order;   GLA_B2T: column-major order reversed.
+ * One continuous scan covers all L = H*W tokens.  The output is always
+ * written at each token's original grid position, so no caller-side
+ * reordering is needed for any direction.
+ *
+ * Layout: q, k, gate_logits: [B, L, NH, d_k]; v, r, out: [B, L, NH, d_v];
+ * all dense row-major, L = H*W.  q, k, v, r, out share one storage type
+ * (opts->dtype); gate_logits and norm_weight are binary32.
+ *
+ * Memory and ownership: every tensor pointer is a DEVICE pointer owned by the
+ * caller and must be 16-byte aligned.  The library allocates nothing and
+ * keeps no mutable global state.  Calls run asynchronously on opts->stream.
+ *
+ * Errors: every function returns a gla_status.  Argument checks run before
+ * anything is launched; on any error nothing is launched and out is not
+ * touched.  A launch failure is reported as GLA_EHIP.  Faults inside a kernel
+ * surface at the caller's next synchronisation.  Non-finite inputs propagate
+ * (a NaN gate logit yields NaN outputs downstream of it).
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GLA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define GLA_API __attribute__((visibility("default")))
+#else
+#define GLA_API
+#endif
+
+enum gla_dir { GLA_L2R = 0, GLA_R2L = 1, GLA_T2B = 2, GLA_B2T = 3 };
+enum gla_dtype { GLA_F16 = 0, GLA_F32 = 1 };
+enum gla_status {
+    GLA_OK = 0,
+    GLA_EINVAL = 1,       /* null or misaligned pointer, bad size or direction,
+                             out overlapping an input                          */
+    GLA_EUNSUPPORTED = 2, /* d_k, d_v, chunk, dtype or size outside the built set */
+    GLA_EWORKSPACE = 3,   /* workspace missing or smaller than gla_workspace_size */
+    GLA_EHIP = 4          /* the HIP runtime reported an error at launch         */
+};
+
+typedef struct gla_opts {
+    int32_t batch;   /* B  >= 1 */
+    int32_t heads;   /* NH >= 1 */
+    int32_t dk;      /* key/query head dim; supported: 16, 32, 64, 128        */
+    int32_t dv;      /* value head dim; this build requires dv == dk           */
+    int32_t dtype;   /* GLA_F16 or GLA_F32: storage of q, k, v, r and out      */
+    float tau;       /* gate temperature; <= 0 selects 16 (paper Sec. 2.1)     */
+    float scale;     /* output scale; <= 0 selects dk^-1/2 (paper Sec. 2.1)    */
+    float eps;       /* RMSNorm epsilon, inside the square root; used iff r    */
+    const float *norm_weight; /* [dv] device pointer, shared by all heads;
+                                 NULL selects ones; used iff r                  */
+    void *workspace;          /* device scratch, see gla_workspace_size         */
+    size_t workspace_bytes;
+    void *stream;             /* hipStream_t; NULL selects the null stream      */
+    int32_t segment_chunks;   /* chunks per sequence segment; 0 lets the library
+                                 choose; a value >= the chunk count runs one
+                                 workgroup per (batch, head)                    */
+} gla_opts;
+
+/*
+ * gla_fwd -- chunkwise forward (paper Section 2.1, definition above).
+ *   q, k         [B, L, NH, dk] queries and keys (opts->dtype)
+ *   v            [B, L, NH, dv] values (opts->dtype)
+ *   gate_logits  [B, L, NH, dk] binary32 pre-sigmoid gate logits z
+ *   dir          GLA_L2R | GLA_R2L | GLA_T2B | GLA_B2T
+ *   H, W         patch grid, H >= 1, W >= 1, H*W < 2^24
+ *   chunk        tokens per chunk: 16, 32, 64 or 128; the result does not
+ *                depend on it beyond rounding.  Combinations whose workgroup
+ *                shared memory exceeds a gfx950 CU's 160 KiB return
+ *                GLA_EUNSUPPORTED (binary16: d = 128 with chunk 128;
+ *                binary32: d = 64 with chunk 128, d = 128 with chunk >= 32)
+ *   out          [B, L, NH, dv] output (opts->dtype); must not overlap inputs
+ *   r            [B, L, NH, dv] output-gate pre-activation x W_r, or NULL for
+ *                out = o (no gate, no RMSNorm)
+ *   opts         sizes, dtype, stream, workspace (must not be NULL)
+ * The workspace must hold gla_workspace_size() bytes when that is nonzero
+ * (scans split into segments: one fp32 d_k x d_v state plus d_k decays per
+ * segment boundary).  It needs no initialisation and every call overwrites
+ * it; calls that share a workspace must be ordered on one stream.
+ */
+GLA_API int gla_fwd(const void *q, const void *k, const void *v, const float *gate_logits,
+            int dir, int H, int W, int chunk, void *out, const void *r,
+            const gla_opts *opts);
+
+/* Bytes of workspace gla_fwd needs for these arguments (0: none needed).
+ * Returns 0 as well for arguments gla_fwd would reject. */
+GLA_API size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla_opts *opts);
+
+/* Static, NUL-terminated description of a gla_status value. */
+GLA_API const char *gla_status_str(int status);
+
+/* GLA_ABI_VERSION of the loaded library. */
+GLA_API int gla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

@@ -1,0 +1,58 @@
+// gla_api.cpp -- the C ABI (include/gla.h) over the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include "gla.h"
+#include "gla_launch.h"
+#include "gla_plan.h"
+
+extern "C" int gla_fwd(const void* q, const void* k, const void* v, const float* gate_logits,
+                       int dir, int H, int W, int chunk, void* out, const void* r,
+                       const gla_opts* opts)
+{
+    gla_plan plan;
+    const int st = gla_validate(q, k, v, gate_logits, dir, H, W, chunk, out, r, opts, &plan);
+    if (st != GLA_OK) return st;
+    gla::Params P;
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.z = gate_logits;
+    P.r = r;
+    P.w = r ? opts->norm_weight : nullptr;
+    P.out = out;
+    P.ws = (float*)opts->workspace;
+    P.B = opts->batch;
+    P.NH = opts->heads;
+    P.H = H;
+    P.W = W;
+    P.L = plan.L;
+    P.dir = dir;
+    P.nchunks = plan.nchunks;
+    P.seg_chunks = plan.seg_chunks;
+    P.nseg = plan.nseg;
+    P.scale = plan.scale;
+    P.inv_tau = 1.0f / plan.tau;
+    P.eps = plan.eps;
+    return gla::launch_fwd(P, opts->dtype, opts->dk, chunk, opts->stream);
+}
+
+extern "C" size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla_opts* opts)
+{
+    gla_plan plan;
+    if (gla_make_plan(dir, H, W, chunk, opts, 0, &plan) != GLA_OK) return 0;
+    return plan.workspace_bytes;
+}
+
+extern "C" const char* gla_status_str(int status)
+{
+    switch (status) {
+    case GLA_OK: return "GLA_OK: success";
+    case GLA_EINVAL: return "GLA_EINVAL: invalid argument (null or misaligned pointer, bad size or direction, or overlapping output)";
+    case GLA_EUNSUPPORTED: return "GLA_EUNSUPPORTED: head dim, chunk, dtype or size outside the built set";
+    case GLA_EWORKSPACE: return "GLA_EWORKSPACE: workspace missing, misaligned or smaller than gla_workspace_size()";
+    case GLA_EHIP: return "GLA_EHIP: HIP runtime error at launch";
+    default: return "unknown gla status";
+    }
+}
+
+extern "C" int gla_abi_version(void) { return GLA_ABI_VERSION; }

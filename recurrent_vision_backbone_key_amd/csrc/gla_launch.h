@@ -1,0 +1,34 @@
+// gla_launch.h -- internal interface between the C-ABI layer and the kernels.
+#ifndef GLA_LAUNCH_H
+#define GLA_LAUNCH_H
+
+#include <stddef.h>
+
+namespace gla {
+
+// Arguments of one forward call, already validated.
+struct Params {
+    const void* q;      // [B, L, NH, DK]
+    const void* k;      // [B, L, NH, DK]
+    const void* v;      // [B, L, NH, DV]
+    const float* z;     // [B, L, NH, DK] gate logits
+    const void* r;      // [B, L, NH, DV] output-gate pre-activation, or null
+    const float* w;     // [DV] RMSNorm weight, or null (ones)
+    void* out;          // [B, L, NH, DV]
+    float* ws;          // segment slots: [units][nseg-1][DK*DV + DK] fp32
+    int B, NH, H, W, L, dir;
+    int nchunks;        // ceil(L / chunk)
+    int seg_chunks;     // chunks per segment
+    int nseg;           // segments per scan
+    float scale;        // output scale
+    float inv_tau;      // 1 / tau
+    float eps;          // RMSNorm epsilon
+};
+
+// Launches the aggregate, fold and output passes (or only the output pass
+// when nseg == 1) on `stream`.  Returns a gla_status value.
+int launch_fwd(const Params& P, int dtype, int d, int chunk, void* stream);
+
+}  // namespace gla
+
+#endif

@@ -1,0 +1,104 @@
+// gla_plan.cpp -- argument validation and work planning for gla_fwd.
+// Compiled without HIP so that every error path can be exercised on a host
+// without a GPU.
+#include "gla_plan.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "gla_geometry.h"
+
+namespace {
+
+constexpr int kCUs = 256;          // compute units of one MI355X
+constexpr int kTargetGroups = 2 * kCUs;
+
+bool is_pow2_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+extern "C" int gla_config_built(int dtype, int d, int chunk)
+{
+    if (dtype != GLA_F16 && dtype != GLA_F32) return 0;
+    if (!is_pow2_dim(d) || !is_pow2_dim(chunk)) return 0;
+    return gla::config_fits(dtype == GLA_F16 ? 2 : 4, d, chunk) ? 1 : 0;
+}
+
+extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o,
+                             int has_gate, gla_plan* plan)
+{
+    if (!o || !plan) return GLA_EINVAL;
+    if (o->batch < 1 || o->heads < 1 || H < 1 || W < 1) return GLA_EINVAL;
+    if (dir < GLA_L2R || dir > GLA_B2T) return GLA_EINVAL;
+    if (o->dtype != GLA_F16 && o->dtype != GLA_F32) return GLA_EUNSUPPORTED;
+    if (!is_pow2_dim(o->dk) || !is_pow2_dim(o->dv) || o->dk != o->dv) return GLA_EUNSUPPORTED;
+    if (!is_pow2_dim(chunk) || !gla_config_built(o->dtype, o->dk, chunk)) return GLA_EUNSUPPORTED;
+    const int64_t L = (int64_t)H * W;
+    if (L >= (int64_t)1 << 24) return GLA_EUNSUPPORTED;
+    const int64_t rows = (int64_t)o->batch * L * o->heads;  // kernel row index is int32
+    if (rows >= (int64_t)1 << 31) return GLA_EUNSUPPORTED;
+    if (isnan(o->tau) || isnan(o->scale) || isinf(o->tau) || isinf(o->scale)) return GLA_EINVAL;
+    if (has_gate && (isnan(o->eps) || o->eps < 0.0f || isinf(o->eps))) return GLA_EINVAL;
+
+    // Work plan: segments of seg_chunks chunks, enough workgroups for the chip.
+    const int nchunks = (int)((L + chunk - 1) / chunk);
+    const int64_t units = (int64_t)o->batch * o->heads;
+    int seg = o->segment_chunks;
+    if (seg <= 0) {
+        const int64_t want = (units * nchunks + kTargetGroups - 1) / kTargetGroups;
+        seg = (int)(want < 1 ? 1 : want);
+    }
+    if (seg > nchunks) seg = nchunks;
+    const int nseg = (nchunks + seg - 1) / seg;
+    plan->L = (int)L;
+    plan->nchunks = nchunks;
+    plan->seg_chunks = seg;
+    plan->nseg = nseg;
+    plan->workspace_bytes =
+        nseg > 1 ? (size_t)units * (nseg - 1) * ((size_t)o->dk * o->dv + o->dk) * 4 : 0;
+    plan->tau = o->tau > 0.0f ? o->tau : 16.0f;
+    plan->scale = o->scale > 0.0f ? o->scale : (float)(1.0 / sqrt((double)o->dk));
+    plan->eps = o->eps;
+    return GLA_OK;
+}
+
+extern "C" int gla_validate(const void* q, const void* k, const void* v, const float* z,
+                            int dir, int H, int W, int chunk, const void* out, const void* r,
+                            const gla_opts* o, gla_plan* plan)
+{
+    if (!o || !plan) return GLA_EINVAL;
+    if (!q || !k || !v || !z || !out) return GLA_EINVAL;
+    const int st = gla_make_plan(dir, H, W, chunk, o, r != nullptr, plan);
+    if (st != GLA_OK) return st;
+
+    const size_t es = o->dtype == GLA_F16 ? 2 : 4;
+    const size_t rows = (size_t)o->batch * plan->L * o->heads;
+    const size_t nk = rows * o->dk, nv = rows * o->dv;
+    const void* ins[6] = {q, k, v, z, r, r ? o->norm_weight : nullptr};
+    const size_t insz[6] = {nk * es, nk * es, nv * es, nk * 4, nv * es, (size_t)o->dv * 4};
+    for (int i = 0; i < 5; ++i)
+        if (ins[i] && !aligned(ins[i], 16)) return GLA_EINVAL;
+    if (!aligned(out, 16)) return GLA_EINVAL;
+    if (ins[5] && !aligned(ins[5], 4)) return GLA_EINVAL;
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(out, nv * es, ins[i], insz[i])) return GLA_EINVAL;
+
+    if (plan->workspace_bytes) {
+        if (!o->workspace || o->workspace_bytes < plan->workspace_bytes ||
+            !aligned(o->workspace, 16))
+            return GLA_EWORKSPACE;
+        if (overlaps(o->workspace, plan->workspace_bytes, out, nv * es)) return GLA_EINVAL;
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(o->workspace, plan->workspace_bytes, ins[i], insz[i])) return GLA_EINVAL;
+    }
+    return GLA_OK;
+}

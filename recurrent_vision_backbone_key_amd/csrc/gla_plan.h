@@ -1,0 +1,36 @@
+// gla_plan.h -- argument validation and work planning (no HIP dependency).
+#ifndef GLA_PLAN_H
+#define GLA_PLAN_H
+
+#include <stddef.h>
+#include "gla.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gla_plan {
+    int L, nchunks, seg_chunks, nseg;
+    size_t workspace_bytes;
+    float tau, scale, eps;
+} gla_plan;
+
+// Size-only checks and the work plan (segments, workspace bytes).
+int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* opts, int has_gate,
+                  gla_plan* plan);
+
+// Pure host check of every argument of gla_fwd (pointers are compared, never
+// dereferenced).  Fills *plan on success.  Returns a gla_status.
+int gla_validate(const void* q, const void* k, const void* v, const float* gate_logits,
+                 int dir, int H, int W, int chunk, const void* out, const void* r,
+                 const gla_opts* opts, gla_plan* plan);
+
+// Whether a (dtype, head dim, chunk) instantiation is built (shared-memory
+// footprint of one workgroup within the 160 KiB of a gfx950 CU).
+int gla_config_built(int dtype, int d, int chunk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
