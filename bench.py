@@ -1,0 +1,243 @@
+"""Throughput of the chunkwise key-only GLA forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch: every call of the
+workload (for the 640 px frame: one call per scan direction L2R, R2L, T2B,
+B2T), each call doing gate stage, intra/inter-chunk products, state carry,
+direction remap and epilogue.  Inputs are resident in HBM before the timed
+region; enough distinct input sets rotate through the steps that the 256 MB
+last-level cache cannot serve them.  Steps are replayed from HIP graphs and
+timed with HIP events on the stream they run on.
+
+Prints one JSON line (metric, value in Gtok*head/s, roofline of the forward
+call, CPU-oracle baseline on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunkwise GLA fwd: µs/call + Gtok·head/s at L=1600; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20     # last-level (Infinity) cache
+
+
+def algorithmic_bytes_per_token_head(dk, dv, es, gated):
+    """Compulsory HBM traffic: q, k, v, z (fp32) read, out written, r read if gated."""
+    return es * (2 * dk + dv) + 4 * dk + es * dv + (es * dv if gated else 0)
+
+
+def algorithmic_flops_per_token_head(dk, dv, chunk):
+    """Chunkwise causal form: intra-chunk scores and values (dk+dv)(C+1), inter
+    output and state update 4 dk dv (multiply-add = 2 flops)."""
+    return (dk + dv) * (chunk + 1) + 4 * dk * dv
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recurrent_vision_backbone_key_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, calls_per_step):
+    """HBM bytes per call from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(spec, name, seconds):
+    import numpy as np  # noqa: F401
+
+    import oracle
+    from recurrent_vision_backbone_key_amd.inputs import workload_inputs
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    H, W = spec["H"], spec["W"]
+    units_total = spec["B"] * spec["NH"]
+    # bounded sample: whole (batch, head) scans of the workload's calls, in call
+    # order, until the time budget is spent (inputs drawn before the clock starts)
+    per_call_units = min(units_total, max(cores, 1))
+    inputs = [workload_inputs(name, call=c) for c in range(len(spec["dirs"]))]
+    done_th = 0
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        call = calls % len(spec["dirs"])
+        x = inputs[call]
+        u0 = (calls * per_call_units) % units_total
+        u1 = min(units_total, u0 + per_call_units)
+        oracle.fwd(x["q"], x["k"], x["v"], x["z"], spec["dirs"][call], H, W, r=x["r"],
+                   w=x["w"], units=(u0, u1), threads=cores)
+        done_th += (u1 - u0) * H * W
+        calls += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_th / dt / 1e9, "unit": "Gtok·head/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{calls} oracle calls of {name} ({spec['H']}x{spec['W']}, d={spec['dk']}), "
+                      f"{per_call_units} of {units_total} (batch, head) scans each, "
+                      f"{done_th} token-heads in {dt:.1f} s"}
+
+
+def main():
+    from recurrent_vision_backbone_key_amd.inputs import WORKLOADS
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="frame640", choices=sorted(WORKLOADS))
+    ap.add_argument("--segment-chunks", type=int, default=0)
+    ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--rotate", type=int, default=0, help="input sets (0: enough to exceed 2x MALL)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards across GPUs by batch/head with no communication; "
+              "see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from recurrent_vision_backbone_key_amd import gla
+    from recurrent_vision_backbone_key_amd.inputs import make_inputs_device, tokens_per_call
+
+    spec = WORKLOADS[args.workload]
+    name = args.workload
+    chunk = args.chunk or spec["chunk"]
+    dirs = spec["dirs"]
+    calls_per_step = len(dirs)
+    B, NH, H, W, dk, dv = spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"], spec["dv"]
+    es = 2 if spec["dtype"] == "f16" else 4
+    gated = spec["gated"]
+    th_call = tokens_per_call(spec)
+    bytes_call = th_call * algorithmic_bytes_per_token_head(dk, dv, es, gated) + (4 * dv if gated else 0)
+    flops_call = th_call * algorithmic_flops_per_token_head(dk, dv, chunk)
+    step_bytes = bytes_call * calls_per_step
+    rotate = args.rotate or max(1, math.ceil(2 * MALL_BYTES / step_bytes))
+    big = step_bytes > (1 << 30)
+    steps = args.steps if args.steps is not None else (12 if big else 400)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 100)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] {name}: {calls_per_step} calls/step, {bytes_call / 1e6:.2f} MB/call, "
+          f"{rotate} input sets, steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+
+    # resident inputs, outputs and workspaces
+    sets = []
+    for r in range(rotate):
+        calls = []
+        for c, d in enumerate(dirs):
+            x = make_inputs_device(B, NH, H, W, dk, dv, spec["dtype"], spec["z"], gated,
+                                   seed=1000 * spec["index"] + 100 * r + c, device=dev)
+            out = torch.empty((B, H * W, NH, dv), dtype=x["q"].dtype, device=dev)
+            opts = gla.make_opts(B, NH, dk, dv, gla.F16 if es == 2 else gla.F32,
+                                 segment_chunks=args.segment_chunks)
+            need = gla.workspace_size(d, H, W, chunk, opts)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            calls.append((x, d, out, ws))
+        sets.append(calls)
+    opts_probe = gla.make_opts(B, NH, dk, dv, 0, segment_chunks=args.segment_chunks)
+    nseg_bytes = gla.workspace_size(0, H, W, chunk, opts_probe)
+
+    def step(r):
+        for x, d, out, ws in sets[r]:
+            gla.fwd(x["q"], x["k"], x["v"], x["z"], d, H, W, chunk=chunk, r=x["r"],
+                    norm_weight=x["w"], eps=1e-6, out=out, segment_chunks=args.segment_chunks,
+                    workspace=ws)
+
+    stream = torch.cuda.current_stream()
+    graphs = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for r in range(rotate):
+                step(r)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % rotate].replay()
+        else:
+            step(i % rotate)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(steps):
+        run(warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / steps
+    us_call = 1e3 * ms_step / calls_per_step
+    value = calls_per_step * th_call / (ms_step * 1e-3) / 1e9
+
+    achieved = bytes_call / (us_call * 1e-6) / 1e9
+    traffic = load_traffic(name, calls_per_step)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "gla_fwd call (aggregate + fold + output passes; output pass "
+                          "only when the scan is one segment)",
+                "algorithmic_bytes_per_call": bytes_call,
+                "mfma_frac": round(flops_call / (us_call * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 5)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 4), "unit": "Gtok·head/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
+        "us_per_call": round(us_call, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
+        "config": {"workload": name, "B": B, "heads": NH, "grid": f"{H}x{W}", "L": H * W,
+                   "dk": dk, "dv": dv, "chunk": chunk,
+                   "dirs": ",".join("L2R R2L T2B B2T".split()[d] for d in dirs),
+                   "gated": gated, "calls_per_step": calls_per_step,
+                   "input_sets": rotate, "hip_graph": graphs is not None,
+                   "workspace_bytes_per_call": nseg_bytes, "accumulate": "f32"},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(spec, name, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

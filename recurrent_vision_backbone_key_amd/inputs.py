@@ -72,3 +72,30 @@ def workload_inputs(name: str, call: int = 0, **overrides):
     return make_inputs(spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"], spec["dv"],
                        spec["dtype"], spec["z"], spec["gated"],
                        seed=1000 * spec["index"] + call)
+
+
+def make_inputs_device(B, NH, H, W, dk, dv, dtype="f16", z=(0.0, 1.0), gated=False, seed=0,
+                       device="cuda"):
+    """Same distributions as :func:`make_inputs`, drawn on the device with a
+    seeded torch generator (for large timing inputs; parity tests use the
+    numpy generator)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    L = H * W
+    dt = {"f16": torch.float16, "f32": torch.float32}[dtype]
+
+    def normal(shape, mean=0.0, std=1.0):
+        return (torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std
+                + mean)
+
+    q = normal((B, L, NH, dk)).to(dt)
+    k = normal((B, L, NH, dk)).to(dt)
+    v = normal((B, L, NH, dv)).to(dt)
+    zz = normal((B, L, NH, dk), z[0], z[1])
+    r = w = None
+    if gated:
+        r = normal((B, L, NH, dv)).to(dt)
+        w = torch.rand((dv,), generator=gen, device=device, dtype=torch.float32) + 0.5
+    return dict(q=q, k=k, v=v, z=zz, r=r, w=w)
