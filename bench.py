@@ -158,7 +158,7 @@ def main():
             opts = gla.make_opts(B, NH, dk, dv, gla.F16 if es == 2 else gla.F32,
                                  segment_chunks=args.segment_chunks)
             need = gla.workspace_size(d, H, W, chunk, opts)
-            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
             calls.append((x, d, out, ws))
         sets.append(calls)
     opts_probe = gla.make_opts(B, NH, dk, dv, 0, segment_chunks=args.segment_chunks)

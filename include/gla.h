@@ -82,7 +82,16 @@ typedef struct gla_opts {
     int32_t segment_chunks;   /* chunks per sequence segment; 0 lets the library
                                  choose; a value >= the chunk count runs one
                                  workgroup per (batch, head)                    */
+    int32_t algorithm;        /* GLA_ALGO_AUTO, GLA_ALGO_SINGLE_PASS or
+                                 GLA_ALGO_THREE_PASS (see below)                 */
 } gla_opts;
+
+/* Algorithms.  SINGLE_PASS (binary16, d_k = d_v = 64, chunk 64, segments of
+ * at most 6 chunks, at most 65 segments per scan) reads every input once: one
+ * workgroup per segment, segments exchange states through the workspace.
+ * THREE_PASS (every built configuration) runs an aggregate pass, a fold pass
+ * and an output pass.  AUTO picks SINGLE_PASS whenever it applies. */
+enum gla_algorithm { GLA_ALGO_AUTO = 0, GLA_ALGO_SINGLE_PASS = 1, GLA_ALGO_THREE_PASS = 2 };
 
 /*
  * gla_fwd -- chunkwise forward (paper Section 2.1, definition above).
@@ -100,10 +109,12 @@ typedef struct gla_opts {
  *   r            [B, L, NH, dv] output-gate pre-activation x W_r, or NULL for
  *                out = o (no gate, no RMSNorm)
  *   opts         sizes, dtype, stream, workspace (must not be NULL)
- * The workspace must hold gla_workspace_size() bytes when that is nonzero
- * (scans split into segments: one fp32 d_k x d_v state plus d_k decays per
- * segment boundary).  It needs no initialisation and every call overwrites
- * it; calls that share a workspace must be ordered on one stream.
+ * The workspace must hold gla_workspace_size() bytes when that is nonzero.
+ * It holds per-segment fp32 states and, for the single pass, a ticket
+ * counter, per-scan counters and per-segment flags.  Before its first use
+ * (and after any call that did not complete) it must be cleared with
+ * gla_workspace_init(); every completed call leaves the counters and flags
+ * cleared again.  Calls that share a workspace must be ordered on one stream.
  */
 GLA_API int gla_fwd(const void *q, const void *k, const void *v, const float *gate_logits,
             int dir, int H, int W, int chunk, void *out, const void *r,
@@ -112,6 +123,15 @@ GLA_API int gla_fwd(const void *q, const void *k, const void *v, const float *ga
 /* Bytes of workspace gla_fwd needs for these arguments (0: none needed).
  * Returns 0 as well for arguments gla_fwd would reject. */
 GLA_API size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla_opts *opts);
+
+/*
+ * gla_workspace_init -- clears `bytes` bytes of a workspace (counters, flags)
+ * on `stream` (hipStream_t, NULL selects the null stream) with a fill kernel.
+ * Call once after allocating a workspace for gla_fwd.  workspace: device
+ * pointer, 16-byte aligned; bytes: a multiple of 4 (0 does nothing).
+ * GLA_EINVAL on a bad pointer or size, GLA_EHIP on a launch failure.
+ */
+GLA_API int gla_workspace_init(void *workspace, size_t bytes, void *stream);
 
 /* Static, NUL-terminated description of a gla_status value. */
 GLA_API const char *gla_status_str(int status);

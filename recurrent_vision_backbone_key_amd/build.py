@@ -36,6 +36,7 @@ UNITS = [
     ("gla_plan.cpp", "host", []),
     ("gla_api.cpp", "hip", []),
     ("gla_kernel.hip", "hip", []),
+    ("gla_onepass.hip", "hip", []),
 ]
 
 

@@ -1,5 +1,6 @@
 // gla_api.cpp -- the C ABI (include/gla.h) over the HIP kernels.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 #include "gla.h"
 #include "gla_launch.h"
@@ -33,6 +34,18 @@ extern "C" int gla_fwd(const void* q, const void* k, const void* v, const float*
     P.scale = plan.scale;
     P.inv_tau = 1.0f / plan.tau;
     P.eps = plan.eps;
+    P.ticket = P.err = P.done = P.flags = nullptr;
+    P.agg = P.incl = nullptr;
+    if (plan.onepass) {
+        char* ws = (char*)opts->workspace;
+        P.ticket = (unsigned*)ws;
+        P.err = (unsigned*)ws + 1;
+        P.done = (unsigned*)(ws + plan.off_done);
+        P.flags = (unsigned*)(ws + plan.off_flags);
+        P.agg = (float*)(ws + plan.off_agg);
+        P.incl = (float*)(ws + plan.off_incl);
+        return gla::launch_onepass(P, opts->stream);
+    }
     return gla::launch_fwd(P, opts->dtype, opts->dk, chunk, opts->stream);
 }
 
@@ -41,6 +54,13 @@ extern "C" size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla
     gla_plan plan;
     if (gla_make_plan(dir, H, W, chunk, opts, 0, &plan) != GLA_OK) return 0;
     return plan.workspace_bytes;
+}
+
+extern "C" int gla_workspace_init(void* workspace, size_t bytes, void* stream)
+{
+    if (bytes == 0) return GLA_OK;
+    if (!workspace || ((uintptr_t)workspace & 15u) != 0 || (bytes & 3u) != 0) return GLA_EINVAL;
+    return gla::launch_workspace_init(workspace, bytes, stream);
 }
 
 extern "C" const char* gla_status_str(int status)

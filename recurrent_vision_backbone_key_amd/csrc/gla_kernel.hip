@@ -38,89 +38,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "gla.h"
 #include "gla_geometry.h"
+#include "gla_device.h"
 #include "gla_launch.h"
 
 namespace gla {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kSub = 16;            // tokens per sub-chunk (MFMA tile edge)
-constexpr float kLog2e = 1.4426950408889634f;
-// Per-token log-decay floor, natural-log units (gamma >= e^-40 per token).
-constexpr float kMinLog2Decay = -40.0f * kLog2e;
-
-// Operand-format traits: the widest safe decay span (log2 units) of the
-// factorised diagonal block and the largest operand magnitude allowed there.
-template <typename T> struct Fmt;
-template <> struct Fmt<_Float16> {
-    static constexpr float kSpan = 8.0f;          // key factor <= 2^8
-    static constexpr float kMaxOperand = 30000.0f;
-};
-template <> struct Fmt<float> {
-    static constexpr float kSpan = 60.0f;
-    static constexpr float kMaxOperand = 1e30f;
-};
-
-// MFMA shape for a contraction of length K: K-step, elements per lane per
-// K-step (lane group g = lane/16 holds k = KPL*g .. KPL*g+KPL-1), fragment type.
-//   binary16, K >= 32: v_mfma_f32_16x16x32_f16  (KSTEP 32, KPL 8)
-//   binary16, K == 16: v_mfma_f32_16x16x16_f16  (KSTEP 16, KPL 4)
-//   binary32:          v_mfma_f32_16x16x4_f32   (KSTEP 4,  KPL 1)
-template <typename T, int K> struct KS;
-template <int K> struct KS<_Float16, K> {
-    static constexpr int KSTEP = K >= 32 ? 32 : 16, KPL = KSTEP / 4;
-    typedef typename std::conditional<KPL == 8, half8, half4>::type frag;
-};
-template <int K> struct KS<float, K> {
-    static constexpr int KSTEP = 4, KPL = 1;
-    typedef float frag;
-};
-
-__device__ __forceinline__ float4v mma(half8 a, half8 b, float4v c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4v mma(half4 a, half4 b, float4v c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4v mma(float a, float b, float4v c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// log2(sigmoid(z)) from the softplus identity
-//   log sigmoid(z) = min(z,0) - log(1 + e^{-|z|}),
-// with log(1+e) evaluated as log(u) * e / (u - 1), u = fl(1 + e) (Goldberg's
-// accurate log1p), so small e keeps full relative accuracy.  NaN propagates.
-__device__ __forceinline__ float log2_sigmoid(float z)
-{
-    const float m = (z < 0.0f) ? z * kLog2e : 0.0f;
-    const float e = exp2_fast(-fabsf(z) * kLog2e);
-    const float u = 1.0f + e;
-    const float l1p = (u == 1.0f) ? e * kLog2e : __log2f(u) * (e / (u - 1.0f));
-    return m - l1p;
-}
-
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + exp2_fast(-x * kLog2e)); }
-
-template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
-
-// x rounded to binary16 and back: the high part of a hi + lo split.
-__device__ __forceinline__ float lo_part_base(float x) { return (float)(_Float16)x; }
-// The binary16 low part x - fl16(x) of a hi + lo split.
-__device__ __forceinline__ _Float16 lo_part(float x) { return (_Float16)(x - (float)(_Float16)x); }
 
 // ---------------------------------------------------------------------------
 // Compile-time geometry of one instantiation.
@@ -159,118 +85,6 @@ struct Geo {
     static constexpr int MT = DV / 16;  // output column tiles
     static_assert(C % kSub == 0, "chunk must be a multiple of 16");
     static_assert(LDS_BYTES == lds_bytes(TS, DK, DV, C), "LDS layout and host footprint disagree");
-};
-
-// Coalesced 16-byte-per-thread row loader for a [ROWS][ROWBYTES] tile whose
-// rows sit at scattered global row indices (the scan-order remap).
-template <int ROWS, int ROWBYTES>
-struct RowTile {
-    static constexpr int PIECES = ROWBYTES / 16;
-    static constexpr int PASSES = (ROWS * PIECES + kThreads - 1) / kThreads;
-    u32x4 reg[PASSES];
-
-    __device__ __forceinline__ void load(const char* base, const int* tok, int tid)
-    {
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int idx = tid + p * kThreads;
-            const int row = idx / PIECES, piece = idx % PIECES;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (row < ROWS) {
-                const int t = tok[row];
-                if (t >= 0)
-                    val = *(const u32x4*)(base + (size_t)t * ROWBYTES + piece * 16);
-            }
-            reg[p] = val;
-        }
-    }
-    // Row-major store into LDS with a padded row stride (bytes).
-    __device__ __forceinline__ void store_rows(char* lds, int stride, int tid) const
-    {
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int idx = tid + p * kThreads;
-            const int row = idx / PIECES, piece = idx % PIECES;
-            if (row < ROWS)
-                *(u32x4*)(lds + row * stride + piece * 16) = reg[p];
-        }
-    }
-    // Transposed store: element e of row `row` goes to ldsT[col][row].
-    template <typename T>
-    __device__ __forceinline__ void store_transposed(T* ldsT, int strideT, int tid) const
-    {
-        constexpr int EPP = 16 / sizeof(T);
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int idx = tid + p * kThreads;
-            const int row = idx / PIECES, piece = idx % PIECES;
-            if (row < ROWS) {
-                const T* vals = (const T*)&reg[p];
-#pragma unroll
-                for (int e = 0; e < EPP; ++e)
-                    ldsT[(piece * EPP + e) * strideT + row] = vals[e];
-            }
-        }
-    }
-};
-
-// Scan position -> global row index ((b*L + t)*NH + h), or -1 past the end.
-// The four orders of paper Sec. 2.1: raster (L2R), reversed raster (R2L),
-// column-major (T2B), reversed column-major (B2T); t = h_grid*W + w_grid.
-__device__ __forceinline__ int scan_row(const Params& P, int unit, int pos)
-{
-    if (pos >= P.L) return -1;
-    const int pp = (P.dir & 1) ? (P.L - 1 - pos) : pos;
-    int t = pp;
-    if (P.dir >= 2) {
-        const int wcol = pp / P.H;
-        const int hrow = pp - wcol * P.H;
-        t = hrow * P.W + wcol;
-    }
-    const int b = unit / P.NH, h = unit - (unit / P.NH) * P.NH;
-    return (b * P.L + t) * P.NH + h;
-}
-
-template <typename T, int N>
-__device__ __forceinline__ void ld_f(const T* p, float (&x)[N])
-{
-#pragma unroll
-    for (int i = 0; i < N; ++i) x[i] = to_f(p[i]);
-}
-
-template <int N>
-__device__ __forceinline__ void ld_f32(const float* p, float (&x)[N])
-{
-#pragma unroll
-    for (int i = 0; i < N; ++i) x[i] = p[i];
-}
-
-__device__ __forceinline__ half8 pack(const float (&x)[8])
-{
-    half8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];
-    return r;
-}
-__device__ __forceinline__ half4 pack(const float (&x)[4])
-{
-    half4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (_Float16)x[i];
-    return r;
-}
-__device__ __forceinline__ float pack(const float (&x)[1]) { return x[0]; }
-
-// KPL consecutive elements from LDS as an MFMA fragment.
-template <typename T, int KPL> struct Frag;
-template <> struct Frag<_Float16, 8> {
-    static __device__ __forceinline__ half8 ld(const _Float16* p) { return *(const half8*)p; }
-};
-template <> struct Frag<_Float16, 4> {
-    static __device__ __forceinline__ half4 ld(const _Float16* p) { return *(const half4*)p; }
-};
-template <> struct Frag<float, 1> {
-    static __device__ __forceinline__ float ld(const float* p) { return *p; }
 };
 
 // ---------------------------------------------------------------------------
@@ -646,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void gla_chunk_kernel(Params P)
                 if (gated) {
                     ss += __shfl_xor(ss, 16);
                     ss += __shfl_xor(ss, 32);
-                    const float inv = 1.0f / sqrtf(ss * (1.0f / DV) + P.eps);
+                    const float inv = rsq_fast(ss * (1.0f / DV) + P.eps);
 #pragma unroll
                     for (int m = 0; m < G::MT; ++m)
 #pragma unroll

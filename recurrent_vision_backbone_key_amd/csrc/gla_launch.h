@@ -6,6 +6,9 @@
 
 namespace gla {
 
+// Largest segment (in chunks) the single-pass kernel keeps on chip.
+constexpr int kOnePassMaxChunks = 5;
+
 // Arguments of one forward call, already validated.
 struct Params {
     const void* q;      // [B, L, NH, DK]
@@ -15,7 +18,15 @@ struct Params {
     const void* r;      // [B, L, NH, DV] output-gate pre-activation, or null
     const float* w;     // [DV] RMSNorm weight, or null (ones)
     void* out;          // [B, L, NH, DV]
-    float* ws;          // segment slots: [units][nseg-1][DK*DV + DK] fp32
+    float* ws;          // three-pass: segment slots [units][nseg-1][DK*DV + DK] fp32
+    // single-pass exchange (workspace): ticket and error word, one flag per
+    // (scan, segment), segment aggregates and inclusive states
+    unsigned* ticket;
+    unsigned* err;
+    unsigned* done;     // [units]: workgroups of the scan past their look-back
+    unsigned* flags;    // [units][nseg]: 0 none, 1 aggregate, 2 inclusive
+    float* agg;         // [units][nseg][DK*DV + DK]
+    float* incl;        // [units][nseg][DK*DV]
     int B, NH, H, W, L, dir;
     int nchunks;        // ceil(L / chunk)
     int seg_chunks;     // chunks per segment
@@ -28,6 +39,12 @@ struct Params {
 // Launches the aggregate, fold and output passes (or only the output pass
 // when nseg == 1) on `stream`.  Returns a gla_status value.
 int launch_fwd(const Params& P, int dtype, int d, int chunk, void* stream);
+
+// Single-pass kernel (binary16, d = 64, chunk 64): one launch.
+int launch_onepass(const Params& P, void* stream);
+
+// Zero-fills a workspace (counters, flags) on `stream`.
+int launch_workspace_init(void* ws, size_t bytes, void* stream);
 
 }  // namespace gla
 

@@ -1,0 +1,744 @@
+// gla_onepass.hip -- single-pass chunkwise forward of key-only gated linear
+// attention for gfx950 (binary16 storage, d_k = d_v = 64, 64-token chunks).
+//
+// Same mathematics as gla_kernel.hip (paper "GTR: Gated Token Recurrence for
+// Efficient Dense Prediction", Section 2.1; chunkwise regrouping of the GLA
+// recurrence), organised so every input byte is read from HBM once:
+//
+//  phase 1  each workgroup (8 wavefronts) takes a ticket, which fixes its
+//           (scan, segment), and walks the segment's chunks with a local state
+//           that starts at zero, keeping the partial outputs and the query
+//           operand relative to the segment start in registers.
+//  phase 2  it publishes its segment aggregate (local state, total decay),
+//           looks back over earlier segments of the same scan until every one
+//           has published, and folds forward from the latest inclusive state:
+//               S_in = fold_{i < seg} (S -> Diag(2^{G_i}) S + L_i),
+//           with the multipliers 2^{G_i} published as computed by segment i.
+//           The fold always runs in segment order from a state that is itself
+//           that fold, so the bits do not depend on which predecessor was
+//           found (deterministic).  Workgroups only wait on smaller tickets.
+//  phase 3  adds (q (.) 2^{b from segment start}) S_in to the kept partial
+//           outputs, applies the epilogue and stores every row.
+//
+// Work split inside a chunk: wavefront w handles the 16-token sub-chunk
+// i = w & 3 and the half h = w >> 2 of the channels.  A lane holds 8 channels
+// of one token, which is both the row layout of the MFMA operands and the
+// layout the gate stage needs: the log-decay is accumulated along the 16
+// tokens of the sub-chunk with a DPP prefix scan across the lane row.  With
+// bl the cumulative log2-decay inside the sub-chunk, tot_m the total of
+// sub-chunk m and R_i = sum_{m < i} tot_m:
+//     Qbase_t = q_t (.) 2^{bl_t}                   (<= |q|)
+//     E_s     = k_s (.) 2^{tot_j - bl_s}           (<= |k|, key relative to its sub-chunk end)
+//     A(t, s) = (Qbase_t (.) 2^{R_i - R_j - tot_j}) . E_s   for s in sub-chunk j <= i
+// The factor is 1 for adjacent sub-chunks and <= 1 for earlier ones; on the
+// diagonal it is 2^{-tot_i} >= 1, so that block uses split binary16
+// operands and falls back to an exact pairwise fp32 evaluation when the
+// sub-chunk's decay span exceeds 2^8.  The two wavefronts of a sub-chunk each
+// contract their own 32 channels and exchange the partial score tiles.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gla.h"
+#include "gla_device.h"
+#include "gla_geometry.h"
+#include "gla_launch.h"
+
+namespace gla {
+namespace onepass {
+
+constexpr int NT = 512;   // threads per workgroup
+constexpr int NW = 8;     // wavefronts
+constexpr int D = 64;     // head dim (d_k = d_v)
+constexpr int C = 64;     // chunk
+constexpr int NSUB = 4;   // 16-token sub-chunks per chunk
+constexpr int NCH = kOnePassMaxChunks;  // chunks per segment (upper bound)
+constexpr int SH = D + 8; // binary16 row stride (elements): 144-byte rows
+constexpr int SF = D + 4; // fp32 row stride (elements): 272-byte rows
+// Per-wave factor table rows (sub-chunk i of the wave, 32 channels of its half):
+constexpr int FD = 0;     // 2^{-tot_i}                 diagonal query factor (>= 1)
+constexpr int FQ = 1;     // 2^{R_i}                    q (.) 2^b for the local inter-chunk term
+constexpr int FS = 2;     // 2^{R_i + D_seg}            q (.) 2^b from the segment start
+constexpr int FK = 3;     // 2^{total - R_i - tot_i}    k-hat from E
+constexpr int F1 = 4;     // 2^{tot_{i-1}}              query factor for key sub-chunk i-2
+constexpr int F2 = 5;     // 2^{tot_{i-1} + tot_{i-2}}  query factor for key sub-chunk i-3
+
+// LDS layout (bytes)
+constexpr int L_E = 0;                        // E hi          [C][SH] f16 ([token][ch])
+constexpr int L_EL = L_E + C * SH * 2;        // E lo          [C][SH] f16
+constexpr int L_KT = L_EL + C * SH * 2;       // k-hat^T       [D][SH] f16 ([ch][token])
+constexpr int L_VT = L_KT + D * SH * 2;       // v^T           [D][SH] f16 ([dv][token])
+constexpr int L_ST = L_VT + D * SH * 2;       // S^T           [D][SH] f16 ([dv][ch])
+constexpr int L_QH = L_ST + D * SH * 2;       // q (.) 2^b     [C][SH] f16 ([token][ch])
+constexpr int L_PA = L_QH + C * SH * 2;       // partial scores [NW][NSUB][64 lanes][4] f32
+constexpr int L_FQ = L_PA + NW * NSUB * 64 * 16;  // raw q      [C][SH] f16 (pairwise fallback)
+constexpr int L_FK = L_FQ + C * SH * 2;       // raw k         [C][SH] f16 (pairwise fallback)
+constexpr int L_FB = L_FK + C * SH * 2;       // bl            [C][SF] f32 (pairwise fallback)
+constexpr int L_TOT = L_FB + C * SF * 4;      // sub-chunk totals [NSUB][D] f32
+constexpr int L_DEC = L_TOT + NSUB * D * 4;   // 2^{chunk total} [D] f32
+constexpr int L_FAC = L_DEC + D * 4;         // per-wave factors [NW][NFAC][32] f32
+constexpr int L_ROWS = L_FAC + NW * 8 * 32 * 4;  // row tables  [NCH][C] i32
+constexpr int L_SS = L_ROWS + NCH * C * 4;    // RMS partials   [NCH][2][C] f32
+constexpr int L_MISC = L_SS + NCH * 2 * C * 4;  // ticket, wide flags, look-back result
+constexpr int LDS_TOTAL = L_MISC + 64;
+// phase-2/3 aliases
+constexpr int L_LSEG = L_PA;                  // segment local state [D][D] f32 (16 KiB)
+constexpr int L_GSEG = L_PA + D * D * 4;      // segment total decay [D] f32
+constexpr int L_STL = L_E;                    // S_in^T lo [D][SH] f16
+constexpr int L_OUT = L_PA;                   // output staging [NCH][C][SH] f16
+static_assert(L_GSEG + D * 4 <= L_TOT, "segment aggregate overlaps live buffers");
+static_assert(L_OUT + NCH * C * SH * 2 <= L_TOT, "output staging overlaps live buffers");
+static_assert(LDS_TOTAL <= kLdsLimit, "LDS budget of one CU exceeded");
+
+// Exchange through device memory.  Every exchanged word (states, decays,
+// flags, counters) is accessed with agent-scope atomics, which on gfx950
+// bypass the per-XCD L2's non-coherent state (sc1 loads and stores), so no L2
+// write-back or invalidate is needed.  A publisher waits until all its state
+// stores are acknowledged (s_waitcnt) before any wave sets the flag; a reader
+// issues its state loads only after it has seen the flag.
+__device__ __forceinline__ unsigned ld_u(const unsigned* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u(unsigned* p, unsigned v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_x(const float* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_x(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// One forward step of the segment fold, S -> Diag(2^G) S + L, with the
+// multiplier 2^G as published (identical wherever it is evaluated).
+__device__ __forceinline__ float fold_step(float g_mul, float s, float l)
+{
+    return __builtin_fmaf(g_mul, s, l);
+}
+
+template <int N>
+__device__ __forceinline__ void ld8f(const float* p, float (&x)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = p[i];
+}
+
+// x from the lane N places lower in the same 16-lane row (0 for the first N).
+template <int N>
+__device__ __forceinline__ float row_shr(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
+}
+
+// Inclusive prefix sum along the 16 lanes of each row (Hillis-Steele).
+__device__ __forceinline__ float row_scan(float x)
+{
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    return x;
+}
+
+struct Raw {
+    u32x4 q, k, v, z0, z1;  // 8 channels of one token (q, k, v binary16; z binary32)
+};
+
+__device__ __forceinline__ void load_raw(Raw& r, const Params& P, int row, int c0)
+{
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    r.q = r.k = r.v = r.z0 = r.z1 = zero;
+    if (row >= 0) {
+        const size_t o = (size_t)row * D + c0;
+        r.q = *(const u32x4*)((const _Float16*)P.q + o);
+        r.k = *(const u32x4*)((const _Float16*)P.k + o);
+        r.v = *(const u32x4*)((const _Float16*)P.v + o);
+        r.z0 = *(const u32x4*)(P.z + o);
+        r.z1 = *(const u32x4*)(P.z + o + 4);
+    }
+}
+
+__global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
+{
+    __shared__ __attribute__((aligned(16))) char lds[LDS_TOTAL];
+    _Float16* sE = (_Float16*)(lds + L_E);
+    _Float16* sEL = (_Float16*)(lds + L_EL);
+    _Float16* sKT = (_Float16*)(lds + L_KT);
+    _Float16* sVT = (_Float16*)(lds + L_VT);
+    _Float16* sST = (_Float16*)(lds + L_ST);
+    _Float16* sQH = (_Float16*)(lds + L_QH);
+    float* sPA = (float*)(lds + L_PA);
+    _Float16* sFQ = (_Float16*)(lds + L_FQ);
+    _Float16* sFK = (_Float16*)(lds + L_FK);
+    float* sFB = (float*)(lds + L_FB);
+    float* sTot = (float*)(lds + L_TOT);
+    float* sDec = (float*)(lds + L_DEC);
+    float* sFac = (float*)(lds + L_FAC);
+    int* sRows = (int*)(lds + L_ROWS);
+    float* sSS = (float*)(lds + L_SS);
+    int* sMisc = (int*)(lds + L_MISC);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int si = wave & 3;        // sub-chunk of this wave
+    const int h = wave >> 2;        // channel half (phase 1) / value half (outputs)
+    const int cht = lane & 31;      // table layout: channel 32*h + cht
+    const int ht = lane >> 5;       //               first or second group of tables
+    const int c0 = 32 * h + 8 * g;  // this lane's 8 channels (row layout)
+    const int tl = 16 * si + l16;   // this lane's token in the chunk
+    const int nunits = P.B * P.NH;
+    const int grid = nunits * P.nseg;
+
+    // ---- ticket: logical (segment, scan) in start order
+    if (tid == 0) {
+        const unsigned t = atomicAdd(P.ticket, 1u);
+        if (t == (unsigned)grid - 1u) st_u(P.ticket, 0u);  // every ticket is taken
+        sMisc[0] = (int)t;
+    }
+    __syncthreads();
+    const int ticket = sMisc[0];
+    if (ticket >= grid) {  // workspace not initialised: report, do nothing
+        if (tid == 0) atomicOr(P.err, 2u);
+        return;
+    }
+    const int seg = ticket / nunits;
+    const int unit = ticket - seg * nunits;
+    const int c_begin = seg * P.seg_chunks;
+    const int nch = min(P.nchunks, c_begin + P.seg_chunks) - c_begin;
+    const bool gated = (P.r != nullptr);
+
+    // ---- row tables of every chunk of the segment
+    for (int i = tid; i < nch * C; i += NT) sRows[i] = scan_row(P, unit, c_begin * C + i);
+    __syncthreads();
+
+    Raw raw;
+    load_raw(raw, P, sRows[tl], c0);
+
+    float4v okeep[NCH][2];
+    half8 qkeep[NCH];    // this lane's 8 channels of the segment-relative query
+    float4v S[2];        // this wave's two 16x16 tiles of the local state
+    S[0] = S[1] = float4v{0.f, 0.f, 0.f, 0.f};
+    const int sa = wave >> 1;         // state tile row block (key channels)
+    const int sb0 = 2 * (wave & 1);   // first state tile column block (value channels)
+    float dseg = 0.f;                 // decay since segment start, channel 32*h + cht
+
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (c >= nch) break;
+        const int cpos = (c_begin + c) * C;
+        const bool valid = (cpos + tl < P.L);
+        float qv[8], kv[8], zv[8];
+        const u32x4 raw_v = raw.v;
+        {
+            const half8 qh = __builtin_bit_cast(half8, raw.q);
+            const half8 kh = __builtin_bit_cast(half8, raw.k);
+            const float4v z0 = __builtin_bit_cast(float4v, raw.z0);
+            const float4v z1 = __builtin_bit_cast(float4v, raw.z1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qv[e] = (float)qh[e];
+                kv[e] = (float)kh[e];
+                zv[e] = e < 4 ? z0[e] : z1[e - 4];
+            }
+            // raw copies for the pairwise fallback of a wide diagonal block
+            *(u32x4*)(sFQ + tl * SH + c0) = raw.q;
+            *(u32x4*)(sFK + tl * SH + c0) = raw.k;
+        }
+        if (c + 1 < nch) load_raw(raw, P, sRows[(c + 1) * C + tl], c0);
+
+        // ---- gate stage: log2-decay, prefix along the 16 tokens of the sub-chunk
+        float bl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a = log2_sigmoid(zv[e]) * P.inv_tau;
+            a = (a < kMinLog2Decay) ? kMinLog2Decay : a;
+            bl[e] = row_scan(valid ? a : 0.f);
+        }
+        if (l16 == 15) {
+            *(float4v*)(sTot + si * D + c0) = float4v{bl[0], bl[1], bl[2], bl[3]};
+            *(float4v*)(sTot + si * D + c0 + 4) = float4v{bl[4], bl[5], bl[6], bl[7]};
+        }
+        *(float4v*)(sFB + tl * SF + c0) = float4v{bl[0], bl[1], bl[2], bl[3]};
+        *(float4v*)(sFB + tl * SF + c0 + 4) = float4v{bl[4], bl[5], bl[6], bl[7]};
+        __syncthreads();  // (1) sub-chunk totals
+
+        // ---- per-channel factors of this wave's sub-chunk and channel half,
+        //      computed once per channel (table layout) and read back per lane
+        float* fac = sFac + wave * 8 * 32;
+        bool wide = false;
+        {
+            const int ch = 32 * h + cht;
+            float tm[NSUB];
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m) tm[m] = sTot[m * D + ch];
+            float rr = 0.f, ti = 0.f, all = 0.f, t1 = 0.f, t2 = 0.f;
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m) {
+                all += tm[m];
+                if (m < si) rr += tm[m];
+                if (m == si) ti = tm[m];
+                if (m == si - 1) t1 = tm[m];
+                if (m == si - 2) t2 = tm[m];
+            }
+            if (ht == 0) {
+                fac[FD * 32 + cht] = exp2_fast(-ti);
+                fac[FQ * 32 + cht] = exp2_fast(rr);
+                fac[FS * 32 + cht] = exp2_fast(rr + dseg);
+                wide = !(-ti <= Fmt<_Float16>::kSpan);
+                if (si == 0) sDec[ch] = exp2_fast(all);
+            } else {
+                fac[FK * 32 + cht] = exp2_fast(all - rr - ti);
+                fac[F1 * 32 + cht] = exp2_fast(t1);
+                fac[F2 * 32 + cht] = exp2_fast(t1 + t2);
+            }
+            dseg += all;
+        }
+        // the tables are read back by other lanes of the same wavefront
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- operands of this token and channel group
+        float ti8[8], fd[8], fq[8], fs[8], fk[8];
+        ld8f(sTot + si * D + c0, ti8);
+        ld8f(fac + FD * 32 + 8 * g, fd);
+        ld8f(fac + FQ * 32 + 8 * g, fq);
+        ld8f(fac + FS * 32 + 8 * g, fs);
+        ld8f(fac + FK * 32 + 8 * g, fk);
+        float qb[8];
+        half8 eh, el, kt8, qd_h, qd_l, qhat, qs, qa;
+        float maxqd = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qb[e] = qv[e] * exp2_fast(bl[e]);
+            const float ef = kv[e] * exp2_fast(ti8[e] - bl[e]);
+            eh[e] = (_Float16)ef;
+            el[e] = (_Float16)(ef - (float)eh[e]);
+            kt8[e] = (_Float16)(ef * fk[e]);
+            const float qd = qb[e] * fd[e];
+            maxqd = fmaxf(maxqd, fabsf(qd));
+            qd_h[e] = (_Float16)qd;
+            qd_l[e] = (_Float16)(qd - (float)qd_h[e]);
+            qhat[e] = (_Float16)(qb[e] * fq[e]);
+            qs[e] = (_Float16)(qb[e] * fs[e]);
+            qa[e] = (_Float16)qb[e];
+        }
+        // the amplified diagonal query operand must stay in binary16 range
+        // (a NaN also takes the pairwise path, which propagates it)
+        wide |= !(maxqd <= Fmt<_Float16>::kMaxOperand);
+        *(half8*)(sE + tl * SH + c0) = eh;
+        *(half8*)(sEL + tl * SH + c0) = el;
+        *(half8*)(sQH + tl * SH + c0) = qhat;
+        {
+            const half8 vh = __builtin_bit_cast(half8, raw_v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sKT[(c0 + e) * SH + tl] = kt8[e];
+                sVT[(c0 + e) * SH + tl] = vh[e];
+            }
+        }
+        {
+            const bool ww = __any(wide);
+            if (lane == 0) sMisc[4 + wave] = ww ? 1 : 0;
+        }
+        qkeep[c] = qs;
+        // off-diagonal query operands for key sub-chunks i-2 and i-3
+        half8 qo1 = qa, qo2 = qa;
+        if (si >= 2) {
+            float f[8];
+            ld8f(fac + F1 * 32 + 8 * g, f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qo1[e] = (_Float16)(qb[e] * f[e]);
+        }
+        if (si == 3) {
+            float f[8];
+            ld8f(fac + F2 * 32 + 8 * g, f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qo2[e] = (_Float16)(qb[e] * f[e]);
+        }
+        __syncthreads();  // (2) operands of every wave
+
+        // ---- M1 partial scores over this wave's 32 channels, tiles j <= si
+        const bool wide_i = (sMisc[4 + si] | sMisc[4 + si + 4]) != 0;
+        float4v part[NSUB];
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j) {
+            part[j] = float4v{0.f, 0.f, 0.f, 0.f};
+            if (j > si) continue;
+            const half8 ek = *(const half8*)(sE + (16 * j + l16) * SH + c0);
+            if (j < si) {
+                const half8 qf = (j == si - 1) ? qa : (j == si - 2) ? qo1 : qo2;
+                part[j] = mma(ek, qf, part[j]);
+            } else if (!wide_i) {
+                const half8 ekl = *(const half8*)(sEL + (16 * j + l16) * SH + c0);
+                part[j] = mma(ek, qd_h, part[j]);
+                part[j] = mma(ekl, qd_h, part[j]);
+                part[j] = mma(ek, qd_l, part[j]);
+            } else {
+                // exact pairwise over this wave's channels: q_t k_s 2^{bl_t - bl_s}
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sl = 4 * g + e;
+                    float acc = 0.f;
+                    if (sl <= l16) {
+                        const int ts = 16 * si + sl;
+                        for (int cc = 32 * h; cc < 32 * h + 32; ++cc)
+                            acc += (float)sFQ[tl * SH + cc] * (float)sFK[ts * SH + cc] *
+                                   exp2_fast(sFB[tl * SF + cc] - sFB[ts * SF + cc]);
+                    }
+                    part[j][e] = acc;
+                }
+            }
+            *(float4v*)(sPA + ((wave * NSUB + j) * 64 + lane) * 4) = part[j];
+        }
+        __syncthreads();  // (3) partial scores of both halves
+        float4v at[NSUB];
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j) {
+            at[j] = float4v{0.f, 0.f, 0.f, 0.f};
+            if (j > si) continue;
+            const float4v other = *(const float4v*)(sPA + (((wave ^ 4) * NSUB + j) * 64 + lane) * 4);
+            at[j] = part[j] + other;
+            if (j == si) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * g + e > l16) at[j][e] = 0.f;
+            }
+        }
+
+        // ---- M2: O^T[dv][t] += V^T A^T, this wave's 32 value channels
+        float4v o[2];
+        o[0] = o[1] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NSUB / 2; ++p) {
+            if (2 * p > si) continue;
+            const bool hi = (2 * p + 1 <= si);
+            half8 bfr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bfr[e] = (_Float16)at[2 * p][e];
+                bfr[4 + e] = hi ? (_Float16)at[2 * p + 1][e] : (_Float16)0.f;
+            }
+            half8 blo = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (2 * p == si) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) blo[e] = lo_part(at[2 * p][e]);
+            }
+            if (2 * p + 1 == si) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) blo[4 + e] = lo_part(at[2 * p + 1][e]);
+            }
+            const bool has_diag = (2 * p == si) || (2 * p + 1 == si);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const _Float16* vrow = sVT + (32 * h + 16 * m + l16) * SH;
+                const half4 v0 = *(const half4*)(vrow + 32 * p + 4 * g);
+                half4 v1 = {0, 0, 0, 0};
+                if (hi) v1 = *(const half4*)(vrow + 32 * p + 16 + 4 * g);
+                half8 afr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    afr[e] = v0[e];
+                    afr[4 + e] = v1[e];
+                }
+                o[m] = mma(afr, bfr, o[m]);
+                if (has_diag) o[m] = mma(afr, blo, o[m]);
+            }
+        }
+        // ---- M3: O^T += S_loc^T (q (.) 2^b)^T, local state from the segment start
+        if (c > 0) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const half8 qf = *(const half8*)(sQH + tl * SH + 32 * kb + 8 * g);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const half8 sfr = *(const half8*)(sST + (32 * h + 16 * m + l16) * SH + 32 * kb + 8 * g);
+                    o[m] = mma(sfr, qf, o[m]);
+                }
+            }
+        }
+        okeep[c][0] = o[0];
+        okeep[c][1] = o[1];
+
+        // ---- M4: local state update S = Diag(2^{chunk total}) S + k-hat^T v
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int bb = sb0 + jj;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[jj][e] *= sDec[16 * sa + 4 * g + e];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const half8 kf = *(const half8*)(sKT + (16 * sa + l16) * SH + 32 * kb + 8 * g);
+                const half8 vf = *(const half8*)(sVT + (16 * bb + l16) * SH + 32 * kb + 8 * g);
+                S[jj] = mma(kf, vf, S[jj]);
+            }
+        }
+        __syncthreads();  // (4) all readers of this chunk's buffers are done
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int bb = sb0 + jj;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sST[(16 * bb + l16) * SH + 16 * sa + 4 * g + e] = (_Float16)S[jj][e];
+        }
+    }
+
+    // r rows of every chunk: loads issued now, in flight during the exchange
+    constexpr int RPT = (NCH * C * 8 + NT - 1) / NT;  // 16-byte pieces per thread
+    u32x4 rreg[RPT];
+    if (gated) {
+#pragma unroll
+        for (int p = 0; p < RPT; ++p) {
+            const int idx = tid + p * NT;
+            const int row = idx >> 3, piece = idx & 7;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (row < nch * C) {
+                const int t = sRows[row];
+                if (t >= 0) val = *(const u32x4*)((const char*)P.r + (size_t)t * D * 2 + piece * 16);
+            }
+            rreg[p] = val;
+        }
+    }
+
+    // ================= phase 2: segment exchange =================
+    const size_t aggf = (size_t)D * D + D;
+    const size_t slot = (size_t)unit * P.nseg + seg;
+    float* sL = (float*)(lds + L_LSEG);
+    float* sG = (float*)(lds + L_GSEG);
+    _Float16* sSTL = (_Float16*)(lds + L_STL);
+    const bool need_in = (seg > 0);
+    if (P.nseg > 1) {
+        // local state and total decay into LDS, row-major [ch][dv]
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int bb = sb0 + jj;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sL[(16 * sa + 4 * g + e) * D + 16 * bb + l16] = S[jj][e];
+        }
+        // total decay of the segment as the factor 2^G (the fold's multiplier)
+        if (si == 0 && ht == 0) sG[32 * h + cht] = exp2_fast(dseg);
+        __syncthreads();
+        const bool last = (seg == P.nseg - 1);
+        unsigned* flags = P.flags + (size_t)unit * P.nseg;
+        if (seg > 0 && !last) {
+            float* dst = P.agg + slot * aggf;
+            for (int i = tid; i < D * D; i += NT) st_x(dst + i, sL[i]);
+            if (tid < D) st_x(dst + D * D + tid, sG[tid]);
+            wait_mem();
+            __syncthreads();
+            if (tid == 0) st_u(flags + seg, 1u);
+        }
+        if (need_in) {
+            // look back: wait until every earlier segment has published, then
+            // start from the latest inclusive state
+            if (wave == 0) {
+                unsigned spins = 0;
+                int k = -1;
+                for (;;) {
+                    const int idx = seg - 1 - lane;
+                    const unsigned f = (idx >= 0) ? ld_u(flags + idx) : 2u;
+                    if (__all(f >= 1u)) {
+                        const unsigned long long inc = __ballot(idx >= 0 && f == 2u);
+                        // lowest lane with an inclusive state = latest segment
+                        // (segment 0 always publishes one, so inc != 0)
+                        k = inc ? seg - 1 - (int)__builtin_ctzll(inc) : -1;
+                        break;
+                    }
+                    if (++spins > (1u << 22)) {
+                        if (lane == 0) atomicOr(P.err, 1u);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                if (lane == 0) sMisc[1] = k;
+            }
+            __syncthreads();
+            const int k = sMisc[1];
+            // forward fold from the inclusive state of segment k
+            constexpr int EPT = D * D / NT;  // state entries per thread
+            const float* inc = P.incl + ((size_t)unit * P.nseg + (k < 0 ? 0 : k)) * D * D;
+            float sv[EPT];
+#pragma unroll
+            for (int u = 0; u < EPT; ++u) sv[u] = (k >= 0) ? ld_x(inc + tid + u * NT) : 0.f;
+            constexpr int FW = 8;  // aggregates per round of loads
+            for (int sg0 = k + 1; sg0 < seg; sg0 += FW) {
+                // issue the loads of up to FW aggregates, then fold them in order
+                float lv[FW][EPT], gv[FW][EPT];
+#pragma unroll
+                for (int b = 0; b < FW; ++b) {
+                    const int sg = min(sg0 + b, seg - 1);
+                    const float* ag = P.agg + ((size_t)unit * P.nseg + sg) * aggf;
+#pragma unroll
+                    for (int u = 0; u < EPT; ++u) {
+                        lv[b][u] = ld_x(ag + tid + u * NT);
+                        gv[b][u] = ld_x(ag + D * D + (tid + u * NT) / D);
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < FW; ++b)
+                    if (sg0 + b < seg) {
+#pragma unroll
+                        for (int u = 0; u < EPT; ++u) sv[u] = fold_step(gv[b][u], sv[u], lv[b][u]);
+                    }
+            }
+#pragma unroll
+            for (int u = 0; u < EPT; ++u) {
+                const int i = tid + u * NT;
+                const int chn = i / D;
+                const float s = sv[u];
+                // S_in^T (hi, lo) for phase 3; inclusive state for successors
+                const int dv = i - chn * D;
+                const _Float16 hs = (_Float16)s;
+                sST[dv * SH + chn] = hs;
+                sSTL[dv * SH + chn] = (_Float16)(s - (float)hs);
+                if (!last) st_x(P.incl + slot * D * D + i, fold_step(sG[chn], s, sL[i]));
+            }
+        } else {
+            // first segment: its local state is the inclusive state
+            float* dst = P.incl + slot * D * D;
+            for (int i = tid; i < D * D; i += NT) st_x(dst + i, sL[i]);
+        }
+        if (!last) {
+            wait_mem();
+            __syncthreads();
+            if (tid == 0) st_u(flags + seg, 2u);
+        }
+        // the last workgroup of this scan to get here clears its flags
+        if (tid == 0) {
+            const unsigned done = atomicAdd(P.done + unit, 1u);
+            if (done == (unsigned)P.nseg - 1u) {
+                for (int s = 0; s < P.nseg; ++s) st_u(flags + s, 0u);
+                st_u(P.done + unit, 0u);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ================= phase 3: incoming state, epilogue, stores =================
+    _Float16* sOut = (_Float16*)(lds + L_OUT);
+    if (need_in) {
+        // exchange the query-operand halves through the staging area
+#pragma unroll
+        for (int cc = 0; cc < NCH; ++cc)
+            if (cc < nch) *(half8*)(sOut + (cc * C + tl) * SH + c0) = qkeep[cc];
+        __syncthreads();
+    }
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+        if (cc >= nch) break;
+        float4v o0 = okeep[cc][0], o1 = okeep[cc][1];
+        if (need_in) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int k0 = 32 * kb + 8 * g;
+                const half8 qf = *(const half8*)(sOut + (cc * C + tl) * SH + k0);
+                const half8 h0 = *(const half8*)(sST + (32 * h + l16) * SH + k0);
+                const half8 l0 = *(const half8*)(sSTL + (32 * h + l16) * SH + k0);
+                const half8 h1 = *(const half8*)(sST + (32 * h + 16 + l16) * SH + k0);
+                const half8 l1 = *(const half8*)(sSTL + (32 * h + 16 + l16) * SH + k0);
+                o0 = mma(h0, qf, o0);
+                o0 = mma(l0, qf, o0);
+                o1 = mma(h1, qf, o1);
+                o1 = mma(l1, qf, o1);
+            }
+        }
+        okeep[cc][0] = o0 * P.scale;
+        okeep[cc][1] = o1 * P.scale;
+        if (gated) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ss += okeep[cc][0][e] * okeep[cc][0][e] + okeep[cc][1][e] * okeep[cc][1][e];
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            if (g == 0) sSS[(cc * 2 + h) * C + tl] = ss;
+        }
+    }
+    __syncthreads();
+    if (gated) {
+        // r rows into the staging area (the epilogue overwrites them in place)
+#pragma unroll
+        for (int p = 0; p < RPT; ++p) {
+            const int idx = tid + p * NT;
+            const int row = idx >> 3, piece = idx & 7;
+            if (row < nch * C) *(u32x4*)((char*)(sOut + row * SH) + piece * 16) = rreg[p];
+        }
+        __syncthreads();
+    }
+    float wv[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            wv[m][e] = (gated && P.w) ? P.w[32 * h + 16 * m + 4 * g + e] : 1.f;
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+        if (cc >= nch) break;
+        float inv = 1.f;
+        if (gated) {
+            const float ss = sSS[(cc * 2) * C + tl] + sSS[(cc * 2 + 1) * C + tl];
+            inv = rsq_fast(ss * (1.0f / D) + P.eps);
+        }
+        _Float16* orow = sOut + (cc * C + tl) * SH + 32 * h;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            half4 hv;
+            if (gated) {
+                const half4 rv = *(const half4*)(orow + 16 * m + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hv[e] = (_Float16)(silu((float)rv[e]) * wv[m][e] * okeep[cc][m][e] * inv);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = (_Float16)okeep[cc][m][e];
+            }
+            *(half4*)(orow + 16 * m + 4 * g) = hv;
+        }
+    }
+    __syncthreads();
+    // coalesced row stores: 8 pieces of 16 bytes per row
+    for (int idx = tid; idx < nch * C * 8; idx += NT) {
+        const int row = idx >> 3, piece = idx & 7;
+        const int t = sRows[row];
+        if (t >= 0)
+            *(u32x4*)((char*)P.out + (size_t)t * D * 2 + piece * 16) =
+                *(const u32x4*)((const char*)(sOut + row * SH) + piece * 16);
+    }
+}
+
+// Zero-fills the single-pass workspace header, counters and flags.
+__global__ __launch_bounds__(256) void gla_onepass_init(unsigned* words, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        words[i] = 0u;
+}
+
+}  // namespace onepass
+
+int launch_onepass(const Params& P, void* stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    const int grid = P.B * P.NH * P.nseg;
+    hipLaunchKernelGGL(onepass::gla_onepass_kernel, dim3(grid), dim3(onepass::NT), 0, st, P);
+    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
+}
+
+int launch_workspace_init(void* ws, size_t bytes, void* stream)
+{
+    const size_t n = bytes / 4;
+    if (n == 0) return GLA_OK;
+    unsigned blocks = (unsigned)((n + 255) / 256);
+    if (blocks > 1024u) blocks = 1024u;
+    hipLaunchKernelGGL(onepass::gla_onepass_init, dim3(blocks), dim3(256), 0,
+                       (hipStream_t)stream, (unsigned*)ws, n);
+    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
+}
+
+}  // namespace gla

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "gla_geometry.h"
+#include "gla_launch.h"
 
 namespace {
 
@@ -49,22 +50,56 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     if (isnan(o->tau) || isnan(o->scale) || isinf(o->tau) || isinf(o->scale)) return GLA_EINVAL;
     if (has_gate && (isnan(o->eps) || o->eps < 0.0f || isinf(o->eps))) return GLA_EINVAL;
 
-    // Work plan: segments of seg_chunks chunks, enough workgroups for the chip.
     const int nchunks = (int)((L + chunk - 1) / chunk);
     const int64_t units = (int64_t)o->batch * o->heads;
-    int seg = o->segment_chunks;
-    if (seg <= 0) {
-        const int64_t want = (units * nchunks + kTargetGroups - 1) / kTargetGroups;
-        seg = (int)(want < 1 ? 1 : want);
-    }
-    if (seg > nchunks) seg = nchunks;
-    const int nseg = (nchunks + seg - 1) / seg;
+    if (o->algorithm < GLA_ALGO_AUTO || o->algorithm > GLA_ALGO_THREE_PASS) return GLA_EINVAL;
     plan->L = (int)L;
     plan->nchunks = nchunks;
-    plan->seg_chunks = seg;
-    plan->nseg = nseg;
-    plan->workspace_bytes =
-        nseg > 1 ? (size_t)units * (nseg - 1) * ((size_t)o->dk * o->dv + o->dk) * 4 : 0;
+    plan->onepass = 0;
+    plan->off_done = plan->off_flags = plan->off_agg = plan->off_incl = 0;
+
+    // Single pass: binary16, d = 64, 64-token chunks; segments of at most
+    // kOnePassMaxChunks chunks, at most 65 segments per scan (one wavefront
+    // of look-back), about one workgroup per compute unit.
+    const bool sp_shape = o->dtype == GLA_F16 && o->dk == 64 && o->dv == 64 && chunk == 64;
+    if (o->algorithm != GLA_ALGO_THREE_PASS && sp_shape) {
+        const int min_seg = (nchunks + 64) / 65;
+        int seg = o->segment_chunks;
+        if (seg <= 0) {
+            const int64_t want = (units * nchunks + kCUs - 1) / kCUs;
+            seg = (int)(want < 1 ? 1 : want);
+            if (seg > gla::kOnePassMaxChunks) seg = gla::kOnePassMaxChunks;
+            if (seg < min_seg) seg = min_seg;
+        }
+        if (seg > nchunks) seg = nchunks;
+        if (seg >= min_seg && seg <= gla::kOnePassMaxChunks) {
+            const int nseg = (nchunks + seg - 1) / seg;
+            const size_t nflag = (size_t)units * nseg;
+            plan->onepass = 1;
+            plan->seg_chunks = seg;
+            plan->nseg = nseg;
+            plan->off_done = 256;
+            plan->off_flags = plan->off_done + (((size_t)units * 4 + 255) / 256) * 256;
+            plan->off_agg = plan->off_flags + ((nflag * 4 + 255) / 256) * 256;
+            plan->off_incl = plan->off_agg + nflag * ((size_t)64 * 64 + 64) * 4;
+            plan->workspace_bytes = plan->off_incl + nflag * (size_t)64 * 64 * 4;
+        }
+    }
+    if (!plan->onepass) {
+        if (o->algorithm == GLA_ALGO_SINGLE_PASS) return GLA_EUNSUPPORTED;
+        // Three passes: segments of seg_chunks chunks, enough workgroups for the chip.
+        int seg = o->segment_chunks;
+        if (seg <= 0) {
+            const int64_t want = (units * nchunks + kTargetGroups - 1) / kTargetGroups;
+            seg = (int)(want < 1 ? 1 : want);
+        }
+        if (seg > nchunks) seg = nchunks;
+        const int nseg = (nchunks + seg - 1) / seg;
+        plan->seg_chunks = seg;
+        plan->nseg = nseg;
+        plan->workspace_bytes =
+            nseg > 1 ? (size_t)units * (nseg - 1) * ((size_t)o->dk * o->dv + o->dk) * 4 : 0;
+    }
     plan->tau = o->tau > 0.0f ? o->tau : 16.0f;
     plan->scale = o->scale > 0.0f ? o->scale : (float)(1.0 / sqrt((double)o->dk));
     plan->eps = o->eps;

@@ -11,7 +11,9 @@ extern "C" {
 
 typedef struct gla_plan {
     int L, nchunks, seg_chunks, nseg;
+    int onepass;                 // 1: single-pass kernel, 0: three passes
     size_t workspace_bytes;
+    size_t off_done, off_flags, off_agg, off_incl;  // single-pass workspace layout (bytes)
     float tau, scale, eps;
 } gla_plan;
 

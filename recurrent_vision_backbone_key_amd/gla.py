@@ -14,8 +14,10 @@ LIB_PATH = os.path.join(PKG, "_lib", "libgla.so")
 
 L2R, R2L, T2B, B2T = 0, 1, 2, 3
 F16, F32 = 0, 1
+ALGO_AUTO, ALGO_SINGLE_PASS, ALGO_THREE_PASS = 0, 1, 2
 STATUS = {0: "GLA_OK", 1: "GLA_EINVAL", 2: "GLA_EUNSUPPORTED", 3: "GLA_EWORKSPACE", 4: "GLA_EHIP"}
-EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_status_str", "gla_abi_version")
+EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_workspace_init", "gla_status_str",
+           "gla_abi_version")
 
 
 class GlaOpts(ctypes.Structure):
@@ -34,6 +36,7 @@ class GlaOpts(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("segment_chunks", ctypes.c_int32),
+        ("algorithm", ctypes.c_int32),
     ]
 
 
@@ -60,6 +63,8 @@ def lib():
             [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(GlaOpts)]
         h.gla_workspace_size.restype = ctypes.c_size_t
         h.gla_workspace_size.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(GlaOpts)]
+        h.gla_workspace_init.restype = ctypes.c_int
+        h.gla_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         h.gla_status_str.restype = ctypes.c_char_p
         h.gla_status_str.argtypes = [ctypes.c_int]
         h.gla_abi_version.restype = ctypes.c_int
@@ -77,15 +82,36 @@ def abi_version() -> int:
 
 
 def make_opts(batch, heads, dk, dv, dtype, tau=16.0, scale=None, eps=1e-6, norm_weight=0,
-              workspace=0, workspace_bytes=0, stream=0, segment_chunks=0) -> GlaOpts:
+              workspace=0, workspace_bytes=0, stream=0, segment_chunks=0,
+              algorithm=ALGO_AUTO) -> GlaOpts:
     return GlaOpts(batch, heads, dk, dv, dtype, float(tau),
                    0.0 if scale is None else float(scale), float(eps),
                    norm_weight or None, workspace or None, workspace_bytes, stream or None,
-                   segment_chunks)
+                   segment_chunks, algorithm)
 
 
 def workspace_size(direction, H, W, chunk, opts: GlaOpts) -> int:
     return lib().gla_workspace_size(direction, H, W, chunk, ctypes.byref(opts))
+
+
+def workspace_init(workspace, stream=None):
+    """Clear a device workspace tensor (include/gla.h: gla_workspace_init)."""
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().gla_workspace_init(workspace.data_ptr(), nbytes & ~3, stream)
+    if st != 0:
+        raise GlaError(st, f"gla_workspace_init failed: {status_str(st)}")
+
+
+def new_workspace(direction, H, W, chunk, opts: GlaOpts, device):
+    """A cleared workspace tensor sized for these arguments (or None)."""
+    torch = _torch()
+    need = workspace_size(direction, H, W, chunk, opts)
+    if not need:
+        return None
+    return torch.zeros(need, dtype=torch.uint8, device=device)
 
 
 def _torch():
@@ -94,7 +120,8 @@ def _torch():
 
 
 def fwd(q, k, v, z, direction, H, W, chunk=64, r=None, norm_weight=None, eps=1e-6, out=None,
-        tau=16.0, scale=None, segment_chunks=0, workspace=None, stream=None):
+        tau=16.0, scale=None, segment_chunks=0, workspace=None, stream=None,
+        algorithm=ALGO_AUTO):
     """Chunkwise key-only GLA forward (include/gla.h: gla_fwd) on CUDA tensors.
 
     q, k, z: [B, L, NH, dk]; v, r: [B, L, NH, dv]; q, k, v, r float16 or float32,
@@ -123,11 +150,13 @@ def fwd(q, k, v, z, direction, H, W, chunk=64, r=None, norm_weight=None, eps=1e-
         stream = torch.cuda.current_stream(q.device).cuda_stream
     opts = make_opts(B, NH, dk, dv, dtype, tau, scale, eps,
                      norm_weight.data_ptr() if norm_weight is not None else 0,
-                     stream=stream, segment_chunks=segment_chunks)
+                     stream=stream, segment_chunks=segment_chunks, algorithm=algorithm)
     need = workspace_size(direction, H, W, chunk, opts)
     if need:
+        # a workspace passed in must have been cleared once (workspace_init);
+        # one allocated here starts cleared
         if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         opts.workspace = workspace.data_ptr()
         opts.workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib().gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), z.data_ptr(), direction, H, W,

@@ -16,11 +16,26 @@ def to_dev(x, torch):
     return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def run_gpu(x, direction, H, W, chunk, torch, eps=1e-6, segment_chunks=0, out=None, tau=16.0):
+def run_gpu(x, direction, H, W, chunk, torch, eps=1e-6, segment_chunks=0, out=None, tau=16.0,
+            algorithm=gla.ALGO_AUTO):
     d = {n: to_dev(x[n], torch) for n in ("q", "k", "v", "z", "r", "w")}
+    B, L, NH, dk = x["q"].shape
+    opts = gla.make_opts(B, NH, dk, x["v"].shape[3],
+                         gla.F16 if x["q"].dtype == np.float16 else gla.F32,
+                         segment_chunks=segment_chunks, algorithm=algorithm)
+    need = gla.workspace_size(direction, H, W, chunk, opts)
+    # a garbage-filled workspace cleared by the library's own init call
+    ws = torch.full((max(need, 16),), 0xA5, dtype=torch.uint8, device="cuda")
+    gla.workspace_init(ws)
     y = gla.fwd(d["q"], d["k"], d["v"], d["z"], direction, H, W, chunk=chunk, r=d["r"],
-                norm_weight=d["w"], eps=eps, out=out, tau=tau, segment_chunks=segment_chunks)
+                norm_weight=d["w"], eps=eps, out=out, tau=tau, segment_chunks=segment_chunks,
+                workspace=ws, algorithm=algorithm)
     torch.cuda.synchronize()
+    # single pass: word 1 of the workspace is the error word (sticky until the
+    # next init), set only if a look-back wait gave up or a ticket was bad
+    if algorithm == gla.ALGO_SINGLE_PASS:
+        err = int(ws[4:8].cpu().numpy().view(np.uint32)[0])
+        assert err == 0, f"look-back error flag set: {err:#x}"
     return y.cpu().numpy()
 
 

@@ -128,9 +128,43 @@ def test_workspace_size_and_errors():
     assert gla.workspace_size(0, 0, 40, 64, o) == 0
 
 
-def test_workspace_formula():
+def test_workspace_formula_three_pass():
     """(units) x (segments - 1) slots of (dk*dv + dk) fp32."""
-    o = _opts(batch=2, heads=3, segment_chunks=4)
+    o = _opts(batch=2, heads=3, segment_chunks=4, algorithm=gla.ALGO_THREE_PASS)
     nchunks = -(-(40 * 40) // 64)
     nseg = -(-nchunks // 4)
     assert gla.workspace_size(1, 40, 40, 64, o) == 6 * (nseg - 1) * (64 * 64 + 64) * 4
+
+
+def test_workspace_formula_single_pass():
+    """256-byte header, one counter per scan and one flag per (scan, segment),
+    each rounded to 256 bytes, then an aggregate (dk*dv + dk fp32) and an
+    inclusive state (dk*dv fp32) per (scan, segment)."""
+    o = _opts(batch=2, heads=3, segment_chunks=4, algorithm=gla.ALGO_SINGLE_PASS)
+    nseg = -(-25 // 4)
+    n = 6 * nseg
+    want = 256 + 256 + -(-n * 4 // 256) * 256 + n * (64 * 64 + 64) * 4 + n * 64 * 64 * 4
+    assert gla.workspace_size(1, 40, 40, 64, o) == want
+
+
+def test_workspace_init_argument_checks():
+    h = gla.lib()
+    assert h.gla_workspace_init(None, 0, None) == 0
+    assert h.gla_workspace_init(None, 256, None) == 1
+    assert h.gla_workspace_init(A + 8, 256, None) == 1
+    assert h.gla_workspace_init(A, 254, None) == 1
+
+
+def test_algorithm_selection():
+    """The single pass applies to binary16, d = 64, chunk 64 with segments of
+    at most 5 chunks and at most 65 segments per scan; forcing it elsewhere
+    is GLA_EUNSUPPORTED; an unknown algorithm is GLA_EINVAL."""
+    ok = _opts(algorithm=gla.ALGO_SINGLE_PASS)
+    assert gla.workspace_size(0, 40, 40, 64, ok) > 0
+    assert _call(chunk=32, opts=_opts(algorithm=gla.ALGO_SINGLE_PASS)) == 2
+    assert _call(opts=_opts(dk=32, dv=32, algorithm=gla.ALGO_SINGLE_PASS)) == 2
+    assert _call(opts=_opts(dtype=gla.F32, algorithm=gla.ALGO_SINGLE_PASS)) == 2
+    assert _call(opts=_opts(segment_chunks=6, algorithm=gla.ALGO_SINGLE_PASS)) == 2
+    # 157 chunks in 2-chunk segments: 79 segments exceed the look-back window
+    assert _call(H=100, W=100, opts=_opts(segment_chunks=2, algorithm=gla.ALGO_SINGLE_PASS)) == 2
+    assert _call(opts=_opts(algorithm=7)) == 1

@@ -13,6 +13,7 @@ from parity import TOL, rel_err, report, run_gpu, run_oracle, unit_mask
 pytestmark = pytest.mark.gpu
 
 DIRS = (0, 1, 2, 3)
+ALGOS = [pytest.param(1, id="single"), pytest.param(2, id="three")]
 
 
 @pytest.fixture(scope="module")
@@ -46,25 +47,30 @@ def test_tiny_fp32(torch):
     _check("tiny", x, 0, s["H"], s["W"], s["chunk"], "f32", torch)
 
 
+@pytest.mark.parametrize("algorithm", ALGOS)
 @pytest.mark.parametrize("direction", DIRS)
-def test_frame640(torch, direction):
+def test_frame640(torch, direction, algorithm):
     s = WORKLOADS["frame640"]
     x = workload_inputs("frame640", call=direction)
-    _check("frame640", x, direction, s["H"], s["W"], s["chunk"], "f16", torch)
+    _check("frame640", x, direction, s["H"], s["W"], s["chunk"], "f16", torch, algorithm=algorithm)
 
 
+@pytest.mark.parametrize("algorithm", ALGOS)
 @pytest.mark.parametrize("call", range(4))
-def test_batch640_gated(torch, call):
+def test_batch640_gated(torch, call, algorithm):
     s = WORKLOADS["batch640_gated"]
     x = workload_inputs("batch640_gated", call=call)
-    _check("batch640_gated", x, s["dirs"][call], s["H"], s["W"], s["chunk"], "f16", torch)
+    _check("batch640_gated", x, s["dirs"][call], s["H"], s["W"], s["chunk"], "f16", torch,
+           algorithm=algorithm)
 
 
+@pytest.mark.parametrize("algorithm", ALGOS)
 @pytest.mark.parametrize("direction", DIRS)
-def test_frame1280_gated(torch, direction):
+def test_frame1280_gated(torch, direction, algorithm):
     s = WORKLOADS["frame1280_gated"]
     x = workload_inputs("frame1280_gated", call=direction)
-    _check("frame1280_gated", x, direction, s["H"], s["W"], s["chunk"], "f16", torch)
+    _check("frame1280_gated", x, direction, s["H"], s["W"], s["chunk"], "f16", torch,
+           algorithm=algorithm)
 
 
 @pytest.mark.parametrize("call", [0, 5, 10, 11])
@@ -90,12 +96,33 @@ def test_chunk_size_invariance(torch, chunk):
 
 
 @pytest.mark.parametrize("seg", [1, 2, 3, 7, 1000])
-def test_segment_split_invariance(torch, seg):
+def test_segment_split_invariance_three_pass(torch, seg):
     """Sequence splitting (aggregate, fold, output passes) matches the oracle
     for any segment length, including one segment per scan."""
     x = make_inputs(1, 4, 24, 40, 64, 64, "f16", (0.5, 1.0), True, seed=103)
     for d in DIRS:
-        _check(f"seg{seg}", x, d, 24, 40, 64, "f16", torch, segment_chunks=seg)
+        _check(f"seg{seg}", x, d, 24, 40, 64, "f16", torch, segment_chunks=seg, algorithm=2)
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3, 4, 5])
+def test_segment_split_invariance_single_pass(torch, seg):
+    """Single pass with every segment length it supports (look-back over up to
+    15 segments per scan, ragged last segment)."""
+    x = make_inputs(1, 4, 24, 40, 64, 64, "f16", (0.5, 1.0), True, seed=103)
+    for d in DIRS:
+        _check(f"sp-seg{seg}", x, d, 24, 40, 64, "f16", torch, segment_chunks=seg, algorithm=1)
+
+
+def test_single_pass_long_scan_many_segments(torch):
+    """A 100x100 grid (157 chunks) in 2-chunk segments: 79 segments per scan is
+    over the look-back window, so the plan falls back to three passes; 3-chunk
+    segments (53 per scan) stay in the single pass."""
+    from recurrent_vision_backbone_key_amd import gla
+    x = make_inputs(1, 2, 100, 100, 64, 64, "f16", (1.0, 1.0), True, seed=139)
+    _check("sp-long", x, 2, 100, 100, 64, "f16", torch, segment_chunks=3, algorithm=1)
+    with pytest.raises(gla.GlaError):
+        run_gpu_forced = __import__("parity").run_gpu
+        run_gpu_forced(x, 2, 100, 100, 64, torch, segment_chunks=2, algorithm=1)
 
 
 def test_deterministic_and_direction_identities_bitwise(torch):
@@ -115,20 +142,22 @@ def test_deterministic_and_direction_identities_bitwise(torch):
         b, L, nh, d = a.shape
         return np.ascontiguousarray(a.reshape(b, HH, WW, nh, d).transpose(0, 2, 1, 3, 4).reshape(b, L, nh, d))
 
-    for seg in (0, 1000):
-        print(f"[case] determinism seg={seg}", flush=True)
-        a1 = run_gpu(x, 2, H, W, 64, torch, segment_chunks=seg)
-        a2 = run_gpu(x, 2, H, W, 64, torch, segment_chunks=seg)
-        assert np.array_equal(a1.view(np.uint16), a2.view(np.uint16))
-        r2l = run_gpu(x, 1, H, W, 64, torch, segment_chunks=seg)
-        alt = flip(run_gpu(tr(x, flip), 0, H, W, 64, torch, segment_chunks=seg))
+    for seg, algo in ((0, 2), (1000, 2), (1, 1), (3, 1)):
+        kw = dict(segment_chunks=seg, algorithm=algo)
+        print(f"[case] determinism seg={seg} algorithm={algo}", flush=True)
+        a1 = run_gpu(x, 2, H, W, 64, torch, **kw)
+        for _ in range(3):
+            a2 = run_gpu(x, 2, H, W, 64, torch, **kw)
+            assert np.array_equal(a1.view(np.uint16), a2.view(np.uint16))
+        r2l = run_gpu(x, 1, H, W, 64, torch, **kw)
+        alt = flip(run_gpu(tr(x, flip), 0, H, W, 64, torch, **kw))
         assert np.array_equal(r2l.view(np.uint16), alt.view(np.uint16))
         xt = tr(x, lambda a: transpose(a, H, W))
-        t2b = run_gpu(x, 2, H, W, 64, torch, segment_chunks=seg)
-        alt = transpose(run_gpu(xt, 0, W, H, 64, torch, segment_chunks=seg), W, H)
+        t2b = run_gpu(x, 2, H, W, 64, torch, **kw)
+        alt = transpose(run_gpu(xt, 0, W, H, 64, torch, **kw), W, H)
         assert np.array_equal(t2b.view(np.uint16), alt.view(np.uint16))
-        b2t = run_gpu(x, 3, H, W, 64, torch, segment_chunks=seg)
-        alt = transpose(run_gpu(xt, 1, W, H, 64, torch, segment_chunks=seg), W, H)
+        b2t = run_gpu(x, 3, H, W, 64, torch, **kw)
+        alt = transpose(run_gpu(xt, 1, W, H, 64, torch, **kw), W, H)
         assert np.array_equal(b2t.view(np.uint16), alt.view(np.uint16))
 
 
