@@ -37,6 +37,7 @@ UNITS = [
     ("gla_api.cpp", "hip", []),
     ("gla_kernel.hip", "hip", []),
     ("gla_onepass.hip", "hip", []),
+    ("gla_wide.hip", "hip", []),
 ]
 
 

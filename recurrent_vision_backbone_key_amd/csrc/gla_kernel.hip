@@ -630,9 +630,28 @@ static int run_dim(const Params& P, int d, int chunk, hipStream_t st)
     }
 }
 
+int launch_fold(const Params& P, int d, void* stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    const unsigned units = (unsigned)(P.B * P.NH);
+    switch (d) {
+    case 64:
+        hipLaunchKernelGGL((gla_fold_kernel<64, 64>), dim3(units * ((64 * 64 + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, st, P);
+        break;
+    case 128:
+        hipLaunchKernelGGL((gla_fold_kernel<128, 128>),
+                           dim3(units * ((128 * 128 + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, P);
+        break;
+    default: return GLA_EUNSUPPORTED;
+    }
+    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
+}
+
 int launch_fwd(const Params& P, int dtype, int d, int chunk, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
+    if (dtype == GLA_F16 && d == 128 && chunk == 64) return launch_wide(P, stream);
     if (dtype == GLA_F16) return run_dim<_Float16>(P, d, chunk, st);
     if (dtype == GLA_F32) return run_dim<float>(P, d, chunk, st);
     return GLA_EUNSUPPORTED;

@@ -40,6 +40,13 @@ struct Params {
 // when nseg == 1) on `stream`.  Returns a gla_status value.
 int launch_fwd(const Params& P, int dtype, int d, int chunk, void* stream);
 
+// Fold pass alone: turns the segment aggregates in P.ws into incoming states.
+int launch_fold(const Params& P, int d, void* stream);
+
+// Aggregate, fold and output passes of the d = 128 binary16 chunk-64 path
+// (8-wavefront kernels; the fold pass when nseg > 1).
+int launch_wide(const Params& P, void* stream);
+
 // Single-pass kernel (binary16, d = 64, chunk 64): one launch.
 int launch_onepass(const Params& P, void* stream);
 

@@ -366,38 +366,43 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         __syncthreads();  // (2) operands of every wave
 
         // ---- M1 partial scores over this wave's 32 channels, tiles j <= si
+        //      (j < si off the diagonal; the diagonal tile separately)
         const bool wide_i = (sMisc[4 + si] | sMisc[4 + si + 4]) != 0;
         float4v part[NSUB];
 #pragma unroll
-        for (int j = 0; j < NSUB; ++j) {
+        for (int j = 0; j < NSUB - 1; ++j) {
             part[j] = float4v{0.f, 0.f, 0.f, 0.f};
-            if (j > si) continue;
+            if (j >= si) continue;
             const half8 ek = *(const half8*)(sE + (16 * j + l16) * SH + c0);
-            if (j < si) {
-                const half8 qf = (j == si - 1) ? qa : (j == si - 2) ? qo1 : qo2;
-                part[j] = mma(ek, qf, part[j]);
-            } else if (!wide_i) {
-                const half8 ekl = *(const half8*)(sEL + (16 * j + l16) * SH + c0);
-                part[j] = mma(ek, qd_h, part[j]);
-                part[j] = mma(ekl, qd_h, part[j]);
-                part[j] = mma(ek, qd_l, part[j]);
-            } else {
-                // exact pairwise over this wave's channels: q_t k_s 2^{bl_t - bl_s}
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int sl = 4 * g + e;
-                    float acc = 0.f;
-                    if (sl <= l16) {
-                        const int ts = 16 * si + sl;
-                        for (int cc = 32 * h; cc < 32 * h + 32; ++cc)
-                            acc += (float)sFQ[tl * SH + cc] * (float)sFK[ts * SH + cc] *
-                                   exp2_fast(sFB[tl * SF + cc] - sFB[ts * SF + cc]);
-                    }
-                    part[j][e] = acc;
-                }
-            }
+            const half8 qf = (j == si - 1) ? qa : (j == si - 2) ? qo1 : qo2;
+            part[j] = mma(ek, qf, part[j]);
             *(float4v*)(sPA + ((wave * NSUB + j) * 64 + lane) * 4) = part[j];
         }
+        float4v pd = float4v{0.f, 0.f, 0.f, 0.f};
+        if (!wide_i) {
+            const half8 ek = *(const half8*)(sE + tl * SH + c0);
+            const half8 ekl = *(const half8*)(sEL + tl * SH + c0);
+            pd = mma(ek, qd_h, pd);
+            pd = mma(ekl, qd_h, pd);
+            pd = mma(ek, qd_l, pd);
+        } else {
+            // exact pairwise over this wave's channels: q_t k_s 2^{bl_t - bl_s}
+            // (rare: a sub-chunk whose decay span is too wide for binary16)
+#pragma unroll 1
+            for (int e = 0; e < 4; ++e) {
+                const int sl = 4 * g + e;
+                float acc = 0.f;
+                if (sl <= l16) {
+                    const int ts = 16 * si + sl;
+#pragma unroll 1
+                    for (int cc = 32 * h; cc < 32 * h + 32; ++cc)
+                        acc += (float)sFQ[tl * SH + cc] * (float)sFK[ts * SH + cc] *
+                               exp2_fast(sFB[tl * SF + cc] - sFB[ts * SF + cc]);
+                }
+                pd[e] = acc;
+            }
+        }
+        *(float4v*)(sPA + ((wave * NSUB + si) * 64 + lane) * 4) = pd;
         __syncthreads();  // (3) partial scores of both halves
         float4v at[NSUB];
 #pragma unroll
@@ -405,8 +410,10 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             at[j] = float4v{0.f, 0.f, 0.f, 0.f};
             if (j > si) continue;
             const float4v other = *(const float4v*)(sPA + (((wave ^ 4) * NSUB + j) * 64 + lane) * 4);
-            at[j] = part[j] + other;
-            if (j == si) {
+            if (j < si) {
+                at[j] = part[j] + other;
+            } else {
+                at[j] = pd + other;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (4 * g + e > l16) at[j][e] = 0.f;

@@ -87,10 +87,14 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     }
     if (!plan->onepass) {
         if (o->algorithm == GLA_ALGO_SINGLE_PASS) return GLA_EUNSUPPORTED;
-        // Three passes: segments of seg_chunks chunks, enough workgroups for the chip.
+        // Three passes: segments of seg_chunks chunks, enough workgroups for
+        // the chip (the d = 128 binary16 chunk-64 kernels hold one workgroup
+        // per compute unit: three full rounds).
+        const bool wide = o->dtype == GLA_F16 && o->dk == 128 && chunk == 64;
+        const int64_t target = wide ? 3 * kCUs : kTargetGroups;
         int seg = o->segment_chunks;
         if (seg <= 0) {
-            const int64_t want = (units * nchunks + kTargetGroups - 1) / kTargetGroups;
+            const int64_t want = (units * nchunks + target - 1) / target;
             seg = (int)(want < 1 ? 1 : want);
         }
         if (seg > nchunks) seg = nchunks;

@@ -205,3 +205,37 @@ def test_first_scanned_token_rms_conditioning(torch):
     x = make_inputs(1, 6, 40, 40, 64, 64, "f16", (0.0, 1.0), True, seed=131)
     for d in DIRS:
         _check("first-token", x, d, 40, 40, 64, "f16", torch)
+
+
+# ---------------------------------------------------------------- d = 128 path
+
+@pytest.mark.parametrize("seg", [1, 2, 3, 1000])
+def test_d128_segment_split_invariance(torch, seg):
+    """d = 128 binary16 chunk 64 (aggregate, fold and output passes of the
+    8-wavefront kernels) for several segment lengths, gated, every direction."""
+    x = make_inputs(1, 3, 20, 30, 128, 128, "f16", (1.0, 1.0), True, seed=151)
+    for d in DIRS:
+        _check(f"d128-seg{seg}", x, d, 20, 30, 64, "f16", torch, segment_chunks=seg)
+
+
+@pytest.mark.parametrize("H,W", [(7, 9), (1, 1), (3, 200), (65, 1)])
+def test_d128_ragged_grids(torch, H, W):
+    """d = 128 tail chunks and tiny grids, ungated; unwritten rows stay NaN."""
+    x = make_inputs(1, 2, H, W, 128, 128, "f16", (0.0, 1.0), False, seed=157 + H * W)
+    for d in DIRS:
+        _check(f"d128-grid{H}x{W}", x, d, H, W, 64, "f16", torch, segment_chunks=2,
+               out=torch.full((1, H * W, 2, 128), float("nan"), dtype=torch.float16, device="cuda"))
+
+
+@pytest.mark.parametrize("zval,label", [(40.0, "gamma=1"), (-1000.0, "gamma->0"), (None, "wide")])
+def test_d128_extreme_gates(torch, zval, label):
+    """d = 128 with gamma == 1, gamma -> 0 (pairwise diagonal blocks) and logits
+    ~ N(0, 8) mixing both regimes."""
+    x = make_inputs(1, 2, 16, 20, 128, 128, "f16", (0.0, 1.0), True, seed=163)
+    if zval is None:
+        rng = np.random.default_rng(7)
+        x["z"] = (8.0 * rng.standard_normal(x["z"].shape)).astype(np.float32)
+    else:
+        x["z"] = np.full_like(x["z"], zval)
+    for d in DIRS:
+        _check(f"d128-{label}", x, d, 16, 20, 64, "f16", torch, segment_chunks=2)
