@@ -63,6 +63,72 @@ def load_traffic(workload, calls_per_step):
     return rec.get("hbm_bytes_per_call")
 
 
+def kernel_label(spec, chunk):
+    """The kernels one call launches (the plan picks the single pass for
+    binary16, d = 64, 64-token chunks; the three passes otherwise)."""
+    if spec["dtype"] == "f16" and spec["dk"] == 64 and chunk == 64:
+        return "gla_onepass_kernel (single pass: one launch per call)"
+    if spec["dtype"] == "f16" and spec["dk"] == 128 and chunk == 64:
+        return ("gla_wide_kernel<aggregate> + gla_fold_kernel + gla_wide_kernel<output> "
+                "(three launches per call)")
+    return "gla_chunk_kernel<aggregate> + gla_fold_kernel + gla_chunk_kernel<output>"
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size (src -> dst, `mib` MiB each way), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 4}), flush=True)
+
+
+def traffic_from_pmc(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, copy_bytes,
+                     kernel_substr):
+    """HBM bytes per call of one workload from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by the same
+    counter's reading for a plain copy of `copy_bytes` bytes; written to
+    profiles/traffic_<workload>.json with the kernel source hash."""
+    import csv
+
+    def per_kernel(path, substr):
+        """Counter sum per dispatch, averaged per kernel name."""
+        tot = {}
+        for row in csv.DictReader(open(path)):
+            name = row["Kernel_Name"]
+            if substr in name and "init" not in name:
+                key = (name, row["Dispatch_Id"])
+                tot[key] = tot.get(key, 0.0) + float(row["Counter_Value"])
+        names = {}
+        for (name, _), v in tot.items():
+            names.setdefault(name, []).append(v)
+        return {n: sum(v) / len(v) for n, v in names.items()}, len(tot)
+
+    cf, _ = per_kernel(calib_fetch_csv, "copy")
+    cw, _ = per_kernel(calib_write_csv, "copy")
+    fetch_factor = max(cf.values()) * 1024.0 / copy_bytes
+    write_factor = max(cw.values()) * 1024.0 / copy_bytes
+    kf, nd = per_kernel(fetch_csv, kernel_substr)
+    kw, _ = per_kernel(write_csv, kernel_substr)
+    # one call = one dispatch of every kernel name of the call
+    fetch = sum(kf.values()) * 1024.0 / fetch_factor
+    write = sum(kw.values()) * 1024.0 / write_factor
+    rec = {"workload": workload, "kernel": kernel_substr, "kernel_source_hash": kernel_source_hash(),
+           "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4),
+           "hbm_fetch_bytes_per_call": round(fetch), "hbm_write_bytes_per_call": round(write),
+           "hbm_bytes_per_call": round(fetch + write), "dispatches": nd,
+           "kernels": sorted(kf)}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(spec, name, seconds):
     import numpy as np  # noqa: F401
 
@@ -112,7 +178,22 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run only a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_MIB"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc counter files")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        f, w, cf, cw, mib = args.traffic_from
+        spec = WORKLOADS[args.workload]
+        sub = "gla::"
+        traffic_from_pmc(args.workload, f, w, cf, cw, int(mib) << 20, sub)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -215,8 +296,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "gla_fwd call (aggregate + fold + output passes; output pass "
-                          "only when the scan is one segment)",
+                "kernel": kernel_label(spec, chunk),
                 "algorithmic_bytes_per_call": bytes_call,
                 "mfma_frac": round(flops_call / (us_call * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 5)}
 

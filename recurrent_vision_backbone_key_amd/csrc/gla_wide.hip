@@ -60,6 +60,11 @@ constexpr int F1 = 3;   // 2^{tot_{i-1}}              query factor for key sub-c
 constexpr int F2 = 4;   // 2^{tot_{i-1} + tot_{i-2}}  query factor for key sub-chunk i-3
 constexpr int NFAC = 5;
 constexpr int NPA = 10; // partial score tiles exchanged per chunk
+// The state enters the inter-chunk product as binary16 hi + lo parts.
+#ifndef GLA_WIDE_STATE_LO
+#define GLA_WIDE_STATE_LO 0
+#endif
+constexpr bool kStateLo = GLA_WIDE_STATE_LO;
 
 // LDS layout (bytes)
 constexpr int L_E = 0;                          // E hi            [C][SH] f16
@@ -124,28 +129,39 @@ struct Raw {
     u32x4 q[2], k[2], v[2], r[2], z[4];
 };
 
-template <bool AGG>
-__device__ __forceinline__ void load_raw(Raw& x, const Params& P, int row, int cb, bool gated)
+enum Part { PZ, PK, PQ, PV, PR };
+
+// One input of one token (the lane's 16 channels), zero past the end.
+template <int PART>
+__device__ __forceinline__ void load_part(Raw& x, const Params& P, int row, int cb)
 {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        x.q[kb] = x.k[kb] = x.v[kb] = x.r[kb] = zero;
-        x.z[2 * kb] = x.z[2 * kb + 1] = zero;
-    }
-    if (row < 0) return;
-    const size_t o = (size_t)row * D + cb;
+    const size_t o = (size_t)(row < 0 ? 0 : row) * D + cb;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const size_t oo = o + 32 * kb;
-        x.k[kb] = *(const u32x4*)((const _Float16*)P.k + oo);
-        x.v[kb] = *(const u32x4*)((const _Float16*)P.v + oo);
-        x.z[2 * kb] = *(const u32x4*)(P.z + oo);
-        x.z[2 * kb + 1] = *(const u32x4*)(P.z + oo + 4);
-        if (!AGG) {
-            x.q[kb] = *(const u32x4*)((const _Float16*)P.q + oo);
-            if (gated) x.r[kb] = *(const u32x4*)((const _Float16*)P.r + oo);
+        if (PART == PZ) {
+            x.z[2 * kb] = row < 0 ? zero : *(const u32x4*)(P.z + oo);
+            x.z[2 * kb + 1] = row < 0 ? zero : *(const u32x4*)(P.z + oo + 4);
         }
+        if (PART == PK) x.k[kb] = row < 0 ? zero : *(const u32x4*)((const _Float16*)P.k + oo);
+        if (PART == PQ) x.q[kb] = row < 0 ? zero : *(const u32x4*)((const _Float16*)P.q + oo);
+        if (PART == PV) x.v[kb] = row < 0 ? zero : *(const u32x4*)((const _Float16*)P.v + oo);
+        if (PART == PR) x.r[kb] = row < 0 ? zero : *(const u32x4*)((const _Float16*)P.r + oo);
+    }
+}
+
+template <bool AGG>
+__device__ __forceinline__ void load_raw(Raw& x, const Params& P, int row, int cb, bool gated)
+{
+    load_part<PZ>(x, P, row, cb);
+    load_part<PK>(x, P, row, cb);
+    load_part<PV>(x, P, row, cb);
+    if (!AGG) {
+        load_part<PQ>(x, P, row, cb);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        x.r[0] = x.r[1] = zero;
+        if (gated) load_part<PR>(x, P, row, cb);
     }
 }
 
@@ -397,8 +413,11 @@ __global__ __launch_bounds__(NT) void gla_wide_kernel(Params P)
         const int myrow = sRows[buf * C + tl];
         __syncthreads();  // (2) operands of every wave
 
-        // prefetch the next chunk (its row table was written after (1))
-        if (c + 1 < c_end) load_raw<AGG>(raw, P, sRows[(buf ^ 1) * C + tl], cb, gated);
+        // the next chunk's inputs (row table written after (1)) are fetched in
+        // parts spread over this chunk, so the loads stream while it computes
+        const bool pf = (c + 1 < c_end);
+        const int nrow = pf ? sRows[(buf ^ 1) * C + tl] : -1;
+        if (pf) load_part<PZ>(raw, P, nrow, cb);
 
         // value fragments, shared by the value product and the state update:
         // lane (g, l16) holds v[32p + 8g + e][16 wave + l16]
@@ -444,6 +463,7 @@ __global__ __launch_bounds__(NT) void gla_wide_kernel(Params P)
                     if (j < si) *(float4v*)(sPA + ((4 + tri + j) * 64 + lane) * 4) = part[j];
             }
 
+            if (pf) load_part<PK>(raw, P, nrow, cb);
             // ================= state role: inter-chunk term =================
             // o^T[16 wave + 4g + e][16 i + l16] = sum_c S[c][dv] (q (.) 2^b)[t][c]
 #pragma unroll
@@ -467,11 +487,12 @@ __global__ __launch_bounds__(NT) void gla_wide_kernel(Params P)
                         const half4 b1 = *(const half4*)(qrow + 16);
                         const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
                         o[i] = mma(ah, bq, o[i]);
-                        o[i] = mma(al, bq, o[i]);
+                        if (kStateLo) o[i] = mma(al, bq, o[i]);
                     }
                 }
             }
             __syncthreads();  // (3) partial scores
+            if (pf) load_part<PQ>(raw, P, nrow, cb);
 
             // ---- row role: full scores of sub-chunk si into the score matrix
             if (h == 0) {
@@ -497,6 +518,7 @@ __global__ __launch_bounds__(NT) void gla_wide_kernel(Params P)
                 *(half4*)(sAL + tl * SAL + 4 * g) = lo;
             }
             __syncthreads();  // (4) scores
+            if (pf) load_part<PV>(raw, P, nrow, cb);
 
             // ================= state role: scores times values =================
 #pragma unroll
@@ -524,8 +546,10 @@ __global__ __launch_bounds__(NT) void gla_wide_kernel(Params P)
         }
 
         // ================= state role: S = Diag(2^{chunk total}) S + k-hat^T v =================
+        if (AGG && pf) load_part<PK>(raw, P, nrow, cb);
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
+            if (AGG && pf && a == 4) load_part<PV>(raw, P, nrow, cb);
             const float4v dec = *(const float4v*)(sDec + 16 * a + 4 * g);
             S[a] = S[a] * dec;
 #pragma unroll
@@ -535,6 +559,7 @@ __global__ __launch_bounds__(NT) void gla_wide_kernel(Params P)
 
         if (!AGG) {
             if (gated) __syncthreads();  // (5) sums of squares
+            if (pf && gated) load_part<PR>(raw, P, nrow, cb);
             // epilogue, part 2: u = SiLU(r) (.) w (.) o / rms(o), staged over r
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
