@@ -104,14 +104,27 @@ __device__ __forceinline__ void st_u(unsigned* p, unsigned v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_x(const float* p)
+// Bulk exchange data moves 16 bytes per lane through buffer instructions with
+// the same cache policy (sc1) that the compiler gives the relaxed agent-scope
+// atomics above; the buffer's record count bounds every access.
+constexpr int kSC1 = 16;  // cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const float* base, unsigned bytes)
 {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void st_x(float* p, float v)
+__device__ __forceinline__ float4v ld_x4(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSC1));
 }
+__device__ __forceinline__ float ld_x1(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kSC1));
+}
+__device__ __forceinline__ void st_x4(__amdgpu_buffer_rsrc_t r, unsigned off, float4v v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kSC1);
+}
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -534,10 +547,18 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         __syncthreads();
         const bool last = (seg == P.nseg - 1);
         unsigned* flags = P.flags + (size_t)unit * P.nseg;
+        // this thread's 8 state entries: rows ch0 = tid / 16 and ch0 + 32,
+        // columns 4 (tid % 16) .. +3 (16 contiguous bytes in each row)
+        const int ch0 = tid >> 4, cl0 = 4 * (tid & 15);
+        const unsigned off0 = 16u * tid, off1 = off0 + 16u * NT;  // bytes
+        const float4v l0 = *(const float4v*)(sL + ch0 * D + cl0);
+        const float4v l1 = *(const float4v*)(sL + (ch0 + 32) * D + cl0);
+        const unsigned agg_bytes = (unsigned)(aggf * 4), st_bytes = (unsigned)(D * D * 4);
         if (seg > 0 && !last) {
-            float* dst = P.agg + slot * aggf;
-            for (int i = tid; i < D * D; i += NT) st_x(dst + i, sL[i]);
-            if (tid < D) st_x(dst + D * D + tid, sG[tid]);
+            const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
+            st_x4(r, off0, l0);
+            st_x4(r, off1, l1);
+            if (tid < D / 4) st_x4(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
             wait_mem();
             __syncthreads();
             if (tid == 0) st_u(flags + seg, 1u);
@@ -569,48 +590,62 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             __syncthreads();
             const int k = sMisc[1];
             // forward fold from the inclusive state of segment k
-            constexpr int EPT = D * D / NT;  // state entries per thread
-            const float* inc = P.incl + ((size_t)unit * P.nseg + (k < 0 ? 0 : k)) * D * D;
-            float sv[EPT];
-#pragma unroll
-            for (int u = 0; u < EPT; ++u) sv[u] = (k >= 0) ? ld_x(inc + tid + u * NT) : 0.f;
+            float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+            if (k >= 0) {
+                const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + ((size_t)unit * P.nseg + k) * D * D, st_bytes);
+                s0 = ld_x4(r, off0);
+                s1 = ld_x4(r, off1);
+            }
             constexpr int FW = 8;  // aggregates per round of loads
             for (int sg0 = k + 1; sg0 < seg; sg0 += FW) {
                 // issue the loads of up to FW aggregates, then fold them in order
-                float lv[FW][EPT], gv[FW][EPT];
+                float4v a0[FW], a1[FW];
+                float g0[FW], g1[FW];
 #pragma unroll
                 for (int b = 0; b < FW; ++b) {
                     const int sg = min(sg0 + b, seg - 1);
-                    const float* ag = P.agg + ((size_t)unit * P.nseg + sg) * aggf;
-#pragma unroll
-                    for (int u = 0; u < EPT; ++u) {
-                        lv[b][u] = ld_x(ag + tid + u * NT);
-                        gv[b][u] = ld_x(ag + D * D + (tid + u * NT) / D);
-                    }
+                    const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + ((size_t)unit * P.nseg + sg) * aggf, agg_bytes);
+                    a0[b] = ld_x4(r, off0);
+                    a1[b] = ld_x4(r, off1);
+                    g0[b] = ld_x1(r, st_bytes + 4u * ch0);
+                    g1[b] = ld_x1(r, st_bytes + 4u * (ch0 + 32));
                 }
 #pragma unroll
                 for (int b = 0; b < FW; ++b)
                     if (sg0 + b < seg) {
 #pragma unroll
-                        for (int u = 0; u < EPT; ++u) sv[u] = fold_step(gv[b][u], sv[u], lv[b][u]);
+                        for (int e = 0; e < 4; ++e) {
+                            s0[e] = fold_step(g0[b], s0[e], a0[b][e]);
+                            s1[e] = fold_step(g1[b], s1[e], a1[b][e]);
+                        }
                     }
             }
+            // S_in^T (hi, lo) for phase 3; inclusive state for successors
 #pragma unroll
-            for (int u = 0; u < EPT; ++u) {
-                const int i = tid + u * NT;
-                const int chn = i / D;
-                const float s = sv[u];
-                // S_in^T (hi, lo) for phase 3; inclusive state for successors
-                const int dv = i - chn * D;
-                const _Float16 hs = (_Float16)s;
-                sST[dv * SH + chn] = hs;
-                sSTL[dv * SH + chn] = (_Float16)(s - (float)hs);
-                if (!last) st_x(P.incl + slot * D * D + i, fold_step(sG[chn], s, sL[i]));
+            for (int e = 0; e < 4; ++e) {
+                const _Float16 h0 = (_Float16)s0[e], h1 = (_Float16)s1[e];
+                sST[(cl0 + e) * SH + ch0] = h0;
+                sSTL[(cl0 + e) * SH + ch0] = (_Float16)(s0[e] - (float)h0);
+                sST[(cl0 + e) * SH + ch0 + 32] = h1;
+                sSTL[(cl0 + e) * SH + ch0 + 32] = (_Float16)(s1[e] - (float)h1);
+            }
+            if (!last) {
+                const float gm0 = sG[ch0], gm1 = sG[ch0 + 32];
+                float4v i0, i1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    i0[e] = fold_step(gm0, s0[e], l0[e]);
+                    i1[e] = fold_step(gm1, s1[e], l1[e]);
+                }
+                const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * D * D, st_bytes);
+                st_x4(r, off0, i0);
+                st_x4(r, off1, i1);
             }
         } else {
             // first segment: its local state is the inclusive state
-            float* dst = P.incl + slot * D * D;
-            for (int i = tid; i < D * D; i += NT) st_x(dst + i, sL[i]);
+            const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * D * D, st_bytes);
+            st_x4(r, off0, l0);
+            st_x4(r, off1, l1);
         }
         if (!last) {
             wait_mem();
