@@ -176,6 +176,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0: enough to exceed 2x MALL)")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--steps-per-graph", type=int, default=0,
+                    help="steps captured in one HIP graph (0: 10, or 1 for steps over 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -251,6 +253,16 @@ def main():
                     norm_weight=x["w"], eps=1e-6, out=out, segment_chunks=args.segment_chunks,
                     workspace=ws)
 
+    # Steps are replayed from HIP graphs of G consecutive steps each (a replay
+    # has a fixed cost of about 15 us on this platform, so several steps share
+    # one); graph r holds steps on input sets r*G .. r*G+G-1 (mod rotate).
+    G = 1
+    if not args.no_graph:
+        G = args.steps_per_graph or (1 if big else 10)
+        G = math.gcd(G, steps) if steps > 0 else 1
+        G = math.gcd(G, warmup) if warmup > 0 else G
+    # enough graphs that the input sets cycle without repeating back to back
+    n_graphs = rotate // math.gcd(rotate, G)
     stream = torch.cuda.current_stream()
     graphs = None
     if not args.no_graph:
@@ -262,28 +274,30 @@ def main():
         stream.wait_stream(side)
         torch.cuda.synchronize()
         graphs = []
-        for r in range(rotate):
+        for gi in range(n_graphs):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(r)
+                for j in range(G):
+                    step((gi * G + j) % rotate)
             graphs.append(g)
         torch.cuda.synchronize()
 
     def run(i):
+        # i counts graph replays (G steps each) or single eager steps
         if graphs is not None:
-            graphs[i % rotate].replay()
+            graphs[i % n_graphs].replay()
         else:
             step(i % rotate)
 
-    for i in range(warmup):
+    for i in range(warmup // G):
         run(i)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
-    for i in range(steps):
-        run(warmup + i)
+    for i in range(steps // G):
+        run(warmup // G + i)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
@@ -310,6 +324,7 @@ def main():
                    "dirs": ",".join("L2R R2L T2B B2T".split()[d] for d in dirs),
                    "gated": gated, "calls_per_step": calls_per_step,
                    "input_sets": rotate, "hip_graph": graphs is not None,
+                   "steps_per_graph": G,
                    "workspace_bytes_per_call": nseg_bytes, "accumulate": "f32"},
         "roofline": roofline,
         "cpu_baseline": None,

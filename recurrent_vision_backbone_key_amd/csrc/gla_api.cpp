@@ -35,6 +35,8 @@ extern "C" int gla_fwd(const void* q, const void* k, const void* v, const float*
     P.inv_tau = 1.0f / plan.tau;
     P.eps = plan.eps;
     P.ticket = P.err = P.done = P.flags = nullptr;
+    P.xcd_local = plan.xcd_local;
+    P.xcd_tasks = plan.xcd_tasks;
     P.agg = P.incl = nullptr;
     if (plan.onepass) {
         char* ws = (char*)opts->workspace;

@@ -21,7 +21,7 @@ struct Params {
     float* ws;          // three-pass: segment slots [units][nseg-1][DK*DV + DK] fp32
     // single-pass exchange (workspace): ticket and error word, one flag per
     // (scan, segment), segment aggregates and inclusive states
-    unsigned* ticket;
+    unsigned* ticket;   // word 0: ticket counter; words 16 (1 + x): counter of XCD x
     unsigned* err;
     unsigned* done;     // [units]: workgroups of the scan past their look-back
     unsigned* flags;    // [units][nseg]: 0 none, 1 aggregate, 2 inclusive
@@ -31,6 +31,8 @@ struct Params {
     int nchunks;        // ceil(L / chunk)
     int seg_chunks;     // chunks per segment
     int nseg;           // segments per scan
+    int xcd_local;      // single pass: scan u runs on XCD u mod 8 (exchange in that L2)
+    int xcd_tasks;      // single pass, xcd_local: workgroups per XCD (grid / 8)
     float scale;        // output scale
     float inv_tau;      // 1 / tau
     float eps;          // RMSNorm epsilon

@@ -104,26 +104,55 @@ __device__ __forceinline__ void st_u(unsigned* p, unsigned v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Bulk exchange data moves 16 bytes per lane through buffer instructions with
-// the same cache policy (sc1) that the compiler gives the relaxed agent-scope
-// atomics above; the buffer's record count bounds every access.
-constexpr int kSC1 = 16;  // cache-policy operand: sc1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const float* base, unsigned bytes)
+// Bulk exchange data moves 16 bytes per lane through buffer instructions whose
+// record count bounds every access.  Loads always use sc1, which misses the
+// CU's L1 and reads the XCD's L2 (or memory).  Stores: when the workgroups of
+// a scan may run on different XCDs, sc1 as well (write-through to memory: the
+// policy the compiler gives the relaxed agent-scope atomics above, coherent
+// across the per-XCD L2s); when every workgroup of a scan runs on one XCD
+// (LOCAL), the default policy, which leaves the line in that XCD's L2 where
+// the sc1 loads of the same XCD find it (about half the round-trip latency).
+template <bool LOCAL> struct Pol {
+    static constexpr int kLoad = 16;
+    static constexpr int kStore = LOCAL ? 0 : 16;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const void* base, unsigned bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+template <bool LOCAL>
 __device__ __forceinline__ float4v ld_x4(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
-    return __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSC1));
+    return __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, Pol<LOCAL>::kLoad));
 }
+template <bool LOCAL>
 __device__ __forceinline__ float ld_x1(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kSC1));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, Pol<LOCAL>::kLoad));
 }
+template <bool LOCAL>
 __device__ __forceinline__ void st_x4(__amdgpu_buffer_rsrc_t r, unsigned off, float4v v)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kSC1);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, Pol<LOCAL>::kStore);
 }
+// Segment flags of one scan (0 none, 1 aggregate, 2 inclusive state).
+template <bool LOCAL>
+__device__ __forceinline__ unsigned ld_flag(const unsigned* flags, int nseg, int i)
+{
+    if (!LOCAL) return ld_u(flags + i);
+    return (unsigned)__builtin_amdgcn_raw_buffer_load_b32(xrsrc(flags, 4u * nseg), 4 * i, 0, Pol<LOCAL>::kLoad);
+}
+template <bool LOCAL>
+__device__ __forceinline__ void st_flag(unsigned* flags, int nseg, int i, unsigned v)
+{
+    if (!LOCAL) {
+        st_u(flags + i, v);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(v, xrsrc(flags, 4u * nseg), 4 * i, 0, Pol<LOCAL>::kStore);
+    }
+}
+// Hardware register XCC_ID: bits 3:0 hold the XCD that runs this workgroup.
+constexpr int kXccIdReg = 20 | (0 << 6) | ((4 - 1) << 11);
 
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
@@ -178,6 +207,7 @@ __device__ __forceinline__ void load_raw(Raw& r, const Params& P, int row, int c
     }
 }
 
+template <bool LOCAL>
 __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 {
     __shared__ __attribute__((aligned(16))) char lds[LDS_TOTAL];
@@ -210,20 +240,44 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     const int nunits = P.B * P.NH;
     const int grid = nunits * P.nseg;
 
-    // ---- ticket: logical (segment, scan) in start order
+    // ---- ticket: logical (segment, scan) in start order.  LOCAL: scan u runs
+    //      on XCD u mod 8; the workgroups of an XCD number their tasks with the
+    //      XCD's own counter (the grid gives every XCD the same count).
     if (tid == 0) {
-        const unsigned t = atomicAdd(P.ticket, 1u);
-        if (t == (unsigned)grid - 1u) st_u(P.ticket, 0u);  // every ticket is taken
-        sMisc[0] = (int)t;
+        if (LOCAL) {
+            const unsigned x = __builtin_amdgcn_s_getreg(kXccIdReg) & 7u;
+            unsigned* ctr = P.ticket + 16 * (1 + x);
+            const unsigned t = atomicAdd(ctr, 1u);
+            if (t == (unsigned)P.xcd_tasks - 1u) st_u(ctr, 0u);  // every ticket is taken
+            sMisc[0] = (int)t;
+            sMisc[2] = (int)x;
+        } else {
+            const unsigned t = atomicAdd(P.ticket, 1u);
+            if (t == (unsigned)grid - 1u) st_u(P.ticket, 0u);  // every ticket is taken
+            sMisc[0] = (int)t;
+        }
     }
     __syncthreads();
     const int ticket = sMisc[0];
-    if (ticket >= grid) {  // workspace not initialised: report, do nothing
-        if (tid == 0) atomicOr(P.err, 2u);
-        return;
+    int seg, unit;
+    if (LOCAL) {
+        const int x = sMisc[2];
+        if (ticket >= P.xcd_tasks) {  // workspace not initialised: report, do nothing
+            if (tid == 0) atomicOr(P.err, 2u);
+            return;
+        }
+        const int units_x = (nunits - x + 7) / 8;  // scans x, x + 8, ... run here
+        if (ticket >= units_x * P.nseg) return;     // spare workgroup of this XCD
+        seg = ticket / units_x;
+        unit = x + 8 * (ticket - seg * units_x);
+    } else {
+        if (ticket >= grid) {  // workspace not initialised: report, do nothing
+            if (tid == 0) atomicOr(P.err, 2u);
+            return;
+        }
+        seg = ticket / nunits;
+        unit = ticket - seg * nunits;
     }
-    const int seg = ticket / nunits;
-    const int unit = ticket - seg * nunits;
     const int c_begin = seg * P.seg_chunks;
     const int nch = min(P.nchunks, c_begin + P.seg_chunks) - c_begin;
     const bool gated = (P.r != nullptr);
@@ -556,12 +610,12 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         const unsigned agg_bytes = (unsigned)(aggf * 4), st_bytes = (unsigned)(D * D * 4);
         if (seg > 0 && !last) {
             const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
-            st_x4(r, off0, l0);
-            st_x4(r, off1, l1);
-            if (tid < D / 4) st_x4(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
+            st_x4<LOCAL>(r, off0, l0);
+            st_x4<LOCAL>(r, off1, l1);
+            if (tid < D / 4) st_x4<LOCAL>(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
             wait_mem();
             __syncthreads();
-            if (tid == 0) st_u(flags + seg, 1u);
+            if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 1u);
         }
         if (need_in) {
             // look back: wait until every earlier segment has published, then
@@ -571,7 +625,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 int k = -1;
                 for (;;) {
                     const int idx = seg - 1 - lane;
-                    const unsigned f = (idx >= 0) ? ld_u(flags + idx) : 2u;
+                    const unsigned f = (idx >= 0) ? ld_flag<LOCAL>(flags, P.nseg, idx) : 2u;
                     if (__all(f >= 1u)) {
                         const unsigned long long inc = __ballot(idx >= 0 && f == 2u);
                         // lowest lane with an inclusive state = latest segment
@@ -593,8 +647,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
             if (k >= 0) {
                 const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + ((size_t)unit * P.nseg + k) * D * D, st_bytes);
-                s0 = ld_x4(r, off0);
-                s1 = ld_x4(r, off1);
+                s0 = ld_x4<LOCAL>(r, off0);
+                s1 = ld_x4<LOCAL>(r, off1);
             }
             constexpr int FW = 8;  // aggregates per round of loads
             for (int sg0 = k + 1; sg0 < seg; sg0 += FW) {
@@ -605,10 +659,10 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 for (int b = 0; b < FW; ++b) {
                     const int sg = min(sg0 + b, seg - 1);
                     const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + ((size_t)unit * P.nseg + sg) * aggf, agg_bytes);
-                    a0[b] = ld_x4(r, off0);
-                    a1[b] = ld_x4(r, off1);
-                    g0[b] = ld_x1(r, st_bytes + 4u * ch0);
-                    g1[b] = ld_x1(r, st_bytes + 4u * (ch0 + 32));
+                    a0[b] = ld_x4<LOCAL>(r, off0);
+                    a1[b] = ld_x4<LOCAL>(r, off1);
+                    g0[b] = ld_x1<LOCAL>(r, st_bytes + 4u * ch0);
+                    g1[b] = ld_x1<LOCAL>(r, st_bytes + 4u * (ch0 + 32));
                 }
 #pragma unroll
                 for (int b = 0; b < FW; ++b)
@@ -638,25 +692,25 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                     i1[e] = fold_step(gm1, s1[e], l1[e]);
                 }
                 const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * D * D, st_bytes);
-                st_x4(r, off0, i0);
-                st_x4(r, off1, i1);
+                st_x4<LOCAL>(r, off0, i0);
+                st_x4<LOCAL>(r, off1, i1);
             }
         } else {
             // first segment: its local state is the inclusive state
             const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * D * D, st_bytes);
-            st_x4(r, off0, l0);
-            st_x4(r, off1, l1);
+            st_x4<LOCAL>(r, off0, l0);
+            st_x4<LOCAL>(r, off1, l1);
         }
         if (!last) {
             wait_mem();
             __syncthreads();
-            if (tid == 0) st_u(flags + seg, 2u);
+            if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 2u);
         }
         // the last workgroup of this scan to get here clears its flags
         if (tid == 0) {
             const unsigned done = atomicAdd(P.done + unit, 1u);
             if (done == (unsigned)P.nseg - 1u) {
-                for (int s = 0; s < P.nseg; ++s) st_u(flags + s, 0u);
+                for (int s = 0; s < P.nseg; ++s) st_flag<LOCAL>(flags, P.nseg, s, 0u);
                 st_u(P.done + unit, 0u);
             }
         }
@@ -767,8 +821,13 @@ __global__ __launch_bounds__(256) void gla_onepass_init(unsigned* words, size_t 
 int launch_onepass(const Params& P, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
-    const int grid = P.B * P.NH * P.nseg;
-    hipLaunchKernelGGL(onepass::gla_onepass_kernel, dim3(grid), dim3(onepass::NT), 0, st, P);
+    if (P.xcd_local) {
+        hipLaunchKernelGGL(onepass::gla_onepass_kernel<true>, dim3(8 * P.xcd_tasks), dim3(onepass::NT),
+                           0, st, P);
+    } else {
+        hipLaunchKernelGGL(onepass::gla_onepass_kernel<false>, dim3(P.B * P.NH * P.nseg),
+                           dim3(onepass::NT), 0, st, P);
+    }
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
 }
 

@@ -12,6 +12,11 @@
 namespace {
 
 constexpr int kCUs = 256;          // compute units of one MI355X
+constexpr int kXcds = 8;           // accelerator dies (XCDs), each with its own L2
+constexpr int kCUsPerXcd = kCUs / kXcds;
+// Single-pass workspace header: word 0 ticket counter, word 1 error word,
+// word 16 (1 + x) ticket counter of XCD x.
+constexpr size_t kOnePassHeader = 1024;
 constexpr int kTargetGroups = 2 * kCUs;
 
 bool is_pow2_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -60,25 +65,39 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
 
     // Single pass: binary16, d = 64, 64-token chunks; segments of at most
     // kOnePassMaxChunks chunks, at most 65 segments per scan (one wavefront
-    // of look-back), about one workgroup per compute unit.
+    // of look-back), about one workgroup per compute unit.  When the scans
+    // spread over the 8 XCDs without costing a second round of workgroups on
+    // any of them (or divide evenly), scan u runs on XCD u mod 8 and the
+    // segment exchange stays in that XCD's L2.
     const bool sp_shape = o->dtype == GLA_F16 && o->dk == 64 && o->dv == 64 && chunk == 64;
+    plan->xcd_local = 0;
+    plan->xcd_tasks = 0;
     if (o->algorithm != GLA_ALGO_THREE_PASS && sp_shape) {
         const int min_seg = (nchunks + 64) / 65;
+        const int64_t upx = (units + kXcds - 1) / kXcds;  // scans per XCD (most)
+        auto clamp_seg = [&](int64_t want) {
+            int sg = (int)(want < 1 ? 1 : want);
+            if (sg > gla::kOnePassMaxChunks) sg = gla::kOnePassMaxChunks;
+            if (sg < min_seg) sg = min_seg;
+            if (sg > nchunks) sg = nchunks;
+            return sg;
+        };
         int seg = o->segment_chunks;
-        if (seg <= 0) {
-            const int64_t want = (units * nchunks + kCUs - 1) / kCUs;
-            seg = (int)(want < 1 ? 1 : want);
-            if (seg > gla::kOnePassMaxChunks) seg = gla::kOnePassMaxChunks;
-            if (seg < min_seg) seg = min_seg;
-        }
         if (seg > nchunks) seg = nchunks;
+        const int seg_local =
+            seg > 0 ? seg : clamp_seg((upx * nchunks + kCUsPerXcd - 1) / kCUsPerXcd);
+        const int64_t tasks = upx * ((nchunks + seg_local - 1) / seg_local);
+        const bool local = tasks <= kCUsPerXcd || units % kXcds == 0;
+        if (seg <= 0) seg = local ? seg_local : clamp_seg((units * nchunks + kCUs - 1) / kCUs);
         if (seg >= min_seg && seg <= gla::kOnePassMaxChunks) {
             const int nseg = (nchunks + seg - 1) / seg;
             const size_t nflag = (size_t)units * nseg;
             plan->onepass = 1;
             plan->seg_chunks = seg;
             plan->nseg = nseg;
-            plan->off_done = 256;
+            plan->xcd_local = local ? 1 : 0;
+            plan->xcd_tasks = local ? (int)(upx * nseg) : 0;
+            plan->off_done = kOnePassHeader;
             plan->off_flags = plan->off_done + (((size_t)units * 4 + 255) / 256) * 256;
             plan->off_agg = plan->off_flags + ((nflag * 4 + 255) / 256) * 256;
             plan->off_incl = plan->off_agg + nflag * ((size_t)64 * 64 + 64) * 4;

@@ -12,6 +12,8 @@ extern "C" {
 typedef struct gla_plan {
     int L, nchunks, seg_chunks, nseg;
     int onepass;                 // 1: single-pass kernel, 0: three passes
+    int xcd_local;               // single pass: every scan on one XCD (u mod 8)
+    int xcd_tasks;               // single pass, xcd_local: workgroups per XCD
     size_t workspace_bytes;
     size_t off_done, off_flags, off_agg, off_incl;  // single-pass workspace layout (bytes)
     float tau, scale, eps;

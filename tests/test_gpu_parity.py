@@ -113,6 +113,16 @@ def test_segment_split_invariance_single_pass(torch, seg):
         _check(f"sp-seg{seg}", x, d, 24, 40, 64, "f16", torch, segment_chunks=seg, algorithm=1)
 
 
+@pytest.mark.parametrize("B,NH,H,W,seg", [(3, 4, 30, 40, 1), (1, 6, 40, 40, 1), (2, 8, 16, 40, 2)])
+def test_single_pass_xcd_placement(torch, B, NH, H, W, seg):
+    """Scans spread over XCDs (12 scans x 19 segments: exchange coherent across
+    XCDs) and scans pinned to one XCD each (6 and 16 scans: exchange in that
+    XCD's L2, spare workgroups on the XCDs without a scan)."""
+    x = make_inputs(B, NH, H, W, 64, 64, "f16", (0.0, 1.0), True, seed=149 + B * NH)
+    for d in DIRS:
+        _check(f"sp-xcd{B}x{NH}", x, d, H, W, 64, "f16", torch, segment_chunks=seg, algorithm=1)
+
+
 def test_single_pass_long_scan_many_segments(torch):
     """A 100x100 grid (157 chunks) in 2-chunk segments: 79 segments per scan is
     over the look-back window, so the plan falls back to three passes; 3-chunk
