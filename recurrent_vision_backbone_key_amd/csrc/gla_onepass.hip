@@ -55,6 +55,11 @@ constexpr int NSUB = 4;   // 16-token sub-chunks per chunk
 constexpr int NCH = kOnePassMaxChunks;  // chunks per segment (upper bound)
 constexpr int SH = D + 8; // binary16 row stride (elements): 144-byte rows
 constexpr int SF = D + 4; // fp32 row stride (elements): 272-byte rows
+// The incoming state of a segment enters its outputs as binary16 hi + lo.
+#ifndef GLA_ONEPASS_IN_LO
+#define GLA_ONEPASS_IN_LO 0
+#endif
+constexpr bool kInLo = GLA_ONEPASS_IN_LO;
 // Per-wave factor table rows (sub-chunk i of the wave, 32 channels of its half):
 constexpr int FD = 0;     // 2^{-tot_i}                 diagonal query factor (>= 1)
 constexpr int FQ = 1;     // 2^{R_i}                    q (.) 2^b for the local inter-chunk term
@@ -564,20 +569,21 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         }
     }
 
-    // r rows of every chunk: loads issued now, in flight during the exchange
-    constexpr int RPT = (NCH * C * 8 + NT - 1) / NT;  // 16-byte pieces per thread
-    u32x4 rreg[RPT];
-    if (gated) {
+    // r of every chunk at this lane's output positions (token tl, value
+    // channels 32h + 16m + 4g .. +3): loads issued now, in flight during the
+    // exchange
+    half4 rreg[NCH][2];
 #pragma unroll
-        for (int p = 0; p < RPT; ++p) {
-            const int idx = tid + p * NT;
-            const int row = idx >> 3, piece = idx & 7;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (row < nch * C) {
-                const int t = sRows[row];
-                if (t >= 0) val = *(const u32x4*)((const char*)P.r + (size_t)t * D * 2 + piece * 16);
+    for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) rreg[cc][m] = half4{0, 0, 0, 0};
+        if (gated && cc < nch) {
+            const int t = sRows[cc * C + tl];
+            if (t >= 0) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    rreg[cc][m] = *(const half4*)((const _Float16*)P.r + (size_t)t * D + 32 * h + 16 * m + 4 * g);
             }
-            rreg[p] = val;
         }
     }
 
@@ -679,9 +685,9 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             for (int e = 0; e < 4; ++e) {
                 const _Float16 h0 = (_Float16)s0[e], h1 = (_Float16)s1[e];
                 sST[(cl0 + e) * SH + ch0] = h0;
-                sSTL[(cl0 + e) * SH + ch0] = (_Float16)(s0[e] - (float)h0);
+                if (kInLo) sSTL[(cl0 + e) * SH + ch0] = (_Float16)(s0[e] - (float)h0);
                 sST[(cl0 + e) * SH + ch0 + 32] = h1;
-                sSTL[(cl0 + e) * SH + ch0 + 32] = (_Float16)(s1[e] - (float)h1);
+                if (kInLo) sSTL[(cl0 + e) * SH + ch0 + 32] = (_Float16)(s1[e] - (float)h1);
             }
             if (!last) {
                 const float gm0 = sG[ch0], gm1 = sG[ch0 + 32];
@@ -736,13 +742,15 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 const int k0 = 32 * kb + 8 * g;
                 const half8 qf = *(const half8*)(sOut + (cc * C + tl) * SH + k0);
                 const half8 h0 = *(const half8*)(sST + (32 * h + l16) * SH + k0);
-                const half8 l0 = *(const half8*)(sSTL + (32 * h + l16) * SH + k0);
                 const half8 h1 = *(const half8*)(sST + (32 * h + 16 + l16) * SH + k0);
-                const half8 l1 = *(const half8*)(sSTL + (32 * h + 16 + l16) * SH + k0);
                 o0 = mma(h0, qf, o0);
-                o0 = mma(l0, qf, o0);
                 o1 = mma(h1, qf, o1);
-                o1 = mma(l1, qf, o1);
+                if (kInLo) {
+                    const half8 l0 = *(const half8*)(sSTL + (32 * h + l16) * SH + k0);
+                    const half8 l1 = *(const half8*)(sSTL + (32 * h + 16 + l16) * SH + k0);
+                    o0 = mma(l0, qf, o0);
+                    o1 = mma(l1, qf, o1);
+                }
             }
         }
         okeep[cc][0] = o0 * P.scale;
@@ -757,23 +765,15 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             if (g == 0) sSS[(cc * 2 + h) * C + tl] = ss;
         }
     }
-    __syncthreads();
-    if (gated) {
-        // r rows into the staging area (the epilogue overwrites them in place)
-#pragma unroll
-        for (int p = 0; p < RPT; ++p) {
-            const int idx = tid + p * NT;
-            const int row = idx >> 3, piece = idx & 7;
-            if (row < nch * C) *(u32x4*)((char*)(sOut + row * SH) + piece * 16) = rreg[p];
-        }
-        __syncthreads();
-    }
+    if (gated) __syncthreads();  // sums of squares of both value halves
     float wv[2][4];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             wv[m][e] = (gated && P.w) ? P.w[32 * h + 16 * m + 4 * g + e] : 1.f;
+    // epilogue and stores straight from the output fragments: 8 bytes per lane
+    // and value block (the two halves' stores of a row meet in the L2)
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
         if (cc >= nch) break;
@@ -782,30 +782,20 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             const float ss = sSS[(cc * 2) * C + tl] + sSS[(cc * 2 + 1) * C + tl];
             inv = rsq_fast(ss * (1.0f / D) + P.eps);
         }
-        _Float16* orow = sOut + (cc * C + tl) * SH + 32 * h;
+        const int t = sRows[cc * C + tl];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             half4 hv;
             if (gated) {
-                const half4 rv = *(const half4*)(orow + 16 * m + 4 * g);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    hv[e] = (_Float16)(silu((float)rv[e]) * wv[m][e] * okeep[cc][m][e] * inv);
+                    hv[e] = (_Float16)(silu((float)rreg[cc][m][e]) * wv[m][e] * okeep[cc][m][e] * inv);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) hv[e] = (_Float16)okeep[cc][m][e];
             }
-            *(half4*)(orow + 16 * m + 4 * g) = hv;
+            if (t >= 0) *(half4*)((_Float16*)P.out + (size_t)t * D + 32 * h + 16 * m + 4 * g) = hv;
         }
-    }
-    __syncthreads();
-    // coalesced row stores: 8 pieces of 16 bytes per row
-    for (int idx = tid; idx < nch * C * 8; idx += NT) {
-        const int row = idx >> 3, piece = idx & 7;
-        const int t = sRows[row];
-        if (t >= 0)
-            *(u32x4*)((char*)P.out + (size_t)t * D * 2 + piece * 16) =
-                *(const u32x4*)((const char*)(sOut + row * SH) + piece * 16);
     }
 }
 
