@@ -84,6 +84,20 @@ constexpr int L_MISC = L_ROWS + 2 * C * 4;      // wide flags      [NW] i32
 constexpr int LDS_TOTAL = L_MISC + 64;
 static_assert(LDS_TOTAL <= kLdsLimit, "LDS budget of one CU exceeded");
 
+// The aggregate pass uses only k-hat, v and the gate tables: its own compact
+// layout lets two of its workgroups share a CU.
+template <bool AGG> struct Lay {
+    static constexpr int KH = AGG ? 0 : L_KH;
+    static constexpr int V = AGG ? C * SH * 2 : L_V;
+    static constexpr int FAC = AGG ? V + C * SH * 2 : L_FAC;
+    static constexpr int TOT = AGG ? FAC + NW * NFAC * 64 * 4 : L_TOT;
+    static constexpr int DEC = AGG ? TOT + NSUB * D * 4 : L_DEC;
+    static constexpr int ROWS = AGG ? DEC + D * 4 : L_ROWS;
+    static constexpr int MISC = AGG ? ROWS + 2 * C * 4 : L_MISC;
+    static constexpr int TOTAL = AGG ? MISC + 64 : LDS_TOTAL;
+};
+static_assert(2 * Lay<true>::TOTAL <= kLdsLimit, "two aggregate workgroups must share a CU");
+
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
@@ -217,24 +231,31 @@ __device__ __forceinline__ float4v diag_pairwise(const Params& P, int row, int c
     return res;
 }
 
+// Aggregate pass: at most 128 VGPRs (four waves per SIMD) and the compact LDS
+// layout, so two workgroups share a CU.  Output pass: one workgroup per CU
+// (LDS), up to 256 VGPRs.
 template <bool AGG>
-__global__ __launch_bounds__(NT) void gla_wide_kernel(Params P)
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(AGG ? 4 : 2, AGG ? 4 : 2)))
+void gla_wide_kernel(Params P)
 {
-    __shared__ __attribute__((aligned(16))) char lds[LDS_TOTAL];
-    _Float16* sE = (_Float16*)(lds + L_E);
-    _Float16* sQH = (_Float16*)(lds + L_QH);
-    _Float16* sKH = (_Float16*)(lds + L_KH);
-    _Float16* sV = (_Float16*)(lds + L_V);
-    _Float16* sR = (_Float16*)(lds + L_R);
-    float* sPA = (float*)(lds + L_PA);
-    _Float16* sA = (_Float16*)(lds + L_A);
-    _Float16* sAL = (_Float16*)(lds + L_AL);
-    float* sFac = (float*)(lds + L_FAC);
-    float* sTot = (float*)(lds + L_TOT);
-    float* sDec = (float*)(lds + L_DEC);
-    float* sSS = (float*)(lds + L_SS);
-    int* sRows = (int*)(lds + L_ROWS);
-    int* sMisc = (int*)(lds + L_MISC);
+    typedef Lay<AGG> LY;
+    __shared__ __attribute__((aligned(16))) char lds[LY::TOTAL];
+    // buffers of the output pass only (not touched by the aggregate pass)
+    _Float16* sE = (_Float16*)(lds + (AGG ? 0 : L_E));
+    _Float16* sQH = (_Float16*)(lds + (AGG ? 0 : L_QH));
+    _Float16* sR = (_Float16*)(lds + (AGG ? 0 : L_R));
+    float* sPA = (float*)(lds + (AGG ? 0 : L_PA));
+    _Float16* sA = (_Float16*)(lds + (AGG ? 0 : L_A));
+    _Float16* sAL = (_Float16*)(lds + (AGG ? 0 : L_AL));
+    float* sSS = (float*)(lds + (AGG ? 0 : L_SS));
+    // buffers of both passes
+    _Float16* sKH = (_Float16*)(lds + LY::KH);
+    _Float16* sV = (_Float16*)(lds + LY::V);
+    float* sFac = (float*)(lds + LY::FAC);
+    float* sTot = (float*)(lds + LY::TOT);
+    float* sDec = (float*)(lds + LY::DEC);
+    int* sRows = (int*)(lds + LY::ROWS);
+    int* sMisc = (int*)(lds + LY::MISC);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
