@@ -180,6 +180,8 @@ def main():
                     help="steps captured in one HIP graph (0: 10, or 1 for steps over 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every length/batch sweep point (one JSON line each)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=5, default=None,
@@ -195,6 +197,14 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.sweep:
+        from recurrent_vision_backbone_key_amd.inputs import SWEEP
+        for name in SWEEP:
+            cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--no-cpu",
+                   "--steps", str(args.steps or 100), "--warmup", str(args.warmup or 20)]
+            import subprocess
+            subprocess.run(cmd, check=True)
         return
 
     if args.gpus != 1:

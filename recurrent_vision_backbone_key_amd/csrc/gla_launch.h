@@ -7,7 +7,7 @@
 namespace gla {
 
 // Largest segment (in chunks) the single-pass kernel keeps on chip.
-constexpr int kOnePassMaxChunks = 5;
+constexpr int kOnePassMaxChunks = 7;
 
 // Arguments of one forward call, already validated.
 struct Params {

@@ -75,20 +75,25 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     if (o->algorithm != GLA_ALGO_THREE_PASS && sp_shape) {
         const int min_seg = (nchunks + 64) / 65;
         const int64_t upx = (units + kXcds - 1) / kXcds;  // scans per XCD (most)
-        auto clamp_seg = [&](int64_t want) {
-            int sg = (int)(want < 1 ? 1 : want);
-            if (sg > gla::kOnePassMaxChunks) sg = gla::kOnePassMaxChunks;
-            if (sg < min_seg) sg = min_seg;
-            if (sg > nchunks) sg = nchunks;
-            return sg;
+        const int max_seg = nchunks < gla::kOnePassMaxChunks ? nchunks : gla::kOnePassMaxChunks;
+        // the shortest segment whose workgroups fit in `slots` at `per` scans
+        // (the longest allowed when none does)
+        auto fit_seg = [&](int64_t per, int64_t slots) {
+            for (int sg = min_seg; sg <= max_seg; ++sg)
+                if (per * ((nchunks + sg - 1) / sg) <= slots) return sg;
+            return max_seg;
         };
+        const int seg_g = fit_seg(units, kCUs);
+        const int seg_l = fit_seg(upx, kCUsPerXcd);
         int seg = o->segment_chunks;
         if (seg > nchunks) seg = nchunks;
-        const int seg_local =
-            seg > 0 ? seg : clamp_seg((upx * nchunks + kCUsPerXcd - 1) / kCUsPerXcd);
-        const int64_t tasks = upx * ((nchunks + seg_local - 1) / seg_local);
-        const bool local = tasks <= kCUsPerXcd || units % kXcds == 0;
-        if (seg <= 0) seg = local ? seg_local : clamp_seg((units * nchunks + kCUs - 1) / kCUs);
+        // XCD-local when it keeps segments as short as the chip-wide plan and
+        // either fits one round per XCD or the scans divide evenly over XCDs
+        const int seg_chk = seg > 0 ? seg : seg_l;
+        const int64_t tasks = upx * ((nchunks + seg_chk - 1) / seg_chk);
+        const bool local = (seg > 0 || seg_l <= seg_g) &&
+                           (tasks <= kCUsPerXcd || units % kXcds == 0);
+        if (seg <= 0) seg = local ? seg_l : seg_g;
         if (seg >= min_seg && seg <= gla::kOnePassMaxChunks) {
             const int nseg = (nchunks + seg - 1) / seg;
             const size_t nflag = (size_t)units * nseg;

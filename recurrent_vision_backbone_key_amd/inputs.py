@@ -31,6 +31,18 @@ WORKLOADS = {
                            z=(2.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T) * 3, gated=True),
 }
 
+# Length and batch sweep at the pages' own kernel points (16x16 = 256 tokens,
+# the 1.6K frame, 128x128 = 16.4K tokens) at d = 64 with 6 heads, plus a tail
+# grid (42x42 = 1764 tokens, not a multiple of the 64-token chunk); the four
+# directions per step, ungated as in the pages' kernel comparison.
+SWEEP = {}
+for _i, (_h, _w, _b) in enumerate(((16, 16, 1), (16, 16, 8), (40, 40, 1), (40, 40, 8),
+                                   (42, 42, 1), (42, 42, 8), (128, 128, 1), (128, 128, 8))):
+    SWEEP[f"sweep{_h}x{_w}_b{_b}"] = dict(index=10 + _i, B=_b, NH=6, H=_h, W=_w, dk=64, dv=64,
+                                          dtype="f16", z=(0.0, 1.0), chunk=64,
+                                          dirs=(L2R, R2L, T2B, B2T), gated=False)
+WORKLOADS.update(SWEEP)
+
 EPS = 1e-6
 TAU = 16.0
 

@@ -84,6 +84,16 @@ def test_stack16k_gated_sampled_units(torch, call):
            units=(u0, u0 + 2))
 
 
+@pytest.mark.parametrize("name", ["sweep16x16_b8", "sweep42x42_b1", "sweep128x128_b1"])
+def test_sweep_points(torch, name):
+    """The length/batch sweep points (256, 1764 and 16384 tokens at d = 64,
+    6 heads), every direction, against the oracle over all scans."""
+    s = WORKLOADS[name]
+    for d in DIRS:
+        x = workload_inputs(name, call=d)
+        _check(name, x, d, s["H"], s["W"], s["chunk"], "f16", torch)
+
+
 # ---------------------------------------------------------------- invariances
 
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128])
@@ -104,7 +114,7 @@ def test_segment_split_invariance_three_pass(torch, seg):
         _check(f"seg{seg}", x, d, 24, 40, 64, "f16", torch, segment_chunks=seg, algorithm=2)
 
 
-@pytest.mark.parametrize("seg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("seg", [1, 2, 3, 4, 5, 6, 7])
 def test_segment_split_invariance_single_pass(torch, seg):
     """Single pass with every segment length it supports (look-back over up to
     15 segments per scan, ragged last segment)."""
