@@ -76,6 +76,30 @@ __device__ __forceinline__ float log2_sigmoid(float z)
     return m - __builtin_amdgcn_logf(1.0f + e);
 }
 
+// x from the lane N places lower in the same 16-lane row (0 for the first N).
+template <int N>
+__device__ __forceinline__ float row_shr(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
+}
+
+// Inclusive prefix sums along the 16 lanes of each row for M independent
+// values, stage by stage (Hillis-Steele): the M shifted adds of a stage are
+// independent, so the DPP hazards of one value overlap the others.
+template <int M>
+__device__ __forceinline__ void row_scan_n(float (&x)[M])
+{
+#pragma unroll
+    for (int i = 0; i < M; ++i) x[i] += row_shr<1>(x[i]);
+#pragma unroll
+    for (int i = 0; i < M; ++i) x[i] += row_shr<2>(x[i]);
+#pragma unroll
+    for (int i = 0; i < M; ++i) x[i] += row_shr<4>(x[i]);
+#pragma unroll
+    for (int i = 0; i < M; ++i) x[i] += row_shr<8>(x[i]);
+}
+
 // Hardware reciprocal and reciprocal square root (about 1 ulp).
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float rsq_fast(float x) { return __builtin_amdgcn_rsqf(x); }

@@ -176,24 +176,6 @@ __device__ __forceinline__ void ld8f(const float* p, float (&x)[N])
     for (int i = 0; i < N; ++i) x[i] = p[i];
 }
 
-// x from the lane N places lower in the same 16-lane row (0 for the first N).
-template <int N>
-__device__ __forceinline__ float row_shr(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
-}
-
-// Inclusive prefix sum along the 16 lanes of each row (Hillis-Steele).
-__device__ __forceinline__ float row_scan(float x)
-{
-    x += row_shr<1>(x);
-    x += row_shr<2>(x);
-    x += row_shr<4>(x);
-    x += row_shr<8>(x);
-    return x;
-}
-
 struct Raw {
     u32x4 q, k, v, z0, z1;  // 8 channels of one token (q, k, v binary16; z binary32)
 };
@@ -332,8 +314,9 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         for (int e = 0; e < 8; ++e) {
             float a = log2_sigmoid(zv[e]) * P.inv_tau;
             a = (a < kMinLog2Decay) ? kMinLog2Decay : a;
-            bl[e] = row_scan(valid ? a : 0.f);
+            bl[e] = valid ? a : 0.f;
         }
+        row_scan_n(bl);
         if (l16 == 15) {
             *(float4v*)(sTot + si * D + c0) = float4v{bl[0], bl[1], bl[2], bl[3]};
             *(float4v*)(sTot + si * D + c0 + 4) = float4v{bl[4], bl[5], bl[6], bl[7]};

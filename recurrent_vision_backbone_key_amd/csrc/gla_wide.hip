@@ -120,24 +120,6 @@ __device__ __forceinline__ half8 tr_frag(const _Float16* base, int row0, int col
     return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// x from the lane N places lower in the same 16-lane row (0 for the first N).
-template <int N>
-__device__ __forceinline__ float row_shr(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
-}
-
-// Inclusive prefix sum along the 16 lanes of each row (Hillis-Steele).
-__device__ __forceinline__ float row_scan(float x)
-{
-    x += row_shr<1>(x);
-    x += row_shr<2>(x);
-    x += row_shr<4>(x);
-    x += row_shr<8>(x);
-    return x;
-}
-
 // Inputs of one token for the lane's 16 channels cb + {0..7} and cb + 32 + {0..7}.
 struct Raw {
     u32x4 q[2], k[2], v[2], r[2], z[4];
@@ -188,8 +170,9 @@ __device__ __forceinline__ void gate_prefix(const Raw& x, float inv_tau, bool va
         const float4v zz = __builtin_bit_cast(float4v, x.z[j >> 2]);
         float a = log2_sigmoid(zz[j & 3]) * inv_tau;
         a = (a < kMinLog2Decay) ? kMinLog2Decay : a;
-        bl[j] = row_scan(valid ? a : 0.f);
+        bl[j] = valid ? a : 0.f;
     }
+    row_scan_n(bl);
 }
 
 // Exact diagonal block over the wave's 64 channels, pairwise in fp32:
