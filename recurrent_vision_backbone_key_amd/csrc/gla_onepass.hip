@@ -194,6 +194,113 @@ __device__ __forceinline__ void load_raw(Raw& r, const Params& P, int row, int c
     }
 }
 
+// Intra-chunk scores (M1, with the exchange of the two channel halves) and
+// scores times values (M2) for query sub-chunk SI: a compile-time sub-chunk
+// keeps every tile selection out of the control flow, so no register array is
+// merged across branches.
+template <int SI>
+__device__ __forceinline__ void scores_values(const Params& P, const _Float16* sE, const _Float16* sEL,
+                                              const _Float16* sVT, float* sPA, const int* sMisc,
+                                              const _Float16* sFQ, const _Float16* sFK, const float* sFB,
+                                              int wave, int lane, int g, int l16, int h, int c0, int tl,
+                                              const half8& qa, const half8& qo1, const half8& qo2,
+                                              const half8& qd_h, const half8& qd_l, float4v (&o)[2])
+{
+    // ---- M1 partial scores over this wave's 32 channels, tiles j <= SI
+    //      (j < SI off the diagonal; the diagonal tile separately)
+    const bool wide_i = (sMisc[4 + SI] | sMisc[4 + SI + 4]) != 0;
+    float4v part[NSUB];
+#pragma unroll
+    for (int j = 0; j < NSUB - 1; ++j) {
+        part[j] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (j >= SI) continue;
+        const half8 ek = *(const half8*)(sE + (16 * j + l16) * SH + c0);
+        const half8 qf = (j == SI - 1) ? qa : (j == SI - 2) ? qo1 : qo2;
+        part[j] = mma(ek, qf, part[j]);
+        *(float4v*)(sPA + ((wave * NSUB + j) * 64 + lane) * 4) = part[j];
+    }
+    float4v pd = float4v{0.f, 0.f, 0.f, 0.f};
+    if (!wide_i) {
+        const half8 ek = *(const half8*)(sE + tl * SH + c0);
+        const half8 ekl = *(const half8*)(sEL + tl * SH + c0);
+        pd = mma(ek, qd_h, pd);
+        pd = mma(ekl, qd_h, pd);
+        pd = mma(ek, qd_l, pd);
+    } else {
+        // exact pairwise over this wave's channels: q_t k_s 2^{bl_t - bl_s}
+        // (rare: a sub-chunk whose decay span is too wide for binary16)
+#pragma unroll 1
+        for (int e = 0; e < 4; ++e) {
+            const int sl = 4 * g + e;
+            float acc = 0.f;
+            if (sl <= l16) {
+                const int ts = 16 * SI + sl;
+#pragma unroll 1
+                for (int cc = 32 * h; cc < 32 * h + 32; ++cc)
+                    acc += (float)sFQ[tl * SH + cc] * (float)sFK[ts * SH + cc] *
+                           exp2_fast(sFB[tl * SF + cc] - sFB[ts * SF + cc]);
+            }
+            pd[e] = acc;
+        }
+    }
+    *(float4v*)(sPA + ((wave * NSUB + SI) * 64 + lane) * 4) = pd;
+    __syncthreads();  // (3) partial scores of both halves
+    float4v at[NSUB];
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+        at[j] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (j > SI) continue;
+        const float4v other = *(const float4v*)(sPA + (((wave ^ 4) * NSUB + j) * 64 + lane) * 4);
+        if (j < SI) {
+            at[j] = part[j] + other;
+        } else {
+            at[j] = pd + other;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * g + e > l16) at[j][e] = 0.f;
+        }
+    }
+
+    // ---- M2: O^T[dv][t] += V^T A^T, this wave's 32 value channels
+    o[0] = o[1] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NSUB / 2; ++p) {
+        if (2 * p > SI) continue;
+        const bool hi = (2 * p + 1 <= SI);
+        half8 bfr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bfr[e] = (_Float16)at[2 * p][e];
+            bfr[4 + e] = hi ? (_Float16)at[2 * p + 1][e] : (_Float16)0.f;
+        }
+        half8 blo = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (2 * p == SI) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) blo[e] = lo_part(at[2 * p][e]);
+        }
+        if (2 * p + 1 == SI) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) blo[4 + e] = lo_part(at[2 * p + 1][e]);
+        }
+        const bool has_diag = (2 * p == SI) || (2 * p + 1 == SI);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const _Float16* vrow = sVT + (32 * h + 16 * m + l16) * SH;
+            const half4 v0 = *(const half4*)(vrow + 32 * p + 4 * g);
+            half4 v1 = {0, 0, 0, 0};
+            if (hi) v1 = *(const half4*)(vrow + 32 * p + 16 + 4 * g);
+            half8 afr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                afr[e] = v0[e];
+                afr[4 + e] = v1[e];
+            }
+            o[m] = mma(afr, bfr, o[m]);
+            if (has_diag) o[m] = mma(afr, blo, o[m]);
+        }
+    }
+}
+
 template <bool LOCAL>
 __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 {
@@ -420,99 +527,12 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         }
         __syncthreads();  // (2) operands of every wave
 
-        // ---- M1 partial scores over this wave's 32 channels, tiles j <= si
-        //      (j < si off the diagonal; the diagonal tile separately)
-        const bool wide_i = (sMisc[4 + si] | sMisc[4 + si + 4]) != 0;
-        float4v part[NSUB];
-#pragma unroll
-        for (int j = 0; j < NSUB - 1; ++j) {
-            part[j] = float4v{0.f, 0.f, 0.f, 0.f};
-            if (j >= si) continue;
-            const half8 ek = *(const half8*)(sE + (16 * j + l16) * SH + c0);
-            const half8 qf = (j == si - 1) ? qa : (j == si - 2) ? qo1 : qo2;
-            part[j] = mma(ek, qf, part[j]);
-            *(float4v*)(sPA + ((wave * NSUB + j) * 64 + lane) * 4) = part[j];
-        }
-        float4v pd = float4v{0.f, 0.f, 0.f, 0.f};
-        if (!wide_i) {
-            const half8 ek = *(const half8*)(sE + tl * SH + c0);
-            const half8 ekl = *(const half8*)(sEL + tl * SH + c0);
-            pd = mma(ek, qd_h, pd);
-            pd = mma(ekl, qd_h, pd);
-            pd = mma(ek, qd_l, pd);
-        } else {
-            // exact pairwise over this wave's channels: q_t k_s 2^{bl_t - bl_s}
-            // (rare: a sub-chunk whose decay span is too wide for binary16)
-#pragma unroll 1
-            for (int e = 0; e < 4; ++e) {
-                const int sl = 4 * g + e;
-                float acc = 0.f;
-                if (sl <= l16) {
-                    const int ts = 16 * si + sl;
-#pragma unroll 1
-                    for (int cc = 32 * h; cc < 32 * h + 32; ++cc)
-                        acc += (float)sFQ[tl * SH + cc] * (float)sFK[ts * SH + cc] *
-                               exp2_fast(sFB[tl * SF + cc] - sFB[ts * SF + cc]);
-                }
-                pd[e] = acc;
-            }
-        }
-        *(float4v*)(sPA + ((wave * NSUB + si) * 64 + lane) * 4) = pd;
-        __syncthreads();  // (3) partial scores of both halves
-        float4v at[NSUB];
-#pragma unroll
-        for (int j = 0; j < NSUB; ++j) {
-            at[j] = float4v{0.f, 0.f, 0.f, 0.f};
-            if (j > si) continue;
-            const float4v other = *(const float4v*)(sPA + (((wave ^ 4) * NSUB + j) * 64 + lane) * 4);
-            if (j < si) {
-                at[j] = part[j] + other;
-            } else {
-                at[j] = pd + other;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * g + e > l16) at[j][e] = 0.f;
-            }
-        }
-
-        // ---- M2: O^T[dv][t] += V^T A^T, this wave's 32 value channels
         float4v o[2];
-        o[0] = o[1] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < NSUB / 2; ++p) {
-            if (2 * p > si) continue;
-            const bool hi = (2 * p + 1 <= si);
-            half8 bfr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bfr[e] = (_Float16)at[2 * p][e];
-                bfr[4 + e] = hi ? (_Float16)at[2 * p + 1][e] : (_Float16)0.f;
-            }
-            half8 blo = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (2 * p == si) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) blo[e] = lo_part(at[2 * p][e]);
-            }
-            if (2 * p + 1 == si) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) blo[4 + e] = lo_part(at[2 * p + 1][e]);
-            }
-            const bool has_diag = (2 * p == si) || (2 * p + 1 == si);
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const _Float16* vrow = sVT + (32 * h + 16 * m + l16) * SH;
-                const half4 v0 = *(const half4*)(vrow + 32 * p + 4 * g);
-                half4 v1 = {0, 0, 0, 0};
-                if (hi) v1 = *(const half4*)(vrow + 32 * p + 16 + 4 * g);
-                half8 afr;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    afr[e] = v0[e];
-                    afr[4 + e] = v1[e];
-                }
-                o[m] = mma(afr, bfr, o[m]);
-                if (has_diag) o[m] = mma(afr, blo, o[m]);
-            }
+        switch (si) {
+        case 0: scores_values<0>(P, sE, sEL, sVT, sPA, sMisc, sFQ, sFK, sFB, wave, lane, g, l16, h, c0, tl, qa, qo1, qo2, qd_h, qd_l, o); break;
+        case 1: scores_values<1>(P, sE, sEL, sVT, sPA, sMisc, sFQ, sFK, sFB, wave, lane, g, l16, h, c0, tl, qa, qo1, qo2, qd_h, qd_l, o); break;
+        case 2: scores_values<2>(P, sE, sEL, sVT, sPA, sMisc, sFQ, sFK, sFB, wave, lane, g, l16, h, c0, tl, qa, qo1, qo2, qd_h, qd_l, o); break;
+        default: scores_values<3>(P, sE, sEL, sVT, sPA, sMisc, sFQ, sFK, sFB, wave, lane, g, l16, h, c0, tl, qa, qo1, qo2, qd_h, qd_l, o); break;
         }
         // ---- M3: O^T += S_loc^T (q (.) 2^b)^T, local state from the segment start
         if (c > 0) {
