@@ -259,3 +259,89 @@ def test_d128_extreme_gates(torch, zval, label):
         x["z"] = np.full_like(x["z"], zval)
     for d in DIRS:
         _check(f"d128-{label}", x, d, 16, 20, 64, "f16", torch, segment_chunks=2)
+
+
+# ---------------------------------------------------------------- runtime behaviour
+
+def _dev(x, torch):
+    from parity import to_dev
+    return {n: to_dev(x[n], torch) for n in ("q", "k", "v", "z", "r", "w")}
+
+
+@pytest.mark.parametrize("B,NH,H,W,d", [(2, 6, 24, 40, 64), (1, 2, 16, 20, 128), (1, 2, 9, 11, 32)])
+def test_graph_replays_match_eager(torch, B, NH, H, W, d):
+    """A call captured in a HIP graph and replayed several times, with eager
+    work and synchronisations between replays, gives the eager result bit for
+    bit every time (single pass, d = 128 three passes, generic three passes)."""
+    from recurrent_vision_backbone_key_amd import gla
+    x = make_inputs(B, NH, H, W, d, d, "f16", (0.0, 1.0), True, seed=171 + d)
+    t = _dev(x, torch)
+    opts = gla.make_opts(B, NH, d, d, gla.F16)
+    ws = gla.new_workspace(2, H, W, 64, opts, "cuda")
+    kw = dict(r=t["r"], norm_weight=t["w"], workspace=ws)
+    eager = gla.fwd(t["q"], t["k"], t["v"], t["z"], 2, H, W, **kw).clone()
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gla.fwd(t["q"], t["k"], t["v"], t["z"], 2, H, W, out=out, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gla.fwd(t["q"], t["k"], t["v"], t["z"], 2, H, W, out=out, **kw)
+    for i in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager call"
+        # eager work on the same workspace between replays
+        gla.fwd(t["q"], t["k"], t["v"], t["z"], 1, H, W, **kw)
+        torch.cuda.synchronize()
+    if ws is not None and gla.workspace_size(2, H, W, 64, opts) and d == 64:
+        assert int(ws[4:8].cpu().numpy().view(np.uint32)[0]) == 0
+
+
+def test_workspace_reused_across_shapes(torch):
+    """One workspace (cleared once) serves a sequence of single-pass calls with
+    different grids, batch sizes and segment plans; every result matches the
+    oracle and the error word stays clear."""
+    from recurrent_vision_backbone_key_amd import gla
+    shapes = [(1, 6, 40, 40), (2, 3, 17, 23), (4, 4, 30, 40), (1, 6, 40, 40), (3, 2, 64, 9)]
+    need = 0
+    for B, NH, H, W in shapes:
+        for d in DIRS:
+            need = max(need, gla.workspace_size(d, H, W, 64, gla.make_opts(B, NH, 64, 64, gla.F16)))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (B, NH, H, W) in enumerate(shapes):
+        x = make_inputs(B, NH, H, W, 64, 64, "f16", (0.5, 1.0), True, seed=181 + i)
+        t = _dev(x, torch)
+        d = DIRS[i % 4]
+        print(f"[case] reuse {i}: B={B} NH={NH} {H}x{W} dir={d}", flush=True)
+        got = gla.fwd(t["q"], t["k"], t["v"], t["z"], d, H, W, r=t["r"], norm_weight=t["w"],
+                      workspace=ws).cpu().numpy()
+        torch.cuda.synchronize()
+        ref = run_oracle(x, d, H, W)
+        assert rel_err(got, ref) <= TOL["f16"]
+        assert int(ws[4:8].cpu().numpy().view(np.uint32)[0]) == 0
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_non_finite_gate_logits_propagate(torch, d):
+    """A NaN gate logit makes the outputs that depend on it NaN (as in the
+    oracle), +inf gives gamma = 1 and -inf gamma -> 0; rows before the NaN in
+    scan order stay finite and match the oracle."""
+    x = make_inputs(1, 2, 8, 12, d, d, "f16", (0.0, 1.0), False, seed=191 + d)
+    L = 8 * 12
+    x["z"][0, 30, 0, 5] = np.nan
+    x["z"][0, 10, 1, :] = np.inf
+    x["z"][0, 50, 1, 7] = -np.inf
+    got = run_gpu(x, 0, 8, 12, 64, torch)
+    ref = run_oracle(x, 0, 8, 12)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), "NaN pattern differs from the oracle"
+    fin = ~nan_ref
+    assert np.all(np.isfinite(got[fin]))
+    err = float(np.max(np.abs(got[fin].astype(np.float64) - ref[fin])) / np.max(np.abs(ref[fin])))
+    print(f"[parity] nonfinite d{d}: {err:.3e}", flush=True)
+    assert err <= TOL["f16"]
