@@ -9,6 +9,8 @@ Recurrence for Efficient Dense Prediction", paper Section 2.1):
 
 * :func:`fwd` -- the token-by-token fp64 recurrence in plain C
   (``gla_oracle.c``), OpenMP over the (batch, head) units;
+* :func:`gate_logits` -- the low-rank gate logits z = (x W1) W2 + b of
+  the retention gate (same section), plain C loops in fp64;
 * :func:`closed_form_fwd` -- the O(L^2) unrolled sum
   ``o_t = scale * sum_{s<=t} (q_t (.) prod_{j=s+1..t} gamma_j (.) k_s) v_s``
   in numpy fp64 with explicit per-pair gate sums, for tiny inputs.  Its scan
@@ -67,6 +69,12 @@ def _load():
         ctypes.c_int, ctypes.c_int,
         ctypes.c_double, ctypes.c_double, ctypes.c_double,
         ctypes.c_long, ctypes.c_long, ctypes.c_void_p]
+    lib.gla_oracle_fwd_zd.restype = ctypes.c_int
+    lib.gla_oracle_fwd_zd.argtypes = lib.gla_oracle_fwd.argtypes
+    lib.gla_oracle_gate_logits.restype = ctypes.c_int
+    lib.gla_oracle_gate_logits.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.gla_oracle_half_to_double.restype = ctypes.c_double
     lib.gla_oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.gla_oracle_scan_token.restype = ctypes.c_long
@@ -91,8 +99,9 @@ def _ptr(a):
 def fwd(q, k, v, z, direction, H, W, r=None, w=None, tau=16.0, scale=None,
         eps=1e-6, units=None, threads=None):
     """fp64 recurrence.  q, k: [B, L, NH, dk]; v, r: [B, L, NH, dv] (float16 or
-    float32 arrays, read exactly as stored); z: [B, L, NH, dk] float32;
-    w: [dv] float32 or None.  Returns float64 [B, L, NH, dv].
+    float32 arrays, read exactly as stored); z: [B, L, NH, dk] float32, or
+    float64 (used as is, e.g. from :func:`gate_logits`); w: [dv] float32 or
+    None.  Returns float64 [B, L, NH, dv].
 
     ``units=(u0, u1)`` restricts the work to (batch*NH + head) units in
     [u0, u1); other rows of the result are NaN.
@@ -101,7 +110,8 @@ def fwd(q, k, v, z, direction, H, W, r=None, w=None, tau=16.0, scale=None,
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v)
-    z = np.ascontiguousarray(z, dtype=np.float32)
+    z64 = np.asarray(z).dtype == np.float64
+    z = np.ascontiguousarray(z, dtype=np.float64 if z64 else np.float32)
     if q.dtype == np.float16:
         dtype = 0
     elif q.dtype == np.float32:
@@ -131,9 +141,10 @@ def fwd(q, k, v, z, direction, H, W, r=None, w=None, tau=16.0, scale=None,
     if threads is not None:
         os.environ["OMP_NUM_THREADS"] = str(threads)
     try:
-        rc = lib.gla_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(r), _ptr(w), dtype,
-                                B, NH, H, W, dk, dv, direction, float(tau), float(scale),
-                                float(eps), u0, u1, _ptr(out))
+        entry = lib.gla_oracle_fwd_zd if z64 else lib.gla_oracle_fwd
+        rc = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(r), _ptr(w), dtype,
+                   B, NH, H, W, dk, dv, direction, float(tau), float(scale),
+                   float(eps), u0, u1, _ptr(out))
     finally:
         if threads is not None:
             if old is None:
@@ -143,6 +154,52 @@ def fwd(q, k, v, z, direction, H, W, r=None, w=None, tau=16.0, scale=None,
     if rc != 0:
         raise RuntimeError(f"gla_oracle_fwd failed with status {rc}")
     return out
+
+
+def gate_logits(x, w1, w2, bias, heads, threads=None):
+    """Low-rank gate logits z = (x W1) W2 + b in fp64 (paper Section 2.1,
+    retention gate).  x: [B, L, d_model] float16 or float32; w1: [rank, d_model]
+    with x's dtype (W1 transposed); w2: [heads*dk, rank] float32 (W2
+    transposed, head h owns rows h*dk .. h*dk+dk-1); bias: [heads*dk] float32
+    or None.  Returns float64 [B, L, heads, dk].
+    """
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    w1 = np.ascontiguousarray(w1)
+    w2 = np.ascontiguousarray(w2, dtype=np.float32)
+    if x.dtype == np.float16:
+        dtype = 0
+    elif x.dtype == np.float32:
+        dtype = 1
+    else:
+        raise TypeError("x must be float16 or float32")
+    if w1.dtype != x.dtype:
+        raise TypeError("w1 must have x's dtype")
+    B, L, d_model = x.shape
+    rank = w1.shape[0]
+    nout = w2.shape[0]
+    if w1.shape != (rank, d_model) or w2.shape != (nout, rank) or nout % heads:
+        raise ValueError("shape mismatch")
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (nout,):
+            raise ValueError("bias must have shape [heads*dk]")
+    z = np.empty((B, L, heads, nout // heads), dtype=np.float64)
+    old = os.environ.get("OMP_NUM_THREADS")
+    if threads is not None:
+        os.environ["OMP_NUM_THREADS"] = str(threads)
+    try:
+        rc = lib.gla_oracle_gate_logits(_ptr(x), _ptr(w1), _ptr(w2), _ptr(bias), dtype,
+                                        B * L, d_model, rank, nout, _ptr(z))
+    finally:
+        if threads is not None:
+            if old is None:
+                os.environ.pop("OMP_NUM_THREADS", None)
+            else:
+                os.environ["OMP_NUM_THREADS"] = old
+    if rc != 0:
+        raise RuntimeError(f"gla_oracle_gate_logits failed with status {rc}")
+    return z
 
 
 # ---------------------------------------------------------------------------

@@ -29,7 +29,18 @@
  *
  * Layouts: q, k, z are [B, L, NH, dk]; v, r, out are [B, L, NH, dv];
  * all contiguous row-major.  q, k, v, r are binary16 or binary32 (dtype),
- * z and w are binary32, out is binary64.
+ * z is binary32 (gla_oracle_fwd) or binary64 (gla_oracle_fwd_zd), w is
+ * binary32, out is binary64.
+ *
+ * The gate logits themselves come from a low-rank projection of the block
+ * input x (Sec. 2.1, retention gate, rank r = 16):
+ *   z_t = (x_t W1) W2 + b,  W1: d_model x rank,  W2: rank x (NH*dk)
+ * computed by gla_oracle_gate_logits in binary64.  Reading taken where the
+ * pages are silent: the first factor is shared by all heads and the second
+ * factor and bias hold every head's d_k columns side by side (head h owns
+ * columns h*dk .. h*dk + dk - 1), as in GLA's low-rank gate.  Both factors
+ * are stored transposed, as the weights of linear layers: w1 is
+ * [rank][d_model], w2 is [NH*dk][rank].
  */
 #include <math.h>
 #include <stddef.h>
@@ -38,6 +49,7 @@
 
 #define ORACLE_F16 0
 #define ORACLE_F32 1
+#define ORACLE_F64 2
 
 /* IEEE 754 binary16 -> double, from the format's definition: 1 sign bit,
  * 5 exponent bits with bias 15, 10 fraction bits. */
@@ -60,6 +72,8 @@ static double load_elem(const void *base, int dtype, size_t idx)
 {
     if (dtype == ORACLE_F16)
         return gla_oracle_half_to_double(((const uint16_t *)base)[idx]);
+    if (dtype == ORACLE_F64)
+        return ((const double *)base)[idx];
     return (double)((const float *)base)[idx];
 }
 
@@ -98,11 +112,11 @@ long gla_oracle_scan_token(int dir, long i, long H, long W)
  * r == NULL: out = o.  w == NULL: RMSNorm weight of ones.
  * Returns 0 on success, 1 on a bad argument, 2 on allocation failure.
  */
-int gla_oracle_fwd(const void *q, const void *k, const void *v, const float *z,
-                   const void *r, const float *w, int dtype,
-                   int B, int NH, int H, int W, int dk, int dv, int dir,
-                   double tau, double scale, double eps,
-                   long unit_begin, long unit_end, double *out)
+static int fwd_impl(const void *q, const void *k, const void *v, const void *z, int zdtype,
+                    const void *r, const float *w, int dtype,
+                    int B, int NH, int H, int W, int dk, int dv, int dir,
+                    double tau, double scale, double eps,
+                    long unit_begin, long unit_end, double *out)
 {
     if (!q || !k || !v || !z || !out || B < 1 || NH < 1 || H < 1 || W < 1 ||
         dk < 1 || dv < 1 || dir < 0 || dir > 3 || !(tau > 0.0) ||
@@ -132,7 +146,7 @@ int gla_oracle_fwd(const void *q, const void *k, const void *v, const float *z,
             for (int c = 0; c < dk; ++c) {
                 qt[c] = load_elem(q, dtype, rk + c);
                 kt[c] = load_elem(k, dtype, rk + c);
-                gt[c] = exp(log_sigmoid((double)z[rk + c]) / tau);
+                gt[c] = exp(log_sigmoid(load_elem(z, zdtype, rk + c)) / tau);
             }
             for (int j = 0; j < dv; ++j)
                 vt[j] = load_elem(v, dtype, rv + j);
@@ -163,6 +177,71 @@ int gla_oracle_fwd(const void *q, const void *k, const void *v, const float *z,
             }
         }
         free(S); free(qt); free(kt); free(gt); free(vt); free(ot);
+    }
+    return failed ? 2 : 0;
+}
+
+/* Forward pass with binary32 gate logits z. */
+int gla_oracle_fwd(const void *q, const void *k, const void *v, const float *z,
+                   const void *r, const float *w, int dtype,
+                   int B, int NH, int H, int W, int dk, int dv, int dir,
+                   double tau, double scale, double eps,
+                   long unit_begin, long unit_end, double *out)
+{
+    return fwd_impl(q, k, v, z, ORACLE_F32, r, w, dtype, B, NH, H, W, dk, dv, dir,
+                    tau, scale, eps, unit_begin, unit_end, out);
+}
+
+/* Forward pass with binary64 gate logits z (for logits computed by
+ * gla_oracle_gate_logits, used without rounding). */
+int gla_oracle_fwd_zd(const void *q, const void *k, const void *v, const double *z,
+                      const void *r, const float *w, int dtype,
+                      int B, int NH, int H, int W, int dk, int dv, int dir,
+                      double tau, double scale, double eps,
+                      long unit_begin, long unit_end, double *out)
+{
+    return fwd_impl(q, k, v, z, ORACLE_F64, r, w, dtype, B, NH, H, W, dk, dv, dir,
+                    tau, scale, eps, unit_begin, unit_end, out);
+}
+
+/*
+ * Gate logits of `tokens` tokens from the low-rank projection (Sec. 2.1,
+ * retention gate):
+ *   hproj = x_t W1            (rank values;  W1[m][j] = w1[j * d_model + m])
+ *   z_t   = hproj W2 + b      (nout values;  W2[j][o] = w2[o * rank + j])
+ * x: [tokens][d_model] and w1 in `dtype` (binary16 or binary32), w2 and bias
+ * binary32 (bias NULL means zeros), z: [tokens][nout] binary64.  With
+ * nout = NH * dk, z read as [B, L, NH, dk] gives every head its columns.
+ * Returns 0 on success, 1 on a bad argument, 2 on allocation failure.
+ */
+int gla_oracle_gate_logits(const void *x, const void *w1, const float *w2, const float *bias,
+                           int dtype, long tokens, int d_model, int rank, int nout, double *z)
+{
+    if (!x || !w1 || !w2 || !z || tokens < 0 || d_model < 1 || rank < 1 || nout < 1 ||
+        (dtype != ORACLE_F16 && dtype != ORACLE_F32))
+        return 1;
+    int failed = 0;
+#pragma omp parallel for schedule(static) reduction(| : failed)
+    for (long t = 0; t < tokens; ++t) {
+        double *hp = malloc(sizeof(double) * rank);
+        if (!hp) {
+            failed = 1;
+            continue;
+        }
+        for (int j = 0; j < rank; ++j) {
+            double acc = 0.0;
+            for (int m = 0; m < d_model; ++m)
+                acc += load_elem(x, dtype, (size_t)t * d_model + m) *
+                       load_elem(w1, dtype, (size_t)j * d_model + m);
+            hp[j] = acc;
+        }
+        for (int o = 0; o < nout; ++o) {
+            double acc = bias ? (double)bias[o] : 0.0;
+            for (int j = 0; j < rank; ++j)
+                acc += hp[j] * (double)w2[(size_t)o * rank + j];
+            z[(size_t)t * nout + o] = acc;
+        }
+        free(hp);
     }
     return failed ? 2 : 0;
 }

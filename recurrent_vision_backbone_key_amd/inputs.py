@@ -77,6 +77,26 @@ def make_inputs(B, NH, H, W, dk, dv, dtype="f16", z=(0.0, 1.0), gated=False, see
     return dict(q=q, k=k, v=v, z=zz, r=r, w=w)
 
 
+def make_gate_proj_inputs(B, L, NH, dk, d_model, rank=16, dtype="f16", seed=0):
+    """Draw the retention gate's low-rank projection inputs from PCG64(seed),
+    in the order x, w1, w2, bias.
+
+    x ~ N(0, 1) [B, L, d_model] and w1 ~ N(0, 1/d_model) [rank, d_model]
+    rounded to ``dtype``; w2 ~ N(0, 1/rank) [NH*dk, rank] and
+    bias ~ U(-1/sqrt(rank), 1/sqrt(rank)) [NH*dk] in float32.  With these
+    scales x W1 W2 is about N(0, 1), the gate-logit distribution of the
+    other workloads.
+    """
+    rng = np.random.default_rng(seed)
+    dt = np_dtype(dtype)
+    x = rng.standard_normal((B, L, d_model)).astype(dt)
+    w1 = (rng.standard_normal((rank, d_model)) / np.sqrt(d_model)).astype(dt)
+    w2 = (rng.standard_normal((NH * dk, rank)) / np.sqrt(rank)).astype(np.float32)
+    lim = 1.0 / np.sqrt(rank)
+    bias = rng.uniform(-lim, lim, size=(NH * dk,)).astype(np.float32)
+    return dict(x=x, w1=w1, w2=w2, bias=bias)
+
+
 def workload_inputs(name: str, call: int = 0, **overrides):
     """Inputs of call ``call`` of a named workload; seed = 1000*index + call."""
     spec = dict(WORKLOADS[name])

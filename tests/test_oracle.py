@@ -269,3 +269,105 @@ def test_nonfinite_gate_logits():
         assert oracle.fwd(q, k, v, z, 0, 1, 2)[0, 1, 0, 0] == want
     z = np.array([0.0, np.nan], dtype=np.float32).reshape(1, 2, 1, 1)
     assert np.isnan(oracle.fwd(q, k, v, z, 0, 1, 2)[0, 1, 0, 0])
+
+
+# ---------------------------------------------------------------------------
+# Low-rank gate logits z = (x W1) W2 + b (Sec. 2.1, retention gate, r = 16)
+# ---------------------------------------------------------------------------
+
+def test_gate_logits_by_hand():
+    """d_model = 2, rank 1, one head of d_k = 2: x W1 = 3 - 2 = 1, so
+    z = W2 column + b = [0.5 + 0.25, 2 - 1]; a dropped bias, a wrong product
+    order or a sign slip changes a printed digit."""
+    x = np.array([[[1.0, 2.0]]], np.float32)
+    w1 = np.array([[3.0, -1.0]], np.float32)       # W1 = [[3], [-1]], stored transposed
+    w2 = np.array([[0.5], [2.0]], np.float32)      # W2 = [[0.5, 2]], stored transposed
+    b = np.array([0.25, -1.0], np.float32)
+    z = oracle.gate_logits(x, w1, w2, b, heads=1)
+    assert z.shape == (1, 1, 1, 2)
+    assert z[0, 0, 0].tolist() == [0.75, 1.0]
+    # two tokens, two heads of d_k = 1, rank 2, by hand
+    x = np.array([[[1.0, 0.0, -2.0], [0.5, 1.0, 0.0]]], np.float32)
+    w1 = np.array([[1.0, 1.0, 1.0], [0.0, 2.0, -1.0]], np.float32)
+    w2 = np.array([[1.0, 0.0], [-1.0, 0.5]], np.float32)
+    z = oracle.gate_logits(x, w1, w2, None, heads=2)
+    # token 0: x W1 = [-1, 2];   z = [-1, 1 + 1]      = [-1, 2]
+    # token 1: x W1 = [1.5, 2];  z = [1.5, -1.5 + 1] = [1.5, -0.5]
+    assert z[0, :, :, 0].tolist() == [[-1.0, 2.0], [1.5, -0.5]]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("d_model,rank,NH,dk", [(8, 3, 2, 4), (32, 16, 3, 8), (5, 1, 1, 6)])
+def test_gate_logits_equal_numpy_products(dtype, d_model, rank, NH, dk):
+    """The C loops against numpy's fp64 matrix products of the same stored
+    values (a transposed factor, a head-slicing or a bias-index mistake
+    changes the result far beyond the summation-order noise)."""
+    from recurrent_vision_backbone_key_amd.inputs import make_gate_proj_inputs
+    g = make_gate_proj_inputs(2, 7, NH, dk, d_model, rank, dtype, seed=11)
+    z = oracle.gate_logits(g["x"], g["w1"], g["w2"], g["bias"], heads=NH)
+    x = g["x"].astype(np.float64)
+    ref = (x @ g["w1"].astype(np.float64).T) @ g["w2"].astype(np.float64).T + g["bias"]
+    assert _rel(z.reshape(2, 7, NH * dk), ref) < 1e-13
+
+
+def test_gate_logits_structure():
+    """W2 = 0 gives z = b exactly (and zeros without a bias); a one-hot token
+    with a one-hot W1 row picks one column of W2 (stored transposed) per
+    head slot, which pins the head layout of the second factor."""
+    NH, dk, d_model, rank = 3, 4, 6, 5
+    x = np.zeros((1, 2, d_model), np.float32)
+    x[0, 0, 2] = 1.0
+    x[0, 1, 4] = 1.0
+    w1 = np.zeros((rank, d_model), np.float32)
+    w1[3, 2] = 1.0                       # token 0 -> hproj = e_3
+    w1[1, 4] = 1.0                       # token 1 -> hproj = e_1
+    w2 = np.arange(NH * dk * rank, dtype=np.float32).reshape(NH * dk, rank)
+    bias = (100.0 + np.arange(NH * dk)).astype(np.float32)
+    z = oracle.gate_logits(x, w1, w2, bias, heads=NH)
+    for h in range(NH):
+        for c in range(dk):
+            o = h * dk + c
+            assert z[0, 0, h, c] == w2[o, 3] + bias[o]
+            assert z[0, 1, h, c] == w2[o, 1] + bias[o]
+    z0 = oracle.gate_logits(x, w1, np.zeros_like(w2), bias, heads=NH)
+    assert np.array_equal(z0.reshape(2, NH * dk), np.broadcast_to(bias.astype(np.float64), (2, NH * dk)))
+    assert not oracle.gate_logits(x, w1, np.zeros_like(w2), None, heads=NH).any()
+
+
+def test_gate_logits_rank_bound():
+    """(z - b) over many tokens has rank at most r: the projection is low
+    rank (a full-rank slip, e.g. adding x itself, would show)."""
+    from recurrent_vision_backbone_key_amd.inputs import make_gate_proj_inputs
+    g = make_gate_proj_inputs(1, 200, 4, 16, 96, rank=5, dtype="f32", seed=3)
+    z = oracle.gate_logits(g["x"], g["w1"], g["w2"], g["bias"], heads=4)
+    m = z.reshape(200, 64) - g["bias"]
+    sv = np.linalg.svd(m, compute_uv=False)
+    assert sv[4] > 1e-3 * sv[0]
+    assert sv[5] < 1e-12 * sv[0]
+
+
+def test_fp64_logits_path_equals_fp32_path():
+    """float32 logits widened to float64 give bit-identical outputs through
+    the binary64-logit entry (same arithmetic, only the load differs)."""
+    inp = make_inputs(2, 2, 4, 5, 8, 8, "f16", gated=True, seed=5)
+    a = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["z"], 2, 4, 5, r=inp["r"], w=inp["w"])
+    b = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["z"].astype(np.float64), 2, 4, 5,
+                   r=inp["r"], w=inp["w"])
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("direction", oracle.DIRS)
+def test_projected_gate_forward_equals_closed_form(direction):
+    """The recurrence on projected logits against the O(L^2) closed form fed
+    with numpy's fp64 products (two independent routes end to end)."""
+    from recurrent_vision_backbone_key_amd.inputs import make_gate_proj_inputs
+    B, NH, H, W, dk, d_model = 1, 2, 3, 4, 8, 16
+    inp = make_inputs(B, NH, H, W, dk, dk, "f16", gated=True, seed=21)
+    g = make_gate_proj_inputs(B, H * W, NH, dk, d_model, 4, "f16", seed=22)
+    z = oracle.gate_logits(g["x"], g["w1"], g["w2"], g["bias"], heads=NH)
+    got = oracle.fwd(inp["q"], inp["k"], inp["v"], z, direction, H, W, r=inp["r"], w=inp["w"])
+    zn = ((g["x"].astype(np.float64) @ g["w1"].astype(np.float64).T)
+          @ g["w2"].astype(np.float64).T + g["bias"]).reshape(B, H * W, NH, dk)
+    ref = oracle.closed_form_fwd(inp["q"], inp["k"], inp["v"], zn, direction, H, W,
+                                 r=inp["r"], w=inp["w"])
+    assert _rel(got, ref) < 1e-11
