@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 1
+#define GLA_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define GLA_API __attribute__((visibility("default")))
@@ -87,7 +87,7 @@ typedef struct gla_opts {
 } gla_opts;
 
 /* Algorithms.  SINGLE_PASS (binary16, d_k = d_v = 64, chunk 64, segments of
- * at most 6 chunks, at most 65 segments per scan) reads every input once: one
+ * at most 7 chunks, at most 65 segments per scan) reads every input once: one
  * workgroup per segment, segments exchange states through the workspace.
  * THREE_PASS (every built configuration) runs an aggregate pass, a fold pass
  * and an output pass.  AUTO picks SINGLE_PASS whenever it applies. */
@@ -132,6 +132,60 @@ GLA_API size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla_op
  * GLA_EINVAL on a bad pointer or size, GLA_EHIP on a launch failure.
  */
 GLA_API int gla_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/*
+ * Low-rank retention-gate projection (paper Section 2.1, definition of the
+ * retention gate: the gate logits are x_t W1 W2 + b with W1 of shape
+ * d_model x rank, W2 of shape rank x d_k and rank 16).  This library reads
+ * the formula for all heads at once, as in GLA's low-rank gate: W1 is shared
+ * by the heads and W2, b hold the heads' d_k columns side by side, so head h
+ * uses columns h*dk .. h*dk + dk - 1 of W2 and b:
+ *     z[b, t, h, c] = bias[h*dk + c] + sum_j (sum_m x[b, t, m] W1[m][j]) W2[j][h*dk + c]
+ * Both factors are passed transposed, the layout of a linear layer's weight.
+ */
+typedef struct gla_gate_proj {
+    const void *x;       /* [B, L, d_model] block input, storage opts->dtype
+                            (or the dtype argument of gla_gate_logits)         */
+    const void *w1;      /* [rank, d_model] W1 transposed, same storage as x   */
+    const float *w2;     /* [NH*dk, rank] W2 transposed, binary32             */
+    const float *bias;   /* [NH*dk] binary32; NULL selects zeros              */
+    int32_t d_model;     /* >= 8, a multiple of 8                             */
+    int32_t rank;        /* 1 .. 64 (the pages use 16)                        */
+} gla_gate_proj;
+
+/*
+ * gla_gate_logits -- the projection alone: writes z [batch, tokens, heads, dk]
+ * binary32 (the gate_logits operand of gla_fwd) on `stream` (hipStream_t,
+ * NULL selects the null stream).  x, w1 and z are 16-byte aligned device
+ * pointers, w2 and bias 4-byte aligned; z must not overlap an input.
+ * dtype: GLA_F16 or GLA_F32, the storage of x and w1; dk in {16, 32, 64, 128}.
+ * GLA_EINVAL on a bad pointer, size or overlap, GLA_EUNSUPPORTED on a dtype
+ * or dk outside the built set, GLA_EHIP on a launch failure.
+ */
+GLA_API int gla_gate_logits(const gla_gate_proj *gate, int batch, int tokens, int heads, int dk,
+                            int dtype, float *z, void *stream);
+
+/*
+ * gla_fwd_gate_proj -- gla_fwd with the gate logits computed from the block
+ * input by the low-rank projection above instead of read from memory.
+ * Arguments as for gla_fwd, with `gate` in place of gate_logits (x and w1
+ * stored as opts->dtype).  For the single-pass configuration with rank 16,
+ * d_model a multiple of 64 and d_model <= 384, the projection runs inside
+ * the single-pass kernel (the 64 x rank products of x and W1 on the matrix
+ * cores, the rank x d_k product with W2 in binary32), so z never reaches
+ * memory.  Every other configuration writes z into the workspace with the
+ * kernel of gla_gate_logits first and then runs the ordinary forward.  The
+ * workspace must hold gla_workspace_size_gate_proj() bytes, cleared once with
+ * gla_workspace_init() as for gla_fwd.  Returns a gla_status as gla_fwd.
+ */
+GLA_API int gla_fwd_gate_proj(const void *q, const void *k, const void *v,
+                              const gla_gate_proj *gate, int dir, int H, int W, int chunk,
+                              void *out, const void *r, const gla_opts *opts);
+
+/* Bytes of workspace gla_fwd_gate_proj needs (0: none; also 0 for arguments
+ * it would reject). */
+GLA_API size_t gla_workspace_size_gate_proj(int dir, int H, int W, int chunk,
+                                            const gla_gate_proj *gate, const gla_opts *opts);
 
 /* Static, NUL-terminated description of a gla_status value. */
 GLA_API const char *gla_status_str(int status);

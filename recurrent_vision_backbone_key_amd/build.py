@@ -38,6 +38,7 @@ UNITS = [
     ("gla_kernel.hip", "hip", []),
     ("gla_onepass.hip", "hip", []),
     ("gla_wide.hip", "hip", []),
+    ("gla_proj.hip", "hip", []),
 ]
 
 

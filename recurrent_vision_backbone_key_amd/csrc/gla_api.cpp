@@ -6,18 +6,15 @@
 #include "gla_launch.h"
 #include "gla_plan.h"
 
-extern "C" int gla_fwd(const void* q, const void* k, const void* v, const float* gate_logits,
-                       int dir, int H, int W, int chunk, void* out, const void* r,
-                       const gla_opts* opts)
+namespace {
+
+// Launches the planned forward; P.z (or the fused projection operands) set.
+int run_fwd(gla::Params& P, const void* q, const void* k, const void* v, int dir, int H, int W,
+            int chunk, void* out, const void* r, const gla_opts* opts, const gla_plan& plan)
 {
-    gla_plan plan;
-    const int st = gla_validate(q, k, v, gate_logits, dir, H, W, chunk, out, r, opts, &plan);
-    if (st != GLA_OK) return st;
-    gla::Params P;
     P.q = q;
     P.k = k;
     P.v = v;
-    P.z = gate_logits;
     P.r = r;
     P.w = r ? opts->norm_weight : nullptr;
     P.out = out;
@@ -49,6 +46,84 @@ extern "C" int gla_fwd(const void* q, const void* k, const void* v, const float*
         return gla::launch_onepass(P, opts->stream);
     }
     return gla::launch_fwd(P, opts->dtype, opts->dk, chunk, opts->stream);
+}
+
+gla::GateProj gate_of(const gla_gate_proj* g)
+{
+    gla::GateProj G;
+    G.x = g->x;
+    G.w1 = g->w1;
+    G.w2 = g->w2;
+    G.bias = g->bias;
+    G.d_model = g->d_model;
+    G.rank = g->rank;
+    return G;
+}
+
+void no_proj(gla::Params& P)
+{
+    P.gx = P.gw1 = nullptr;
+    P.gw2 = P.gb = nullptr;
+    P.d_model = 0;
+}
+
+}  // namespace
+
+extern "C" int gla_fwd(const void* q, const void* k, const void* v, const float* gate_logits,
+                       int dir, int H, int W, int chunk, void* out, const void* r,
+                       const gla_opts* opts)
+{
+    gla_plan plan;
+    const int st = gla_validate(q, k, v, gate_logits, dir, H, W, chunk, out, r, opts, &plan);
+    if (st != GLA_OK) return st;
+    gla::Params P;
+    P.z = gate_logits;
+    no_proj(P);
+    return run_fwd(P, q, k, v, dir, H, W, chunk, out, r, opts, plan);
+}
+
+extern "C" int gla_fwd_gate_proj(const void* q, const void* k, const void* v,
+                                 const gla_gate_proj* gate, int dir, int H, int W, int chunk,
+                                 void* out, const void* r, const gla_opts* opts)
+{
+    gla_plan plan;
+    const int st = gla_validate_gate_proj(q, k, v, gate, dir, H, W, chunk, out, r, opts, &plan);
+    if (st != GLA_OK) return st;
+    gla::Params P;
+    no_proj(P);
+    if (plan.proj_fused) {
+        P.z = nullptr;
+        P.gx = gate->x;
+        P.gw1 = gate->w1;
+        P.gw2 = gate->w2;
+        P.gb = gate->bias;
+        P.d_model = gate->d_model;
+    } else {
+        // z staged in the workspace by the projection kernel, then the
+        // ordinary forward on the same stream
+        float* z = (float*)((char*)opts->workspace + plan.off_z);
+        const int ls = gla::launch_gate_logits(gate_of(gate), opts->dtype, opts->batch * plan.L,
+                                               opts->heads * opts->dk, z, opts->stream);
+        if (ls != GLA_OK) return ls;
+        P.z = z;
+    }
+    return run_fwd(P, q, k, v, dir, H, W, chunk, out, r, opts, plan);
+}
+
+extern "C" size_t gla_workspace_size_gate_proj(int dir, int H, int W, int chunk,
+                                               const gla_gate_proj* gate, const gla_opts* opts)
+{
+    gla_plan plan;
+    if (gla_make_plan_gate_proj(dir, H, W, chunk, gate, opts, 0, &plan) != GLA_OK) return 0;
+    return plan.workspace_bytes;
+}
+
+extern "C" int gla_gate_logits(const gla_gate_proj* gate, int batch, int tokens, int heads, int dk,
+                               int dtype, float* z, void* stream)
+{
+    const int st = gla_validate_gate_logits(gate, batch, tokens, heads, dk, dtype, z);
+    if (st != GLA_OK) return st;
+    return gla::launch_gate_logits(gate_of(gate), dtype, batch * tokens, heads * dk, z, stream);
 }
 
 extern "C" size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla_opts* opts)

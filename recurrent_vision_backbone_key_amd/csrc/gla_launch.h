@@ -36,7 +36,28 @@ struct Params {
     float scale;        // output scale
     float inv_tau;      // 1 / tau
     float eps;          // RMSNorm epsilon
+    // single pass with the gate projection fused (z == null): rank 16
+    const void* gx;     // [B, L, d_model] block input (binary16)
+    const void* gw1;    // [16, d_model] W1 transposed (binary16)
+    const float* gw2;   // [NH*DK, 16] W2 transposed
+    const float* gb;    // [NH*DK] gate bias, or null (zeros)
+    int d_model;
 };
+
+// Low-rank gate projection operands (include/gla.h, gla_gate_proj).
+struct GateProj {
+    const void* x;
+    const void* w1;
+    const float* w2;
+    const float* bias;
+    int d_model;
+    int rank;
+};
+
+// Largest d_model of the gate projection fused into the single pass (its W1
+// is staged in shared memory) and the rank it is built for.
+constexpr int kFusedProjMaxDModel = 384;
+constexpr int kFusedProjRank = 16;
 
 // Launches the aggregate, fold and output passes (or only the output pass
 // when nseg == 1) on `stream`.  Returns a gla_status value.
@@ -51,6 +72,9 @@ int launch_wide(const Params& P, void* stream);
 
 // Single-pass kernel (binary16, d = 64, chunk 64): one launch.
 int launch_onepass(const Params& P, void* stream);
+
+// Gate logits z [tokens, nout] binary32 from the low-rank projection.
+int launch_gate_logits(const GateProj& G, int dtype, int tokens, int nout, float* z, void* stream);
 
 // Zero-fills a workspace (counters, flags) on `stream`.
 int launch_workspace_init(void* ws, size_t bytes, void* stream);

@@ -61,6 +61,8 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     plan->L = (int)L;
     plan->nchunks = nchunks;
     plan->onepass = 0;
+    plan->proj_fused = 0;
+    plan->off_z = 0;
     plan->off_done = plan->off_flags = plan->off_agg = plan->off_incl = 0;
 
     // Single pass: binary16, d = 64, 64-token chunks; segments of at most
@@ -134,6 +136,59 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     return GLA_OK;
 }
 
+namespace {
+
+// One input operand: pointer, bytes, required alignment.
+struct Operand {
+    const void* p;
+    size_t bytes;
+    uintptr_t align;
+};
+
+// Alignment of every operand and of out, no overlap of out with an input,
+// and the workspace (size, alignment, no overlap with anything).
+int check_operands(const Operand* ins, int n, const void* out, size_t out_bytes,
+                   const gla_opts* o, const gla_plan* plan)
+{
+    for (int i = 0; i < n; ++i)
+        if (ins[i].p && !aligned(ins[i].p, ins[i].align)) return GLA_EINVAL;
+    if (!aligned(out, 16)) return GLA_EINVAL;
+    for (int i = 0; i < n; ++i)
+        if (overlaps(out, out_bytes, ins[i].p, ins[i].bytes)) return GLA_EINVAL;
+    if (plan->workspace_bytes) {
+        if (!o->workspace || o->workspace_bytes < plan->workspace_bytes ||
+            !aligned(o->workspace, 16))
+            return GLA_EWORKSPACE;
+        if (overlaps(o->workspace, plan->workspace_bytes, out, out_bytes)) return GLA_EINVAL;
+        for (int i = 0; i < n; ++i)
+            if (overlaps(o->workspace, plan->workspace_bytes, ins[i].p, ins[i].bytes))
+                return GLA_EINVAL;
+    }
+    return GLA_OK;
+}
+
+// Sizes of the gate projection operands.
+int check_gate_sizes(const gla_gate_proj* gate)
+{
+    if (!gate || !gate->x || !gate->w1 || !gate->w2) return GLA_EINVAL;
+    if (gate->d_model < 8 || gate->d_model > (1 << 16) || gate->d_model % 8 != 0) return GLA_EINVAL;
+    if (gate->rank < 1 || gate->rank > 64) return GLA_EINVAL;
+    return GLA_OK;
+}
+
+// The gate projection operands as a list (x, w1, w2, bias).
+void gate_operands(const gla_gate_proj* gate, size_t tokens, int heads, int dk, size_t es,
+                   Operand* ops)
+{
+    const size_t nout = (size_t)heads * dk;
+    ops[0] = Operand{gate->x, tokens * gate->d_model * es, 16};
+    ops[1] = Operand{gate->w1, (size_t)gate->rank * gate->d_model * es, 16};
+    ops[2] = Operand{gate->w2, nout * gate->rank * 4, 4};
+    ops[3] = Operand{gate->bias, nout * 4, 4};
+}
+
+}  // namespace
+
 extern "C" int gla_validate(const void* q, const void* k, const void* v, const float* z,
                             int dir, int H, int W, int chunk, const void* out, const void* r,
                             const gla_opts* o, gla_plan* plan)
@@ -146,22 +201,67 @@ extern "C" int gla_validate(const void* q, const void* k, const void* v, const f
     const size_t es = o->dtype == GLA_F16 ? 2 : 4;
     const size_t rows = (size_t)o->batch * plan->L * o->heads;
     const size_t nk = rows * o->dk, nv = rows * o->dv;
-    const void* ins[6] = {q, k, v, z, r, r ? o->norm_weight : nullptr};
-    const size_t insz[6] = {nk * es, nk * es, nv * es, nk * 4, nv * es, (size_t)o->dv * 4};
-    for (int i = 0; i < 5; ++i)
-        if (ins[i] && !aligned(ins[i], 16)) return GLA_EINVAL;
-    if (!aligned(out, 16)) return GLA_EINVAL;
-    if (ins[5] && !aligned(ins[5], 4)) return GLA_EINVAL;
-    for (int i = 0; i < 6; ++i)
-        if (overlaps(out, nv * es, ins[i], insz[i])) return GLA_EINVAL;
+    const Operand ins[6] = {{q, nk * es, 16}, {k, nk * es, 16}, {v, nv * es, 16}, {z, nk * 4, 16},
+                            {r, nv * es, 16}, {r ? o->norm_weight : nullptr, (size_t)o->dv * 4, 4}};
+    return check_operands(ins, 6, out, nv * es, o, plan);
+}
 
-    if (plan->workspace_bytes) {
-        if (!o->workspace || o->workspace_bytes < plan->workspace_bytes ||
-            !aligned(o->workspace, 16))
-            return GLA_EWORKSPACE;
-        if (overlaps(o->workspace, plan->workspace_bytes, out, nv * es)) return GLA_EINVAL;
-        for (int i = 0; i < 6; ++i)
-            if (overlaps(o->workspace, plan->workspace_bytes, ins[i], insz[i])) return GLA_EINVAL;
+extern "C" int gla_make_plan_gate_proj(int dir, int H, int W, int chunk, const gla_gate_proj* gate,
+                                       const gla_opts* o, int has_gate, gla_plan* plan)
+{
+    int st = check_gate_sizes(gate);
+    if (st != GLA_OK) return st;
+    st = gla_make_plan(dir, H, W, chunk, o, has_gate, plan);
+    if (st != GLA_OK) return st;
+    // fused: single pass, rank 16, d_model a multiple of 64 whose W1 fits
+    // the kernel's shared-memory stage
+    if (plan->onepass && gate->rank == gla::kFusedProjRank && gate->d_model % 64 == 0 &&
+        gate->d_model <= gla::kFusedProjMaxDModel) {
+        plan->proj_fused = 1;
+        return GLA_OK;
     }
+    plan->off_z = ((plan->workspace_bytes + 255) / 256) * 256;
+    plan->workspace_bytes = plan->off_z + (size_t)o->batch * plan->L * o->heads * o->dk * 4;
+    return GLA_OK;
+}
+
+extern "C" int gla_validate_gate_proj(const void* q, const void* k, const void* v,
+                                      const gla_gate_proj* gate, int dir, int H, int W, int chunk,
+                                      const void* out, const void* r, const gla_opts* o,
+                                      gla_plan* plan)
+{
+    if (!o || !plan || !gate) return GLA_EINVAL;
+    if (!q || !k || !v || !out) return GLA_EINVAL;
+    const int st = gla_make_plan_gate_proj(dir, H, W, chunk, gate, o, r != nullptr, plan);
+    if (st != GLA_OK) return st;
+    const size_t es = o->dtype == GLA_F16 ? 2 : 4;
+    const size_t tokens = (size_t)o->batch * plan->L;
+    const size_t rows = tokens * o->heads;
+    const size_t nk = rows * o->dk, nv = rows * o->dv;
+    Operand ins[9] = {{q, nk * es, 16}, {k, nk * es, 16}, {v, nv * es, 16}, {r, nv * es, 16},
+                      {r ? o->norm_weight : nullptr, (size_t)o->dv * 4, 4}};
+    gate_operands(gate, tokens, o->heads, o->dk, es, ins + 5);
+    return check_operands(ins, 9, out, nv * es, o, plan);
+}
+
+extern "C" int gla_validate_gate_logits(const gla_gate_proj* gate, int batch, int tokens, int heads,
+                                        int dk, int dtype, const float* z)
+{
+    int st = check_gate_sizes(gate);
+    if (st != GLA_OK) return st;
+    if (!z || batch < 1 || tokens < 1 || heads < 1) return GLA_EINVAL;
+    if (dtype != GLA_F16 && dtype != GLA_F32) return GLA_EUNSUPPORTED;
+    if (!is_pow2_dim(dk)) return GLA_EUNSUPPORTED;
+    const int64_t ntok = (int64_t)batch * tokens;
+    if (ntok >= (int64_t)1 << 31 || ntok * heads >= (int64_t)1 << 31) return GLA_EUNSUPPORTED;
+    const size_t es = dtype == GLA_F16 ? 2 : 4;
+    Operand ins[4];
+    gate_operands(gate, (size_t)ntok, heads, dk, es, ins);
+    for (int i = 0; i < 4; ++i)
+        if (ins[i].p && !aligned(ins[i].p, ins[i].align)) return GLA_EINVAL;
+    const size_t zb = (size_t)ntok * heads * dk * 4;
+    if (!aligned(z, 16)) return GLA_EINVAL;
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(z, zb, ins[i].p, ins[i].bytes)) return GLA_EINVAL;
     return GLA_OK;
 }

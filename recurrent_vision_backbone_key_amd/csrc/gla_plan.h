@@ -16,6 +16,8 @@ typedef struct gla_plan {
     int xcd_tasks;               // single pass, xcd_local: workgroups per XCD
     size_t workspace_bytes;
     size_t off_done, off_flags, off_agg, off_incl;  // single-pass workspace layout (bytes)
+    int proj_fused;              // gate projection inside the single pass
+    size_t off_z;                // gate projection not fused: z staged here (bytes)
     float tau, scale, eps;
 } gla_plan;
 
@@ -28,6 +30,21 @@ int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* opts, int ha
 int gla_validate(const void* q, const void* k, const void* v, const float* gate_logits,
                  int dir, int H, int W, int chunk, const void* out, const void* r,
                  const gla_opts* opts, gla_plan* plan);
+
+// Plan of gla_fwd_gate_proj: the plan of gla_fwd plus whether the projection
+// is fused into the single pass; otherwise z takes B*L*NH*dk binary32 words
+// at off_z of the workspace (included in workspace_bytes).
+int gla_make_plan_gate_proj(int dir, int H, int W, int chunk, const gla_gate_proj* gate,
+                            const gla_opts* opts, int has_gate, gla_plan* plan);
+
+// Host check of every argument of gla_fwd_gate_proj.  Fills *plan on success.
+int gla_validate_gate_proj(const void* q, const void* k, const void* v, const gla_gate_proj* gate,
+                           int dir, int H, int W, int chunk, const void* out, const void* r,
+                           const gla_opts* opts, gla_plan* plan);
+
+// Host check of every argument of gla_gate_logits.
+int gla_validate_gate_logits(const gla_gate_proj* gate, int batch, int tokens, int heads, int dk,
+                             int dtype, const float* z);
 
 // Whether a (dtype, head dim, chunk) instantiation is built (shared-memory
 // footprint of one workgroup within the 160 KiB of a gfx950 CU).

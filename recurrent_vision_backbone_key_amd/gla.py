@@ -16,7 +16,8 @@ L2R, R2L, T2B, B2T = 0, 1, 2, 3
 F16, F32 = 0, 1
 ALGO_AUTO, ALGO_SINGLE_PASS, ALGO_THREE_PASS = 0, 1, 2
 STATUS = {0: "GLA_OK", 1: "GLA_EINVAL", 2: "GLA_EUNSUPPORTED", 3: "GLA_EWORKSPACE", 4: "GLA_EHIP"}
-EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_workspace_init", "gla_status_str",
+EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_workspace_init", "gla_gate_logits",
+           "gla_fwd_gate_proj", "gla_workspace_size_gate_proj", "gla_status_str",
            "gla_abi_version")
 
 
@@ -37,6 +38,18 @@ class GlaOpts(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("segment_chunks", ctypes.c_int32),
         ("algorithm", ctypes.c_int32),
+    ]
+
+
+class GlaGateProj(ctypes.Structure):
+    """Mirror of ``gla_gate_proj`` (include/gla.h)."""
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("w1", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("d_model", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
     ]
 
 
@@ -65,6 +78,15 @@ def lib():
         h.gla_workspace_size.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(GlaOpts)]
         h.gla_workspace_init.restype = ctypes.c_int
         h.gla_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        h.gla_gate_logits.restype = ctypes.c_int
+        h.gla_gate_logits.argtypes = [ctypes.POINTER(GlaGateProj)] + [ctypes.c_int] * 5 + \
+            [ctypes.c_void_p, ctypes.c_void_p]
+        h.gla_fwd_gate_proj.restype = ctypes.c_int
+        h.gla_fwd_gate_proj.argtypes = [ctypes.c_void_p] * 3 + [ctypes.POINTER(GlaGateProj)] + \
+            [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(GlaOpts)]
+        h.gla_workspace_size_gate_proj.restype = ctypes.c_size_t
+        h.gla_workspace_size_gate_proj.argtypes = [ctypes.c_int] * 4 + \
+            [ctypes.POINTER(GlaGateProj), ctypes.POINTER(GlaOpts)]
         h.gla_status_str.restype = ctypes.c_char_p
         h.gla_status_str.argtypes = [ctypes.c_int]
         h.gla_abi_version.restype = ctypes.c_int
@@ -164,4 +186,96 @@ def fwd(q, k, v, z, direction, H, W, chunk=64, r=None, norm_weight=None, eps=1e-
                        ctypes.byref(opts))
     if st != 0:
         raise GlaError(st, f"gla_fwd failed: {status_str(st)}")
+    return out
+
+
+def make_gate(x, w1, w2, bias=None) -> GlaGateProj:
+    """``gla_gate_proj`` over device tensors x [B, L, d_model], w1 [rank, d_model]
+    (x's dtype), w2 [NH*dk, rank] and bias [NH*dk] (float32)."""
+    torch = _torch()
+    for name, t in (("x", x), ("w1", w1), ("w2", w2), ("bias", bias)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if w1.dtype != x.dtype:
+        raise TypeError("w1 must have x's dtype")
+    if w2.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise TypeError("w2 and bias must be float32")
+    rank, d_model = w1.shape
+    if x.shape[-1] != d_model or w2.shape[1] != rank:
+        raise ValueError("gate projection shapes do not match")
+    return GlaGateProj(x.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                       bias.data_ptr() if bias is not None else None, d_model, rank)
+
+
+def gate_logits(x, w1, w2, bias, heads, out=None, stream=None):
+    """Gate logits z = (x W1) W2 + b (include/gla.h: gla_gate_logits).
+    x: [B, L, d_model] float16/float32; returns z [B, L, heads, dk] float32."""
+    torch = _torch()
+    B, L, _ = x.shape
+    nout = w2.shape[0]
+    if nout % heads:
+        raise ValueError("w2 rows must be heads * dk")
+    dk = nout // heads
+    dtype = F16 if x.dtype == torch.float16 else F32 if x.dtype == torch.float32 else None
+    if dtype is None:
+        raise TypeError("x must be float16 or float32")
+    gate = make_gate(x, w1, w2, bias)
+    if out is None:
+        out = torch.empty((B, L, heads, dk), dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = lib().gla_gate_logits(ctypes.byref(gate), B, L, heads, dk, dtype, out.data_ptr(), stream)
+    if st != 0:
+        raise GlaError(st, f"gla_gate_logits failed: {status_str(st)}")
+    return out
+
+
+def workspace_size_gate_proj(direction, H, W, chunk, gate: GlaGateProj, opts: GlaOpts) -> int:
+    return lib().gla_workspace_size_gate_proj(direction, H, W, chunk, ctypes.byref(gate),
+                                              ctypes.byref(opts))
+
+
+def fwd_gate_proj(q, k, v, x, w1, w2, bias, direction, H, W, chunk=64, r=None,
+                  norm_weight=None, eps=1e-6, out=None, tau=16.0, scale=None, segment_chunks=0,
+                  workspace=None, stream=None, algorithm=ALGO_AUTO):
+    """gla_fwd with the gate logits projected from x in the library
+    (include/gla.h: gla_fwd_gate_proj).  q, k: [B, L, NH, dk]; v, r:
+    [B, L, NH, dv]; x: [B, L, d_model] and w1: [rank, d_model] in q's dtype;
+    w2: [NH*dk, rank], bias: [NH*dk] float32 (or None)."""
+    torch = _torch()
+    B, L, NH, dk = q.shape
+    dv = v.shape[3]
+    if q.dtype == torch.float16:
+        dtype = F16
+    elif q.dtype == torch.float32:
+        dtype = F32
+    else:
+        raise TypeError("q must be float16 or float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("r", r), ("norm_weight", norm_weight)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    for name, t in (("k", k), ("v", v), ("r", r), ("x", x)):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    if tuple(x.shape[:2]) != (B, L) or w2.shape[0] != NH * dk:
+        raise ValueError("x must be [B, L, d_model] and w2 [NH*dk, rank]")
+    gate = make_gate(x, w1, w2, bias)
+    if out is None:
+        out = torch.empty((B, L, NH, dv), dtype=q.dtype, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = make_opts(B, NH, dk, dv, dtype, tau, scale, eps,
+                     norm_weight.data_ptr() if norm_weight is not None else 0,
+                     stream=stream, segment_chunks=segment_chunks, algorithm=algorithm)
+    need = workspace_size_gate_proj(direction, H, W, chunk, gate, opts)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().gla_fwd_gate_proj(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(gate),
+                                 direction, H, W, chunk, out.data_ptr(),
+                                 r.data_ptr() if r is not None else None, ctypes.byref(opts))
+    if st != 0:
+        raise GlaError(st, f"gla_fwd_gate_proj failed: {status_str(st)}")
     return out

@@ -31,6 +31,19 @@ WORKLOADS = {
                            z=(2.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T) * 3, gated=True),
 }
 
+# The retention gate's logits computed in the library from the block input
+# (x W1 W2 + b, rank 16; d_model = NH * dk = 384 as in a 6-head, 64-dim
+# backbone stage) instead of read as z: the 640 px frame and batch shapes.
+GATE_PROJ = {
+    "frame640_gateproj": dict(index=6, B=1, NH=6, H=40, W=40, dk=64, dv=64, dtype="f16",
+                              z=(0.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T), gated=False,
+                              gate_proj=dict(d_model=384, rank=16)),
+    "batch640_gateproj": dict(index=7, B=8, NH=6, H=40, W=40, dk=64, dv=64, dtype="f16",
+                              z=(0.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T), gated=True,
+                              gate_proj=dict(d_model=384, rank=16)),
+}
+WORKLOADS.update(GATE_PROJ)
+
 # Length and batch sweep at the pages' own kernel points (16x16 = 256 tokens,
 # the 1.6K frame, 128x128 = 16.4K tokens) at d = 64 with 6 heads, plus a tail
 # grid (42x42 = 1764 tokens, not a multiple of the 64-token chunk); the four
@@ -101,9 +114,15 @@ def workload_inputs(name: str, call: int = 0, **overrides):
     """Inputs of call ``call`` of a named workload; seed = 1000*index + call."""
     spec = dict(WORKLOADS[name])
     spec.update(overrides)
-    return make_inputs(spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"], spec["dv"],
-                       spec["dtype"], spec["z"], spec["gated"],
-                       seed=1000 * spec["index"] + call)
+    x = make_inputs(spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"], spec["dv"],
+                    spec["dtype"], spec["z"], spec["gated"], seed=1000 * spec["index"] + call)
+    gp = spec.get("gate_proj")
+    if gp:
+        # projection operands from their own stream (seed + 500); z is unused
+        x.update(make_gate_proj_inputs(spec["B"], spec["H"] * spec["W"], spec["NH"], spec["dk"],
+                                       gp["d_model"], gp["rank"], spec["dtype"],
+                                       seed=1000 * spec["index"] + 500 + call))
+    return x
 
 
 def make_inputs_device(B, NH, H, W, dk, dv, dtype="f16", z=(0.0, 1.0), gated=False, seed=0,
@@ -131,3 +150,24 @@ def make_inputs_device(B, NH, H, W, dk, dv, dtype="f16", z=(0.0, 1.0), gated=Fal
         r = normal((B, L, NH, dv)).to(dt)
         w = torch.rand((dv,), generator=gen, device=device, dtype=torch.float32) + 0.5
     return dict(q=q, k=k, v=v, z=zz, r=r, w=w)
+
+
+def make_gate_proj_inputs_device(B, L, NH, dk, d_model, rank=16, dtype="f16", seed=0,
+                                 device="cuda"):
+    """Same distributions as :func:`make_gate_proj_inputs`, drawn on the device
+    with a seeded torch generator (timing inputs)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = {"f16": torch.float16, "f32": torch.float32}[dtype]
+
+    def normal(shape, std=1.0):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std
+
+    x = normal((B, L, d_model)).to(dt)
+    w1 = normal((rank, d_model), d_model ** -0.5).to(dt)
+    w2 = normal((NH * dk, rank), rank ** -0.5)
+    lim = rank ** -0.5
+    bias = (torch.rand((NH * dk,), generator=gen, device=device, dtype=torch.float32) * 2 - 1) * lim
+    return dict(x=x, w1=w1, w2=w2, bias=bias)

@@ -1,0 +1,243 @@
+"""Low-rank retention-gate projection (paper "GTR: Gated Token Recurrence for
+Efficient Dense Prediction", Section 2.1: the gate logits are x W1 W2 + b with
+rank 16).
+
+CPU part: argument checks and workspace sizes of gla_gate_logits and
+gla_fwd_gate_proj through the C ABI (fake addresses, never dereferenced).
+GPU part: the projection kernel and the forward with the projection (fused
+into the single pass, or staged through the workspace) against the fp64
+oracle on the same seeded inputs, to the bars of the other parity tests.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from recurrent_vision_backbone_key_amd import gla
+from recurrent_vision_backbone_key_amd.inputs import (WORKLOADS, make_gate_proj_inputs,
+                                                      make_inputs, workload_inputs)
+
+A = 1 << 32
+MB = 1 << 26
+
+
+def _gate(x=A + 8 * MB, w1=A + 9 * MB, w2=A + 10 * MB, bias=A + 11 * MB, d_model=384, rank=16):
+    return gla.GlaGateProj(x, w1, w2, bias, d_model, rank)
+
+
+def _fwdp(gate=None, q=A, k=A + MB, v=A + 2 * MB, out=A + 5 * MB, r=None, direction=0, H=40,
+          W=40, chunk=64, opts=None):
+    gate = gate if gate is not None else _gate()
+    opts = opts or gla.make_opts(1, 6, 64, 64, gla.F16, segment_chunks=1000)
+    return gla.lib().gla_fwd_gate_proj(q, k, v, ctypes.byref(gate), direction, H, W, chunk, out,
+                                       r, ctypes.byref(opts))
+
+
+def test_abi_version_two():
+    assert gla.abi_version() == 2
+
+
+def test_fwd_gate_proj_argument_checks():
+    h = gla.lib()
+    opts = gla.make_opts(1, 6, 64, 64, gla.F16, segment_chunks=1000)
+    assert h.gla_fwd_gate_proj(A, A + MB, A + 2 * MB, None, 0, 40, 40, 64, A + 5 * MB, None,
+                               ctypes.byref(opts)) == 1
+    for field in ("x", "w1", "w2"):
+        g = _gate()
+        setattr(g, field, None)
+        assert _fwdp(gate=g) == 1, field
+    for d_model, rank in ((0, 16), (12, 16), (384, 0), (384, 65), (1 << 17, 16)):
+        assert _fwdp(gate=_gate(d_model=d_model, rank=rank)) == 1, (d_model, rank)
+    assert _fwdp(gate=_gate(x=A + 8 * MB + 8)) == 1      # x not 16-byte aligned
+    assert _fwdp(gate=_gate(w1=A + 9 * MB + 4)) == 1     # w1 not 16-byte aligned
+    assert _fwdp(gate=_gate(w2=A + 10 * MB + 2)) == 1    # w2 not 4-byte aligned
+    # out overlapping each projection operand
+    assert _fwdp(out=A + 8 * MB + 64) == 1
+    assert _fwdp(out=A + 9 * MB) == 1
+    assert _fwdp(gate=_gate(w2=A + 5 * MB + 1024)) == 1
+    assert _fwdp(gate=_gate(bias=A + 5 * MB + 4)) == 1
+    assert _fwdp(q=None) == 1
+
+
+def test_workspace_sizes_gate_proj():
+    opts = gla.make_opts(8, 6, 64, 64, gla.F16)
+    base = gla.workspace_size(0, 40, 40, 64, opts)
+    # fused into the single pass: same workspace as gla_fwd
+    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(), opts) == base
+    zbytes = 8 * 1600 * 6 * 64 * 4
+    staged = ((base + 255) // 256) * 256 + zbytes
+    # not fused (d_model too large for the staged W1, or rank != 16): z staged
+    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(d_model=768), opts) == staged
+    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(rank=8), opts) == staged
+    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(d_model=352), opts) == staged
+    # three passes in one segment: only z
+    o3 = gla.make_opts(8, 6, 64, 64, gla.F16, segment_chunks=1000)
+    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(), o3) == zbytes
+    # rejected arguments give 0
+    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(rank=0), opts) == 0
+    # a workspace that only fits gla_fwd is too small when z is staged
+    o3.workspace = A + 64 * MB
+    o3.workspace_bytes = zbytes - 16
+    assert _fwdp(opts=o3) == 3
+
+
+def test_gate_logits_argument_checks():
+    h = gla.lib()
+
+    def call(gate=None, B=2, L=100, NH=6, dk=64, dtype=gla.F16, z=A + 20 * MB):
+        gate = gate if gate is not None else _gate()
+        return h.gla_gate_logits(ctypes.byref(gate), B, L, NH, dk, dtype, z, None)
+
+    assert h.gla_gate_logits(None, 2, 100, 6, 64, gla.F16, A + 20 * MB, None) == 1
+    assert call(z=None) == 1
+    assert call(B=0) == 1
+    assert call(L=0) == 1
+    assert call(NH=0) == 1
+    assert call(dk=48) == 2
+    assert call(dtype=5) == 2
+    assert call(z=A + 20 * MB + 4) == 1
+    assert call(z=A + 8 * MB + 1024) == 1   # z overlapping x
+    assert call(gate=_gate(rank=70)) == 1
+
+
+# ------------------------------------------------------------------- GPU
+
+def _dev(a, torch):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    return t
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("B,L,NH,dk,d_model,rank", [
+    (2, 1600, 6, 64, 384, 16),
+    (1, 77, 2, 16, 40, 1),      # ragged token count, odd k-steps
+    (1, 130, 3, 32, 72, 5),
+    (1, 64, 1, 128, 256, 64),   # four rank tiles
+    (3, 33, 4, 64, 1024, 16),
+])
+def test_gate_logits_kernel(torch, dtype, B, L, NH, dk, d_model, rank):
+    g = make_gate_proj_inputs(B, L, NH, dk, d_model, rank, dtype, seed=100 + L)
+    print(f"[case] gate_logits {dtype} B={B} L={L} NH={NH} dk={dk} d_model={d_model} "
+          f"rank={rank}", flush=True)
+    d = {n: _dev(g[n], torch) for n in g}
+    z = gla.gate_logits(d["x"], d["w1"], d["w2"], d["bias"], NH)
+    torch.cuda.synchronize()
+    ref = oracle.gate_logits(g["x"], g["w1"], g["w2"], g["bias"], NH)
+    err = float(np.max(np.abs(z.cpu().numpy() - ref)) / np.max(np.abs(ref)))
+    print(f"[parity] gate_logits: {err:.3e}", flush=True)
+    assert err <= 1e-5
+
+
+def _run_fwd_proj(x, direction, H, W, chunk, torch, **kw):
+    d = {n: _dev(x[n], torch) for n in ("q", "k", "v", "r", "w", "x", "w1", "w2", "bias")}
+    B, L, NH, dk = x["q"].shape
+    gate = gla.make_gate(d["x"], d["w1"], d["w2"], d["bias"])
+    opts = gla.make_opts(B, NH, dk, x["v"].shape[3],
+                         gla.F16 if x["q"].dtype == np.float16 else gla.F32,
+                         segment_chunks=kw.get("segment_chunks", 0),
+                         algorithm=kw.get("algorithm", gla.ALGO_AUTO))
+    need = gla.workspace_size_gate_proj(direction, H, W, chunk, gate, opts)
+    ws = torch.full((max(need, 16),), 0xA5, dtype=torch.uint8, device="cuda")
+    gla.workspace_init(ws)
+    y = gla.fwd_gate_proj(d["q"], d["k"], d["v"], d["x"], d["w1"], d["w2"], d["bias"], direction,
+                          H, W, chunk=chunk, r=d["r"], norm_weight=d["w"], workspace=ws, **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ws
+
+
+def _oracle_proj(x, direction, H, W):
+    NH = x["q"].shape[2]
+    z = oracle.gate_logits(x["x"], x["w1"], x["w2"], x["bias"], NH)
+    return oracle.fwd(x["q"], x["k"], x["v"], z, direction, H, W, r=x["r"], w=x["w"])
+
+
+def _check_proj(name, x, direction, H, W, chunk, tol, torch, **kw):
+    print(f"[case] {name} dir={direction} H={H} W={W} chunk={chunk} {kw}", flush=True)
+    got, ws = _run_fwd_proj(x, direction, H, W, chunk, torch, **kw)
+    ref = _oracle_proj(x, direction, H, W)
+    err = float(np.max(np.abs(got.astype(np.float64) - ref)) / np.max(np.abs(ref)))
+    print(f"[parity] {name}: {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err <= tol, f"{name}: {err:.3e} > {tol:.0e}"
+    return got, ws
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("direction", (0, 1, 2, 3))
+def test_frame640_gateproj(torch, direction):
+    s = WORKLOADS["frame640_gateproj"]
+    x = workload_inputs("frame640_gateproj", call=direction)
+    _check_proj("frame640_gateproj", x, direction, s["H"], s["W"], 64, 2e-3, torch)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("call", range(4))
+def test_batch640_gateproj(torch, call):
+    s = WORKLOADS["batch640_gateproj"]
+    x = workload_inputs("batch640_gateproj", call=call)
+    _, ws = _check_proj("batch640_gateproj", x, s["dirs"][call], s["H"], s["W"], 64, 2e-3, torch)
+    err = int(ws[4:8].cpu().numpy().view(np.uint32)[0])
+    assert err == 0, f"look-back error flag set: {err:#x}"
+
+
+def _proj_inputs(B, NH, H, W, dk, d_model, rank, dtype="f16", gated=True, seed=0):
+    x = make_inputs(B, NH, H, W, dk, dk, dtype, gated=gated, seed=seed)
+    x.update(make_gate_proj_inputs(B, H * W, NH, dk, d_model, rank, dtype, seed=seed + 1))
+    return x
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,NH,H,W,d_model,seg", [
+    (1, 2, 42, 42, 384, 0),    # ragged tail chunk
+    (2, 3, 9, 7, 64, 0),       # one chunk, smallest fused d_model
+    (1, 4, 40, 40, 128, 1),    # one-chunk segments
+    (1, 2, 40, 40, 256, 7),    # seven-chunk segments
+    (3, 4, 30, 40, 384, 0),    # scans spread over the XCDs
+])
+def test_fused_projection_shapes(torch, B, NH, H, W, d_model, seg):
+    x = _proj_inputs(B, NH, H, W, 64, d_model, 16, seed=7 * H + W)
+    for direction in (0, 3):
+        _check_proj(f"fused d_model={d_model}", x, direction, H, W, 64, 2e-3, torch,
+                    segment_chunks=seg)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,B,NH,H,W,dk,d_model,rank,dtype,algo", [
+    ("staged d_model=768", 1, 6, 40, 40, 64, 768, 16, "f16", 0),
+    ("staged rank=8", 2, 3, 20, 24, 64, 192, 8, "f16", 0),
+    ("staged three-pass", 1, 6, 40, 40, 64, 384, 16, "f16", 2),
+    ("staged d=128", 1, 2, 32, 40, 128, 256, 16, "f16", 0),
+    ("staged d=32", 2, 2, 16, 20, 32, 64, 16, "f16", 0),
+    ("staged fp32", 1, 1, 8, 8, 16, 32, 16, "f32", 0),
+])
+def test_staged_projection(torch, name, B, NH, H, W, dk, d_model, rank, dtype, algo):
+    x = _proj_inputs(B, NH, H, W, dk, d_model, rank, dtype, seed=H * W + dk)
+    tol = 2e-3 if dtype == "f16" else 1e-5
+    chunk = 16 if dtype == "f32" else 64
+    for direction in (1, 2):
+        _check_proj(name, x, direction, H, W, chunk, tol, torch, algorithm=algo)
+
+
+@pytest.mark.gpu
+def test_fused_equals_staged_within_rounding(torch):
+    """The fused single pass and the staged path (projection kernel + the
+    ordinary single pass) agree closely: same scan, only z's rounding order
+    differs."""
+    x = _proj_inputs(2, 6, 40, 40, 64, 384, 16, seed=3)
+    fused, _ = _run_fwd_proj(x, 0, 40, 40, 64, torch)
+    d = {n: _dev(x[n], torch) for n in ("q", "k", "v", "r", "w", "x", "w1", "w2", "bias")}
+    z = gla.gate_logits(d["x"], d["w1"], d["w2"], d["bias"], 6)
+    staged = gla.fwd(d["q"], d["k"], d["v"], z, 0, 40, 40, r=d["r"], norm_weight=d["w"])
+    torch.cuda.synchronize()
+    s = staged.cpu().numpy().astype(np.float64)
+    err = float(np.max(np.abs(fused.astype(np.float64) - s)) / np.max(np.abs(s)))
+    print(f"[parity] fused vs staged: {err:.3e}", flush=True)
+    assert err <= 1e-3
