@@ -30,9 +30,22 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20     # last-level (Infinity) cache
 
 
-def algorithmic_bytes_per_token_head(dk, dv, es, gated):
-    """Compulsory HBM traffic: q, k, v, z (fp32) read, out written, r read if gated."""
-    return es * (2 * dk + dv) + 4 * dk + es * dv + (es * dv if gated else 0)
+def algorithmic_bytes_per_token_head(dk, dv, es, gated, gate_proj=None, heads=1):
+    """Compulsory HBM traffic: q, k, v, z (fp32) read, out written, r read if
+    gated.  With the gate projection, x (d_model values per token, shared by
+    the heads) is read in place of z."""
+    gate_in = 4 * dk if gate_proj is None else es * gate_proj["d_model"] / heads
+    return es * (2 * dk + dv) + gate_in + es * dv + (es * dv if gated else 0)
+
+
+def weight_bytes_per_call(spec, es):
+    """Per-call parameters: RMSNorm weight if gated, projection weights."""
+    n = 4 * spec["dv"] if spec["gated"] else 0
+    gp = spec.get("gate_proj")
+    if gp:
+        nout = spec["NH"] * spec["dk"]
+        n += es * gp["rank"] * gp["d_model"] + 4 * nout * gp["rank"] + 4 * nout
+    return n
 
 
 def algorithmic_flops_per_token_head(dk, dv, chunk):
@@ -63,10 +76,14 @@ def load_traffic(workload, calls_per_step):
     return rec.get("hbm_bytes_per_call")
 
 
-def kernel_label(spec, chunk):
+def kernel_label(spec, chunk, staged=False):
     """The kernels one call launches (the plan picks the single pass for
     binary16, d = 64, 64-token chunks; the three passes otherwise)."""
     if spec["dtype"] == "f16" and spec["dk"] == 64 and chunk == 64:
+        if spec.get("gate_proj"):
+            if staged:
+                return "gla_gate_logits_kernel + gla_onepass_kernel (projection staged: two launches)"
+            return "gla_onepass_kernel<gate projection fused> (single pass: one launch per call)"
         return "gla_onepass_kernel (single pass: one launch per call)"
     if spec["dtype"] == "f16" and spec["dk"] == 128 and chunk == 64:
         return ("gla_wide_kernel<aggregate> + gla_fold_kernel + gla_wide_kernel<output> "
@@ -150,7 +167,11 @@ def cpu_baseline(spec, name, seconds):
         x = inputs[call]
         u0 = (calls * per_call_units) % units_total
         u1 = min(units_total, u0 + per_call_units)
-        oracle.fwd(x["q"], x["k"], x["v"], x["z"], spec["dirs"][call], H, W, r=x["r"],
+        z = x["z"]
+        if spec.get("gate_proj"):
+            z = oracle.gate_logits(x["x"], x["w1"], x["w2"], x["bias"], spec["NH"],
+                                   threads=cores)
+        oracle.fwd(x["q"], x["k"], x["v"], z, spec["dirs"][call], H, W, r=x["r"],
                    w=x["w"], units=(u0, u1), threads=cores)
         done_th += (u1 - u0) * H * W
         calls += 1
@@ -160,7 +181,9 @@ def cpu_baseline(spec, name, seconds):
     return {"value": done_th / dt / 1e9, "unit": "Gtok·head/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{calls} oracle calls of {name} ({spec['H']}x{spec['W']}, d={spec['dk']}), "
-                      f"{per_call_units} of {units_total} (batch, head) scans each, "
+                      + ("gate logits of every token projected per call, "
+                         if spec.get("gate_proj") else "")
+                      + f"{per_call_units} of {units_total} (batch, head) scans each, "
                       f"{done_th} token-heads in {dt:.1f} s"}
 
 
@@ -180,6 +203,8 @@ def main():
                     help="steps captured in one HIP graph (0: 10, or 1 for steps over 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--staged", action="store_true",
+                    help="gate-projection workloads: gla_gate_logits then gla_fwd (unfused)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every length/batch sweep point (one JSON line each)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -216,7 +241,8 @@ def main():
     import torch
 
     from recurrent_vision_backbone_key_amd import gla
-    from recurrent_vision_backbone_key_amd.inputs import make_inputs_device, tokens_per_call
+    from recurrent_vision_backbone_key_amd.inputs import (make_gate_proj_inputs_device,
+                                                          make_inputs_device, tokens_per_call)
 
     spec = WORKLOADS[args.workload]
     name = args.workload
@@ -226,8 +252,11 @@ def main():
     B, NH, H, W, dk, dv = spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"], spec["dv"]
     es = 2 if spec["dtype"] == "f16" else 4
     gated = spec["gated"]
+    gp = spec.get("gate_proj")
+    staged = bool(args.staged and gp)
     th_call = tokens_per_call(spec)
-    bytes_call = th_call * algorithmic_bytes_per_token_head(dk, dv, es, gated) + (4 * dv if gated else 0)
+    bytes_call = int(th_call * algorithmic_bytes_per_token_head(dk, dv, es, gated, gp, NH)
+                     + weight_bytes_per_call(spec, es))
     flops_call = th_call * algorithmic_flops_per_token_head(dk, dv, chunk)
     step_bytes = bytes_call * calls_per_step
     rotate = args.rotate or max(1, math.ceil(2 * MALL_BYTES / step_bytes))
@@ -250,7 +279,20 @@ def main():
             out = torch.empty((B, H * W, NH, dv), dtype=x["q"].dtype, device=dev)
             opts = gla.make_opts(B, NH, dk, dv, gla.F16 if es == 2 else gla.F32,
                                  segment_chunks=args.segment_chunks)
-            need = gla.workspace_size(d, H, W, chunk, opts)
+            if gp:
+                # z is not an input: the projection operands replace it (the
+                # staged variant writes z into a buffer of its own)
+                x["z"] = torch.empty_like(x["z"]) if staged else None
+                x.update(make_gate_proj_inputs_device(B, H * W, NH, dk, gp["d_model"], gp["rank"],
+                                                      spec["dtype"],
+                                                      seed=1000 * spec["index"] + 500 + 100 * r + c,
+                                                      device=dev))
+            if gp and not staged:
+                need = gla.workspace_size_gate_proj(d, H, W, chunk,
+                                                    gla.make_gate(x["x"], x["w1"], x["w2"], x["bias"]),
+                                                    opts)
+            else:
+                need = gla.workspace_size(d, H, W, chunk, opts)
             ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
             calls.append((x, d, out, ws))
         sets.append(calls)
@@ -259,6 +301,13 @@ def main():
 
     def step(r):
         for x, d, out, ws in sets[r]:
+            if gp and not staged:
+                gla.fwd_gate_proj(x["q"], x["k"], x["v"], x["x"], x["w1"], x["w2"], x["bias"], d,
+                                  H, W, chunk=chunk, r=x["r"], norm_weight=x["w"], eps=1e-6,
+                                  out=out, segment_chunks=args.segment_chunks, workspace=ws)
+                continue
+            if staged:
+                gla.gate_logits(x["x"], x["w1"], x["w2"], x["bias"], NH, out=x["z"])
             gla.fwd(x["q"], x["k"], x["v"], x["z"], d, H, W, chunk=chunk, r=x["r"],
                     norm_weight=x["w"], eps=1e-6, out=out, segment_chunks=args.segment_chunks,
                     workspace=ws)
@@ -316,11 +365,11 @@ def main():
     value = calls_per_step * th_call / (ms_step * 1e-3) / 1e9
 
     achieved = bytes_call / (us_call * 1e-6) / 1e9
-    traffic = load_traffic(name, calls_per_step)
+    traffic = None if staged else load_traffic(name, calls_per_step)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": kernel_label(spec, chunk),
+                "kernel": kernel_label(spec, chunk, staged),
                 "algorithmic_bytes_per_call": bytes_call,
                 "mfma_frac": round(flops_call / (us_call * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 5)}
 
@@ -333,6 +382,7 @@ def main():
                    "dk": dk, "dv": dv, "chunk": chunk,
                    "dirs": ",".join("L2R R2L T2B B2T".split()[d] for d in dirs),
                    "gated": gated, "calls_per_step": calls_per_step,
+                   **({"gate_projection": dict(gp, staged=staged)} if gp else {}),
                    "input_sets": rotate, "hip_graph": graphs is not None,
                    "steps_per_graph": G,
                    "workspace_bytes_per_call": nseg_bytes, "accumulate": "f32"},

@@ -149,6 +149,7 @@ typedef struct gla_gate_proj {
     const void *w1;      /* [rank, d_model] W1 transposed, same storage as x   */
     const float *w2;     /* [NH*dk, rank] W2 transposed, binary32             */
     const float *bias;   /* [NH*dk] binary32; NULL selects zeros              */
+    /* every pointer above: device memory, 16-byte aligned                     */
     int32_t d_model;     /* >= 8, a multiple of 8                             */
     int32_t rank;        /* 1 .. 64 (the pages use 16)                        */
 } gla_gate_proj;
@@ -156,8 +157,8 @@ typedef struct gla_gate_proj {
 /*
  * gla_gate_logits -- the projection alone: writes z [batch, tokens, heads, dk]
  * binary32 (the gate_logits operand of gla_fwd) on `stream` (hipStream_t,
- * NULL selects the null stream).  x, w1 and z are 16-byte aligned device
- * pointers, w2 and bias 4-byte aligned; z must not overlap an input.
+ * NULL selects the null stream).  z is a 16-byte aligned device pointer that
+ * must not overlap an input.
  * dtype: GLA_F16 or GLA_F32, the storage of x and w1; dk in {16, 32, 64, 128}.
  * GLA_EINVAL on a bad pointer, size or overlap, GLA_EUNSUPPORTED on a dtype
  * or dk outside the built set, GLA_EHIP on a launch failure.
@@ -169,14 +170,15 @@ GLA_API int gla_gate_logits(const gla_gate_proj *gate, int batch, int tokens, in
  * gla_fwd_gate_proj -- gla_fwd with the gate logits computed from the block
  * input by the low-rank projection above instead of read from memory.
  * Arguments as for gla_fwd, with `gate` in place of gate_logits (x and w1
- * stored as opts->dtype).  For the single-pass configuration with rank 16,
- * d_model a multiple of 64 and d_model <= 384, the projection runs inside
- * the single-pass kernel (the 64 x rank products of x and W1 on the matrix
- * cores, the rank x d_k product with W2 in binary32), so z never reaches
- * memory.  Every other configuration writes z into the workspace with the
- * kernel of gla_gate_logits first and then runs the ordinary forward.  The
- * workspace must hold gla_workspace_size_gate_proj() bytes, cleared once with
- * gla_workspace_init() as for gla_fwd.  Returns a gla_status as gla_fwd.
+ * stored as opts->dtype).  For the single-pass configuration with rank 16
+ * (any d_model), a first kernel writes x W1 (16 binary32 values per token,
+ * shared by the heads) into the workspace and the single pass expands it
+ * with each head's W2 columns and bias on the matrix cores in binary32, so
+ * the logits never reach memory.  Every other configuration writes z into
+ * the workspace with the kernel of gla_gate_logits first and then runs the
+ * ordinary forward.  The workspace must hold gla_workspace_size_gate_proj()
+ * bytes, cleared once with gla_workspace_init() as for gla_fwd.  Returns a
+ * gla_status as gla_fwd.
  */
 GLA_API int gla_fwd_gate_proj(const void *q, const void *k, const void *v,
                               const gla_gate_proj *gate, int dir, int H, int W, int chunk,

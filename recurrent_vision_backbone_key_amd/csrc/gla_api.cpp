@@ -62,9 +62,7 @@ gla::GateProj gate_of(const gla_gate_proj* g)
 
 void no_proj(gla::Params& P)
 {
-    P.gx = P.gw1 = nullptr;
-    P.gw2 = P.gb = nullptr;
-    P.d_model = 0;
+    P.ghp = P.gw2 = P.gb = nullptr;
 }
 
 }  // namespace
@@ -92,12 +90,16 @@ extern "C" int gla_fwd_gate_proj(const void* q, const void* k, const void* v,
     gla::Params P;
     no_proj(P);
     if (plan.proj_fused) {
+        // x W1 (16 values per token) into the workspace; the single pass
+        // expands it with W2 and b per head
+        float* hp = (float*)((char*)opts->workspace + plan.off_z);
+        const int ls = gla::launch_gate_rank(gate_of(gate), opts->dtype, opts->batch * plan.L, hp,
+                                             opts->stream);
+        if (ls != GLA_OK) return ls;
         P.z = nullptr;
-        P.gx = gate->x;
-        P.gw1 = gate->w1;
+        P.ghp = hp;
         P.gw2 = gate->w2;
         P.gb = gate->bias;
-        P.d_model = gate->d_model;
     } else {
         // z staged in the workspace by the projection kernel, then the
         // ordinary forward on the same stream

@@ -36,12 +36,10 @@ struct Params {
     float scale;        // output scale
     float inv_tau;      // 1 / tau
     float eps;          // RMSNorm epsilon
-    // single pass with the gate projection fused (z == null): rank 16
-    const void* gx;     // [B, L, d_model] block input (binary16)
-    const void* gw1;    // [16, d_model] W1 transposed (binary16)
+    // single pass with the gate expansion fused (z == null): rank 16
+    const float* ghp;   // [B*L, 16] x W1 of every token
     const float* gw2;   // [NH*DK, 16] W2 transposed
     const float* gb;    // [NH*DK] gate bias, or null (zeros)
-    int d_model;
 };
 
 // Low-rank gate projection operands (include/gla.h, gla_gate_proj).
@@ -54,9 +52,7 @@ struct GateProj {
     int rank;
 };
 
-// Largest d_model of the gate projection fused into the single pass (its W1
-// is staged in shared memory) and the rank it is built for.
-constexpr int kFusedProjMaxDModel = 384;
+// Rank of the gate projection whose W2 expansion is fused into the single pass.
 constexpr int kFusedProjRank = 16;
 
 // Launches the aggregate, fold and output passes (or only the output pass
@@ -75,6 +71,9 @@ int launch_onepass(const Params& P, void* stream);
 
 // Gate logits z [tokens, nout] binary32 from the low-rank projection.
 int launch_gate_logits(const GateProj& G, int dtype, int tokens, int nout, float* z, void* stream);
+
+// First factor alone: hp = x W1, [tokens, 16 ceil(rank / 16)] binary32.
+int launch_gate_rank(const GateProj& G, int dtype, int tokens, float* hp, void* stream);
 
 // Zero-fills a workspace (counters, flags) on `stream`.
 int launch_workspace_init(void* ws, size_t bytes, void* stream);

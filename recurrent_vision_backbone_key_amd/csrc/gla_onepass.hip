@@ -87,17 +87,13 @@ constexpr int L_SS = L_ROWS + NCH * C * 4;    // RMS partials   [NCH][2][C] f32
 constexpr int L_MISC = L_SS + NCH * 2 * C * 4;  // ticket, wide flags, look-back result
 constexpr int LDS_TOTAL = L_MISC + 64;
 static_assert(LDS_TOTAL <= kLdsLimit, "LDS budget of one CU exceeded");
-// fused gate projection (z = x W1 W2 + b, rank 16): extra buffers
-constexpr int KX = kFusedProjMaxDModel / 64;  // k-steps of x W1 per channel half
-constexpr int W1S = kFusedProjMaxDModel + 8;  // W1^T row stride (elements)
-constexpr int L_W1 = LDS_TOTAL;               // W1^T          [16][W1S] f16
-constexpr int L_W2 = L_W1 + 16 * W1S * 2;     // W2^T of the head [D][16] f32
+// fused gate expansion (z = hp W2 + b with hp = x W1 of rank 16 read per
+// token): this head's W2 rows and bias
+constexpr int L_W2 = LDS_TOTAL;               // W2^T of the head [D][16] f32
 constexpr int L_GB = L_W2 + D * 16 * 4;       // gate bias of the head [D] f32
 constexpr int LDS_PROJ = L_GB + D * 4;
-constexpr int L_HP = L_FAC;                   // partial x W1 of each wave [NW][64][4] f32
-static_assert(kFusedProjRank == 16, "the fused projection is built for rank 16");
-static_assert(NW * 64 * 16 <= NW * 8 * 32 * 4, "projection partials exceed the factor tables");
-static_assert(LDS_PROJ <= kLdsLimit, "LDS budget of one CU exceeded (fused projection)");
+static_assert(kFusedProjRank == 16, "the fused gate expansion is built for rank 16");
+static_assert(LDS_PROJ <= kLdsLimit, "LDS budget of one CU exceeded (fused gate expansion)");
 // phase-2/3 aliases
 constexpr int L_LSEG = L_PA;                  // segment local state [D][D] f32 (16 KiB)
 constexpr int L_GSEG = L_PA + D * D * 4;      // segment total decay [D] f32
@@ -191,8 +187,10 @@ struct Raw {
     u32x4 q, k, v, z0, z1;  // 8 channels of one token (q, k, v binary16; z binary32)
 };
 
+// PROJ: instead of the 8 gate logits, the lane loads the 4 rank values
+// hp[token][4g .. 4g + 3] of its token (the B fragment of the expansion below).
 template <bool PROJ>
-__device__ __forceinline__ void load_raw(Raw& r, const Params& P, int row, int c0)
+__device__ __forceinline__ void load_raw(Raw& r, const Params& P, int row, int c0, int g)
 {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     r.q = r.k = r.v = r.z0 = r.z1 = zero;
@@ -201,45 +199,19 @@ __device__ __forceinline__ void load_raw(Raw& r, const Params& P, int row, int c
         r.q = *(const u32x4*)((const _Float16*)P.q + o);
         r.k = *(const u32x4*)((const _Float16*)P.k + o);
         r.v = *(const u32x4*)((const _Float16*)P.v + o);
-        if (!PROJ) {
+        if (PROJ) {
+            r.z0 = *(const u32x4*)(P.ghp + (size_t)(row / P.NH) * kFusedProjRank + 4 * g);
+        } else {
             r.z0 = *(const u32x4*)(P.z + o);
             r.z1 = *(const u32x4*)(P.z + o + 4);
         }
     }
 }
 
-// Fused gate projection.  x W1 for the 16 tokens of a sub-chunk is one
-// 16 x 16 tile hp^T (rows: the 16 ranks, columns: the tokens) accumulated over
-// d_model with v_mfma_f32_16x16x32_f16 (A: W1^T rows from LDS, B: the x row
-// of the lane's token, 16 bytes per k-step); the two waves of a sub-chunk
-// take one half of the k-steps each and add their partial tiles.  A lane
-// (token l16, group g) then holds hp[token][4g + e].
-//
-// x fragments of this lane's token for its half of the k-steps (kh steps of
-// 32 columns, kh = d_model / 64).
-__device__ __forceinline__ void load_x(half8 (&xr)[KX], const Params& P, int row, int h, int g, int kh)
-{
-    const half8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-    const _Float16* xp = (const _Float16*)P.gx + (size_t)(row >= 0 ? row / P.NH : 0) * P.d_model +
-                         8 * g + 32 * h * kh;
-#pragma unroll
-    for (int s = 0; s < KX; ++s) xr[s] = (row >= 0 && s < kh) ? *(const half8*)(xp + 32 * s) : zero;
-}
-// This wave's partial hp^T tile over its half of d_model.
-__device__ __forceinline__ float4v proj_partial(const half8 (&xr)[KX], const _Float16* sW1, int h,
-                                                int g, int l16, int kh)
-{
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KX; ++s) {
-        if (s >= kh) break;
-        const half8 a = *(const half8*)(sW1 + l16 * W1S + 32 * (h * kh + s) + 8 * g);
-        acc = mma(a, xr[s], acc);
-    }
-    return acc;
-}
-// Gate logits of this lane's token and 8 channels 32h + 8g + (0..7):
-// z^T = W2^T hp^T + b with v_mfma_f32_16x16x4_f32 in binary32.  Output tile T
+// Fused gate expansion.  Gate logits of this lane's token and 8 channels
+// 32h + 8g + (0..7): z^T = W2^T hp^T + b with v_mfma_f32_16x16x4_f32 in
+// binary32, where the lane (token l16, group g) holds hp[token][4g + e].
+// Output tile T
 // takes as its row r the channel 32h + 8 (r / 4) + 4T + r % 4, so that the
 // accumulator element e of lane (l16, g) is channel 32h + 8g + 4T + e of
 // token l16 -- the gate stage's layout.  At step s the lane's k element is
@@ -247,16 +219,22 @@ __device__ __forceinline__ float4v proj_partial(const half8 (&xr)[KX], const _Fl
 __device__ __forceinline__ void proj_logits(const float4v& hp, const float* sW2, const float* sGB,
                                             int h, int g, int l16, float (&zv)[8])
 {
+    float4v acc[2], w[2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-        float4v acc = *(const float4v*)(sGB + 32 * h + 8 * g + 4 * T);
+        acc[T] = *(const float4v*)(sGB + 32 * h + 8 * g + 4 * T);
         const int ch = 32 * h + 8 * (l16 >> 2) + 4 * T + (l16 & 3);
-        const float4v w = *(const float4v*)(sW2 + ch * 16 + 4 * g);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mma(w[s], hp[s], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) zv[4 * T + e] = acc[e];
+        w[T] = *(const float4v*)(sW2 + ch * 16 + 4 * g);
     }
+    // the two tiles' chains interleaved
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int T = 0; T < 2; ++T) acc[T] = mma(w[T][s], hp[s], acc[T]);
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zv[4 * T + e] = acc[T][e];
 }
 
 // Intra-chunk scores (M1, with the exchange of the two channel halves) and
@@ -441,36 +419,26 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     const int nch = min(P.nchunks, c_begin + P.seg_chunks) - c_begin;
     const bool gated = (P.r != nullptr);
 
+    // ---- first chunk's operands of this lane: issued before anything waits
+    Raw raw;
+    load_raw<PROJ>(raw, P, scan_row(P, unit, c_begin * C + tl), c0, g);
+
     // ---- row tables of every chunk of the segment
     for (int i = tid; i < nch * C; i += NT) sRows[i] = scan_row(P, unit, c_begin * C + i);
-    _Float16* sW1 = (_Float16*)(lds + L_W1);
     float* sW2 = (float*)(lds + L_W2);
     float* sGB = (float*)(lds + L_GB);
-    float* sHP = (float*)(lds + L_HP);
-    const int kh = PROJ ? P.d_model / 64 : 0;
     if (PROJ) {
-        // W1^T, this head's W2^T rows and bias
+        // this head's W2^T rows (D x 16) and bias: one 16-byte load per thread
         const int hd = unit % P.NH;
-        const int r8 = P.d_model / 8;
-        for (int i = tid; i < 16 * r8; i += NT) {
-            const int j = i / r8, m8 = i - j * r8;
-            *(u32x4*)(sW1 + j * W1S + 8 * m8) = *(const u32x4*)((const _Float16*)P.gw1 + (size_t)j * P.d_model + 8 * m8);
+        if (tid < D * 16 / 4) {
+            *(float4v*)(sW2 + 4 * tid) = *(const float4v*)(P.gw2 + (size_t)hd * D * 16 + 4 * tid);
+        } else if (tid < D * 16 / 4 + D / 4) {
+            const int i = tid - D * 16 / 4;
+            *(float4v*)(sGB + 4 * i) =
+                P.gb ? *(const float4v*)(P.gb + hd * D + 4 * i) : float4v{0.f, 0.f, 0.f, 0.f};
         }
-        for (int i = tid; i < D * 16; i += NT) sW2[i] = P.gw2[(size_t)hd * D * 16 + i];
-        if (tid < D) sGB[tid] = P.gb ? P.gb[hd * D + tid] : 0.f;
     }
     __syncthreads();
-
-    Raw raw;
-    load_raw<PROJ>(raw, P, sRows[tl], c0);
-    half8 xr[KX];
-    float4v hp_own = {0.f, 0.f, 0.f, 0.f};  // this wave's partial x W1 tile of the next chunk
-    if (PROJ) {
-        load_x(xr, P, sRows[tl], h, g, kh);
-        hp_own = proj_partial(xr, sW1, h, g, l16, kh);
-        *(float4v*)(sHP + (wave * 64 + lane) * 4) = hp_own;
-        __syncthreads();
-    }
 
     float4v okeep[NCH][2];
     half8 qkeep[NCH];    // this lane's 8 channels of the segment-relative query
@@ -502,15 +470,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             *(u32x4*)(sFQ + tl * SH + c0) = raw.q;
             *(u32x4*)(sFK + tl * SH + c0) = raw.k;
         }
-        if (PROJ) {
-            // both partial tiles of the sub-chunk (the sum is the same in both waves)
-            const float4v hp = hp_own + *(const float4v*)(sHP + ((wave ^ 4) * 64 + lane) * 4);
-            proj_logits(hp, sW2, sGB, h, g, l16, zv);
-        }
-        if (c + 1 < nch) {
-            load_raw<PROJ>(raw, P, sRows[(c + 1) * C + tl], c0);
-            if (PROJ) load_x(xr, P, sRows[(c + 1) * C + tl], h, g, kh);
-        }
+        if (PROJ) proj_logits(__builtin_bit_cast(float4v, raw.z0), sW2, sGB, h, g, l16, zv);
+        if (c + 1 < nch) load_raw<PROJ>(raw, P, sRows[(c + 1) * C + tl], c0, g);
 
         // ---- gate stage: log2-decay, prefix along the 16 tokens of the sub-chunk
         float bl[8];
@@ -658,12 +619,6 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 const half8 vf = *(const half8*)(sVT + (16 * bb + l16) * SH + 32 * kb + 8 * g);
                 S[jj] = mma(kf, vf, S[jj]);
             }
-        }
-        if (PROJ && c + 1 < nch) {
-            // partial x W1 of the next chunk (the factor tables it overwrites
-            // were last read before barrier (2))
-            hp_own = proj_partial(xr, sW1, h, g, l16, kh);
-            *(float4v*)(sHP + (wave * 64 + lane) * 4) = hp_own;
         }
         __syncthreads();  // (4) all readers of this chunk's buffers are done
 #pragma unroll
@@ -918,7 +873,7 @@ int launch_onepass(const Params& P, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
     const dim3 grid(P.xcd_local ? 8 * P.xcd_tasks : P.B * P.NH * P.nseg);
-    const bool proj = (P.gx != nullptr);
+    const bool proj = (P.ghp != nullptr);
     void (*kern)(Params) = P.xcd_local ? (proj ? onepass::gla_onepass_kernel<true, true>
                                                 : onepass::gla_onepass_kernel<true, false>)
                                        : (proj ? onepass::gla_onepass_kernel<false, true>

@@ -183,8 +183,8 @@ void gate_operands(const gla_gate_proj* gate, size_t tokens, int heads, int dk, 
     const size_t nout = (size_t)heads * dk;
     ops[0] = Operand{gate->x, tokens * gate->d_model * es, 16};
     ops[1] = Operand{gate->w1, (size_t)gate->rank * gate->d_model * es, 16};
-    ops[2] = Operand{gate->w2, nout * gate->rank * 4, 4};
-    ops[3] = Operand{gate->bias, nout * 4, 4};
+    ops[2] = Operand{gate->w2, nout * gate->rank * 4, 16};
+    ops[3] = Operand{gate->bias, nout * 4, 16};
 }
 
 }  // namespace
@@ -213,15 +213,16 @@ extern "C" int gla_make_plan_gate_proj(int dir, int H, int W, int chunk, const g
     if (st != GLA_OK) return st;
     st = gla_make_plan(dir, H, W, chunk, o, has_gate, plan);
     if (st != GLA_OK) return st;
-    // fused: single pass, rank 16, d_model a multiple of 64 whose W1 fits
-    // the kernel's shared-memory stage
-    if (plan->onepass && gate->rank == gla::kFusedProjRank && gate->d_model % 64 == 0 &&
-        gate->d_model <= gla::kFusedProjMaxDModel) {
-        plan->proj_fused = 1;
-        return GLA_OK;
-    }
+    // fused (single pass, rank 16): x W1 staged, 16 binary32 values per
+    // token; otherwise the logits themselves, NH*dk per token
     plan->off_z = ((plan->workspace_bytes + 255) / 256) * 256;
-    plan->workspace_bytes = plan->off_z + (size_t)o->batch * plan->L * o->heads * o->dk * 4;
+    const size_t tokens = (size_t)o->batch * plan->L;
+    if (plan->onepass && gate->rank == gla::kFusedProjRank) {
+        plan->proj_fused = 1;
+        plan->workspace_bytes = plan->off_z + tokens * gla::kFusedProjRank * 4;
+    } else {
+        plan->workspace_bytes = plan->off_z + tokens * o->heads * o->dk * 4;
+    }
     return GLA_OK;
 }
 

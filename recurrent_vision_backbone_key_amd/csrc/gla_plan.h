@@ -16,8 +16,8 @@ typedef struct gla_plan {
     int xcd_tasks;               // single pass, xcd_local: workgroups per XCD
     size_t workspace_bytes;
     size_t off_done, off_flags, off_agg, off_incl;  // single-pass workspace layout (bytes)
-    int proj_fused;              // gate projection inside the single pass
-    size_t off_z;                // gate projection not fused: z staged here (bytes)
+    int proj_fused;              // gate expansion (W2, b) inside the single pass
+    size_t off_z;                // gate projection: x W1 (fused) or z staged here (bytes)
     float tau, scale, eps;
 } gla_plan;
 
@@ -31,9 +31,10 @@ int gla_validate(const void* q, const void* k, const void* v, const float* gate_
                  int dir, int H, int W, int chunk, const void* out, const void* r,
                  const gla_opts* opts, gla_plan* plan);
 
-// Plan of gla_fwd_gate_proj: the plan of gla_fwd plus whether the projection
-// is fused into the single pass; otherwise z takes B*L*NH*dk binary32 words
-// at off_z of the workspace (included in workspace_bytes).
+// Plan of gla_fwd_gate_proj: the plan of gla_fwd plus whether the expansion
+// by W2 and b is fused into the single pass.  The workspace grows by the
+// staged x W1 (B*L*16 binary32 words, fused) or the staged logits
+// (B*L*NH*dk binary32 words) at off_z (included in workspace_bytes).
 int gla_make_plan_gate_proj(int dir, int H, int W, int chunk, const gla_gate_proj* gate,
                             const gla_opts* opts, int has_gate, gla_plan* plan);
 

@@ -51,26 +51,27 @@ def test_fwd_gate_proj_argument_checks():
         assert _fwdp(gate=_gate(d_model=d_model, rank=rank)) == 1, (d_model, rank)
     assert _fwdp(gate=_gate(x=A + 8 * MB + 8)) == 1      # x not 16-byte aligned
     assert _fwdp(gate=_gate(w1=A + 9 * MB + 4)) == 1     # w1 not 16-byte aligned
-    assert _fwdp(gate=_gate(w2=A + 10 * MB + 2)) == 1    # w2 not 4-byte aligned
+    assert _fwdp(gate=_gate(w2=A + 10 * MB + 4)) == 1    # w2 not 16-byte aligned
+    assert _fwdp(gate=_gate(bias=A + 11 * MB + 8)) == 1  # bias not 16-byte aligned
     # out overlapping each projection operand
     assert _fwdp(out=A + 8 * MB + 64) == 1
     assert _fwdp(out=A + 9 * MB) == 1
     assert _fwdp(gate=_gate(w2=A + 5 * MB + 1024)) == 1
-    assert _fwdp(gate=_gate(bias=A + 5 * MB + 4)) == 1
+    assert _fwdp(gate=_gate(bias=A + 5 * MB + 16)) == 1
     assert _fwdp(q=None) == 1
 
 
 def test_workspace_sizes_gate_proj():
     opts = gla.make_opts(8, 6, 64, 64, gla.F16)
     base = gla.workspace_size(0, 40, 40, 64, opts)
-    # fused into the single pass: same workspace as gla_fwd
-    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(), opts) == base
+    al = ((base + 255) // 256) * 256
+    # fused expansion in the single pass (rank 16, any d_model): x W1 staged
+    for d_model in (384, 768, 352):
+        assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(d_model=d_model), opts) == \
+            al + 8 * 1600 * 16 * 4
     zbytes = 8 * 1600 * 6 * 64 * 4
-    staged = ((base + 255) // 256) * 256 + zbytes
-    # not fused (d_model too large for the staged W1, or rank != 16): z staged
-    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(d_model=768), opts) == staged
-    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(rank=8), opts) == staged
-    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(d_model=352), opts) == staged
+    # not fused (rank != 16): the logits staged
+    assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(rank=8), opts) == al + zbytes
     # three passes in one segment: only z
     o3 = gla.make_opts(8, 6, 64, 64, gla.F16, segment_chunks=1000)
     assert gla.workspace_size_gate_proj(0, 40, 40, 64, _gate(), o3) == zbytes
@@ -122,6 +123,7 @@ def torch():
     (1, 130, 3, 32, 72, 5),
     (1, 64, 1, 128, 256, 64),   # four rank tiles
     (3, 33, 4, 64, 1024, 16),
+    (1, 200, 12, 128, 384, 16),  # several staged W2 row groups
 ])
 def test_gate_logits_kernel(torch, dtype, B, L, NH, dk, d_model, rank):
     g = make_gate_proj_inputs(B, L, NH, dk, d_model, rank, dtype, seed=100 + L)
@@ -198,9 +200,11 @@ def _proj_inputs(B, NH, H, W, dk, d_model, rank, dtype="f16", gated=True, seed=0
 @pytest.mark.parametrize("B,NH,H,W,d_model,seg", [
     (1, 2, 42, 42, 384, 0),    # ragged tail chunk
     (2, 3, 9, 7, 64, 0),       # one chunk, smallest fused d_model
-    (1, 4, 40, 40, 128, 1),    # one-chunk segments
+    (1, 4, 40, 40, 136, 1),    # one-chunk segments, d_model not a multiple of 32
     (1, 2, 40, 40, 256, 7),    # seven-chunk segments
     (3, 4, 30, 40, 384, 0),    # scans spread over the XCDs
+    (1, 6, 40, 40, 768, 0),    # wider block input
+    (1, 2, 13, 11, 8, 3),      # smallest d_model
 ])
 def test_fused_projection_shapes(torch, B, NH, H, W, d_model, seg):
     x = _proj_inputs(B, NH, H, W, 64, d_model, 16, seed=7 * H + W)
@@ -211,7 +215,7 @@ def test_fused_projection_shapes(torch, B, NH, H, W, d_model, seg):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("name,B,NH,H,W,dk,d_model,rank,dtype,algo", [
-    ("staged d_model=768", 1, 6, 40, 40, 64, 768, 16, "f16", 0),
+    ("staged rank=32", 1, 6, 40, 40, 64, 768, 32, "f16", 0),
     ("staged rank=8", 2, 3, 20, 24, 64, 192, 8, "f16", 0),
     ("staged three-pass", 1, 6, 40, 40, 64, 384, 16, "f16", 2),
     ("staged d=128", 1, 2, 32, 40, 128, 256, 16, "f16", 0),
@@ -228,9 +232,9 @@ def test_staged_projection(torch, name, B, NH, H, W, dk, d_model, rank, dtype, a
 
 @pytest.mark.gpu
 def test_fused_equals_staged_within_rounding(torch):
-    """The fused single pass and the staged path (projection kernel + the
-    ordinary single pass) agree closely: same scan, only z's rounding order
-    differs."""
+    """The fused single pass and the staged path (logits kernel + the
+    ordinary single pass) agree closely: same scan, only the rounding of the
+    logits differs."""
     x = _proj_inputs(2, 6, 40, 40, 64, 384, 16, seed=3)
     fused, _ = _run_fwd_proj(x, 0, 40, 40, 64, torch)
     d = {n: _dev(x[n], torch) for n in ("q", "k", "v", "r", "w", "x", "w1", "w2", "bias")}
