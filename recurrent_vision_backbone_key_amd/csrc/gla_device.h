@@ -61,6 +61,38 @@ __device__ __forceinline__ float4v mma(float a, float b, float4v c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+// Four binary16 values through the gfx950 LDS transpose read: within each
+// group of 16 lanes, lane j supplies the address of 4 consecutive elements
+// and receives element (j mod 4) of the reads of lanes 4e + j/4, e = 0..3.
+// With lane j pointing at row row0 + j/4, columns col0 + 4 (j mod 4) .. +3 of
+// a row-major tile, lane j receives rows row0 .. row0 + 3 of column col0 + j.
+// Every lane of the wavefront must execute it.
+__device__ __forceinline__ half4 ld_tr(const _Float16* p)
+{
+    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p);
+    return __builtin_bit_cast(half4, x);
+}
+// Address lane (l16) supplies so that it receives rows row0 .. row0 + 3 of
+// column col0 + l16 of a row-major tile with row stride STRIDE elements.
+template <int STRIDE>
+__device__ __forceinline__ const _Float16* tr_addr(const _Float16* base, int row0, int col0, int l16)
+{
+    return base + (row0 + (l16 >> 2)) * STRIDE + col0 + 4 * (l16 & 3);
+}
+// MFMA fragment of a row-major [token][col] tile contracted over tokens: lane
+// (g, l16) receives rows row0 + 0..7 of column col0 + l16, where row0 is the
+// first of 8 consecutive tokens of its lane group.
+template <int STRIDE>
+__device__ __forceinline__ half8 tr_frag_s(const _Float16* base, int row0, int col0, int l16)
+{
+    const _Float16* p = tr_addr<STRIDE>(base, row0, col0, l16);
+    const half4 a = ld_tr(p), b = ld_tr(p + 4 * STRIDE);
+    return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // log2(sigmoid(z)) from the softplus identity

@@ -71,9 +71,9 @@ constexpr int F2 = 5;     // 2^{tot_{i-1} + tot_{i-2}}  query factor for key sub
 // LDS layout (bytes)
 constexpr int L_E = 0;                        // E hi          [C][SH] f16 ([token][ch])
 constexpr int L_EL = L_E + C * SH * 2;        // E lo          [C][SH] f16
-constexpr int L_KT = L_EL + C * SH * 2;       // k-hat^T       [D][SH] f16 ([ch][token])
-constexpr int L_VT = L_KT + D * SH * 2;       // v^T           [D][SH] f16 ([dv][token])
-constexpr int L_ST = L_VT + D * SH * 2;       // S^T           [D][SH] f16 ([dv][ch])
+constexpr int L_KT = L_EL + C * SH * 2;       // k-hat         [C][SH] f16 ([token][ch]), read transposed
+constexpr int L_VT = L_KT + C * SH * 2;       // v             [C][SH] f16 ([token][dv]), read transposed
+constexpr int L_ST = L_VT + C * SH * 2;       // S^T           [D][SH] f16 ([dv][ch])
 constexpr int L_QH = L_ST + D * SH * 2;       // q (.) 2^b     [C][SH] f16 ([token][ch])
 constexpr int L_PA = L_QH + C * SH * 2;       // partial scores [NW][NSUB][64 lanes][4] f32
 constexpr int L_FQ = L_PA + NW * NSUB * 64 * 16;  // raw q      [C][SH] f16 (pairwise fallback)
@@ -328,10 +328,10 @@ __device__ __forceinline__ void scores_values(const Params& P, const _Float16* s
         const bool has_diag = (2 * p == SI) || (2 * p + 1 == SI);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const _Float16* vrow = sVT + (32 * h + 16 * m + l16) * SH;
-            const half4 v0 = *(const half4*)(vrow + 32 * p + 4 * g);
+            // value rows 32p + 4g + e and 32p + 16 + 4g + e of column 32h + 16m + l16
+            const half4 v0 = ld_tr(tr_addr<SH>(sVT, 32 * p + 4 * g, 32 * h + 16 * m, l16));
             half4 v1 = {0, 0, 0, 0};
-            if (hi) v1 = *(const half4*)(vrow + 32 * p + 16 + 4 * g);
+            if (hi) v1 = ld_tr(tr_addr<SH>(sVT, 32 * p + 16 + 4 * g, 32 * h + 16 * m, l16));
             half8 afr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -556,14 +556,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         *(half8*)(sE + tl * SH + c0) = eh;
         *(half8*)(sEL + tl * SH + c0) = el;
         *(half8*)(sQH + tl * SH + c0) = qhat;
-        {
-            const half8 vh = __builtin_bit_cast(half8, raw_v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sKT[(c0 + e) * SH + tl] = kt8[e];
-                sVT[(c0 + e) * SH + tl] = vh[e];
-            }
-        }
+        *(half8*)(sKT + tl * SH + c0) = kt8;
+        *(u32x4*)(sVT + tl * SH + c0) = raw_v;
         {
             const bool ww = __any(wide);
             if (lane == 0) sMisc[4 + wave] = ww ? 1 : 0;
@@ -615,8 +609,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             for (int e = 0; e < 4; ++e) S[jj][e] *= sDec[16 * sa + 4 * g + e];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const half8 kf = *(const half8*)(sKT + (16 * sa + l16) * SH + 32 * kb + 8 * g);
-                const half8 vf = *(const half8*)(sVT + (16 * bb + l16) * SH + 32 * kb + 8 * g);
+                const half8 kf = tr_frag_s<SH>(sKT, 32 * kb + 8 * g, 16 * sa, l16);
+                const half8 vf = tr_frag_s<SH>(sVT, 32 * kb + 8 * g, 16 * bb, l16);
                 S[jj] = mma(kf, vf, S[jj]);
             }
         }

@@ -98,26 +98,10 @@ template <bool AGG> struct Lay {
 };
 static_assert(2 * Lay<true>::TOTAL <= kLdsLimit, "two aggregate workgroups must share a CU");
 
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v lds_short4v;
-
-// Four binary16 values through the LDS transpose read: within each group of
-// 16 lanes, lane j supplies the address of 4 consecutive elements and
-// receives element (j mod 4) of the reads of lanes 4e + j/4, e = 0..3.
-__device__ __forceinline__ half4 ld_tr(const _Float16* p)
-{
-    const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p);
-    return __builtin_bit_cast(half4, x);
-}
-
-// MFMA fragment of a row-major [token][col] tile contracted over tokens: lane
-// (g, l16) receives rows row0 + 0..7 of column col0 + l16, where row0 is the
-// first of 8 consecutive tokens of its lane group.
+// MFMA fragment of a row-major [token][col] tile contracted over tokens.
 __device__ __forceinline__ half8 tr_frag(const _Float16* base, int row0, int col0, int l16)
 {
-    const _Float16* p = base + (row0 + (l16 >> 2)) * SH + col0 + 4 * (l16 & 3);
-    const half4 a = ld_tr(p), b = ld_tr(p + 4 * SH);
-    return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return tr_frag_s<SH>(base, row0, col0, l16);
 }
 
 // Inputs of one token for the lane's 16 channels cb + {0..7} and cb + 32 + {0..7}.
