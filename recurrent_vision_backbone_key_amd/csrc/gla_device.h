@@ -95,17 +95,16 @@ __device__ __forceinline__ half8 tr_frag_s(const _Float16* base, int row0, int c
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// log2(sigmoid(z)) from the softplus identity
-//   log sigmoid(z) = min(z,0) - log(1 + e^{-|z|}),
-// in base 2 with the hardware 2^x and log2 (v_exp_f32, v_log_f32).  The
-// absolute error of log2(1 + e) is about one ulp of 1 (6e-8), which after the
-// 1/tau factor and a cumulative sum stays far below the tolerance of any
-// decay product.  NaN propagates; z = +inf gives 0, z = -inf gives -inf.
-__device__ __forceinline__ float log2_sigmoid(float z)
+// Per-token log2-decay a = log2(sigmoid(z)) / tau, floored at kMinLog2Decay,
+// from log2 sigmoid(z) = -log2(1 + 2^{-z log2 e}) with the hardware 2^x and
+// log2 (five VALU operations).  For z < -88.7 the power overflows to +inf,
+// giving -inf and then the floor; z = +inf gives 0; NaN propagates (the
+// floor's comparison is false for NaN).  The result's error is about one ulp
+// of log2(1 + 2^{-z log2 e}), as for the two-sided softplus form.
+__device__ __forceinline__ float log2_decay(float z, float inv_tau)
 {
-    const float m = (z < 0.0f) ? z * kLog2e : 0.0f;
-    const float e = exp2_fast(-fabsf(z) * kLog2e);
-    return m - __builtin_amdgcn_logf(1.0f + e);
+    const float a = __builtin_amdgcn_logf(1.0f + exp2_fast(z * -kLog2e)) * -inv_tau;
+    return (a < kMinLog2Decay) ? kMinLog2Decay : a;
 }
 
 // x from the lane N places lower in the same 16-lane row (0 for the first N).

@@ -227,8 +227,7 @@ __global__ __launch_bounds__(kThreads) void gla_chunk_kernel(Params P)
                     const int t = t0 + u;
                     float a = 0.f;
                     if (c * C + t < P.L) {
-                        a = log2_sigmoid(sB[t * G::SB + ch]) * P.inv_tau;
-                        a = (a < kMinLog2Decay) ? kMinLog2Decay : a;
+                        a = log2_decay(sB[t * G::SB + ch], P.inv_tau);
                     }
                     run += a;
                     bl[it][j][u] = run;

@@ -187,24 +187,44 @@ struct Raw {
     u32x4 q, k, v, z0, z1;  // 8 channels of one token (q, k, v binary16; z binary32)
 };
 
+// Inputs are read through buffer resources whose record count is the
+// tensor's size: a row past the end of the scan (row < 0) takes an offset
+// beyond every record and reads zeros, with no branch and no zero-fill.
+// (The plan keeps the largest tensor below 2^31 bytes.)
+struct Src {
+    __amdgpu_buffer_rsrc_t q, k, v, z;
+};
+constexpr unsigned kPastEnd = 0x80000000u;
+__device__ __forceinline__ Src make_src(const Params& P, bool proj)
+{
+    const unsigned rows = (unsigned)(P.B * P.L * P.NH);
+    Src s;
+    s.q = xrsrc(P.q, rows * D * 2);
+    s.k = xrsrc(P.k, rows * D * 2);
+    s.v = xrsrc(P.v, rows * D * 2);
+    s.z = proj ? xrsrc(P.ghp, (unsigned)(P.B * P.L) * kFusedProjRank * 4) : xrsrc(P.z, rows * D * 4);
+    return s;
+}
+__device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 // PROJ: instead of the 8 gate logits, the lane loads the 4 rank values
 // hp[token][4g .. 4g + 3] of its token (the B fragment of the expansion below).
 template <bool PROJ>
-__device__ __forceinline__ void load_raw(Raw& r, const Params& P, int row, int c0, int g)
+__device__ __forceinline__ void load_raw(Raw& r, const Src& S, const Params& P, int row, int c0, int g)
 {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    r.q = r.k = r.v = r.z0 = r.z1 = zero;
-    if (row >= 0) {
-        const size_t o = (size_t)row * D + c0;
-        r.q = *(const u32x4*)((const _Float16*)P.q + o);
-        r.k = *(const u32x4*)((const _Float16*)P.k + o);
-        r.v = *(const u32x4*)((const _Float16*)P.v + o);
-        if (PROJ) {
-            r.z0 = *(const u32x4*)(P.ghp + (size_t)(row / P.NH) * kFusedProjRank + 4 * g);
-        } else {
-            r.z0 = *(const u32x4*)(P.z + o);
-            r.z1 = *(const u32x4*)(P.z + o + 4);
-        }
+    const unsigned oh = row >= 0 ? (unsigned)(row * D + c0) * 2u : kPastEnd;
+    r.q = ld_b128(S.q, oh);
+    r.k = ld_b128(S.k, oh);
+    r.v = ld_b128(S.v, oh);
+    if (PROJ) {
+        r.z0 = ld_b128(S.z, row >= 0 ? (unsigned)((row / P.NH) * kFusedProjRank + 4 * g) * 4u : kPastEnd);
+        r.z1 = u32x4{0u, 0u, 0u, 0u};
+    } else {
+        const unsigned oz = row >= 0 ? (unsigned)(row * D + c0) * 4u : kPastEnd;
+        r.z0 = ld_b128(S.z, oz);
+        r.z1 = ld_b128(S.z, oz + 16u);
     }
 }
 
@@ -420,8 +440,9 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     const bool gated = (P.r != nullptr);
 
     // ---- first chunk's operands of this lane: issued before anything waits
+    const Src src = make_src(P, PROJ);
     Raw raw;
-    load_raw<PROJ>(raw, P, scan_row(P, unit, c_begin * C + tl), c0, g);
+    load_raw<PROJ>(raw, src, P, scan_row(P, unit, c_begin * C + tl), c0, g);
 
     // ---- row tables of every chunk of the segment
     for (int i = tid; i < nch * C; i += NT) sRows[i] = scan_row(P, unit, c_begin * C + i);
@@ -451,8 +472,6 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         if (c >= nch) break;
-        const int cpos = (c_begin + c) * C;
-        const bool valid = (cpos + tl < P.L);
         float qv[8], kv[8], zv[8];
         const u32x4 raw_v = raw.v;
         {
@@ -471,16 +490,16 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             *(u32x4*)(sFK + tl * SH + c0) = raw.k;
         }
         if (PROJ) proj_logits(__builtin_bit_cast(float4v, raw.z0), sW2, sGB, h, g, l16, zv);
-        if (c + 1 < nch) load_raw<PROJ>(raw, P, sRows[(c + 1) * C + tl], c0, g);
+        if (c + 1 < nch) load_raw<PROJ>(raw, src, P, sRows[(c + 1) * C + tl], c0, g);
 
-        // ---- gate stage: log2-decay, prefix along the 16 tokens of the sub-chunk
+        // ---- gate stage: log2-decay, prefix along the 16 tokens of the sub-chunk.
+        //      Tokens past the end of the scan (zero q, k, v, only in its last
+        //      chunk) keep their finite decay: it enters only quantities after
+        //      every valid token (sub-chunk totals that cancel in the scores,
+        //      the state after the last chunk, which is never published).
         float bl[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = log2_sigmoid(zv[e]) * P.inv_tau;
-            a = (a < kMinLog2Decay) ? kMinLog2Decay : a;
-            bl[e] = valid ? a : 0.f;
-        }
+        for (int e = 0; e < 8; ++e) bl[e] = log2_decay(zv[e], P.inv_tau);
         row_scan_n(bl);
         if (l16 == 15) {
             *(float4v*)(sTot + si * D + c0) = float4v{bl[0], bl[1], bl[2], bl[3]};

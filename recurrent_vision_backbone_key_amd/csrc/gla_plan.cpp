@@ -71,7 +71,10 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     // spread over the 8 XCDs without costing a second round of workgroups on
     // any of them (or divide evenly), scan u runs on XCD u mod 8 and the
     // segment exchange stays in that XCD's L2.
-    const bool sp_shape = o->dtype == GLA_F16 && o->dk == 64 && o->dv == 64 && chunk == 64;
+    // (the kernel addresses its inputs with 32-bit buffer offsets: the fp32
+    // gate logits, 256 bytes per row, stay below 2^31 bytes)
+    const bool sp_shape = o->dtype == GLA_F16 && o->dk == 64 && o->dv == 64 && chunk == 64 &&
+                          rows < ((int64_t)1 << 23);
     plan->xcd_local = 0;
     plan->xcd_tasks = 0;
     if (o->algorithm != GLA_ALGO_THREE_PASS && sp_shape) {

@@ -152,9 +152,7 @@ __device__ __forceinline__ void gate_prefix(const Raw& x, float inv_tau, bool va
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const float4v zz = __builtin_bit_cast(float4v, x.z[j >> 2]);
-        float a = log2_sigmoid(zz[j & 3]) * inv_tau;
-        a = (a < kMinLog2Decay) ? kMinLog2Decay : a;
-        bl[j] = valid ? a : 0.f;
+        bl[j] = valid ? log2_decay(zz[j & 3], inv_tau) : 0.f;
     }
     row_scan_n(bl);
 }
