@@ -61,6 +61,20 @@ __device__ __forceinline__ float4v mma(float a, float b, float4v c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw addressing): a load at an
+// offset past the record count returns zeros, which reads the rows past the
+// end of a scan without a branch or a select.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const void* base, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// Offset past every record (the tensors it is used on stay below 2^31 bytes).
+constexpr unsigned kPastEnd = 0x80000000u;
+__device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 

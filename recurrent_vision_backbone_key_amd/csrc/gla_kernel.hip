@@ -650,7 +650,10 @@ int launch_fold(const Params& P, int d, void* stream)
 int launch_fwd(const Params& P, int dtype, int d, int chunk, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
-    if (dtype == GLA_F16 && d == 128 && chunk == 64) return launch_wide(P, stream);
+    // the d = 128 kernels address inputs with 32-bit buffer offsets: fp32
+    // gate logits (512 bytes per row) below 2^31 bytes
+    const long long rows = (long long)P.B * P.L * P.NH;
+    if (dtype == GLA_F16 && d == 128 && chunk == 64 && rows < (1ll << 22)) return launch_wide(P, stream);
     if (dtype == GLA_F16) return run_dim<_Float16>(P, d, chunk, st);
     if (dtype == GLA_F32) return run_dim<float>(P, d, chunk, st);
     return GLA_EUNSUPPORTED;

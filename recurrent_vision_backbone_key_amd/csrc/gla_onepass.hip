@@ -128,10 +128,6 @@ template <bool LOCAL> struct Pol {
     static constexpr int kLoad = 16;
     static constexpr int kStore = LOCAL ? 0 : 16;
 };
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const void* base, unsigned bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
 template <bool LOCAL>
 __device__ __forceinline__ float4v ld_x4(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
@@ -194,7 +190,6 @@ struct Raw {
 struct Src {
     __amdgpu_buffer_rsrc_t q, k, v, z;
 };
-constexpr unsigned kPastEnd = 0x80000000u;
 __device__ __forceinline__ Src make_src(const Params& P, bool proj)
 {
     const unsigned rows = (unsigned)(P.B * P.L * P.NH);
@@ -204,10 +199,6 @@ __device__ __forceinline__ Src make_src(const Params& P, bool proj)
     s.v = xrsrc(P.v, rows * D * 2);
     s.z = proj ? xrsrc(P.ghp, (unsigned)(P.B * P.L) * kFusedProjRank * 4) : xrsrc(P.z, rows * D * 4);
     return s;
-}
-__device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, unsigned off)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 // PROJ: instead of the 8 gate logits, the lane loads the 4 rank values
 // hp[token][4g .. 4g + 3] of its token (the B fragment of the expansion below).

@@ -111,23 +111,28 @@ struct Raw {
 
 enum Part { PZ, PK, PQ, PV, PR };
 
-// One input of one token (the lane's 16 channels), zero past the end.
+// One input of one token (the lane's 16 channels), zero past the end: read
+// through a buffer resource bounded by the tensor's size, where a row past
+// the end takes an offset beyond every record (no select per dword).
 template <int PART>
 __device__ __forceinline__ void load_part(Raw& x, const Params& P, int row, int cb)
 {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const size_t o = (size_t)(row < 0 ? 0 : row) * D + cb;
+    const unsigned rows = (unsigned)(P.B * P.L * P.NH);
+    const unsigned es = PART == PZ ? 4u : 2u;
+    const void* base = PART == PZ ? (const void*)P.z : PART == PK ? P.k : PART == PQ ? P.q
+                     : PART == PV ? P.v : P.r;
+    const __amdgpu_buffer_rsrc_t rs = xrsrc(base, rows * D * es);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const size_t oo = o + 32 * kb;
+        const unsigned off = row >= 0 ? (unsigned)(row * D + cb + 32 * kb) * es : kPastEnd;
         if (PART == PZ) {
-            x.z[2 * kb] = row < 0 ? zero : *(const u32x4*)(P.z + oo);
-            x.z[2 * kb + 1] = row < 0 ? zero : *(const u32x4*)(P.z + oo + 4);
+            x.z[2 * kb] = ld_b128(rs, off);
+            x.z[2 * kb + 1] = ld_b128(rs, off + 16u);
         }
-        if (PART == PK) x.k[kb] = row < 0 ? zero : *(const u32x4*)((const _Float16*)P.k + oo);
-        if (PART == PQ) x.q[kb] = row < 0 ? zero : *(const u32x4*)((const _Float16*)P.q + oo);
-        if (PART == PV) x.v[kb] = row < 0 ? zero : *(const u32x4*)((const _Float16*)P.v + oo);
-        if (PART == PR) x.r[kb] = row < 0 ? zero : *(const u32x4*)((const _Float16*)P.r + oo);
+        if (PART == PK) x.k[kb] = ld_b128(rs, off);
+        if (PART == PQ) x.q[kb] = ld_b128(rs, off);
+        if (PART == PV) x.v[kb] = ld_b128(rs, off);
+        if (PART == PR) x.r[kb] = ld_b128(rs, off);
     }
 }
 
