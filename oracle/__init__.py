@@ -11,6 +11,9 @@ Recurrence for Efficient Dense Prediction", paper Section 2.1):
   (``gla_oracle.c``), OpenMP over the (batch, head) units;
 * :func:`gate_logits` -- the low-rank gate logits z = (x W1) W2 + b of
   the retention gate (same section), plain C loops in fp64;
+* :func:`spatial_swiglu` (with :func:`dwconv3x3`, :func:`silu`) -- the
+  Spatial SwiGLU core SiLU(a) (.) (3x3 depthwise convolution of v + b)
+  (same section), numpy fp64 shifted sums;
 * :func:`closed_form_fwd` -- the O(L^2) unrolled sum
   ``o_t = scale * sum_{s<=t} (q_t (.) prod_{j=s+1..t} gamma_j (.) k_s) v_s``
   in numpy fp64 with explicit per-pair gate sums, for tiny inputs.  Its scan
@@ -200,6 +203,51 @@ def gate_logits(x, w1, w2, bias, heads, threads=None):
     if rc != 0:
         raise RuntimeError(f"gla_oracle_gate_logits failed with status {rc}")
     return z
+
+
+# ---------------------------------------------------------------------------
+# Spatial SwiGLU core (paper Section 2.1, Spatial SwiGLU paragraph), numpy fp64.
+# ---------------------------------------------------------------------------
+
+def silu(x):
+    """SiLU(x) = x / (1 + e^{-x}) in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def dwconv3x3(value, H, W, weight, bias=None):
+    """3x3 depthwise convolution of the value branch on the H x W patch grid.
+
+    value: [B, L, C] (L = H*W, token t = h*W + w), any float dtype, read as
+    stored; weight: [C, 3, 3]; bias: [C] or None.  Cross-correlation with zero
+    padding of one token on every side (a depthwise Conv2d with padding 1):
+        y[h, w, c] = b[c] + sum_{i, j in 0..2} weight[c, i, j] * v[h + i - 1, w + j - 1, c]
+    written as nine shifted adds of the zero-padded grid.  Returns fp64 [B, L, C].
+    """
+    v = np.asarray(value, dtype=np.float64)
+    B, L, C = v.shape
+    if L != H * W:
+        raise ValueError("L must be H*W")
+    w = np.asarray(weight, dtype=np.float64)
+    if w.shape != (C, 3, 3):
+        raise ValueError("weight must be [C, 3, 3]")
+    grid = v.reshape(B, H, W, C)
+    padded = np.zeros((B, H + 2, W + 2, C))
+    padded[:, 1:H + 1, 1:W + 1, :] = grid
+    out = np.zeros((B, H, W, C))
+    for i in range(3):
+        for j in range(3):
+            out += w[:, i, j] * padded[:, i:i + H, j:j + W, :]
+    if bias is not None:
+        out += np.asarray(bias, dtype=np.float64)
+    return out.reshape(B, L, C)
+
+
+def spatial_swiglu(gate, value, H, W, weight, bias=None):
+    """h = SiLU(gate) (.) dwconv3x3(value): the gating branch stays tokenwise,
+    the value branch is mixed over the 3x3 grid neighbourhood.  gate, value:
+    [B, L, C] as stored.  Returns fp64 [B, L, C]."""
+    return silu(gate) * dwconv3x3(value, H, W, weight, bias)
 
 
 # ---------------------------------------------------------------------------

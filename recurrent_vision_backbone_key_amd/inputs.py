@@ -171,3 +171,21 @@ def make_gate_proj_inputs_device(B, L, NH, dk, d_model, rank=16, dtype="f16", se
     lim = rank ** -0.5
     bias = (torch.rand((NH * dk,), generator=gen, device=device, dtype=torch.float32) * 2 - 1) * lim
     return dict(x=x, w1=w1, w2=w2, bias=bias)
+
+
+def make_sswiglu_inputs(B, H, W, C, dtype="f16", bias=True, seed=0):
+    """Draw the Spatial SwiGLU core's operands from PCG64(seed), in the order
+    gate, value, weight, bias.
+
+    gate, value ~ N(0, 1) [B, H*W, C] rounded to ``dtype`` (the two branch
+    projections of the block input); weight, bias ~ U(-1/3, 1/3) float32
+    ([C, 3, 3] and [C]; the default initialisation range of a depthwise 3x3
+    convolution, fan-in 9).
+    """
+    rng = np.random.default_rng(seed)
+    dt = np_dtype(dtype)
+    a = rng.standard_normal((B, H * W, C)).astype(dt)
+    v = rng.standard_normal((B, H * W, C)).astype(dt)
+    w = rng.uniform(-1.0 / 3.0, 1.0 / 3.0, size=(C, 3, 3)).astype(np.float32)
+    b = rng.uniform(-1.0 / 3.0, 1.0 / 3.0, size=(C,)).astype(np.float32) if bias else None
+    return dict(a=a, v=v, w=w, b=b)

@@ -371,3 +371,82 @@ def test_projected_gate_forward_equals_closed_form(direction):
     ref = oracle.closed_form_fwd(inp["q"], inp["k"], inp["v"], zn, direction, H, W,
                                  r=inp["r"], w=inp["w"])
     assert _rel(got, ref) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# Spatial SwiGLU core (Sec. 2.1, Spatial SwiGLU paragraph; Eq. 1 is missing
+# from the extracted text: readings in the oracle's docstring)
+# ---------------------------------------------------------------------------
+
+def test_silu_known_values():
+    """SiLU(x) = x sigmoid(x) at points whose values are fixed by e alone."""
+    got = oracle.silu(np.array([0.0, 1.0, -1.0, 2.0]))
+    want = [0.0, 1.0 / (1.0 + math.exp(-1.0)), -1.0 / (1.0 + math.e), 2.0 / (1.0 + math.exp(-2.0))]
+    assert np.allclose(got, want, rtol=0, atol=1e-16)
+    assert abs(got[1] - 0.7310585786300049) < 1e-15
+    assert abs(got[2] + 0.2689414213699951) < 1e-15
+
+
+def test_dwconv_by_hand_2x2():
+    """One channel on a 2x2 grid with taps 1..9 (row-major): each output sums
+    the taps that land inside the grid (zero padding), e.g. the top-left
+    output sees v00 at the centre tap 5, v01 at 6, v10 at 8, v11 at 9."""
+    v = np.array([[[1.0], [2.0], [3.0], [4.0]]])          # v00 v01 / v10 v11
+    w = np.arange(1.0, 10.0).reshape(1, 3, 3)
+    y = oracle.dwconv3x3(v, 2, 2, w)[0, :, 0]
+    assert y.tolist() == [5 * 1 + 6 * 2 + 8 * 3 + 9 * 4,   # (0,0)
+                          4 * 1 + 5 * 2 + 7 * 3 + 8 * 4,   # (0,1)
+                          2 * 1 + 3 * 2 + 5 * 3 + 6 * 4,   # (1,0)
+                          1 * 1 + 2 * 2 + 4 * 3 + 5 * 4]   # (1,1)
+    yb = oracle.dwconv3x3(v, 2, 2, w, bias=np.array([0.5]))[0, :, 0]
+    assert np.array_equal(yb, y + 0.5)
+
+
+def test_dwconv_is_correlation_with_zero_padding():
+    """A single top-left tap shifts the grid down-right by one token with a
+    zero first row and column (cross-correlation, not a flipped kernel)."""
+    rng = np.random.default_rng(4)
+    H, W, C = 5, 7, 3
+    v = rng.standard_normal((2, H * W, C))
+    w = np.zeros((C, 3, 3))
+    w[:, 0, 0] = 1.0
+    y = oracle.dwconv3x3(v, H, W, w).reshape(2, H, W, C)
+    g = v.reshape(2, H, W, C)
+    assert np.array_equal(y[:, 1:, 1:], g[:, :-1, :-1])
+    assert not y[:, 0, :].any() and not y[:, :, 0].any()
+
+
+def test_dwconv_against_scipy_correlate2d():
+    """Every channel against scipy's 2-D correlation with zero fill (an
+    independent implementation)."""
+    from scipy.signal import correlate2d
+    rng = np.random.default_rng(5)
+    H, W, C = 6, 9, 4
+    v = rng.standard_normal((2, H * W, C))
+    w = rng.standard_normal((C, 3, 3))
+    b = rng.standard_normal(C)
+    y = oracle.dwconv3x3(v, H, W, w, b).reshape(2, H, W, C)
+    for bb in range(2):
+        for c in range(C):
+            ref = correlate2d(v[bb, :, c].reshape(H, W), w[c], mode="same", boundary="fill") + b[c]
+            assert np.allclose(y[bb, :, :, c], ref, rtol=0, atol=1e-12)
+
+
+def test_spatial_swiglu_special_cases():
+    """Centre-tap identity gives SiLU(a) v; a = 0 gives 0; the gate is
+    tokenwise (changing one token's gate changes only that token)."""
+    rng = np.random.default_rng(6)
+    H, W, C = 4, 3, 5
+    a = rng.standard_normal((1, H * W, C))
+    v = rng.standard_normal((1, H * W, C))
+    w = np.zeros((C, 3, 3))
+    w[:, 1, 1] = 1.0
+    assert np.array_equal(oracle.spatial_swiglu(a, v, H, W, w), oracle.silu(a) * v)
+    assert not oracle.spatial_swiglu(np.zeros_like(a), v, H, W, rng.standard_normal((C, 3, 3))).any()
+    wr = rng.standard_normal((C, 3, 3))
+    y0 = oracle.spatial_swiglu(a, v, H, W, wr)
+    a2 = a.copy()
+    a2[0, 5] += 1.0
+    y1 = oracle.spatial_swiglu(a2, v, H, W, wr)
+    changed = np.any(y0 != y1, axis=2)[0]
+    assert changed.tolist() == [t == 5 for t in range(H * W)]
