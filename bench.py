@@ -187,6 +187,111 @@ def cpu_baseline(spec, name, seconds):
                       f"{done_th} token-heads in {dt:.1f} s"}
 
 
+def bench_sswiglu(args, spec, name):
+    """One step = one gla_spatial_swiglu call over the whole batch; same
+    timing method as the forward (resident inputs rotating past the last-level
+    cache, HIP graphs of several steps, HIP events on the replay stream)."""
+    import torch
+
+    from recurrent_vision_backbone_key_amd import gla
+
+    B, H, W, C = spec["B"], spec["H"], spec["W"], spec["C"]
+    es = 2 if spec["dtype"] == "f16" else 4
+    dt = torch.float16 if es == 2 else torch.float32
+    tokens = B * H * W
+    bytes_call = 3 * es * tokens * C + 40 * C   # gate, value read; out written; taps, bias
+    rotate = args.rotate or max(1, math.ceil(2 * MALL_BYTES / bytes_call))
+    steps = args.steps if args.steps is not None else 400
+    warmup = args.warmup if args.warmup is not None else 100
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    sets = []
+    for r in range(rotate):
+        gen.manual_seed(1000 * spec["index"] + r)
+        a = torch.randn((B, H * W, C), generator=gen, device=dev).to(dt)
+        v = torch.randn((B, H * W, C), generator=gen, device=dev).to(dt)
+        w = (torch.rand((C, 3, 3), generator=gen, device=dev) * 2 - 1) / 3
+        b = (torch.rand((C,), generator=gen, device=dev) * 2 - 1) / 3
+        sets.append((a, v, w, b, torch.empty_like(a)))
+
+    def step(r):
+        a, v, w, b, o = sets[r]
+        gla.spatial_swiglu(a, v, H, W, w, b, out=o)
+
+    G = 1 if args.no_graph else math.gcd(math.gcd(args.steps_per_graph or 10, steps), warmup)
+    n_graphs = rotate // math.gcd(rotate, G)
+    stream = torch.cuda.current_stream()
+    graphs = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for r in range(rotate):
+                step(r)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for gi in range(n_graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for j in range(G):
+                    step((gi * G + j) % rotate)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % n_graphs].replay()
+        else:
+            step(i % rotate)
+
+    for i in range(warmup // G):
+        run(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps // G):
+        run(warmup // G + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / steps
+    achieved = bytes_call / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": "Spatial SwiGLU core: µs/call; % of HBM roofline",
+        "value": round(tokens * C / (ms_step * 1e-3) / 1e9, 3), "unit": "Gtok·channel/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
+        "us_per_call": round(1e3 * ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
+        "config": {"workload": name, "B": B, "grid": f"{H}x{W}", "L": H * W, "channels": C,
+                   "input_sets": rotate, "hip_graph": graphs is not None, "steps_per_graph": G,
+                   "accumulate": "f32"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gla_sswiglu_kernel (one launch per call)",
+                     "algorithmic_bytes_per_call": bytes_call},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        import numpy as np  # noqa: F401
+
+        import oracle
+        from recurrent_vision_backbone_key_amd.inputs import make_sswiglu_inputs
+        x = make_sswiglu_inputs(1, H, W, C, spec["dtype"], True, seed=1)
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.spatial_swiglu(x["a"], x["v"], H, W, x["w"], x["b"])
+            n += 1
+        dt_s = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(n * H * W * C / dt_s / 1e9, 5), "unit": "Gtok·channel/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} oracle calls on one image ({H}x{W}, {C} channels) in {dt_s:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     from recurrent_vision_backbone_key_amd.inputs import WORKLOADS
 
@@ -246,6 +351,9 @@ def main():
 
     spec = WORKLOADS[args.workload]
     name = args.workload
+    if spec.get("kind") == "sswiglu":
+        bench_sswiglu(args, spec, name)
+        return
     chunk = args.chunk or spec["chunk"]
     dirs = spec["dirs"]
     calls_per_step = len(dirs)

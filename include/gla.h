@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 2
+#define GLA_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define GLA_API __attribute__((visibility("default")))
@@ -188,6 +188,35 @@ GLA_API int gla_fwd_gate_proj(const void *q, const void *k, const void *v,
  * it would reject). */
 GLA_API size_t gla_workspace_size_gate_proj(int dir, int H, int W, int chunk,
                                             const gla_gate_proj *gate, const gla_opts *opts);
+
+/*
+ * gla_spatial_swiglu -- the fused core of the Spatial SwiGLU block (paper
+ * Section 2.1, Spatial SwiGLU paragraph; its equation is not available, so
+ * the form below is this library's reading): the value branch is laid out on
+ * the H x W patch grid (token t = h*W + w) and mixed by a 3x3 depthwise
+ * convolution, the gating branch stays tokenwise:
+ *     out[b, t, c] = SiLU(gate[b, t, c]) * (bias[c] + sum_{i,j = 0..2}
+ *                    conv_w[c][i][j] * value[b, (h+i-1)*W + (w+j-1), c])
+ * with zero padding outside the grid (cross-correlation, like a depthwise
+ * Conv2d with padding 1) and SiLU(x) = x / (1 + e^-x), in binary32.
+ *   gate, value  [batch, H*W, channels] rows of ld_in elements (the first
+ *                `channels` used), storage dtype; a fused projection output
+ *                [.., 2*channels] can be passed as gate = base,
+ *                value = base + channels, ld_in = 2*channels
+ *   conv_w       [channels, 3, 3] binary32 (a depthwise Conv2d weight)
+ *   conv_b       [channels] binary32, NULL selects zeros
+ *   out          [batch, H*W, channels] rows of ld_out elements, storage dtype;
+ *                must not overlap an input
+ *   dtype        GLA_F16 or GLA_F32; channels a multiple of 8; ld_in, ld_out
+ *                multiples of 8 and >= channels; H, W, batch >= 1
+ * gate, value and out are 16-byte aligned device pointers, conv_w and conv_b
+ * 4-byte aligned.  Runs on `stream` (hipStream_t, NULL: the null stream); needs
+ * no workspace.  GLA_EINVAL on a bad pointer, size or overlap,
+ * GLA_EUNSUPPORTED on another dtype, GLA_EHIP on a launch failure.
+ */
+GLA_API int gla_spatial_swiglu(const void *gate, const void *value, int64_t ld_in,
+                               const float *conv_w, const float *conv_b, int batch, int H, int W,
+                               int channels, int dtype, void *out, int64_t ld_out, void *stream);
 
 /* Static, NUL-terminated description of a gla_status value. */
 GLA_API const char *gla_status_str(int status);

@@ -39,6 +39,7 @@ UNITS = [
     ("gla_onepass.hip", "hip", []),
     ("gla_wide.hip", "hip", []),
     ("gla_proj.hip", "hip", []),
+    ("gla_sswiglu.hip", "hip", []),
 ]
 
 

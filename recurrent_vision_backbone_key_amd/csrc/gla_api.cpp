@@ -142,6 +142,17 @@ extern "C" int gla_workspace_init(void* workspace, size_t bytes, void* stream)
     return gla::launch_workspace_init(workspace, bytes, stream);
 }
 
+extern "C" int gla_spatial_swiglu(const void* gate, const void* value, int64_t ld_in,
+                                  const float* conv_w, const float* conv_b, int batch, int H, int W,
+                                  int channels, int dtype, void* out, int64_t ld_out, void* stream)
+{
+    const int st = gla_validate_sswiglu(gate, value, ld_in, conv_w, conv_b, batch, H, W, channels,
+                                        dtype, out, ld_out);
+    if (st != GLA_OK) return st;
+    return gla::launch_sswiglu(gate, value, ld_in, conv_w, conv_b, out, ld_out, batch, H, W,
+                               channels, dtype, stream);
+}
+
 extern "C" const char* gla_status_str(int status)
 {
     switch (status) {

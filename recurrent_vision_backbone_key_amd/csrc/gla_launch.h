@@ -75,6 +75,10 @@ int launch_gate_logits(const GateProj& G, int dtype, int tokens, int nout, float
 // First factor alone: hp = x W1, [tokens, 16 ceil(rank / 16)] binary32.
 int launch_gate_rank(const GateProj& G, int dtype, int tokens, float* hp, void* stream);
 
+// Spatial SwiGLU core (include/gla.h, gla_spatial_swiglu), arguments checked.
+int launch_sswiglu(const void* a, const void* v, long long ld_in, const float* w, const float* bias,
+                   void* out, long long ld_out, int B, int H, int W, int C, int dtype, void* stream);
+
 // Zero-fills a workspace (counters, flags) on `stream`.
 int launch_workspace_init(void* ws, size_t bytes, void* stream);
 

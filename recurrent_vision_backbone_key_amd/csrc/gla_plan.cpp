@@ -269,3 +269,30 @@ extern "C" int gla_validate_gate_logits(const gla_gate_proj* gate, int batch, in
         if (overlaps(z, zb, ins[i].p, ins[i].bytes)) return GLA_EINVAL;
     return GLA_OK;
 }
+
+extern "C" int gla_validate_sswiglu(const void* gate, const void* value, int64_t ld_in,
+                                    const float* conv_w, const float* conv_b, int batch, int H,
+                                    int W, int channels, int dtype, const void* out, int64_t ld_out)
+{
+    if (!gate || !value || !conv_w || !out) return GLA_EINVAL;
+    if (batch < 1 || H < 1 || W < 1 || channels < 8 || channels % 8 != 0) return GLA_EINVAL;
+    if (ld_in < channels || ld_out < channels || ld_in % 8 != 0 || ld_out % 8 != 0) return GLA_EINVAL;
+    if (dtype != GLA_F16 && dtype != GLA_F32) return GLA_EUNSUPPORTED;
+    const int64_t tokens = (int64_t)batch * H * W;
+    if ((int64_t)H * W >= ((int64_t)1 << 31) || tokens >= ((int64_t)1 << 40)) return GLA_EINVAL;
+    // one workgroup per 8 x 8 tile and 64 channels (grid below 2^31)
+    const int64_t planes = (int64_t)batch * ((channels + 63) / 64);
+    const int64_t tiles = (int64_t)((H + 7) / 8) * ((W + 7) / 8);
+    if (8 * ((planes + 7) / 8) * tiles >= ((int64_t)1 << 31)) return GLA_EINVAL;
+    const size_t es = dtype == GLA_F16 ? 2 : 4;
+    const size_t in_b = ((size_t)(tokens - 1) * ld_in + channels) * es;
+    const size_t out_b = ((size_t)(tokens - 1) * ld_out + channels) * es;
+    const Operand ins[4] = {{gate, in_b, 16}, {value, in_b, 16}, {conv_w, (size_t)channels * 36, 4},
+                            {conv_b, (size_t)channels * 4, 4}};
+    for (int i = 0; i < 4; ++i)
+        if (ins[i].p && !aligned(ins[i].p, ins[i].align)) return GLA_EINVAL;
+    if (!aligned(out, 16)) return GLA_EINVAL;
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(out, out_b, ins[i].p, ins[i].bytes)) return GLA_EINVAL;
+    return GLA_OK;
+}

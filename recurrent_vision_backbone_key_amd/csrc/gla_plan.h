@@ -47,6 +47,11 @@ int gla_validate_gate_proj(const void* q, const void* k, const void* v, const gl
 int gla_validate_gate_logits(const gla_gate_proj* gate, int batch, int tokens, int heads, int dk,
                              int dtype, const float* z);
 
+// Host check of every argument of gla_spatial_swiglu.
+int gla_validate_sswiglu(const void* gate, const void* value, int64_t ld_in, const float* conv_w,
+                         const float* conv_b, int batch, int H, int W, int channels, int dtype,
+                         const void* out, int64_t ld_out);
+
 // Whether a (dtype, head dim, chunk) instantiation is built (shared-memory
 // footprint of one workgroup within the 160 KiB of a gfx950 CU).
 int gla_config_built(int dtype, int d, int chunk);

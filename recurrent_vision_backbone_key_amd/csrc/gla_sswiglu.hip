@@ -1,0 +1,182 @@
+// gla_sswiglu.hip -- fused Spatial SwiGLU core for gfx950.
+//
+// Paper "GTR: Gated Token Recurrence for Efficient Dense Prediction",
+// Section 2.1 (Spatial SwiGLU paragraph): the value branch of the block's
+// SwiGLU is laid out on the H x W patch grid and mixed by a 3x3 depthwise
+// convolution, the gating branch stays tokenwise:
+//     h[b, t, c] = SiLU(a[b, t, c]) * (bias[c] + sum_{i,j} w[c][i][j] v[b, y+i-1, x+j-1, c])
+// with t = y*W + x, zero padding outside the grid (cross-correlation, as a
+// depthwise Conv2d with padding 1).
+//
+// Memory-bound: 2 + 2 + 2 bytes per token-channel (binary16 a, v, h).  A
+// workgroup of 512 threads owns an 8 x 8 token tile and 64 channels: it stages
+// the tile of v with its one-token halo (10 x 10 tokens x 64 channels) in LDS
+// with 16-byte loads (and the block's 9 x 64 taps, transposed to
+// [tap][channel]); each thread then computes 8 channels of one token from nine
+// 16-byte LDS reads of v and eighteen of taps, with its gate loaded before the
+// staging, and stores 16 bytes.  Lanes run along channels first, so a
+// wavefront covers 8 tokens x 128 contiguous bytes of each.  All tiles of one
+// (image, channel block) plane run on one XCD, in raster order, so halo rows
+// shared by neighbouring tiles stay in its L2: the HBM counters read exactly
+// the compulsory bytes.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gla.h"
+#include "gla_device.h"
+#include "gla_launch.h"
+
+namespace gla {
+namespace sswiglu {
+
+constexpr int TH = 8, TW = 8;          // token tile
+constexpr int CB = 64;                 // channels per workgroup
+constexpr int CG = CB / 8;             // 8-channel groups
+constexpr int NT = TH * TW * CG;       // 512 threads
+constexpr int HH = TH + 2, HW = TW + 2;  // tile with halo
+constexpr int HS = CB + 8;             // LDS token stride (elements): 16-byte pad
+
+// 8 consecutive channels of one token.
+template <typename T> struct V8;
+template <> struct V8<_Float16> {
+    u32x4 x;
+    static __device__ __forceinline__ V8 load(const _Float16* p) { return V8{*(const u32x4*)p}; }
+    static __device__ __forceinline__ V8 zero() { return V8{u32x4{0u, 0u, 0u, 0u}}; }
+    __device__ __forceinline__ void store(_Float16* p) const { *(u32x4*)p = x; }
+    __device__ __forceinline__ float get(int e) const { return (float)__builtin_bit_cast(half8, x)[e]; }
+    static __device__ __forceinline__ V8 from(const float (&f)[8])
+    {
+        half8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)f[e];
+        return V8{__builtin_bit_cast(u32x4, h)};
+    }
+};
+template <> struct V8<float> {
+    float4v x0, x1;
+    static __device__ __forceinline__ V8 load(const float* p)
+    {
+        return V8{*(const float4v*)p, *(const float4v*)(p + 4)};
+    }
+    static __device__ __forceinline__ V8 zero() { return V8{float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}}; }
+    __device__ __forceinline__ void store(float* p) const
+    {
+        *(float4v*)p = x0;
+        *(float4v*)(p + 4) = x1;
+    }
+    __device__ __forceinline__ float get(int e) const { return e < 4 ? x0[e] : x1[e - 4]; }
+    static __device__ __forceinline__ V8 from(const float (&f)[8])
+    {
+        return V8{float4v{f[0], f[1], f[2], f[3]}, float4v{f[4], f[5], f[6], f[7]}};
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(NT) void gla_sswiglu_kernel(const T* __restrict__ a,
+                                                         const T* __restrict__ v, long long ld_in,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ bias,
+                                                         T* __restrict__ out, long long ld_out,
+                                                         int H, int W, int C, int planes)
+{
+    __shared__ __attribute__((aligned(16))) T sv[HH * HW * HS];
+    __shared__ __attribute__((aligned(16))) float sw[9 * CB];  // taps [k][channel]
+    __shared__ __attribute__((aligned(16))) float sb[CB];
+    const int tid = threadIdx.x;
+    // XCD-aware placement: workgroup i runs on XCD i mod 8.  Every (image,
+    // channel block) plane goes to one XCD, its tiles in raster order, so the
+    // halo rows two neighbouring tiles share are found in that XCD's L2.
+    const int tiles_w = (W + TW - 1) / TW, tiles_h = (H + TH - 1) / TH;
+    const int tiles = tiles_w * tiles_h;
+    const int ncb = (C + CB - 1) / CB;
+    const long long local = blockIdx.x / 8;
+    const long long plane = (long long)(blockIdx.x % 8) + 8 * (local / tiles);
+    if (plane >= (long long)planes) return;
+    const int tile = (int)(local % tiles);
+    const int x0 = (tile % tiles_w) * TW, y0 = (tile / tiles_w) * TH;
+    const int b = (int)(plane / ncb);
+    const int c0 = (int)(plane % ncb) * CB;
+    const size_t img = (size_t)b * H * W;
+
+    // ---- the block's taps and bias into LDS (coalesced reads of [C][3][3])
+    for (int i = tid; i < 9 * CB; i += NT) {
+        const int ch = i / 9, k = i - 9 * ch;
+        sw[k * CB + ch] = (c0 + ch < C) ? w[(size_t)c0 * 9 + i] : 0.f;
+    }
+    if (tid < CB) sb[tid] = (bias && c0 + tid < C) ? bias[c0 + tid] : 0.f;
+    // this thread: 8 channels of token (ty, tx) of the tile
+    const int cg = tid % CG, tx = (tid / CG) % TW, ty = tid / (CG * TW);
+    const int cc = c0 + 8 * cg;
+    const int gy = y0 + ty, gx = x0 + tx;
+    const bool live = cc < C && gy < H && gx < W;  // C is a multiple of 8
+    const size_t row = img + (size_t)(live ? gy * W + gx : 0);
+    // the gate of this thread's token, in flight during the staging
+    const V8<T> av = live ? V8<T>::load(a + row * ld_in + cc) : V8<T>::zero();
+
+    // ---- stage v over the tile and its halo (zero outside the grid)
+    for (int i = tid; i < HH * HW * CG; i += NT) {
+        const int g8 = i % CG, tok = i / CG;
+        const int hx = tok % HW, hy = tok / HW;
+        const int yy = y0 + hy - 1, xx = x0 + hx - 1;
+        const int ch = c0 + 8 * g8;
+        V8<T> x = V8<T>::zero();
+        if (yy >= 0 && yy < H && xx >= 0 && xx < W && ch < C)
+            x = V8<T>::load(v + (img + (size_t)yy * W + xx) * ld_in + ch);
+        x.store(sv + tok * HS + 8 * g8);
+    }
+    __syncthreads();
+
+    if (!live) return;
+    float acc[8];
+    {
+        const float4v b0 = *(const float4v*)(sb + 8 * cg), b1 = *(const float4v*)(sb + 8 * cg + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[e] = b0[e];
+            acc[4 + e] = b1[e];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const V8<T> x = V8<T>::load(sv + ((ty + i) * HW + tx + j) * HS + 8 * cg);
+            const float* wk = sw + (3 * i + j) * CB + 8 * cg;
+            const float4v w0 = *(const float4v*)wk, w1 = *(const float4v*)(wk + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] = __builtin_fmaf(w0[e], x.get(e), acc[e]);
+                acc[4 + e] = __builtin_fmaf(w1[e], x.get(4 + e), acc[4 + e]);
+            }
+        }
+    float hv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hv[e] = silu(av.get(e)) * acc[e];
+    V8<T>::from(hv).store(out + row * ld_out + cc);
+}
+
+}  // namespace sswiglu
+
+int launch_sswiglu(const void* a, const void* v, long long ld_in, const float* w, const float* bias,
+                   void* out, long long ld_out, int B, int H, int W, int C, int dtype, void* stream)
+{
+    const long long tiles = (long long)((H + sswiglu::TH - 1) / sswiglu::TH) *
+                            ((W + sswiglu::TW - 1) / sswiglu::TW);
+    const int planes = B * ((C + sswiglu::CB - 1) / sswiglu::CB);
+    // 8 XCDs x ceil(planes / 8) planes each x tiles (spare workgroups exit)
+    const dim3 grid((unsigned)(8 * ((planes + 7) / 8) * tiles));
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == GLA_F16) {
+        hipLaunchKernelGGL(sswiglu::gla_sswiglu_kernel<_Float16>, grid, dim3(sswiglu::NT), 0, st,
+                           (const _Float16*)a, (const _Float16*)v, ld_in, w, bias, (_Float16*)out,
+                           ld_out, H, W, C, planes);
+    } else {
+        hipLaunchKernelGGL(sswiglu::gla_sswiglu_kernel<float>, grid, dim3(sswiglu::NT), 0, st,
+                           (const float*)a, (const float*)v, ld_in, w, bias, (float*)out, ld_out, H,
+                           W, C, planes);
+    }
+    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
+}
+
+}  // namespace gla

@@ -17,8 +17,8 @@ F16, F32 = 0, 1
 ALGO_AUTO, ALGO_SINGLE_PASS, ALGO_THREE_PASS = 0, 1, 2
 STATUS = {0: "GLA_OK", 1: "GLA_EINVAL", 2: "GLA_EUNSUPPORTED", 3: "GLA_EWORKSPACE", 4: "GLA_EHIP"}
 EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_workspace_init", "gla_gate_logits",
-           "gla_fwd_gate_proj", "gla_workspace_size_gate_proj", "gla_status_str",
-           "gla_abi_version")
+           "gla_fwd_gate_proj", "gla_workspace_size_gate_proj", "gla_spatial_swiglu",
+           "gla_status_str", "gla_abi_version")
 
 
 class GlaOpts(ctypes.Structure):
@@ -87,6 +87,10 @@ def lib():
         h.gla_workspace_size_gate_proj.restype = ctypes.c_size_t
         h.gla_workspace_size_gate_proj.argtypes = [ctypes.c_int] * 4 + \
             [ctypes.POINTER(GlaGateProj), ctypes.POINTER(GlaOpts)]
+        h.gla_spatial_swiglu.restype = ctypes.c_int
+        h.gla_spatial_swiglu.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + \
+            [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         h.gla_status_str.restype = ctypes.c_char_p
         h.gla_status_str.argtypes = [ctypes.c_int]
         h.gla_abi_version.restype = ctypes.c_int
@@ -278,4 +282,40 @@ def fwd_gate_proj(q, k, v, x, w1, w2, bias, direction, H, W, chunk=64, r=None,
                                  r.data_ptr() if r is not None else None, ctypes.byref(opts))
     if st != 0:
         raise GlaError(st, f"gla_fwd_gate_proj failed: {status_str(st)}")
+    return out
+
+
+def spatial_swiglu(gate, value, H, W, conv_w, conv_b=None, out=None, stream=None):
+    """Spatial SwiGLU core (include/gla.h: gla_spatial_swiglu):
+    out = SiLU(gate) * (3x3 depthwise conv of value on the H x W grid + conv_b).
+    gate, value: [B, H*W, C] float16/float32 (row strides taken from the
+    tensors: views of one [B, H*W, 2C] tensor work); conv_w [C, 3, 3] and
+    conv_b [C] float32.  Returns out [B, H*W, C] in gate's dtype."""
+    torch = _torch()
+    B, L, C = gate.shape
+    if tuple(value.shape) != (B, L, C) or L != H * W:
+        raise ValueError("gate and value must be [B, H*W, C]")
+    if value.dtype != gate.dtype:
+        raise TypeError("value must have gate's dtype")
+    dtype = F16 if gate.dtype == torch.float16 else F32 if gate.dtype == torch.float32 else None
+    if dtype is None:
+        raise TypeError("gate must be float16 or float32")
+    for name, t in (("gate", gate), ("value", value)):
+        if not t.is_cuda or t.stride(2) != 1 or t.stride(0) != t.stride(1) * L:
+            raise ValueError(f"{name} must be a device tensor with unit channel stride and "
+                             "uniform token stride")
+    if gate.stride(1) != value.stride(1):
+        raise ValueError("gate and value must share a row stride")
+    for name, t in (("conv_w", conv_w), ("conv_b", conv_b)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if out is None:
+        out = torch.empty((B, L, C), dtype=gate.dtype, device=gate.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(gate.device).cuda_stream
+    st = lib().gla_spatial_swiglu(gate.data_ptr(), value.data_ptr(), gate.stride(1),
+                                  conv_w.data_ptr(), conv_b.data_ptr() if conv_b is not None else None,
+                                  B, H, W, C, dtype, out.data_ptr(), out.stride(1), stream)
+    if st != 0:
+        raise GlaError(st, f"gla_spatial_swiglu failed: {status_str(st)}")
     return out

@@ -44,6 +44,15 @@ GATE_PROJ = {
 }
 WORKLOADS.update(GATE_PROJ)
 
+# The Spatial SwiGLU core on the same grids: hidden width 4 x 384 = 1536
+# (expansion 4 of a 384-wide block) and 6 x 384 = 2304 (expansion 6).
+SSWIGLU = {
+    "sswiglu640": dict(index=20, kind="sswiglu", B=8, H=40, W=40, C=1536, dtype="f16"),
+    "sswiglu640_x6": dict(index=21, kind="sswiglu", B=8, H=40, W=40, C=2304, dtype="f16"),
+    "sswiglu1280": dict(index=22, kind="sswiglu", B=1, H=80, W=80, C=1536, dtype="f16"),
+}
+WORKLOADS.update(SSWIGLU)
+
 # Length and batch sweep at the pages' own kernel points (16x16 = 256 tokens,
 # the 1.6K frame, 128x128 = 16.4K tokens) at d = 64 with 6 heads, plus a tail
 # grid (42x42 = 1764 tokens, not a multiple of the 64-token chunk); the four

@@ -34,8 +34,8 @@ def _fwdp(gate=None, q=A, k=A + MB, v=A + 2 * MB, out=A + 5 * MB, r=None, direct
                                        r, ctypes.byref(opts))
 
 
-def test_abi_version_two():
-    assert gla.abi_version() == 2
+def test_abi_version():
+    assert gla.abi_version() == 3
 
 
 def test_fwd_gate_proj_argument_checks():
