@@ -151,13 +151,17 @@ __device__ __forceinline__ void load_raw(Raw& x, const Params& P, int row, int c
 }
 
 // Clamped per-token log2-decay a = log2(sigmoid(z)) / tau of 16 channels,
-// prefix-summed along the sub-chunk (0 for tokens past the end).
-__device__ __forceinline__ void gate_prefix(const Raw& x, float inv_tau, bool valid, float (&bl)[16])
+// prefix-summed along the sub-chunk.  Tokens past the end of the scan (zero
+// inputs, only in the scan's last chunk, which the aggregate pass never
+// takes) keep the finite decay of z = 0: it enters only the state after the
+// last chunk, which is never used, and sub-chunk totals that cancel in the
+// scores.
+__device__ __forceinline__ void gate_prefix(const Raw& x, float inv_tau, float (&bl)[16])
 {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const float4v zz = __builtin_bit_cast(float4v, x.z[j >> 2]);
-        bl[j] = valid ? log2_decay(zz[j & 3], inv_tau) : 0.f;
+        bl[j] = log2_decay(zz[j & 3], inv_tau);
     }
     row_scan_n(bl);
 }
@@ -166,13 +170,13 @@ __device__ __forceinline__ void gate_prefix(const Raw& x, float inv_tau, bool va
 // lane (g, l16) returns A(t = l16, s = 4g + e) = sum_c q_t k_s 2^{bl_t - bl_s}
 // for s <= t (0 above the diagonal).  Taken only when the factorised form
 // would leave the binary16 range; the token's inputs are reloaded.
-__device__ __forceinline__ float4v diag_pairwise(const Params& P, int row, int cb, bool valid, int g,
+__device__ __forceinline__ float4v diag_pairwise(const Params& P, int row, int cb, int g,
                                               int l16)
 {
     Raw x;
     load_raw<false>(x, P, row, cb, false);
     float bl[16], qv[16], kv[16];
-    gate_prefix(x, P.inv_tau, valid, bl);
+    gate_prefix(x, P.inv_tau, bl);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         qv[j] = (float)__builtin_bit_cast(half8, x.q[j >> 3])[j & 7];
@@ -275,11 +279,10 @@ void gla_wide_kernel(Params P)
 
     for (int c = c_begin; c < c_end; ++c) {
         const int buf = (c - c_begin) & 1;
-        const bool valid = (c * C + tl < P.L);
 
         // ================= row role: gate stage =================
         float bl[16];
-        gate_prefix(raw, P.inv_tau, valid, bl);
+        gate_prefix(raw, P.inv_tau, bl);
         if (l16 == 15) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -441,7 +444,7 @@ void gla_wide_kernel(Params P)
                     pd = mma(eh[kb], qdl[kb], pd);
                 }
             } else {
-                pd = diag_pairwise(P, myrow, cb, valid, g, l16);
+                pd = diag_pairwise(P, myrow, cb, g, l16);
             }
             // exchange: half 0 finishes the off-diagonal tiles, half 1 the diagonal
             // slots: [0, 4) diagonal partials of half 0, [4, 10) off-diagonal of half 1
