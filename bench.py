@@ -54,24 +54,46 @@ def algorithmic_flops_per_token_head(dk, dv, chunk):
     return (dk + dv) * (chunk + 1) + 4 * dk * dv
 
 
-def kernel_source_hash():
+# Sources each kernel family is built from (its own file and the headers it
+# includes); the traffic of a workload is tied to these only.
+_COMMON_SOURCES = ("gla_device.h", "gla_launch.h", "gla_geometry.h")
+KERNEL_SOURCES = {
+    "onepass": ("gla_onepass.hip",) + _COMMON_SOURCES,
+    "onepass_proj": ("gla_onepass.hip", "gla_proj.hip") + _COMMON_SOURCES,
+    "wide": ("gla_wide.hip", "gla_kernel.hip") + _COMMON_SOURCES,
+    "generic": ("gla_kernel.hip",) + _COMMON_SOURCES,
+    "sswiglu": ("gla_sswiglu.hip",) + _COMMON_SOURCES,
+}
+
+
+def kernel_family(spec):
+    if spec.get("kind") == "sswiglu":
+        return "sswiglu"
+    if spec["dtype"] == "f16" and spec["dk"] == 64 and spec["chunk"] == 64:
+        return "onepass_proj" if spec.get("gate_proj") else "onepass"
+    if spec["dtype"] == "f16" and spec["dk"] == 128 and spec["chunk"] == 64:
+        return "wide"
+    return "generic"
+
+
+def kernel_source_hash(family):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recurrent_vision_backbone_key_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES[family]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, calls_per_step):
+def load_traffic(workload, family):
     """HBM bytes per call from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+    taken on the current sources of the workload's kernels; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(family):
         return None
     return rec.get("hbm_bytes_per_call")
 
@@ -118,7 +140,8 @@ def traffic_from_pmc(workload, fetch_csv, write_csv, calib_fetch_csv, calib_writ
         tot = {}
         for row in csv.DictReader(open(path)):
             name = row["Kernel_Name"]
-            if substr in name and "init" not in name:
+            # demangled ("gla::...") or mangled ("_ZN3gla...") library kernels
+            if (substr in name or "_ZN3gla" in name) and "init" not in name:
                 key = (name, row["Dispatch_Id"])
                 tot[key] = tot.get(key, 0.0) + float(row["Counter_Value"])
         names = {}
@@ -135,7 +158,10 @@ def traffic_from_pmc(workload, fetch_csv, write_csv, calib_fetch_csv, calib_writ
     # one call = one dispatch of every kernel name of the call
     fetch = sum(kf.values()) * 1024.0 / fetch_factor
     write = sum(kw.values()) * 1024.0 / write_factor
-    rec = {"workload": workload, "kernel": kernel_substr, "kernel_source_hash": kernel_source_hash(),
+    from recurrent_vision_backbone_key_amd.inputs import WORKLOADS
+    family = kernel_family(WORKLOADS[workload])
+    rec = {"workload": workload, "kernel": kernel_substr, "kernel_family": family,
+           "kernel_source_hash": kernel_source_hash(family),
            "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4),
            "hbm_fetch_bytes_per_call": round(fetch), "hbm_write_bytes_per_call": round(write),
            "hbm_bytes_per_call": round(fetch + write), "dispatches": nd,
@@ -268,7 +294,8 @@ def bench_sswiglu(args, spec, name):
                    "input_sets": rotate, "hip_graph": graphs is not None, "steps_per_graph": G,
                    "accumulate": "f32"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(name, "sswiglu"),
                      "kernel": "gla_sswiglu_kernel (one launch per call)",
                      "algorithmic_bytes_per_call": bytes_call},
         "cpu_baseline": None,
@@ -473,7 +500,7 @@ def main():
     value = calls_per_step * th_call / (ms_step * 1e-3) / 1e9
 
     achieved = bytes_call / (us_call * 1e-6) / 1e9
-    traffic = None if staged else load_traffic(name, calls_per_step)
+    traffic = None if staged else load_traffic(name, kernel_family(dict(spec, chunk=chunk)))
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
