@@ -14,6 +14,8 @@ Recurrence for Efficient Dense Prediction", paper Section 2.1):
 * :func:`spatial_swiglu` (with :func:`dwconv3x3`, :func:`silu`) -- the
   Spatial SwiGLU core SiLU(a) (.) (3x3 depthwise convolution of v + b)
   (same section), numpy fp64 shifted sums;
+* :func:`bwd` -- the gradients of q, k, v, z of the ungated forward (the
+  recurrence differentiated, run backwards along the scan), fp64 C;
 * :func:`closed_form_fwd` -- the O(L^2) unrolled sum
   ``o_t = scale * sum_{s<=t} (q_t (.) prod_{j=s+1..t} gamma_j (.) k_s) v_s``
   in numpy fp64 with explicit per-pair gate sums, for tiny inputs.  Its scan
@@ -78,6 +80,13 @@ def _load():
     lib.gla_oracle_gate_logits.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.gla_oracle_bwd.restype = ctypes.c_int
+    lib.gla_oracle_bwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_long, ctypes.c_long,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.gla_oracle_half_to_double.restype = ctypes.c_double
     lib.gla_oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.gla_oracle_scan_token.restype = ctypes.c_long
@@ -115,12 +124,7 @@ def fwd(q, k, v, z, direction, H, W, r=None, w=None, tau=16.0, scale=None,
     v = np.ascontiguousarray(v)
     z64 = np.asarray(z).dtype == np.float64
     z = np.ascontiguousarray(z, dtype=np.float64 if z64 else np.float32)
-    if q.dtype == np.float16:
-        dtype = 0
-    elif q.dtype == np.float32:
-        dtype = 1
-    else:
-        raise TypeError("q must be float16 or float32")
+    dtype = _storage_code(q)
     for name, a in (("k", k), ("v", v)) + ((("r", r),) if r is not None else ()):
         if a.dtype != q.dtype:
             raise TypeError(f"{name} must have q's dtype")
@@ -157,6 +161,56 @@ def fwd(q, k, v, z, direction, H, W, r=None, w=None, tau=16.0, scale=None,
     if rc != 0:
         raise RuntimeError(f"gla_oracle_fwd failed with status {rc}")
     return out
+
+
+def _storage_code(a):
+    if a.dtype == np.float16:
+        return 0
+    if a.dtype == np.float32:
+        return 1
+    if a.dtype == np.float64:
+        return 2
+    raise TypeError("inputs must be float16, float32 or float64")
+
+
+def bwd(q, k, v, z, dout, direction, H, W, tau=16.0, scale=None, units=None, threads=None):
+    """Gradients (dq, dk, dv, dz) of the ungated forward for output gradient
+    dout ([B, L, NH, dv], q's dtype), fp64 reverse recurrence (paper Section
+    2.1 recurrence, differentiated).  q, k, v, dout: float16/32/64 read as
+    stored; z: float32 or float64.  Returns four float64 arrays shaped like
+    q, k, v, z (rows of units outside ``units`` are NaN)."""
+    lib = _load()
+    q, k, v, dout = (np.ascontiguousarray(a) for a in (q, k, v, dout))
+    z64 = np.asarray(z).dtype == np.float64
+    z = np.ascontiguousarray(z, dtype=np.float64 if z64 else np.float32)
+    dtype = _storage_code(q)
+    for name, a in (("k", k), ("v", v), ("dout", dout)):
+        if a.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    B, L, NH, dk = q.shape
+    dv = v.shape[3]
+    if L != H * W or k.shape != q.shape or z.shape != q.shape or dout.shape != v.shape:
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    u0, u1 = (0, B * NH) if units is None else units
+    outs = [np.full(a.shape, np.nan, dtype=np.float64) for a in (q, k, v, z)]
+    old = os.environ.get("OMP_NUM_THREADS")
+    if threads is not None:
+        os.environ["OMP_NUM_THREADS"] = str(threads)
+    try:
+        rc = lib.gla_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(z), 2 if z64 else 1, _ptr(dout),
+                                dtype, B, NH, H, W, dk, dv, direction, float(tau), float(scale),
+                                u0, u1, *[_ptr(o) for o in outs])
+    finally:
+        if threads is not None:
+            if old is None:
+                os.environ.pop("OMP_NUM_THREADS", None)
+            else:
+                os.environ["OMP_NUM_THREADS"] = old
+    if rc != 0:
+        raise RuntimeError(f"gla_oracle_bwd failed with status {rc}")
+    return tuple(outs)
 
 
 def gate_logits(x, w1, w2, bias, heads, threads=None):

@@ -28,7 +28,8 @@
  *     vector of length d_v shared by all heads (NULL means ones).
  *
  * Layouts: q, k, z are [B, L, NH, dk]; v, r, out are [B, L, NH, dv];
- * all contiguous row-major.  q, k, v, r are binary16 or binary32 (dtype),
+ * all contiguous row-major.  q, k, v, r are binary16, binary32 or binary64
+ * (dtype; binary64 serves the finite-difference pins of the backward),
  * z is binary32 (gla_oracle_fwd) or binary64 (gla_oracle_fwd_zd), w is
  * binary32, out is binary64.
  *
@@ -46,6 +47,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #define ORACLE_F16 0
 #define ORACLE_F32 1
@@ -120,7 +122,7 @@ static int fwd_impl(const void *q, const void *k, const void *v, const void *z, 
 {
     if (!q || !k || !v || !z || !out || B < 1 || NH < 1 || H < 1 || W < 1 ||
         dk < 1 || dv < 1 || dir < 0 || dir > 3 || !(tau > 0.0) ||
-        (dtype != ORACLE_F16 && dtype != ORACLE_F32))
+        (dtype != ORACLE_F16 && dtype != ORACLE_F32 && dtype != ORACLE_F64))
         return 1;
     if (unit_begin < 0) unit_begin = 0;
     if (unit_end > (long)B * NH) unit_end = (long)B * NH;
@@ -242,6 +244,136 @@ int gla_oracle_gate_logits(const void *x, const void *w1, const float *w2, const
             z[(size_t)t * nout + o] = acc;
         }
         free(hp);
+    }
+    return failed ? 2 : 0;
+}
+
+/*
+ * Backward pass of the ungated forward (r == NULL): given the gradient dO of
+ * the outputs o, the gradients of q, k, v and of the gate logits z.  With
+ * S_t as in the forward (S_0 = 0) and dS the gradient with respect to S_t,
+ * taken along the scan from its last token back to its first:
+ *     dS    <- dS + scale * q_t^T dO_t          (o_t = scale * q_t S_t)
+ *     dq_t   = scale * dO_t S_t^T
+ *     dk_t   = dS v_t^T ,   dv_t = k_t dS        (S_t = ... + k_t^T v_t)
+ *     dgamma_t[c] = sum_j dS[c][j] S_{t-1}[c][j]  (S_t = Diag(gamma_t) S_{t-1} + ...)
+ *     dz_t   = dgamma_t * gamma_t * (1 - sigmoid(z_t)) / tau
+ *     dS    <- Diag(gamma_t) dS                  (on to S_{t-1})
+ * (gamma = sigmoid(z)^(1/tau), so dgamma/dz = gamma (1 - sigmoid(z)) / tau.)
+ * The states S_{t-1}, S_t of a block of 64 scan positions are recomputed
+ * from a checkpoint taken every 64 positions in a first forward sweep.
+ * dO is [B, L, NH, dv] in `dtype`; the four outputs are binary64 in the
+ * layouts of q, k, v and z.  Returns 0, 1 (bad argument) or 2 (allocation).
+ */
+int gla_oracle_bwd(const void *q, const void *k, const void *v, const void *z, int zdtype,
+                   const void *dout, int dtype, int B, int NH, int H, int W, int dk, int dv,
+                   int dir, double tau, double scale, long unit_begin, long unit_end,
+                   double *dq, double *dkk, double *dvv, double *dz)
+{
+    if (!q || !k || !v || !z || !dout || !dq || !dkk || !dvv || !dz || B < 1 || NH < 1 ||
+        H < 1 || W < 1 || dk < 1 || dv < 1 || dir < 0 || dir > 3 || !(tau > 0.0) ||
+        (dtype != ORACLE_F16 && dtype != ORACLE_F32 && dtype != ORACLE_F64) ||
+        (zdtype != ORACLE_F32 && zdtype != ORACLE_F64))
+        return 1;
+    if (unit_begin < 0) unit_begin = 0;
+    if (unit_end > (long)B * NH) unit_end = (long)B * NH;
+    const long L = (long)H * W;
+    const long BLK = 64;
+    const long nblk = (L + BLK - 1) / BLK;
+    const size_t SS = (size_t)dk * dv;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (long unit = unit_begin; unit < unit_end; ++unit) {
+        const long b = unit / NH, h = unit % NH;
+        double *ck = calloc((size_t)(nblk + 1) * SS, sizeof(double)); /* ck[m]: state before block m */
+        double *st = malloc(sizeof(double) * (size_t)(BLK + 1) * SS);  /* states of one block */
+        double *dS = calloc(SS, sizeof(double));
+        double *gm = malloc(sizeof(double) * (size_t)L * dk);          /* gamma, scan order */
+        double *sg = malloc(sizeof(double) * (size_t)L * dk);          /* sigmoid(z), scan order */
+        double *dot = malloc(sizeof(double) * dv);
+        if (!ck || !st || !dS || !gm || !sg || !dot) {
+            failed = 1;
+            free(ck); free(st); free(dS); free(gm); free(sg); free(dot);
+            continue;
+        }
+        /* forward sweep: gates and one checkpoint per block */
+        double *S = ck; /* running state, copied into ck[m] at block starts */
+        double *run = calloc(SS, sizeof(double));
+        if (!run) { failed = 1; free(ck); free(st); free(dS); free(gm); free(sg); free(dot); continue; }
+        for (long i = 0; i < L; ++i) {
+            const long t = gla_oracle_scan_token(dir, i, H, W);
+            const size_t rk = ((size_t)(b * L + t) * NH + h) * dk;
+            const size_t rv = ((size_t)(b * L + t) * NH + h) * dv;
+            if (i % BLK == 0) memcpy(S + (size_t)(i / BLK) * SS, run, sizeof(double) * SS);
+            for (int c = 0; c < dk; ++c) {
+                const double zc = load_elem(z, zdtype, rk + c);
+                gm[i * dk + c] = exp(log_sigmoid(zc) / tau);
+                sg[i * dk + c] = 1.0 / (1.0 + exp(-zc));
+            }
+            for (int c = 0; c < dk; ++c) {
+                const double kc = load_elem(k, dtype, rk + c);
+                for (int j = 0; j < dv; ++j)
+                    run[(size_t)c * dv + j] = gm[i * dk + c] * run[(size_t)c * dv + j] +
+                                              kc * load_elem(v, dtype, rv + j);
+            }
+        }
+        free(run);
+        /* backward sweep, block by block */
+        for (long m = nblk - 1; m >= 0; --m) {
+            const long i0 = m * BLK, i1 = (i0 + BLK < L) ? i0 + BLK : L;
+            /* st[0] = state before i0; st[1 + (i - i0)] = S_i */
+            memcpy(st, ck + (size_t)m * SS, sizeof(double) * SS);
+            for (long i = i0; i < i1; ++i) {
+                const long t = gla_oracle_scan_token(dir, i, H, W);
+                const size_t rk = ((size_t)(b * L + t) * NH + h) * dk;
+                const size_t rv = ((size_t)(b * L + t) * NH + h) * dv;
+                const double *prev = st + (size_t)(i - i0) * SS;
+                double *cur = st + (size_t)(i - i0 + 1) * SS;
+                for (int c = 0; c < dk; ++c) {
+                    const double kc = load_elem(k, dtype, rk + c);
+                    for (int j = 0; j < dv; ++j)
+                        cur[(size_t)c * dv + j] = gm[i * dk + c] * prev[(size_t)c * dv + j] +
+                                                  kc * load_elem(v, dtype, rv + j);
+                }
+            }
+            for (long i = i1 - 1; i >= i0; --i) {
+                const long t = gla_oracle_scan_token(dir, i, H, W);
+                const size_t rk = ((size_t)(b * L + t) * NH + h) * dk;
+                const size_t rv = ((size_t)(b * L + t) * NH + h) * dv;
+                const double *prev = st + (size_t)(i - i0) * SS;
+                const double *cur = st + (size_t)(i - i0 + 1) * SS;
+                for (int j = 0; j < dv; ++j) dot[j] = load_elem(dout, dtype, rv + j);
+                /* dS += scale q^T dO */
+                for (int c = 0; c < dk; ++c) {
+                    const double qc = scale * load_elem(q, dtype, rk + c);
+                    for (int j = 0; j < dv; ++j) dS[(size_t)c * dv + j] += qc * dot[j];
+                }
+                /* dq = scale dO S^T ; dk = dS v^T ; dgamma = rowsum(dS .* S_prev) */
+                for (int c = 0; c < dk; ++c) {
+                    double aq = 0.0, ak = 0.0, ag = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        aq += dot[j] * cur[(size_t)c * dv + j];
+                        ak += dS[(size_t)c * dv + j] * load_elem(v, dtype, rv + j);
+                        ag += dS[(size_t)c * dv + j] * prev[(size_t)c * dv + j];
+                    }
+                    dq[rk + c] = scale * aq;
+                    dkk[rk + c] = ak;
+                    dz[rk + c] = ag * gm[i * dk + c] * (1.0 - sg[i * dk + c]) / tau;
+                }
+                /* dv = k dS */
+                for (int j = 0; j < dv; ++j) {
+                    double a = 0.0;
+                    for (int c = 0; c < dk; ++c)
+                        a += load_elem(k, dtype, rk + c) * dS[(size_t)c * dv + j];
+                    dvv[rv + j] = a;
+                }
+                /* on to S_{t-1} */
+                for (int c = 0; c < dk; ++c)
+                    for (int j = 0; j < dv; ++j) dS[(size_t)c * dv + j] *= gm[i * dk + c];
+            }
+        }
+        free(ck); free(st); free(dS); free(gm); free(sg); free(dot);
     }
     return failed ? 2 : 0;
 }

@@ -450,3 +450,72 @@ def test_spatial_swiglu_special_cases():
     y1 = oracle.spatial_swiglu(a2, v, H, W, wr)
     changed = np.any(y0 != y1, axis=2)[0]
     assert changed.tolist() == [t == 5 for t in range(H * W)]
+
+
+# ---------------------------------------------------------------------------
+# Backward of the ungated forward (the Sec. 2.1 recurrence differentiated)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", oracle.DIRS)
+@pytest.mark.parametrize("H,W,dk,dv", [(3, 5, 4, 3), (9, 15, 3, 2)])
+def test_bwd_equals_central_differences(direction, H, W, dk, dv):
+    """Every gradient against central differences of the forward oracle on
+    fp64 inputs, f(x) = sum(G * fwd(x)) (9 x 15 spans three 64-position
+    checkpoint blocks of the backward)."""
+    rng = np.random.default_rng(100 + direction + H)
+    B, NH = 1, 2
+    x = make_inputs(B, NH, H, W, dk, dv, "f32", seed=7 + H)
+    q, k, v = (x[n].astype(np.float64) for n in "qkv")
+    z = x["z"].astype(np.float64)
+    G = rng.standard_normal((B, H * W, NH, dv))
+    grads = oracle.bwd(q, k, v, z, G, direction, H, W)
+    base = dict(q=q, k=k, v=v, z=z)
+
+    def f(**kw):
+        a = dict(base, **kw)
+        return float((oracle.fwd(a["q"], a["k"], a["v"], a["z"], direction, H, W) * G).sum())
+
+    h = 1e-6
+    for (name, arr), g in zip(base.items(), grads):
+        for _ in range(5):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += h
+            am[idx] -= h
+            fd = (f(**{name: ap}) - f(**{name: am})) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-5 * (abs(g[idx]) + 1e-2), (name, idx, fd, g[idx])
+
+
+def test_bwd_gamma_one_is_linear_attention_gradient():
+    """z = +40 makes gamma == 1 in fp64: the gradients of causal linear
+    attention o = s tril(Q K^T) V in closed form, with P = G V^T and
+    A = Q K^T: dq = s tril(P) K, dk = s tril(P)^T Q, dv = s tril(A)^T G,
+    and dz = 0 (1 - sigmoid(40) is below 1e-17)."""
+    rng = np.random.default_rng(8)
+    L, dk, dv = 11, 5, 3
+    q, k = rng.standard_normal((2, 1, L, 1, dk))
+    v = rng.standard_normal((1, L, 1, dv))
+    G = rng.standard_normal((1, L, 1, dv))
+    z = np.full((1, L, 1, dk), 40.0)
+    dq, dkk, dvv, dz = oracle.bwd(q, k, v, z, G, 0, 1, L)
+    s = 1.0 / math.sqrt(dk)
+    Q, K, V, Gm = q[0, :, 0], k[0, :, 0], v[0, :, 0], G[0, :, 0]
+    P = np.tril(Gm @ V.T)
+    A = np.tril(Q @ K.T)
+    assert np.allclose(dq[0, :, 0], s * P @ K, rtol=0, atol=1e-12)
+    assert np.allclose(dkk[0, :, 0], s * P.T @ Q, rtol=0, atol=1e-12)
+    assert np.allclose(dvv[0, :, 0], s * A.T @ Gm, rtol=0, atol=1e-12)
+    assert np.max(np.abs(dz)) < 1e-15
+
+
+def test_bwd_direction_identity():
+    """Reversing the token order and the scan together leaves the gradients
+    (read back at the original tokens) unchanged, bit for bit."""
+    H, W = 4, 6
+    x = make_inputs(1, 2, H, W, 4, 4, "f32", seed=12)
+    G = np.random.default_rng(1).standard_normal((1, H * W, 2, 4)).astype(np.float32)
+    g0 = oracle.bwd(x["q"], x["k"], x["v"], x["z"], G, 0, H, W)
+    fl = {n: np.ascontiguousarray(x[n][:, ::-1]) for n in "qkvz"}
+    g1 = oracle.bwd(fl["q"], fl["k"], fl["v"], fl["z"], np.ascontiguousarray(G[:, ::-1]), 1, H, W)
+    for a, b in zip(g0, g1):
+        assert np.array_equal(a, b[:, ::-1])
