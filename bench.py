@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "chunkwise GLA fwd: µs/call + Gtok·head/s at L=1600; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3  # dense binary32 matrix-core peak
 MALL_BYTES = 256 << 20     # last-level (Infinity) cache
 
 
@@ -63,12 +64,13 @@ KERNEL_SOURCES = {
     "wide": ("gla_wide.hip", "gla_kernel.hip") + _COMMON_SOURCES,
     "generic": ("gla_kernel.hip",) + _COMMON_SOURCES,
     "sswiglu": ("gla_sswiglu.hip",) + _COMMON_SOURCES,
+    "bwd": ("gla_bwd.hip", "gla_kernel.hip") + _COMMON_SOURCES,
 }
 
 
 def kernel_family(spec):
-    if spec.get("kind") == "sswiglu":
-        return "sswiglu"
+    if spec.get("kind") in ("sswiglu", "bwd"):
+        return spec["kind"]
     if spec["dtype"] == "f16" and spec["dk"] == 64 and spec["chunk"] == 64:
         return "onepass_proj" if spec.get("gate_proj") else "onepass"
     if spec["dtype"] == "f16" and spec["dk"] == 128 and spec["chunk"] == 64:
@@ -197,8 +199,12 @@ def cpu_baseline(spec, name, seconds):
         if spec.get("gate_proj"):
             z = oracle.gate_logits(x["x"], x["w1"], x["w2"], x["bias"], spec["NH"],
                                    threads=cores)
-        oracle.fwd(x["q"], x["k"], x["v"], z, spec["dirs"][call], H, W, r=x["r"],
-                   w=x["w"], units=(u0, u1), threads=cores)
+        if spec.get("kind") == "bwd":
+            oracle.bwd(x["q"], x["k"], x["v"], z, x["dout"], spec["dirs"][call], H, W,
+                       units=(u0, u1), threads=cores)
+        else:
+            oracle.fwd(x["q"], x["k"], x["v"], z, spec["dirs"][call], H, W, r=x["r"],
+                       w=x["w"], units=(u0, u1), threads=cores)
         done_th += (u1 - u0) * H * W
         calls += 1
         if time.perf_counter() - t0 >= seconds:
@@ -206,11 +212,147 @@ def cpu_baseline(spec, name, seconds):
     dt = time.perf_counter() - t0
     return {"value": done_th / dt / 1e9, "unit": "Gtok·head/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{calls} oracle calls of {name} ({spec['H']}x{spec['W']}, d={spec['dk']}), "
+            "sample": f"{calls} oracle {'backward ' if spec.get('kind') == 'bwd' else ''}calls "
+                      f"of {name} ({spec['H']}x{spec['W']}, d={spec['dk']}), "
                       + ("gate logits of every token projected per call, "
                          if spec.get("gate_proj") else "")
                       + f"{per_call_units} of {units_total} (batch, head) scans each, "
                       f"{done_th} token-heads in {dt:.1f} s"}
+
+
+def time_steps(step, rotate, steps, warmup, args, steps_per_graph):
+    """Replay `step(r)` (r = input set) from HIP graphs of G consecutive steps
+    each (a replay has a fixed cost of about 15 us on this platform, so several
+    steps share one); graph i holds steps on input sets i*G .. i*G+G-1 (mod
+    rotate), enough graphs that the sets cycle without repeating back to back.
+    Runs `warmup` untimed steps, then times `steps` steps with HIP events on
+    the replay stream.  Returns (ms per step, G, whether graphs were used)."""
+    import torch
+
+    G = 1
+    if not args.no_graph:
+        G = args.steps_per_graph or steps_per_graph
+        G = math.gcd(G, steps) if steps > 0 else 1
+        G = math.gcd(G, warmup) if warmup > 0 else G
+    n_graphs = rotate // math.gcd(rotate, G)
+    stream = torch.cuda.current_stream()
+    graphs = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for r in range(rotate):
+                step(r)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for gi in range(n_graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for j in range(G):
+                    step((gi * G + j) % rotate)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        # i counts graph replays (G steps each) or single eager steps
+        if graphs is not None:
+            graphs[i % n_graphs].replay()
+        else:
+            step(i % rotate)
+
+    for i in range(warmup // G):
+        run(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps // G):
+        run(warmup // G + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, G, graphs is not None
+
+
+def algorithmic_flops_bwd_per_token_head(dk, dv, chunk):
+    """Chunkwise backward, causal products counted once: forward and reverse
+    chunk aggregates (k^T v, q^T dO), the entering state and gradient in dq,
+    dk, dv (5 x 2 dk dv), and the intra-chunk scores dO v^T, their products
+    with k (dq) and q (dk), the decayed scores q k^T and their product with dO
+    (dv): chunk/2 positions on average, chunk (3 dk + 2 dv) flops."""
+    return 10 * dk * dv + chunk * (3 * dk + 2 * dv)
+
+
+def bench_bwd(args, spec, name):
+    """One step = one gla_bwd call per direction of the workload, over the
+    whole batch; same timing method as the forward."""
+    import torch
+
+    from recurrent_vision_backbone_key_amd import gla
+    from recurrent_vision_backbone_key_amd.inputs import make_bwd_inputs_device
+
+    B, NH, H, W, d = spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"]
+    dirs = spec["dirs"]
+    es = 2 if spec["dtype"] == "f16" else 4
+    th_call = B * NH * H * W
+    # q, k, v, dO read, dq, dk, dv written (storage type); z read, dz written (binary32)
+    bytes_call = th_call * (7 * es * d + 8 * d)
+    flops_call = th_call * algorithmic_flops_bwd_per_token_head(d, d, spec["chunk"])
+    rotate = args.rotate or max(1, math.ceil(2 * MALL_BYTES / (bytes_call * len(dirs))))
+    steps = args.steps if args.steps is not None else 100
+    warmup = args.warmup if args.warmup is not None else 20
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] {name}: {len(dirs)} calls/step, {bytes_call / 1e6:.2f} MB/call, "
+          f"{rotate} input sets, steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+    opts = gla.make_opts(B, NH, d, d, gla.F16 if es == 2 else gla.F32)
+    ws_bytes = gla.bwd_workspace_size(dirs[0], H, W, opts)
+    sets = []
+    for r in range(rotate):
+        calls = []
+        for c, dr in enumerate(dirs):
+            x = make_bwd_inputs_device(B, NH, H, W, d, spec["dtype"], spec["z"],
+                                       seed=1000 * spec["index"] + 100 * r + c, device=dev)
+            grads = (torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"]),
+                     torch.empty_like(x["z"]))
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+            calls.append((x, dr, grads, ws))
+        sets.append(calls)
+
+    def step(r):
+        for x, dr, grads, ws in sets[r]:
+            gla.bwd(x["q"], x["k"], x["v"], x["z"], x["dout"], dr, H, W, grads=grads, workspace=ws)
+
+    ms_step, G, graphed = time_steps(step, rotate, steps, warmup, args, 10)
+    us_call = 1e3 * ms_step / len(dirs)
+    tflops = flops_call / (us_call * 1e-6) / 1e12
+    gbs = bytes_call / (us_call * 1e-6) / 1e9
+    result = {
+        "metric": "chunkwise GLA bwd: µs/call + Gtok·head/s at L=1600; % of MFMA (fp32) roofline",
+        "value": round(len(dirs) * th_call / (ms_step * 1e-3) / 1e9, 4), "unit": "Gtok·head/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
+        "us_per_call": round(us_call, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
+        "config": {"workload": name, "B": B, "heads": NH, "grid": f"{H}x{W}", "L": H * W,
+                   "dk": d, "dv": d, "chunk": spec["chunk"],
+                   "dirs": ",".join("L2R R2L T2B B2T".split()[x] for x in dirs),
+                   "calls_per_step": len(dirs), "input_sets": rotate, "hip_graph": graphed,
+                   "steps_per_graph": G, "workspace_bytes_per_call": ws_bytes,
+                   "accumulate": "f32", "mfma_operands": "f32"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic(name, "bwd"),
+                     "kernel": "gla_chunk_kernel<aggregate> + gla_fold_kernel + gla_bwd_agg_kernel "
+                               "+ gla_bwd_fold_kernel + gla_bwd_chunk_kernel + gla_bwd_dz_kernel "
+                               "(six launches per call; figures for the whole call)",
+                     "algorithmic_flops_per_call": flops_call,
+                     "algorithmic_bytes_per_call": bytes_call,
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(spec, name, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
 
 
 def bench_sswiglu(args, spec, name):
@@ -245,44 +387,7 @@ def bench_sswiglu(args, spec, name):
         a, v, w, b, o = sets[r]
         gla.spatial_swiglu(a, v, H, W, w, b, out=o)
 
-    G = 1 if args.no_graph else math.gcd(math.gcd(args.steps_per_graph or 10, steps), warmup)
-    n_graphs = rotate // math.gcd(rotate, G)
-    stream = torch.cuda.current_stream()
-    graphs = None
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for r in range(rotate):
-                step(r)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graphs = []
-        for gi in range(n_graphs):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for j in range(G):
-                    step((gi * G + j) % rotate)
-            graphs.append(g)
-        torch.cuda.synchronize()
-
-    def run(i):
-        if graphs is not None:
-            graphs[i % n_graphs].replay()
-        else:
-            step(i % rotate)
-
-    for i in range(warmup // G):
-        run(i)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(steps // G):
-        run(warmup // G + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / steps
+    ms_step, G, graphed = time_steps(step, rotate, steps, warmup, args, 10)
     achieved = bytes_call / (ms_step * 1e-3) / 1e9
     result = {
         "metric": "Spatial SwiGLU core: µs/call; % of HBM roofline",
@@ -291,7 +396,7 @@ def bench_sswiglu(args, spec, name):
         "us_per_call": round(1e3 * ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
         "config": {"workload": name, "B": B, "grid": f"{H}x{W}", "L": H * W, "channels": C,
-                   "input_sets": rotate, "hip_graph": graphs is not None, "steps_per_graph": G,
+                   "input_sets": rotate, "hip_graph": graphed, "steps_per_graph": G,
                    "accumulate": "f32"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -381,6 +486,9 @@ def main():
     if spec.get("kind") == "sswiglu":
         bench_sswiglu(args, spec, name)
         return
+    if spec.get("kind") == "bwd":
+        bench_bwd(args, spec, name)
+        return
     chunk = args.chunk or spec["chunk"]
     dirs = spec["dirs"]
     calls_per_step = len(dirs)
@@ -447,55 +555,7 @@ def main():
                     norm_weight=x["w"], eps=1e-6, out=out, segment_chunks=args.segment_chunks,
                     workspace=ws)
 
-    # Steps are replayed from HIP graphs of G consecutive steps each (a replay
-    # has a fixed cost of about 15 us on this platform, so several steps share
-    # one); graph r holds steps on input sets r*G .. r*G+G-1 (mod rotate).
-    G = 1
-    if not args.no_graph:
-        G = args.steps_per_graph or (1 if big else 10)
-        G = math.gcd(G, steps) if steps > 0 else 1
-        G = math.gcd(G, warmup) if warmup > 0 else G
-    # enough graphs that the input sets cycle without repeating back to back
-    n_graphs = rotate // math.gcd(rotate, G)
-    stream = torch.cuda.current_stream()
-    graphs = None
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for r in range(rotate):
-                step(r)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graphs = []
-        for gi in range(n_graphs):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for j in range(G):
-                    step((gi * G + j) % rotate)
-            graphs.append(g)
-        torch.cuda.synchronize()
-
-    def run(i):
-        # i counts graph replays (G steps each) or single eager steps
-        if graphs is not None:
-            graphs[i % n_graphs].replay()
-        else:
-            step(i % rotate)
-
-    for i in range(warmup // G):
-        run(i)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(steps // G):
-        run(warmup // G + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
-    ms_step = ms / steps
+    ms_step, G, graphed = time_steps(step, rotate, steps, warmup, args, 1 if big else 10)
     us_call = 1e3 * ms_step / calls_per_step
     value = calls_per_step * th_call / (ms_step * 1e-3) / 1e9
 
@@ -518,7 +578,7 @@ def main():
                    "dirs": ",".join("L2R R2L T2B B2T".split()[d] for d in dirs),
                    "gated": gated, "calls_per_step": calls_per_step,
                    **({"gate_projection": dict(gp, staged=staged)} if gp else {}),
-                   "input_sets": rotate, "hip_graph": graphs is not None,
+                   "input_sets": rotate, "hip_graph": graphed,
                    "steps_per_graph": G,
                    "workspace_bytes_per_call": nseg_bytes, "accumulate": "f32"},
         "roofline": roofline,

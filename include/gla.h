@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 3
+#define GLA_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define GLA_API __attribute__((visibility("default")))
@@ -217,6 +217,29 @@ GLA_API size_t gla_workspace_size_gate_proj(int dir, int H, int W, int chunk,
 GLA_API int gla_spatial_swiglu(const void *gate, const void *value, int64_t ld_in,
                                const float *conv_w, const float *conv_b, int batch, int H, int W,
                                int channels, int dtype, void *out, int64_t ld_out, void *stream);
+
+/*
+ * gla_bwd -- gradients of the ungated forward (r == NULL in gla_fwd; paper
+ * Section 2.1 recurrence, differentiated).  With dout = dL/do:
+ *     dS_t = sum_{u >= t} Diag(prod_{t < j <= u} gamma_j) scale q_u^T dout_u
+ *     dq_t = scale dout_t S_t^T,  dk_t = dS_t v_t^T,  dv_t = k_t dS_t
+ *     dz_t = (1 - sigmoid(z_t)) / tau (.) sum_{u >= t} (q_u (.) dq_u - k_u (.) dk_u)
+ * along the scan order of `dir`, results at the original token positions.
+ *   q, k, gate_logits, dq, dk, dz  [B, L, NH, dk]; v, dout, dv [B, L, NH, dv]
+ *   q, k, v, dout, dq, dk, dv in opts->dtype; gate_logits and dz binary32
+ * This build: dk == dv in {16, 32, 64}, binary16 or binary32 storage; 64-position
+ * chunks.  opts->norm_weight, eps, segment_chunks and algorithm are ignored.
+ * The workspace must hold gla_bwd_workspace_size() bytes (no initialisation:
+ * every call rewrites what it reads).  All pointers are 16-byte aligned
+ * device pointers; the four outputs must not overlap each other, an input or
+ * the workspace.  Asynchronous on opts->stream.  Returns a gla_status.
+ */
+GLA_API int gla_bwd(const void *q, const void *k, const void *v, const float *gate_logits,
+                    const void *dout, int dir, int H, int W, void *dq, void *dk, void *dv,
+                    float *dz, const gla_opts *opts);
+
+/* Bytes of workspace gla_bwd needs (0 for arguments it would reject). */
+GLA_API size_t gla_bwd_workspace_size(int dir, int H, int W, const gla_opts *opts);
 
 /* Static, NUL-terminated description of a gla_status value. */
 GLA_API const char *gla_status_str(int status);

@@ -40,6 +40,7 @@ UNITS = [
     ("gla_wide.hip", "hip", []),
     ("gla_proj.hip", "hip", []),
     ("gla_sswiglu.hip", "hip", []),
+    ("gla_bwd.hip", "hip", []),
 ]
 
 

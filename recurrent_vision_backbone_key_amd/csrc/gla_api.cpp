@@ -1,5 +1,6 @@
 // gla_api.cpp -- the C ABI (include/gla.h) over the HIP kernels.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "gla.h"
@@ -151,6 +152,62 @@ extern "C" int gla_spatial_swiglu(const void* gate, const void* value, int64_t l
     if (st != GLA_OK) return st;
     return gla::launch_sswiglu(gate, value, ld_in, conv_w, conv_b, out, ld_out, batch, H, W,
                                channels, dtype, stream);
+}
+
+extern "C" int gla_bwd(const void* q, const void* k, const void* v, const float* gate_logits,
+                       const void* dout, int dir, int H, int W, void* dq, void* dk, void* dv,
+                       float* dz, const gla_opts* opts)
+{
+    int nchunks = 0;
+    size_t off_r = 0, off_s = 0;
+    const int st = gla_validate_bwd(q, k, v, gate_logits, dout, dir, H, W, dq, dk, dv, dz, opts,
+                                    &nchunks, &off_r, &off_s);
+    if (st != GLA_OK) return st;
+    gla::Params P;
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.z = gate_logits;
+    P.r = nullptr;
+    P.w = nullptr;
+    P.out = nullptr;
+    char* ws = (char*)opts->workspace;
+    P.ws = (float*)ws;
+    P.B = opts->batch;
+    P.NH = opts->heads;
+    P.H = H;
+    P.W = W;
+    P.L = H * W;
+    P.dir = dir;
+    P.nchunks = nchunks;
+    P.seg_chunks = 1;
+    P.nseg = nchunks;
+    P.scale = opts->scale > 0.0f ? opts->scale : (float)(1.0 / sqrt((double)opts->dk));
+    P.inv_tau = 1.0f / (opts->tau > 0.0f ? opts->tau : 16.0f);
+    P.eps = 0.0f;
+    P.ticket = P.err = P.done = P.flags = nullptr;
+    P.agg = P.incl = nullptr;
+    P.xcd_local = 0;
+    P.xcd_tasks = 0;
+    no_proj(P);
+    gla::BwdParams Q;
+    Q.dout = dout;
+    Q.dq = dq;
+    Q.dk = dk;
+    Q.dv = dv;
+    Q.dz = dz;
+    Q.ws_f = (float*)ws;
+    Q.ws_r = (float*)(ws + off_r);
+    Q.ws_s = (float*)(ws + off_s);
+    return gla::launch_bwd(P, Q, opts->dtype, opts->dk, opts->stream);
+}
+
+extern "C" size_t gla_bwd_workspace_size(int dir, int H, int W, const gla_opts* opts)
+{
+    int nchunks = 0;
+    size_t off_r = 0, off_s = 0, bytes = 0;
+    if (gla_plan_bwd(dir, H, W, opts, &nchunks, &off_r, &off_s, &bytes) != GLA_OK) return 0;
+    return bytes;
 }
 
 extern "C" const char* gla_status_str(int status)

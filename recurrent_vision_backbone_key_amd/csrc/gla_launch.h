@@ -79,6 +79,27 @@ int launch_gate_rank(const GateProj& G, int dtype, int tokens, float* hp, void* 
 int launch_sswiglu(const void* a, const void* v, long long ld_in, const float* w, const float* bias,
                    void* out, long long ld_out, int B, int H, int W, int C, int dtype, void* stream);
 
+// Backward (include/gla.h, gla_bwd): gradient of the outputs and the
+// gradients written, plus the workspace parts.
+struct BwdParams {
+    const void* dout;   // [B, L, NH, DV]
+    void* dq;           // [B, L, NH, DK]
+    void* dk;           // [B, L, NH, DK]
+    void* dv;           // [B, L, NH, DV]
+    float* dz;          // [B, L, NH, DK] binary32
+    float* ws_f;        // forward chunk-entry states [units][nchunks-1][D*D + D]
+    float* ws_r;        // reverse aggregates, then the entering gradients [units][nchunks-1][D*D + D]
+    float* ws_s;        // chunk sums of q (.) dq - k (.) dk [units][nchunks][D]
+};
+
+// Chunkwise backward, 64-position chunks (P describes the forward call with
+// nseg = nchunks, seg_chunks = 1, ws = Q.ws_f).
+int launch_bwd(const Params& P, const BwdParams& Q, int dtype, int d, void* stream);
+
+// Forward aggregate and fold passes alone (chunk 64, one chunk per segment):
+// leaves in P.ws the state entering every chunk after the first.
+int launch_fwd_states(const Params& P, int dtype, int d, void* stream);
+
 // Zero-fills a workspace (counters, flags) on `stream`.
 int launch_workspace_init(void* ws, size_t bytes, void* stream);
 

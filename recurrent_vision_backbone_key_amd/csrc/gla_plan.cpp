@@ -296,3 +296,58 @@ extern "C" int gla_validate_sswiglu(const void* gate, const void* value, int64_t
         if (overlaps(out, out_b, ins[i].p, ins[i].bytes)) return GLA_EINVAL;
     return GLA_OK;
 }
+
+extern "C" int gla_plan_bwd(int dir, int H, int W, const gla_opts* o, int* nchunks, size_t* off_r,
+                            size_t* off_s, size_t* bytes)
+{
+    if (!o) return GLA_EINVAL;
+    if (o->batch < 1 || o->heads < 1 || H < 1 || W < 1) return GLA_EINVAL;
+    if (dir < GLA_L2R || dir > GLA_B2T) return GLA_EINVAL;
+    if (o->dtype != GLA_F16 && o->dtype != GLA_F32) return GLA_EUNSUPPORTED;
+    if (o->dk != o->dv || (o->dk != 16 && o->dk != 32 && o->dk != 64)) return GLA_EUNSUPPORTED;
+    const int64_t L = (int64_t)H * W;
+    if (L >= (int64_t)1 << 24) return GLA_EUNSUPPORTED;
+    const int64_t rows = (int64_t)o->batch * L * o->heads;
+    if (rows >= (int64_t)1 << 31) return GLA_EUNSUPPORTED;
+    if (isnan(o->tau) || isnan(o->scale) || isinf(o->tau) || isinf(o->scale)) return GLA_EINVAL;
+    const int64_t nc = (L + 63) / 64;
+    const int64_t units = (int64_t)o->batch * o->heads;
+    const size_t slot = ((size_t)o->dk * o->dk + o->dk) * 4;
+    const size_t part = (size_t)units * (nc - 1) * slot;
+    *nchunks = (int)nc;
+    *off_r = ((part + 255) / 256) * 256;
+    *off_s = *off_r + ((part + 255) / 256) * 256;
+    *bytes = *off_s + (size_t)units * nc * o->dk * 4;
+    return GLA_OK;
+}
+
+extern "C" int gla_validate_bwd(const void* q, const void* k, const void* v, const float* z,
+                                const void* dout, int dir, int H, int W, const void* dq,
+                                const void* dk, const void* dv, const float* dz, const gla_opts* o,
+                                int* nchunks, size_t* off_r, size_t* off_s)
+{
+    if (!o || !q || !k || !v || !z || !dout || !dq || !dk || !dv || !dz) return GLA_EINVAL;
+    size_t bytes = 0;
+    const int st = gla_plan_bwd(dir, H, W, o, nchunks, off_r, off_s, &bytes);
+    if (st != GLA_OK) return st;
+    const size_t es = o->dtype == GLA_F16 ? 2 : 4;
+    const size_t n = (size_t)o->batch * H * W * o->heads * o->dk;
+    const Operand ins[5] = {{q, n * es, 16}, {k, n * es, 16}, {v, n * es, 16}, {z, n * 4, 16},
+                            {dout, n * es, 16}};
+    const Operand outs[4] = {{dq, n * es, 16}, {dk, n * es, 16}, {dv, n * es, 16}, {dz, n * 4, 16}};
+    for (int i = 0; i < 5; ++i)
+        if (!aligned(ins[i].p, 16)) return GLA_EINVAL;
+    for (int i = 0; i < 4; ++i) {
+        if (!aligned(outs[i].p, 16)) return GLA_EINVAL;
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes)) return GLA_EINVAL;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes)) return GLA_EINVAL;
+    }
+    if (!o->workspace || o->workspace_bytes < bytes || !aligned(o->workspace, 16)) return GLA_EWORKSPACE;
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(o->workspace, bytes, ins[i].p, ins[i].bytes)) return GLA_EINVAL;
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(o->workspace, bytes, outs[i].p, outs[i].bytes)) return GLA_EINVAL;
+    return GLA_OK;
+}

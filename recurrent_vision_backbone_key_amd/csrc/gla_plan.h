@@ -52,6 +52,17 @@ int gla_validate_sswiglu(const void* gate, const void* value, int64_t ld_in, con
                          const float* conv_b, int batch, int H, int W, int channels, int dtype,
                          const void* out, int64_t ld_out);
 
+// Backward: sizes checks, workspace layout (bytes): forward states at 0,
+// reverse states at *off_r, chunk sums at *off_s, total *bytes.
+int gla_plan_bwd(int dir, int H, int W, const gla_opts* opts, int* nchunks, size_t* off_r,
+                 size_t* off_s, size_t* bytes);
+
+// Host check of every argument of gla_bwd.
+int gla_validate_bwd(const void* q, const void* k, const void* v, const float* z, const void* dout,
+                     int dir, int H, int W, const void* dq, const void* dk, const void* dv,
+                     const float* dz, const gla_opts* opts, int* nchunks, size_t* off_r,
+                     size_t* off_s);
+
 // Whether a (dtype, head dim, chunk) instantiation is built (shared-memory
 // footprint of one workgroup within the 160 KiB of a gfx950 CU).
 int gla_config_built(int dtype, int d, int chunk);

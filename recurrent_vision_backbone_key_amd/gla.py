@@ -18,7 +18,7 @@ ALGO_AUTO, ALGO_SINGLE_PASS, ALGO_THREE_PASS = 0, 1, 2
 STATUS = {0: "GLA_OK", 1: "GLA_EINVAL", 2: "GLA_EUNSUPPORTED", 3: "GLA_EWORKSPACE", 4: "GLA_EHIP"}
 EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_workspace_init", "gla_gate_logits",
            "gla_fwd_gate_proj", "gla_workspace_size_gate_proj", "gla_spatial_swiglu",
-           "gla_status_str", "gla_abi_version")
+           "gla_bwd", "gla_bwd_workspace_size", "gla_status_str", "gla_abi_version")
 
 
 class GlaOpts(ctypes.Structure):
@@ -91,6 +91,11 @@ def lib():
         h.gla_spatial_swiglu.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + \
             [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        h.gla_bwd.restype = ctypes.c_int
+        h.gla_bwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 4 + \
+            [ctypes.POINTER(GlaOpts)]
+        h.gla_bwd_workspace_size.restype = ctypes.c_size_t
+        h.gla_bwd_workspace_size.argtypes = [ctypes.c_int] * 3 + [ctypes.POINTER(GlaOpts)]
         h.gla_status_str.restype = ctypes.c_char_p
         h.gla_status_str.argtypes = [ctypes.c_int]
         h.gla_abi_version.restype = ctypes.c_int
@@ -191,6 +196,56 @@ def fwd(q, k, v, z, direction, H, W, chunk=64, r=None, norm_weight=None, eps=1e-
     if st != 0:
         raise GlaError(st, f"gla_fwd failed: {status_str(st)}")
     return out
+
+
+def bwd_workspace_size(direction, H, W, opts: GlaOpts) -> int:
+    return lib().gla_bwd_workspace_size(direction, H, W, ctypes.byref(opts))
+
+
+def bwd(q, k, v, z, dout, direction, H, W, tau=16.0, scale=None, grads=None, workspace=None,
+        stream=None):
+    """Gradients of the ungated forward (include/gla.h: gla_bwd) on CUDA tensors.
+
+    q, k, z: [B, L, NH, d]; v, dout: [B, L, NH, d]; q, k, v, dout float16 or
+    float32, z float32.  Returns (dq, dk, dv, dz): dq, dk, dv in q's dtype, dz
+    float32.  ``grads`` may supply the four output tensors.
+    """
+    torch = _torch()
+    B, L, NH, dk = q.shape
+    dv = v.shape[3]
+    if q.dtype == torch.float16:
+        dtype = F16
+    elif q.dtype == torch.float32:
+        dtype = F32
+    else:
+        raise TypeError("q must be float16 or float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if z.dtype != torch.float32:
+        raise TypeError("gate logits must be float32")
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty(z.shape, dtype=torch.float32, device=q.device))
+    dq, dk_, dv_, dz = grads
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = make_opts(B, NH, dk, dv, dtype, tau, scale, stream=stream)
+    need = bwd_workspace_size(direction, H, W, opts)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().gla_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), z.data_ptr(), dout.data_ptr(),
+                       direction, H, W, dq.data_ptr(), dk_.data_ptr(), dv_.data_ptr(),
+                       dz.data_ptr(), ctypes.byref(opts))
+    if st != 0:
+        raise GlaError(st, f"gla_bwd failed: {status_str(st)}")
+    return dq, dk_, dv_, dz
 
 
 def make_gate(x, w1, w2, bias=None) -> GlaGateProj:

@@ -65,6 +65,14 @@ for _i, (_h, _w, _b) in enumerate(((16, 16, 1), (16, 16, 8), (40, 40, 1), (40, 4
                                           dirs=(L2R, R2L, T2B, B2T), gated=False)
 WORKLOADS.update(SWEEP)
 
+# Backward of the ungated forward at the batch shape (8 images, 40 x 40
+# patches, 6 heads of 64): the four directions per step.
+BWD = {
+    "bwd640": dict(index=23, kind="bwd", B=8, NH=6, H=40, W=40, dk=64, dv=64, dtype="f16",
+                   z=(0.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T), gated=False),
+}
+WORKLOADS.update(BWD)
+
 EPS = 1e-6
 TAU = 16.0
 
@@ -99,6 +107,30 @@ def make_inputs(B, NH, H, W, dk, dv, dtype="f16", z=(0.0, 1.0), gated=False, see
     return dict(q=q, k=k, v=v, z=zz, r=r, w=w)
 
 
+def make_bwd_inputs(B, NH, H, W, d, dtype="f16", z=(0.0, 1.0), seed=0, dout_seed=None):
+    """Operands of the backward: q, k, v, z as :func:`make_inputs` (ungated)
+    with PCG64(seed), then dout ~ N(0, 1) [B, L, NH, d] rounded to ``dtype``
+    from PCG64(dout_seed), by default seed + 1."""
+    x = make_inputs(B, NH, H, W, d, d, dtype, z=z, gated=False, seed=seed)
+    rng = np.random.default_rng(seed + 1 if dout_seed is None else dout_seed)
+    x["dout"] = rng.standard_normal((B, H * W, NH, d)).astype(np_dtype(dtype))
+    return x
+
+
+def make_bwd_inputs_device(B, NH, H, W, d, dtype="f16", z=(0.0, 1.0), seed=0, device="cuda"):
+    """Same distributions as :func:`make_bwd_inputs`, drawn on the device with
+    seeded torch generators (timing inputs)."""
+    import torch
+
+    x = make_inputs_device(B, NH, H, W, d, d, dtype, z=z, gated=False, seed=seed, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 1)
+    dt = {"f16": torch.float16, "f32": torch.float32}[dtype]
+    x["dout"] = torch.randn((B, H * W, NH, d), generator=gen, device=device,
+                            dtype=torch.float32).to(dt)
+    return x
+
+
 def make_gate_proj_inputs(B, L, NH, dk, d_model, rank=16, dtype="f16", seed=0):
     """Draw the retention gate's low-rank projection inputs from PCG64(seed),
     in the order x, w1, w2, bias.
@@ -123,6 +155,11 @@ def workload_inputs(name: str, call: int = 0, **overrides):
     """Inputs of call ``call`` of a named workload; seed = 1000*index + call."""
     spec = dict(WORKLOADS[name])
     spec.update(overrides)
+    if spec.get("kind") == "bwd":
+        # output gradient from its own stream (seed + 500)
+        return make_bwd_inputs(spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"],
+                               spec["dtype"], spec["z"], seed=1000 * spec["index"] + call,
+                               dout_seed=1000 * spec["index"] + 500 + call)
     x = make_inputs(spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"], spec["dv"],
                     spec["dtype"], spec["z"], spec["gated"], seed=1000 * spec["index"] + call)
     gp = spec.get("gate_proj")
