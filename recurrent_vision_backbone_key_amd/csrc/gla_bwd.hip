@@ -10,31 +10,34 @@
 //     dz_t = (1 - sigmoid(z_t)) / tau (.) sum_{u >= t} (q_u (.) dq_u - k_u (.) dk_u)
 // (the last because L depends on b only through q (.) 2^b and k (.) 2^-b).
 //
-// Passes, chunks of C = 64 scan positions, one workgroup (4 wavefronts) each:
-//   1. forward chunk-entry states S_in (the forward's aggregate and fold
-//      passes with one-chunk segments, gla_kernel.hip);
-//   2. reverse aggregates RA_c = s (q (.) 2^{b - b_start})^T dO per chunk and
-//      the chunk's log2 decay (gla_bwd_agg_kernel), folded from the end of the
-//      scan: R_c = RA_{c+1} + 2^{G_{c+1}} (.) R_{c+1} (gla_bwd_fold_kernel), the
-//      gradient entering chunk c from the later tokens;
-//   3. the chunk kernel (gla_bwd_chunk_kernel): dq, dk, dv of the chunk and the
-//      chunk-local reverse sums of q (.) dq - k (.) dk;
-//   4. gla_bwd_dz_kernel: adds the later chunks' sums and the gate derivative.
-// Inside a chunk, with sub-chunks i of 16 positions and c_i the cumulative
-// decay at the end of sub-chunk i (c_{-1} = 0), every factor applied to an
-// operand is a power of two with exponent <= 0 except inside the diagonal
-// sub-chunk block:
-//   dq_i = 2^{b - c_{i-1}} (.) [ sum_{j<i} 2^{c_{i-1} - c_j} (.) P_ij (K (.) 2^{c_j - b})_j
-//                                + P_ii (K (.) 2^{c_{i-1} - b})_i + s 2^{c_{i-1}} (.) dO_i S_in^T ]
-//   dk_i = 2^{c_i - b} (.) [ sum_{j>i} 2^{c_{j-1} - c_i} (.) P_ji^T (Q (.) 2^{b - c_{j-1}})_j
-//                            + P_ii^T (Q (.) 2^{b - c_i})_i + 2^{B - c_i} (.) V_i R^T ]
-//   dv_i = sum_{j>=i} A_ji^T dO_j + (K (.) 2^{B - b})_i R
-// with P = s dO V^T (lower block triangle), A_ji the decayed scores s q_u k_t
-// 2^{b_u - b_t} (u in j, t in i, u >= t) and B the chunk's total decay.  All
-// products run on v_mfma_f32_16x16x4_f32 (binary32 operands and sums).  The
-// diagonal blocks carry factors up to 2^{c_{i-1} - c_i}; a sub-chunk whose
-// decay exceeds 2^60 on some channel evaluates its diagonal blocks pair by
-// pair instead, each pair's factor 2^{b_u - b_t} <= 1 taken directly.
+// dz needs no pass of its own: the suffix sum from the first position f of
+// chunk c+1 on equals sum_j R_c[ch][j] S_in(c+1)[ch][j] (both sides are the
+// derivative of L by the log-decay at f), so the later chunks' part of dz is a
+// row-wise dot product of two states known before the chunk kernel runs.
+//
+// Passes, chunks of C = 64 scan positions:
+//   1. gla_bwd_states_kernel (4 wavefronts per chunk): the chunk's forward
+//      local state L_c = sum_t 2^{B - b_t} k_t^T v_t and reverse aggregate
+//      RA_c = s sum_u 2^{b_u} q_u^T dO_u with its log2 decay B (b: cumulative
+//      from the chunk start, inclusive);
+//   2. gla_bwd_fold_kernel: S_in(c+1) = 2^{B_c} S_in(c) + L_c along the scan,
+//      R_c = RA_{c+1} + 2^{B_{c+1}} R_{c+1} back from its end, and the carry
+//      sum_j R_c S_in(c+1) per channel;
+//   3. gla_bwd_chunk_kernel (8 wavefronts per chunk): dq, dk, dv of the chunk
+//      and dz = (1 - sigmoid(z)) / tau (.) (in-chunk reverse sum + carry).
+// Inside a chunk, with sub-chunks i of 16 positions, c_i the cumulative decay
+// at the end of sub-chunk i (c_{-1} = 0), for a position of sub-chunk i
+// Qh = q (.) 2^{b - c_{i-1}}, Kh = k (.) 2^{c_i - b} (both <= 1 in size), and
+// E_xy = 2^{c_{x-1} - c_y} per channel (x >= y; x = 4 gives the chunk decay B):
+//   dq_i = 2^{b - c_{i-1}} (.) [ sum_{j<=i} E_ij (.) P_ij Kh_j + s 2^{c_{i-1}} (.) dO_i S_in^T ]
+//   dk_i = 2^{c_i - b} (.) [ sum_{j>=i} E_ji (.) P_ji^T Qh_j + E_4i (.) V_i R^T ]
+//   dv_i = sum_{j>=i} A_ji^T dO_j + (Kh_i (.) E_4i) R,   A_ji = s Qh_j (Kh_i (.) E_ji)^T
+// with P = s dO V^T (lower block triangle, diagonal blocks masked to u >= t)
+// and A_ji masked likewise.  E_xy <= 1 off the diagonal; E_ii = 2^{c_{i-1} -
+// c_i} >= 1 is the diagonal blocks' factor.  All products run on
+// v_mfma_f32_16x16x4_f32 (binary32 operands and sums).  A sub-chunk whose decay
+// exceeds 2^60 on some channel evaluates its diagonal blocks pair by pair
+// instead, each pair's factor 2^{b_u - b_t} <= 1 taken directly.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -47,9 +50,10 @@
 namespace gla {
 namespace bwd {
 
-constexpr int C = 64;   // chunk
-constexpr int NS = 4;   // 16-position sub-chunks
-constexpr int NT = 256; // 4 wavefronts
+constexpr int C = 64;     // chunk
+constexpr int NS = 4;     // 16-position sub-chunks
+constexpr int NT = 512;   // chunk kernel: 8 wavefronts, two per sub-chunk
+constexpr int NTS = 256;  // states and fold kernels: 4 wavefronts
 
 template <int D> struct Lay {
     static constexpr int SD = D + 4;        // row stride (floats), [C][D] and [D][D] tiles
@@ -58,56 +62,105 @@ template <int D> struct Lay {
     static constexpr int P = 0;             // s dO V^T            [C][SC]
     static constexpr int DO = P + C * SC;   // dO                  [C][SD]
     static constexpr int V = DO + TILE;     // v
-    static constexpr int KT = V + TILE;     // k (.) 2^{c_i - b}
-    static constexpr int KB = KT + TILE;    // k (.) 2^{c_{i-1} - b}; then q (.) 2^{b - c_i}
-    static constexpr int SS = KB + TILE;    // S_in [D][SD]; then R [D][SD]
-    static constexpr int QH = SS + D * SD;  // q (.) 2^{b - c_{i-1}}
-    static constexpr int BB = QH + TILE;    // a, then b (log2 decay from the chunk start, inclusive)
-    static constexpr int CB = BB + TILE;    // c_{i-1}: [NS + 1][D], row 0 = 0
-    static constexpr int TOTAL = CB + (NS + 1) * D;  // floats
+    static constexpr int KT = V + TILE;     // Kh = k (.) 2^{c_i - b}
+    static constexpr int QH = KT + TILE;    // Qh = q (.) 2^{b - c_{i-1}}
+    static constexpr int SS = QH + TILE;    // S_in [D][SD]
+    static constexpr int RR = SS + D * SD;  // R [D][SD]
+    static constexpr int BB = RR + D * SD;  // a, then b (log2 decay from the chunk start, inclusive)
+    static constexpr int CC = BB + TILE;    // c_{i-1}: [NS + 1][D], row 0 = 0
+    static constexpr int EE = CC + (NS + 1) * D;  // E_xy: [NS + 1][NS][D]
+    static constexpr int TOT = EE + (NS + 1) * NS * D;  // sub-chunk sums [NS][D]
+    static constexpr int TOTAL = TOT + NS * D;  // floats
     static constexpr int ROWS = TOTAL;      // int rows [C]
     static constexpr int FLAGS = ROWS + C;  // int per sub-chunk: pairwise diagonal
     static constexpr int WORDS = FLAGS + NS;
     static constexpr int BYTES = WORDS * 4;
-    // aggregate kernel: q, dO, a/b tiles and the rows
-    static constexpr int A_Q = 0, A_DO = TILE, A_B = 2 * TILE, A_ROWS = 3 * TILE;
-    static constexpr int A_WORDS = A_ROWS + C;
+    // states kernel: q (.) 2^b, dO, k (.) 2^{B - b}, v ([C][D] each, unpadded,
+    // columns swizzled by row), sub-chunk decays, rows
+    static constexpr int S_TILE = C * D;
+    static constexpr int S_Q = 0, S_DO = S_TILE, S_K = 2 * S_TILE, S_V = 3 * S_TILE;
+    static constexpr int S_CB = 4 * S_TILE, S_ROWS = S_CB + NS * D;
+    static constexpr int S_WORDS = S_ROWS + C;
+    // Element (t, col) of a states tile.  Reads take rows 4ks + g (g = 0..3)
+    // and columns 16x + l16: flipping column bit 4 (D = 32) or bits 4-5
+    // (D = 64) with the row's low bits puts the four rows of a read on
+    // disjoint banks.
+    static __device__ __forceinline__ int sidx(int t, int col)
+    {
+        const int sw = D >= 64 ? 16 * (t & 3) : D == 32 ? 16 * (t & 1) : 0;
+        return t * D + (col ^ sw);
+    }
 };
 static_assert(Lay<64>::BYTES <= kLdsLimit, "LDS budget of one CU exceeded");
+static_assert(2 * Lay<64>::S_WORDS * 4 <= kLdsLimit, "two states workgroups per CU");
 // Largest per-channel decay span (log2) of a sub-chunk whose diagonal blocks
 // take the factorised product: operands grow by at most 2^60.
 constexpr float kDiagSpan = 60.0f;
 
-// One element of a [rows][D] tensor as binary32 (0 for row < 0).
+// One element of a [rows][D] tensor as binary32 (0 for row < 0).  Loads are
+// unconditional (row 0 stands in past the end) so that a batch of them can be
+// in flight together; the value is dropped afterwards.
 template <typename T>
 __device__ __forceinline__ float ld1(const void* base, int row, int D, int col)
 {
-    return row < 0 ? 0.f : (float)((const T*)base)[(size_t)row * D + col];
+    const float x = (float)((const T*)base)[(size_t)(row < 0 ? 0 : row) * D + col];
+    return row < 0 ? 0.f : x;
 }
 
 // Load 8 consecutive elements of a row as binary32 (zeros for row < 0).
+// (unconditional load, as ld1)
 template <typename T>
 __device__ __forceinline__ void load8(const T* base, int row, int D, int col, float (&x)[8])
 {
-    if (row < 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        return;
-    }
-    const T* p = base + (size_t)row * D + col;
+    const T* p = base + (size_t)(row < 0 ? 0 : row) * D + col;
+    const bool ok = row >= 0;
     if constexpr (sizeof(T) == 2) {
         const half8 h = *(const half8*)p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+        for (int e = 0; e < 8; ++e) x[e] = ok ? (float)h[e] : 0.f;
     } else {
         const float4v a = *(const float4v*)p, b = *(const float4v*)(p + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[e] = a[e];
-            x[4 + e] = b[e];
+            x[e] = ok ? a[e] : 0.f;
+            x[4 + e] = ok ? b[e] : 0.f;
         }
     }
 }
+
+// 8 consecutive elements of a row in storage form: all loads of a thread are
+// issued before any is converted, so that their latencies overlap.
+template <typename T> struct Raw8;
+template <> struct Raw8<_Float16> {
+    u32x4 x;
+    __device__ __forceinline__ void load(const _Float16* base, int row, int D, int col)
+    {
+        x = *(const u32x4*)(base + (size_t)(row < 0 ? 0 : row) * D + col);
+    }
+    // binary32 values (0 for row < 0) into dst[0..7]
+    __device__ __forceinline__ void put(float* dst, bool ok) const
+    {
+        const half8 h = __builtin_bit_cast(half8, x);
+        *(float4v*)dst = ok ? float4v{(float)h[0], (float)h[1], (float)h[2], (float)h[3]}
+                            : float4v{0.f, 0.f, 0.f, 0.f};
+        *(float4v*)(dst + 4) = ok ? float4v{(float)h[4], (float)h[5], (float)h[6], (float)h[7]}
+                                  : float4v{0.f, 0.f, 0.f, 0.f};
+    }
+};
+template <> struct Raw8<float> {
+    float4v a, b;
+    __device__ __forceinline__ void load(const float* base, int row, int D, int col)
+    {
+        const float* p = base + (size_t)(row < 0 ? 0 : row) * D + col;
+        a = *(const float4v*)p;
+        b = *(const float4v*)(p + 4);
+    }
+    __device__ __forceinline__ void put(float* dst, bool ok) const
+    {
+        *(float4v*)dst = ok ? a : float4v{0.f, 0.f, 0.f, 0.f};
+        *(float4v*)(dst + 4) = ok ? b : float4v{0.f, 0.f, 0.f, 0.f};
+    }
+};
 
 template <typename T>
 __device__ __forceinline__ void store1(T* base, size_t idx, float x)
@@ -115,112 +168,200 @@ __device__ __forceinline__ void store1(T* base, size_t idx, float x)
     base[idx] = (T)x;
 }
 
-// Chunk geometry shared by the aggregate and chunk kernels: row table, the
-// gate stage and raw tiles.  Loads q into `tq`, k into `tk`, v into `tv`, dO
-// into `tdo` (each [C][SD] binary32, any may be null) and the clamped per-token
-// log2 decay a into `ta` (0 past the end).
-template <typename T, int D>
-__device__ __forceinline__ void load_chunk(const Params& P, const BwdParams& Q, int unit, int c, int tid,
-                                           int* sRows, float* tq, float* tk, float* tv, float* tdo,
-                                           float* ta)
-{
-    constexpr int SD = Lay<D>::SD;
-    for (int i = tid; i < C; i += NT) sRows[i] = scan_row(P, unit, c * C + i);
-    __syncthreads();
-    constexpr int G8 = D / 8;
-    for (int i = tid; i < C * G8; i += NT) {
-        const int t = i / G8, c8 = 8 * (i - t * G8);
-        const int row = sRows[t];
-        float x[8];
-        if (tq) {
-            load8<T>((const T*)P.q, row, D, c8, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tq[t * SD + c8 + e] = x[e];
-        }
-        if (tk) {
-            load8<T>((const T*)P.k, row, D, c8, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tk[t * SD + c8 + e] = x[e];
-        }
-        if (tv) {
-            load8<T>((const T*)P.v, row, D, c8, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tv[t * SD + c8 + e] = x[e];
-        }
-        if (tdo) {
-            load8<T>((const T*)Q.dout, row, D, c8, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tdo[t * SD + c8 + e] = x[e];
-        }
-        load8<float>(P.z, row, D, c8, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ta[t * SD + c8 + e] = row >= 0 ? log2_decay(x[e], P.inv_tau) : 0.f;
-    }
-    __syncthreads();
-}
-
 // ---------------------------------------------------------------------------
-// Reverse aggregates: slot c - 1 <- (RA_c, G_c) for chunks c >= 1.
+// Chunk states: slot c of ws_f <- (L_c, B_c) for c < nchunks - 1 and slot
+// c - 1 of ws_r <- (RA_c, B_c) for c >= 1.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(NT) void gla_bwd_agg_kernel(Params P, BwdParams Q)
+__global__ __launch_bounds__(NTS) void gla_bwd_states_kernel(Params P, BwdParams Q)
 {
     using Y = Lay<D>;
-    constexpr int SD = Y::SD;
-    __shared__ __attribute__((aligned(16))) float lds[Y::A_WORDS];
-    float* sQ = lds + Y::A_Q;
-    float* sDO = lds + Y::A_DO;
-    float* sA = lds + Y::A_B;
-    int* sRows = (int*)(lds + Y::A_ROWS);
+    constexpr int NTL = D / 16;
+    __shared__ __attribute__((aligned(16))) float lds[Y::S_WORDS];
+    float* sQ = lds + Y::S_Q;
+    float* sDO = lds + Y::S_DO;
+    float* sK = lds + Y::S_K;
+    float* sV = lds + Y::S_V;
+    float* sCB = lds + Y::S_CB;
+    int* sRows = (int*)(lds + Y::S_ROWS);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, l16 = lane & 15;
     const int units = P.B * P.NH;
     const int unit = blockIdx.x % units;
-    const int c = 1 + blockIdx.x / units;
-    load_chunk<T, D>(P, Q, unit, c, tid, sRows, sQ, nullptr, nullptr, sDO, sA);
-    // cumulative decay from the chunk start (inclusive), q (.) 2^{b}
-    float* slot = Q.ws_r + ((size_t)unit * (P.nchunks - 1) + (c - 1)) * ((size_t)D * D + D);
-    for (int ch = tid; ch < D; ch += NT) {
-        float b = 0.f;
-        for (int t = 0; t < C; ++t) {
-            b += sA[t * SD + ch];
-            sQ[t * SD + ch] *= exp2_fast(b);
+    const int c = blockIdx.x / units;
+    const bool do_r = c >= 1, do_f = c < P.nchunks - 1;
+    for (int i = tid; i < C; i += NTS) sRows[i] = scan_row(P, unit, c * C + i);
+    __syncthreads();
+    // raw tiles (q, dO for the reverse aggregate, k, v for the local state;
+    // all four are fetched, every load issued before the first conversion)
+    constexpr int G8 = D / 8;
+    constexpr int IT = (C * G8 + NTS - 1) / NTS;
+    Raw8<T> rq[IT], rd[IT], rk[IT], rv[IT];
+    int rows[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int i = tid + it * NTS;
+        const int t = (i < C * G8 ? i : 0) / G8, c8 = 8 * (i % G8);
+        rows[it] = sRows[t];
+        rq[it].load((const T*)P.q, rows[it], D, c8);
+        rd[it].load((const T*)Q.dout, rows[it], D, c8);
+        rk[it].load((const T*)P.k, rows[it], D, c8);
+        rv[it].load((const T*)P.v, rows[it], D, c8);
+    }
+    // the gate logits of thread (ch, i)'s 16 positions, in flight as well
+    const bool gate_thread = tid < D * NS;
+    const int gch = tid % D, gi = tid / D;
+    float br[16];
+    if (gate_thread) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) br[u] = ld1<float>(P.z, sRows[16 * gi + u], D, gch);
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int i = tid + it * NTS;
+        if (i < C * G8) {
+            const int t = i / G8, c8 = 8 * (i % G8);
+            const bool ok = rows[it] >= 0;
+            // 8 consecutive columns stay consecutive under the swizzle
+            const int o = Y::sidx(t, c8);
+            rq[it].put(sQ + o, ok);
+            rd[it].put(sDO + o, ok);
+            rk[it].put(sK + o, ok);
+            rv[it].put(sV + o, ok);
         }
-        slot[D * D + ch] = b;  // log2 decay of the whole chunk
+    }
+
+    // gate: thread (ch, i) over the 16 positions of sub-chunk i, decays in registers
+    if (gate_thread) {
+        float run = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            run += sRows[16 * gi + u] >= 0 ? log2_decay(br[u], P.inv_tau) : 0.f;
+            br[u] = run;
+        }
+        sCB[gi * D + gch] = run;
     }
     __syncthreads();
-    // RA = s Qt^T dO: tile (a, bb), a over key channels, bb over value channels
-    constexpr int NTL = D / 16;
-    for (int tile = wave; tile < NTL * NTL; tile += NT / 64) {
-        const int a = tile / NTL, bb = tile - a * NTL;
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
+    const size_t slot_floats = (size_t)D * D + D;
+    float* dst_f = do_f ? Q.ws_f + ((size_t)unit * (P.nchunks - 1) + c) * slot_floats : nullptr;
+    float* dst_r = do_r ? Q.ws_r + ((size_t)unit * (P.nchunks - 1) + (c - 1)) * slot_floats : nullptr;
+    if (gate_thread) {
+        float off = 0.f, tot = 0.f;
+        for (int m = 0; m < NS; ++m) {
+            const float x = sCB[m * D + gch];
+            off += m < gi ? x : 0.f;
+            tot += x;
+        }
+        float xq[16], xk[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int o = Y::sidx(16 * gi + u, gch);
+            xq[u] = sQ[o];
+            xk[u] = sK[o];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int o = Y::sidx(16 * gi + u, gch);
+            const float b = br[u] + off;
+            sQ[o] = xq[u] * exp2_fast(b);        // <= 1
+            sK[o] = xk[u] * exp2_fast(tot - b);  // <= 1
+        }
+        if (gi == 0) {
+            if (do_f) dst_f[D * D + gch] = tot;
+            if (do_r) dst_r[D * D + gch] = tot;
+        }
+    }
+    __syncthreads();
+    // strip (product, a): rows 16a .. 16a + 15 of RA (product 0) or L (1) over
+    // all value-channel tiles, the key-channel operand read once per k-step
+    constexpr int STRIPS = 2 * NTL;
+    constexpr int BT = NTL;  // value-channel tiles of a strip
+    for (int strip = wave; strip < STRIPS; strip += NTS / 64) {
+        const bool rev = strip < NTL;
+        if (rev ? !do_r : !do_f) continue;
+        const int a = rev ? strip : strip - NTL;
+        const float* X = rev ? sQ : sK;
+        const float* Yt = rev ? sDO : sV;
+        float4v acc[BT];
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) acc[bb] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
         for (int ks = 0; ks < C / 4; ++ks) {
             const int u = 4 * ks + g;
-            acc = mma(sQ[u * SD + 16 * a + l16], sDO[u * SD + 16 * bb + l16], acc);
-        }
+            const float x = X[Y::sidx(u, 16 * a + l16)];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) slot[(size_t)(16 * a + 4 * g + e) * D + 16 * bb + l16] = P.scale * acc[e];
+            for (int bb = 0; bb < BT; ++bb) acc[bb] = mma(x, Yt[Y::sidx(u, 16 * bb + l16)], acc[bb]);
+        }
+        float* dst = rev ? dst_r : dst_f;
+        const float f = rev ? P.scale : 1.f;
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(size_t)(16 * a + 4 * g + e) * D + 16 * bb + l16] = f * acc[bb][e];
     }
 }
 
-// Reverse fold: slot s <- R_s = RA_{s+1} + 2^{G_{s+1}} (.) R_{s+1}, R_{last} = 0.
+// Folds, one thread per state entry (ch, j) of one scan:
+//   forward: slot s <- S_in(s + 1) = 2^{B_s} S_in(s) + L_s, S_in(0) = 0;
+//   reverse: slot s <- R_s = RA_{s+1} + 2^{B_{s+1}} R_{s+1}, R_{last} = 0;
+//   carry:   ws_s[s][ch] = sum_j R_s[ch][j] S_in(s + 1)[ch][j]  (a row of D
+//            entries is D consecutive lanes of one wavefront).
+// Loads of a batch of slots are issued before the dependent multiply-adds.
 template <int D>
-__global__ __launch_bounds__(NT) void gla_bwd_fold_kernel(Params P, BwdParams Q)
+__global__ __launch_bounds__(NTS) void gla_bwd_fold_kernel(Params P, BwdParams Q)
 {
     constexpr int ENTRIES = D * D;
-    constexpr int BLKS = (ENTRIES + NT - 1) / NT;
+    static_assert(ENTRIES % NTS == 0 && 64 % D == 0, "rows must tile the wavefronts");
+    constexpr int BLKS = ENTRIES / NTS;
+    constexpr int BATCH = 8;
     const int unit = blockIdx.x / BLKS;
-    const int idx = (blockIdx.x - unit * BLKS) * NT + threadIdx.x;
-    if (idx >= ENTRIES) return;
-    const int ch = idx / D;
+    const int idx = (blockIdx.x - unit * BLKS) * NTS + threadIdx.x;
+    const int ch = idx / D, j = idx - ch * D;
     const size_t slot_floats = (size_t)D * D + D;
     const int nslot = P.nchunks - 1;
-    float* base = Q.ws_r + (size_t)unit * nslot * slot_floats;
+    float* bf = Q.ws_f + (size_t)unit * nslot * slot_floats;
+    float* br = Q.ws_r + (size_t)unit * nslot * slot_floats;
     float x = 0.f;
-    for (int s = nslot - 1; s >= 0; --s) {
-        x = exp2_fast(base[(size_t)s * slot_floats + ENTRIES + ch]) * x + base[(size_t)s * slot_floats + idx];
-        base[(size_t)s * slot_floats + idx] = x;
+    for (int s0 = 0; s0 < nslot; s0 += BATCH) {
+        float lv[BATCH], gv[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int s = s0 + u;
+            lv[u] = (s < nslot) ? bf[(size_t)s * slot_floats + idx] : 0.f;
+            gv[u] = (s < nslot) ? bf[(size_t)s * slot_floats + ENTRIES + ch] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int s = s0 + u;
+            if (s < nslot) {
+                x = exp2_fast(gv[u]) * x + lv[u];
+                bf[(size_t)s * slot_floats + idx] = x;
+            }
+        }
+    }
+    float y = 0.f;
+    for (int s0 = nslot - 1; s0 >= 0; s0 -= BATCH) {
+        float lv[BATCH], gv[BATCH], sv[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int s = s0 - u;
+            lv[u] = (s >= 0) ? br[(size_t)s * slot_floats + idx] : 0.f;
+            gv[u] = (s >= 0) ? br[(size_t)s * slot_floats + ENTRIES + ch] : 0.f;
+            sv[u] = (s >= 0) ? bf[(size_t)s * slot_floats + idx] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int s = s0 - u;
+            // slot s holds RA_{s+1} and B_{s+1}; y enters as R_{s+1}
+            if (s >= 0) {
+                y = exp2_fast(gv[u]) * y + lv[u];
+                br[(size_t)s * slot_floats + idx] = y;
+                float p = y * sv[u];
+#pragma unroll
+                for (int o = D / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o);
+                if (j == 0) Q.ws_s[((size_t)unit * P.nchunks + s) * D + ch] = p;
+            }
+        }
     }
 }
 
@@ -288,6 +429,7 @@ __device__ __forceinline__ float4v diag_scores(const Params& P, const int* sRows
     const int t = 16 * si + l16;
     const int rt = sRows[t];
     float4v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
     for (int c8 = 0; c8 < D; c8 += 8) {
         float kk[8];
         load8<T>((const T*)P.k, rt, D, c8, kk);
@@ -307,23 +449,28 @@ __device__ __forceinline__ float4v diag_scores(const Params& P, const int* sRows
 }
 
 // ---------------------------------------------------------------------------
-// Chunk kernel: dq, dk, dv and the chunk-local reverse sums for dz.
+// Chunk kernel: dq, dk, dv and dz.  Wavefront w takes sub-chunk si = w / 2
+// and half h = w % 2 of the 16-channel column tiles (the two halves of a
+// sub-chunk sit on different SIMDs next to the halves of another sub-chunk).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q)
 {
     using Y = Lay<D>;
     constexpr int SD = Y::SD, SC = Y::SC, NTL = D / 16, KS = D / 4;
+    constexpr int CT = NTL >= 2 ? NTL / 2 : 1;  // column tiles per wavefront
     __shared__ __attribute__((aligned(16))) float lds[Y::WORDS];
     float* sP = lds + Y::P;
     float* sDO = lds + Y::DO;
     float* sV = lds + Y::V;
     float* sKT = lds + Y::KT;
-    float* sKB = lds + Y::KB;
-    float* sSS = lds + Y::SS;
     float* sQH = lds + Y::QH;
+    float* sSS = lds + Y::SS;
+    float* sRR = lds + Y::RR;
     float* sB = lds + Y::BB;
-    float* sCB = lds + Y::CB;
+    float* sCC = lds + Y::CC;
+    float* sE = lds + Y::EE;
+    float* sTot = lds + Y::TOT;
     int* sRows = (int*)(lds + Y::ROWS);
     int* sFlag = (int*)(lds + Y::FLAGS);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -331,66 +478,135 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
     const int units = P.B * P.NH;
     const int unit = blockIdx.x % units;
     const int c = blockIdx.x / units;
-    const int si = wave;  // this wave's sub-chunk
+    const int si = wave >> 1, h = wave & 1;
+    const int ct0 = h * CT;
+    const bool cols = ct0 < NTL;                // D = 16: the second half has no columns
     const float s = P.scale;
     const size_t slot_floats = (size_t)D * D + D;
-    const bool has_in = c > 0;                 // a state enters from earlier chunks
-    const bool has_r = c < P.nchunks - 1;      // a gradient enters from later chunks
+    const bool has_in = c > 0;                  // a state enters from earlier chunks
+    const bool has_r = c < P.nchunks - 1;       // a gradient enters from later chunks
     if (tid < NS) sFlag[tid] = 0;
+    // E_xy of channel ch: sE[(x * NS + y) * D + ch]
+    auto E = [&](int x, int y, int ch) { return sE[(x * NS + y) * D + ch]; };
 
-    // raw q -> QH, k -> KT, v, dO, a -> BB (the loader's barriers order the flags)
-    load_chunk<T, D>(P, Q, unit, c, tid, sRows, sQH, sKT, sV, sDO, sB);
-
-    // ---- gate: thread (ch, i) runs over the 16 positions of sub-chunk i
+    // ---- one load phase: the states entering from both sides, raw q -> QH,
+    //      k -> KT, v, dO, the gate logits of the gate threads (their 16
+    //      positions of one channel) and the later chunks' part of dz; rows
+    //      come from the scan order directly, and every load is issued before
+    //      the first one is used
     const bool gate_thread = tid < D * NS;
     const int gch = tid % D, gi = tid / D;
-    float qr[16], br[16];
+    float zz[16];
+    unsigned zok = 0;
+    float later_c = 0.f;
+    {
+        constexpr int SQ4 = D * D / 4;
+        constexpr int SIT = (SQ4 + NT - 1) / NT;
+        float4v st_in[SIT], st_r[SIT];
+        const float4v* src_in = (const float4v*)(Q.ws_f + ((size_t)unit * (P.nchunks - 1) + (has_in ? c - 1 : 0)) * slot_floats);
+        const float4v* src_r = (const float4v*)(Q.ws_r + ((size_t)unit * (P.nchunks - 1) + (has_r ? c : 0)) * slot_floats);
+#pragma unroll
+        for (int it = 0; it < SIT; ++it) {
+            const int i = tid + it * NT;
+            const int ii = i < SQ4 ? i : 0;
+            if (has_in) st_in[it] = src_in[ii];
+            if (has_r) st_r[it] = src_r[ii];
+        }
+        constexpr int G8 = D / 8;
+        constexpr int IT = (C * G8 + NT - 1) / NT;
+        Raw8<T> rq[IT], rk[IT], rv[IT], rd[IT];
+        int rows[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int i = tid + it * NT;
+            const int t = (i < C * G8 ? i : 0) / G8, c8 = 8 * (i % G8);
+            rows[it] = scan_row(P, unit, c * C + t);
+            rq[it].load((const T*)P.q, rows[it], D, c8);
+            rk[it].load((const T*)P.k, rows[it], D, c8);
+            rv[it].load((const T*)P.v, rows[it], D, c8);
+            rd[it].load((const T*)Q.dout, rows[it], D, c8);
+        }
+        if (gate_thread) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int row = scan_row(P, unit, c * C + 16 * gi + u);
+                zok |= (row >= 0 ? 1u : 0u) << u;
+                zz[u] = ld1<float>(P.z, row, D, gch);
+            }
+            later_c = has_r ? Q.ws_s[((size_t)unit * P.nchunks + c) * D + gch] : 0.f;
+        }
+        for (int i = tid; i < C; i += NT) sRows[i] = scan_row(P, unit, c * C + i);
+#pragma unroll
+        for (int it = 0; it < SIT; ++it) {
+            const int i = tid + it * NT;
+            if (i < SQ4) {
+                const int r = (4 * i) / D, cc = 4 * i - r * D;
+                if (has_in) *(float4v*)(sSS + r * SD + cc) = st_in[it];
+                if (has_r) *(float4v*)(sRR + r * SD + cc) = st_r[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int i = tid + it * NT;
+            if (i < C * G8) {
+                const int o = (i / G8) * SD + 8 * (i % G8);
+                const bool ok = rows[it] >= 0;
+                rq[it].put(sQH + o, ok);
+                rk[it].put(sKT + o, ok);
+                rv[it].put(sV + o, ok);
+                rd[it].put(sDO + o, ok);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- gate: thread (ch, i) runs over the 16 positions of sub-chunk i
+    float br[16];
     if (gate_thread) {
         float run = 0.f;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            run += sB[(16 * gi + u) * SD + gch];
+            run += ((zok >> u) & 1u) ? log2_decay(zz[u], P.inv_tau) : 0.f;
             br[u] = run;  // within the sub-chunk
         }
-        sCB[(gi + 1) * D + gch] = run;  // sub-chunk total, turned into c_i below
+        sTot[gi * D + gch] = run;
         if (run < -kDiagSpan) sFlag[gi] = 1;
     }
-    if (tid < D) sCB[tid] = 0.f;
-    __syncthreads();
-    float off = 0.f, ci = 0.f;
-    if (gate_thread) {
-        for (int m = 0; m < gi; ++m) off += sCB[(m + 1) * D + gch];
-        ci = off + sCB[(gi + 1) * D + gch];
-    }
     __syncthreads();
     if (gate_thread) {
-        sCB[(gi + 1) * D + gch] = ci;  // c_i; row 0 = c_{-1} = 0
+        // c_{-1} .. c_3 of this channel
+        float cv[NS + 1];
+        cv[0] = 0.f;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) cv[m + 1] = cv[m] + sTot[m * D + gch];
+        const float off = cv[gi], ci = cv[gi + 1];
+        sCC[(gi + 1) * D + gch] = ci;
+        if (gi == 0) sCC[gch] = 0.f;
+        // E_{x, gi} for x = gi .. NS
+#pragma unroll
+        for (int x = 0; x <= NS; ++x)
+            if (x >= gi) sE[(x * NS + gi) * D + gch] = exp2_fast(cv[x] - ci);
+        float xq[16], xk[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            xq[u] = sQH[(16 * gi + u) * SD + gch];
+            xk[u] = sKT[(16 * gi + u) * SD + gch];
+        }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int t = 16 * gi + u;
             const float b = br[u] + off;  // cumulative from the chunk start
-            br[u] = b;
-            qr[u] = sQH[t * SD + gch];
-            const float k = sKT[t * SD + gch];
-            sQH[t * SD + gch] = qr[u] * exp2_fast(b - off);  // <= 1
-            sKT[t * SD + gch] = k * exp2_fast(ci - b);       // <= 1
-            sKB[t * SD + gch] = k * exp2_fast(off - b);      // >= 1 (diagonal block)
+            sQH[t * SD + gch] = xq[u] * exp2_fast(b - off);  // <= 1
+            sKT[t * SD + gch] = xk[u] * exp2_fast(ci - b);   // <= 1
             sB[t * SD + gch] = b;
-        }
-    }
-    // S_in (state entering this chunk) -> SS, zero for the first chunk
-    if (has_in) {
-        const float* src = Q.ws_f + ((size_t)unit * (P.nchunks - 1) + (c - 1)) * slot_floats;
-        for (int i = tid; i < D * D; i += NT) {
-            const int r = i / D, cc = i - r * D;
-            sSS[r * SD + cc] = src[i];
         }
     }
     __syncthreads();
     const bool pairwise = sFlag[si] != 0;  // wave-uniform
 
-    // ---- P = s dO V^T on the blocks j <= i, diagonal blocks masked to u >= t
-    for (int j = 0; j <= si; ++j) {
+    // ---- P = s dO V^T on the blocks j <= si (this half: j = h mod 2),
+    //      diagonal blocks masked to u >= t
+    for (int j = h; j <= si; j += 2) {
         float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
         for (int ks = 0; ks < KS; ++ks) {
@@ -405,168 +621,203 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
     }
     __syncthreads();
 
-    // ---- dq of sub-chunk si (rows 16 si + 4g + e, columns 16 ct + l16)
-    float dqv[NTL][4];
+    float dqv[CT][4], dkv[CT][4];
+    if (cols) {
+        // ---- dq of sub-chunk si (rows 16 si + 4g + e, columns 16 ct + l16);
+        //      the column tiles innermost: one A read serves CT products
+        {
+            float4v acc[CT];
 #pragma unroll
-    for (int ct = 0; ct < NTL; ++ct) {
-        const int ch = 16 * ct + l16;
-        const float cim1 = sCB[si * D + ch];
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j <= si; ++j) {
-            if (j == si && pairwise) break;
-            const float* kt = (j == si) ? sKB : sKT;
-            float4v m = {0.f, 0.f, 0.f, 0.f};
+            for (int cl = 0; cl < CT; ++cl) acc[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+            const int jend = pairwise ? si - 1 : si;
+            for (int j = 0; j <= jend; ++j) {
+                float4v m[CT];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int sp = 16 * j + 4 * ks + g;
-                m = mma(sP[(16 * si + l16) * SC + sp], kt[sp * SD + ch], m);
+                for (int cl = 0; cl < CT; ++cl) m[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int sp = 16 * j + 4 * ks + g;
+                    const float a = sP[(16 * si + l16) * SC + sp];
+#pragma unroll
+                    for (int cl = 0; cl < CT; ++cl)
+                        m[cl] = mma(a, sKT[sp * SD + 16 * (ct0 + cl) + l16], m[cl]);
+                }
+#pragma unroll
+                for (int cl = 0; cl < CT; ++cl) {
+                    const float f = E(si, j, 16 * (ct0 + cl) + l16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[cl][e] += m[cl][e] * f;
+                }
             }
-            const float f = (j == si) ? 1.f : exp2_fast(cim1 - sCB[(j + 1) * D + ch]);
+            if (has_in) {
+                float4v m[CT];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += m[e] * f;
-        }
-        if (has_in) {
-            float4v m = {0.f, 0.f, 0.f, 0.f};
+                for (int cl = 0; cl < CT; ++cl) m[cl] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-            for (int ks = 0; ks < KS; ++ks) {
-                const int jj = 4 * ks + g;
-                m = mma(sDO[(16 * si + l16) * SD + jj], sSS[ch * SD + jj], m);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int jj = 4 * ks + g;
+                    const float a = sDO[(16 * si + l16) * SD + jj];
+#pragma unroll
+                    for (int cl = 0; cl < CT; ++cl)
+                        m[cl] = mma(a, sSS[(16 * (ct0 + cl) + l16) * SD + jj], m[cl]);
+                }
+#pragma unroll
+                for (int cl = 0; cl < CT; ++cl) {
+                    const float f = s * exp2_fast(sCC[si * D + 16 * (ct0 + cl) + l16]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[cl][e] += m[cl][e] * f;
+                }
             }
-            const float f = s * exp2_fast(cim1);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += m[e] * f;
-        }
-        float dg[4] = {0.f, 0.f, 0.f, 0.f};
-        if (pairwise) diag_dq<T, D>(P, sRows, sP, sB, si, g, ch, dg);
+            for (int cl = 0; cl < CT; ++cl) {
+                const int ch = 16 * (ct0 + cl) + l16;
+                const float cim1 = sCC[si * D + ch];
+                float dg[4] = {0.f, 0.f, 0.f, 0.f};
+                if (pairwise) diag_dq<T, D>(P, sRows, sP, sB, si, g, ch, dg);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * si + 4 * g + e;
-            dqv[ct][e] = acc[e] * exp2_fast(sB[t * SD + ch] - cim1) + dg[e];
-            const int row = sRows[t];
-            if (row >= 0) store1<T>((T*)Q.dq, (size_t)row * D + ch, dqv[ct][e]);
-        }
-    }
-    __syncthreads();
-
-    // ---- phase B tiles: R -> SS, q (.) 2^{b - c_i} -> KB
-    if (has_r) {
-        const float* src = Q.ws_r + ((size_t)unit * (P.nchunks - 1) + c) * slot_floats;
-        for (int i = tid; i < D * D; i += NT) {
-            const int r = i / D, cc = i - r * D;
-            sSS[r * SD + cc] = src[i];
-        }
-    }
-    if (gate_thread) {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int t = 16 * gi + u;
-            sKB[t * SD + gch] = qr[u] * exp2_fast(br[u] - ci);  // >= 1 (diagonal block)
-        }
-    }
-    __syncthreads();
-
-    // ---- dk of sub-chunk si
-    float dkv[NTL][4];
-#pragma unroll
-    for (int ct = 0; ct < NTL; ++ct) {
-        const int ch = 16 * ct + l16;
-        const float cic = sCB[(si + 1) * D + ch];
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-        for (int j = pairwise ? si + 1 : si; j < NS; ++j) {
-            const float* qh = (j == si) ? sKB : sQH;
-            float4v m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int up = 16 * j + 4 * ks + g;
-                m = mma(sP[up * SC + 16 * si + l16], qh[up * SD + ch], m);
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * si + 4 * g + e;
+                    dqv[cl][e] = acc[cl][e] * exp2_fast(sB[t * SD + ch] - cim1) + dg[e];
+                    const int row = sRows[t];
+                    if (row >= 0) store1<T>((T*)Q.dq, (size_t)row * D + ch, dqv[cl][e]);
+                }
             }
-            const float f = (j == si) ? 1.f : exp2_fast(sCB[j * D + ch] - cic);
+        }
+
+        // ---- dk of sub-chunk si
+        {
+            float4v acc[CT];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += m[e] * f;
+            for (int cl = 0; cl < CT; ++cl) acc[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+            for (int j = pairwise ? si + 1 : si; j < NS; ++j) {
+                float4v m[CT];
+#pragma unroll
+                for (int cl = 0; cl < CT; ++cl) m[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int up = 16 * j + 4 * ks + g;
+                    const float a = sP[up * SC + 16 * si + l16];
+#pragma unroll
+                    for (int cl = 0; cl < CT; ++cl)
+                        m[cl] = mma(a, sQH[up * SD + 16 * (ct0 + cl) + l16], m[cl]);
+                }
+#pragma unroll
+                for (int cl = 0; cl < CT; ++cl) {
+                    const float f = E(j, si, 16 * (ct0 + cl) + l16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[cl][e] += m[cl][e] * f;
+                }
+            }
+            if (has_r) {
+                float4v m[CT];
+#pragma unroll
+                for (int cl = 0; cl < CT; ++cl) m[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int jj = 4 * ks + g;
+                    const float a = sV[(16 * si + l16) * SD + jj];
+#pragma unroll
+                    for (int cl = 0; cl < CT; ++cl)
+                        m[cl] = mma(a, sRR[(16 * (ct0 + cl) + l16) * SD + jj], m[cl]);
+                }
+#pragma unroll
+                for (int cl = 0; cl < CT; ++cl) {
+                    const float f = E(NS, si, 16 * (ct0 + cl) + l16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[cl][e] += m[cl][e] * f;
+                }
+            }
+#pragma unroll
+            for (int cl = 0; cl < CT; ++cl) {
+                const int ch = 16 * (ct0 + cl) + l16;
+                float dg[4] = {0.f, 0.f, 0.f, 0.f};
+                if (pairwise) diag_dk<T, D>(P, sRows, sP, sB, si, g, ch, dg);
+                const float cic = sCC[(si + 1) * D + ch];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * si + 4 * g + e;
+                    dkv[cl][e] = acc[cl][e] * exp2_fast(cic - sB[t * SD + ch]) + dg[e];
+                    const int row = sRows[t];
+                    if (row >= 0) store1<T>((T*)Q.dk, (size_t)row * D + ch, dkv[cl][e]);
+                }
+            }
+        }
+
+        // ---- dv of sub-chunk si: sum_{j >= si} A_ji^T dO_j + (Kh (.) E_4i)_si R
+        float4v dvacc[CT];
+#pragma unroll
+        for (int cl = 0; cl < CT; ++cl) dvacc[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+        // this lane's Kh values: row 16 si + l16, channels 4 ks + g
+        float kh[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kh[ks] = sKT[(16 * si + l16) * SD + 4 * ks + g];
+        for (int j = si; j < NS; ++j) {
+            // A_ji[u = 16 j + 4g + e][t = 16 si + l16] (both halves form it),
+            // even and odd k-steps on two independent chains
+            float4v a = {0.f, 0.f, 0.f, 0.f};
+            if (j == si && pairwise) {
+                a = diag_scores<T, D>(P, sRows, sB, si, g, l16);
+            } else {
+                float4v a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ks += 2) {
+                    const int ch = 4 * ks + g;
+                    a = mma(sQH[(16 * j + l16) * SD + ch], kh[ks] * E(j, si, ch), a);
+                    a1 = mma(sQH[(16 * j + l16) * SD + ch + 4], kh[ks + 1] * E(j, si, ch + 4), a1);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool keep = (j > si) || (4 * g + e >= l16);
+                    a[e] = keep ? s * (a[e] + a1[e]) : 0.f;
+                }
+            }
+            // dv[t][col] += sum_u A[u][t] dO[u][col], k-slot g of step e is u = 16 j + 4g + e
+#pragma unroll
+            for (int cl = 0; cl < CT; ++cl)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dvacc[cl] = mma(a[e], sDO[(16 * j + 4 * g + e) * SD + 16 * (ct0 + cl) + l16], dvacc[cl]);
         }
         if (has_r) {
-            float4v m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int ks = 0; ks < KS; ++ks) {
-                const int jj = 4 * ks + g;
-                m = mma(sV[(16 * si + l16) * SD + jj], sSS[ch * SD + jj], m);
-            }
-            const float f = exp2_fast(sCB[NS * D + ch] - cic);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += m[e] * f;
-        }
-        float dg[4] = {0.f, 0.f, 0.f, 0.f};
-        if (pairwise) diag_dk<T, D>(P, sRows, sP, sB, si, g, ch, dg);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * si + 4 * g + e;
-            dkv[ct][e] = acc[e] * exp2_fast(cic - sB[t * SD + ch]) + dg[e];
-            const int row = sRows[t];
-            if (row >= 0) store1<T>((T*)Q.dk, (size_t)row * D + ch, dkv[ct][e]);
-        }
-    }
-
-    // ---- dv of sub-chunk si: sum_{j >= si} A_ji^T dO_j + (K (.) 2^{B - b})_si R
-    float4v dvacc[NTL];
-#pragma unroll
-    for (int ct = 0; ct < NTL; ++ct) dvacc[ct] = float4v{0.f, 0.f, 0.f, 0.f};
-    for (int j = si; j < NS; ++j) {
-        // A_ji[u = 16 j + 4g + e][t = 16 si + l16]
-        float4v a = {0.f, 0.f, 0.f, 0.f};
-        if (j == si && pairwise) {
-            a = diag_scores<T, D>(P, sRows, sB, si, g, l16);
-        } else {
-            const float* qh = (j == si) ? sKB : sQH;
-#pragma unroll 4
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = 4 * ks + g;
-                const float f = (j == si) ? 1.f : exp2_fast(sCB[j * D + ch] - sCB[(si + 1) * D + ch]);
-                a = mma(qh[(16 * j + l16) * SD + ch], sKT[(16 * si + l16) * SD + ch] * f, a);
+                const float kf = kh[ks] * E(NS, si, ch);
+#pragma unroll
+                for (int cl = 0; cl < CT; ++cl)
+                    dvacc[cl] = mma(kf, sRR[ch * SD + 16 * (ct0 + cl) + l16], dvacc[cl]);
             }
+        }
+#pragma unroll
+        for (int cl = 0; cl < CT; ++cl)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bool keep = (j > si) || (4 * g + e >= l16);
-                a[e] = keep ? s * a[e] : 0.f;
+                const int row = sRows[16 * si + 4 * g + e];
+                if (row >= 0) store1<T>((T*)Q.dv, (size_t)row * D + 16 * (ct0 + cl) + l16, dvacc[cl][e]);
             }
-        }
-        // dv[t][col] += sum_u A[u][t] dO[u][col], k-slot g of step e is u = 16 j + 4g + e
-#pragma unroll
-        for (int ct = 0; ct < NTL; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dvacc[ct] = mma(a[e], sDO[(16 * j + 4 * g + e) * SD + 16 * ct + l16], dvacc[ct]);
     }
-    if (has_r) {
-#pragma unroll
-        for (int ct = 0; ct < NTL; ++ct) {
-#pragma unroll 4
-            for (int ks = 0; ks < KS; ++ks) {
-                const int ch = 4 * ks + g;
-                const float kf = sKT[(16 * si + l16) * SD + ch] *
-                                 exp2_fast(sCB[NS * D + ch] - sCB[(si + 1) * D + ch]);
-                dvacc[ct] = mma(kf, sSS[ch * SD + 16 * ct + l16], dvacc[ct]);
-            }
-        }
-    }
-#pragma unroll
-    for (int ct = 0; ct < NTL; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = sRows[16 * si + 4 * g + e];
-            if (row >= 0) store1<T>((T*)Q.dv, (size_t)row * D + 16 * ct + l16, dvacc[ct][e]);
-        }
-    __syncthreads();  // every reader of P and CB is done: reuse them
+    __syncthreads();  // every reader of P is done: reuse it
 
     // ---- q (.) dq - k (.) dk into P ([C][SD] view), raw q and k reloaded
     float* sZ = sP;
+    if (cols) {
+        float qv[CT][4], kv[CT][4];
 #pragma unroll
-    for (int ct = 0; ct < NTL; ++ct)
+        for (int cl = 0; cl < CT; ++cl)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * si + 4 * g + e, ch = 16 * ct + l16;
-            const int row = sRows[t];
-            sZ[t * SD + ch] = ld1<T>(P.q, row, D, ch) * dqv[ct][e] - ld1<T>(P.k, row, D, ch) * dkv[ct][e];
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int row = sRows[16 * si + 4 * g + e], ch = 16 * (ct0 + cl) + l16;
+                qv[cl][e] = ld1<T>(P.q, row, D, ch);
+                kv[cl][e] = ld1<T>(P.k, row, D, ch);
+            }
+#pragma unroll
+        for (int cl = 0; cl < CT; ++cl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * si + 4 * g + e, ch = 16 * (ct0 + cl) + l16;
+                sZ[t * SD + ch] = qv[cl][e] * dqv[cl][e] - kv[cl][e] * dkv[cl][e];
+            }
+    }
     __syncthreads();
     // reverse sums inside the chunk: thread (ch, i) over sub-chunk i
     if (gate_thread) {
@@ -576,43 +827,20 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             run += sZ[(16 * gi + u) * SD + gch];
             br[u] = run;
         }
-        sCB[gi * D + gch] = run;  // sub-chunk total
+        sTot[gi * D + gch] = run;  // sub-chunk total
     }
     __syncthreads();
     if (gate_thread) {
-        float later = 0.f;
-        for (int m = gi + 1; m < NS; ++m) later += sCB[m * D + gch];
+        // later chunks: sum_j R_c S_in(c + 1) from the fold
+        float later = later_c;
+        for (int m = gi + 1; m < NS; ++m) later += sTot[m * D + gch];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int row = sRows[16 * gi + u];
-            if (row >= 0) Q.dz[(size_t)row * D + gch] = br[u] + later;
+            // 1 - sigmoid(z) as sigmoid(-z)
+            const float nsig = rcp_fast(1.0f + exp2_fast(zz[u] * kLog2e));
+            if (row >= 0) Q.dz[(size_t)row * D + gch] = (br[u] + later) * nsig * P.inv_tau;
         }
-        if (gi == 0) Q.ws_s[((size_t)unit * P.nchunks + c) * D + gch] = br[0] + later;  // chunk total
-    }
-}
-
-// dz = (1 - sigmoid(z)) / tau (.) (in-chunk reverse sum + later chunks' totals);
-// 1 - sigmoid(z) evaluated as sigmoid(-z).
-template <int D>
-__global__ __launch_bounds__(NT) void gla_bwd_dz_kernel(Params P, BwdParams Q)
-{
-    __shared__ float carry[D];
-    const int units = P.B * P.NH;
-    const int unit = blockIdx.x % units;
-    const int c = blockIdx.x / units;
-    for (int ch = threadIdx.x; ch < D; ch += NT) {
-        float x = 0.f;
-        for (int cc = P.nchunks - 1; cc > c; --cc) x += Q.ws_s[((size_t)unit * P.nchunks + cc) * D + ch];
-        carry[ch] = x;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < C * D; i += NT) {
-        const int ch = i % D, t = i / D;
-        const int row = scan_row(P, unit, c * C + t);
-        if (row < 0) continue;
-        const size_t idx = (size_t)row * D + ch;
-        const float nsig = rcp_fast(1.0f + exp2_fast(P.z[idx] * kLog2e));
-        Q.dz[idx] = (Q.dz[idx] + carry[ch]) * nsig * P.inv_tau;
     }
 }
 
@@ -621,14 +849,11 @@ static int run_bwd(const Params& P, const BwdParams& Q, hipStream_t st)
 {
     const unsigned units = (unsigned)(P.B * P.NH);
     if (P.nchunks > 1) {
-        const int rs = launch_fwd_states(P, sizeof(T) == 2 ? GLA_F16 : GLA_F32, D, st);
-        if (rs != GLA_OK) return rs;
-        hipLaunchKernelGGL((gla_bwd_agg_kernel<T, D>), dim3(units * (P.nchunks - 1)), dim3(NT), 0, st, P, Q);
-        constexpr unsigned blks = (D * D + NT - 1) / NT;
-        hipLaunchKernelGGL((gla_bwd_fold_kernel<D>), dim3(units * blks), dim3(NT), 0, st, P, Q);
+        hipLaunchKernelGGL((gla_bwd_states_kernel<T, D>), dim3(units * P.nchunks), dim3(NTS), 0, st, P, Q);
+        constexpr unsigned blks = D * D / NTS;
+        hipLaunchKernelGGL((gla_bwd_fold_kernel<D>), dim3(units * blks), dim3(NTS), 0, st, P, Q);
     }
     hipLaunchKernelGGL((gla_bwd_chunk_kernel<T, D>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q);
-    hipLaunchKernelGGL((gla_bwd_dz_kernel<D>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q);
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
 }
 

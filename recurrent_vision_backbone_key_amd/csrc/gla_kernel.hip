@@ -647,41 +647,6 @@ int launch_fold(const Params& P, int d, void* stream)
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
 }
 
-template <typename T, int D>
-static int run_states(const Params& P, hipStream_t st)
-{
-    const unsigned units = (unsigned)(P.B * P.NH);
-    if (P.nseg > 1) {
-        constexpr unsigned blks = (D * D + kThreads - 1) / kThreads;
-        hipLaunchKernelGGL((gla_chunk_kernel<T, D, D, 64, true>), dim3((P.nseg - 1) * units),
-                           dim3(kThreads), 0, st, P);
-        hipLaunchKernelGGL((gla_fold_kernel<D, D>), dim3(units * blks), dim3(kThreads), 0, st, P);
-    }
-    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
-}
-
-int launch_fwd_states(const Params& P, int dtype, int d, void* stream)
-{
-    hipStream_t st = (hipStream_t)stream;
-    if (dtype == GLA_F16) {
-        switch (d) {
-        case 16: return run_states<_Float16, 16>(P, st);
-        case 32: return run_states<_Float16, 32>(P, st);
-        case 64: return run_states<_Float16, 64>(P, st);
-        default: return GLA_EUNSUPPORTED;
-        }
-    }
-    if (dtype == GLA_F32) {
-        switch (d) {
-        case 16: return run_states<float, 16>(P, st);
-        case 32: return run_states<float, 32>(P, st);
-        case 64: return run_states<float, 64>(P, st);
-        default: return GLA_EUNSUPPORTED;
-        }
-    }
-    return GLA_EUNSUPPORTED;
-}
-
 int launch_fwd(const Params& P, int dtype, int d, int chunk, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;

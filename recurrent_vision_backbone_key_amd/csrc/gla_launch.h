@@ -87,18 +87,13 @@ struct BwdParams {
     void* dk;           // [B, L, NH, DK]
     void* dv;           // [B, L, NH, DV]
     float* dz;          // [B, L, NH, DK] binary32
-    float* ws_f;        // forward chunk-entry states [units][nchunks-1][D*D + D]
+    float* ws_f;        // chunk local states, then the entering states [units][nchunks-1][D*D + D]
     float* ws_r;        // reverse aggregates, then the entering gradients [units][nchunks-1][D*D + D]
-    float* ws_s;        // chunk sums of q (.) dq - k (.) dk [units][nchunks][D]
+    float* ws_s;        // later chunks' part of dz per chunk [units][nchunks][D]
 };
 
-// Chunkwise backward, 64-position chunks (P describes the forward call with
-// nseg = nchunks, seg_chunks = 1, ws = Q.ws_f).
+// Chunkwise backward, 64-position chunks (P describes the forward call).
 int launch_bwd(const Params& P, const BwdParams& Q, int dtype, int d, void* stream);
-
-// Forward aggregate and fold passes alone (chunk 64, one chunk per segment):
-// leaves in P.ws the state entering every chunk after the first.
-int launch_fwd_states(const Params& P, int dtype, int d, void* stream);
 
 // Zero-fills a workspace (counters, flags) on `stream`.
 int launch_workspace_init(void* ws, size_t bytes, void* stream);
