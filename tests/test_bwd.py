@@ -208,3 +208,14 @@ def test_bwd640_f32(torch, call):
     s = WORKLOADS["bwd640"]
     x = workload_inputs("bwd640", call=call, dtype="f32")
     _check("bwd640 f32", x, s["dirs"][call], s["H"], s["W"], TOL["f32"], torch)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,d,H,W,direction", [
+    ("f16", 64, 128, 128, 0),   # 256 chunks: long folds and dz carries
+    ("f16", 64, 128, 128, 3),
+    ("f32", 32, 100, 100, 2),   # 157 chunks, tail of 16, column-major
+])
+def test_bwd_long_scan(torch, dtype, d, H, W, direction):
+    x = make_bwd_inputs(1, 2, H, W, d, dtype, seed=H + d + direction)
+    _check("long", x, direction, H, W, TOL[dtype], torch)
