@@ -213,6 +213,38 @@ def bwd(q, k, v, z, dout, direction, H, W, tau=16.0, scale=None, units=None, thr
     return tuple(outs)
 
 
+def bwd_gated(q, k, v, z, r, w, du, direction, H, W, tau=16.0, scale=None, eps=1e-6,
+              units=None, threads=None):
+    """Gradients of the gated forward u = SiLU(r) (.) w (.) o / sqrt(mean(o^2) + eps)
+    (paper Section 2.1, output-gate paragraph) for du = dL/du: returns
+    (dq, dk, dv, dz, dr, dw) in float64, dw summed over every (batch, token,
+    head) row (one weight vector shared by the heads; w None means ones).
+
+    o is the fp64 ungated forward; with rho = (mean_j o_j^2 + eps)^(-1/2) and
+    g = du (.) SiLU(r) (.) w per row:
+        do = rho g - (rho^3 / dv) o sum_j(g_j o_j)
+        dr = du (.) w (.) o rho (.) SiLU'(r),  SiLU'(x) = s(x) (1 + x (1 - s(x)))
+        dw = sum_rows du (.) SiLU(r) (.) o rho
+    and dq, dk, dv, dz are the ungated backward's for dout = do."""
+    o = fwd(q, k, v, z, direction, H, W, tau=tau, scale=scale, units=units, threads=threads)
+    dv_ = v.shape[3]
+    r64 = np.asarray(r, dtype=np.float64)
+    du64 = np.asarray(du, dtype=np.float64)
+    w64 = np.ones(dv_) if w is None else np.asarray(w, dtype=np.float64)
+    rho = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    sr = silu(r64)
+    g = du64 * sr * w64
+    do = rho * g - (rho ** 3 / dv_) * o * np.sum(g * o, axis=-1, keepdims=True)
+    sig = 1.0 / (1.0 + np.exp(-r64))
+    dr = du64 * w64 * o * rho * sig * (1.0 + r64 * (1.0 - sig))
+    dw = np.sum(du64 * sr * o * rho, axis=(0, 1, 2))
+    q64, k64, v64 = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    z64 = np.asarray(z, dtype=np.float64)
+    dq, dk, dvv, dz = bwd(q64, k64, v64, z64, do, direction, H, W, tau=tau, scale=scale,
+                          units=units, threads=threads)
+    return dq, dk, dvv, dz, dr, dw
+
+
 def gate_logits(x, w1, w2, bias, heads, threads=None):
     """Low-rank gate logits z = (x W1) W2 + b in fp64 (paper Section 2.1,
     retention gate).  x: [B, L, d_model] float16 or float32; w1: [rank, d_model]

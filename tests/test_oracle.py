@@ -519,3 +519,75 @@ def test_bwd_direction_identity():
     g1 = oracle.bwd(fl["q"], fl["k"], fl["v"], fl["z"], np.ascontiguousarray(G[:, ::-1]), 1, H, W)
     for a, b in zip(g0, g1):
         assert np.array_equal(a, b[:, ::-1])
+
+
+# ---------------------------------------------------------------------------
+# Backward of the gated forward (output gate: SiLU(r) (.) w (.) RMSNorm(o))
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", (0, 3))
+@pytest.mark.parametrize("with_w", (True, False))
+def test_bwd_gated_equals_central_differences(direction, with_w):
+    """q, k, v, z, r gradients against central differences of the gated
+    forward oracle on fp64 inputs, f = sum(dU * fwd(..., r, w))."""
+    H, W, d = 4, 5, 4
+    rng = np.random.default_rng(30 + direction + int(with_w))
+    x = make_inputs(1, 2, H, W, d, d, "f32", gated=True, seed=9 + direction)
+    q, k, v, r = (x[n].astype(np.float64) for n in ("q", "k", "v", "r"))
+    z = x["z"].astype(np.float64)
+    w = x["w"] if with_w else None
+    dU = rng.standard_normal((1, H * W, 2, d))
+    grads = oracle.bwd_gated(q, k, v, z, r, w, dU, direction, H, W)
+    base = dict(q=q, k=k, v=v, z=z, r=r)
+
+    def f(**kw):
+        a = dict(base, **kw)
+        return float((oracle.fwd(a["q"], a["k"], a["v"], a["z"], direction, H, W, r=a["r"], w=w)
+                      * dU).sum())
+
+    h = 1e-6
+    for (name, arr), g in zip(base.items(), grads[:4] + (grads[4],)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += h
+            am[idx] -= h
+            fd = (f(**{name: ap}) - f(**{name: am})) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-5 * (abs(g[idx]) + 1e-2), (name, idx, fd, g[idx])
+
+
+def test_bwd_gated_dw_is_exact_difference():
+    """u is linear in w, so L(w + e_j) - L(w) is dw_j exactly (up to fp64
+    rounding); the weights chosen are exact in binary32, as the forward
+    oracle stores them."""
+    H, W, d = 3, 4, 4
+    x = make_inputs(2, 2, H, W, d, d, "f32", gated=True, seed=21)
+    dU = np.random.default_rng(22).standard_normal((2, H * W, 2, d))
+    w = np.array([0.5, 1.25, -0.75, 2.0], dtype=np.float32)
+    dw = oracle.bwd_gated(x["q"], x["k"], x["v"], x["z"], x["r"], w, dU, 2, H, W)[5]
+
+    def f(ww):
+        return float((oracle.fwd(x["q"], x["k"], x["v"], x["z"], 2, H, W, r=x["r"], w=ww)
+                      * dU).sum())
+
+    base = f(w)
+    for j in range(d):
+        wj = w.copy()
+        wj[j] += np.float32(1.0)
+        assert abs((f(wj) - base) - dw[j]) <= 1e-10 * (abs(dw[j]) + 1.0), j
+
+
+def test_bwd_gated_special_cases():
+    """du = 0 gives zeros; w = 0 zeroes every gradient but dw; with w = 0 and
+    the same inputs dw is unchanged (it does not depend on w)."""
+    H, W, d = 3, 3, 4
+    x = make_inputs(1, 1, H, W, d, d, "f32", gated=True, seed=23)
+    dU = np.random.default_rng(24).standard_normal((1, H * W, 1, d))
+    args = (x["q"], x["k"], x["v"], x["z"], x["r"])
+    for g in oracle.bwd_gated(*args, x["w"], np.zeros_like(dU), 0, H, W):
+        assert not np.any(g)
+    g0 = oracle.bwd_gated(*args, np.zeros(d, np.float32), dU, 0, H, W)
+    for g in g0[:5]:
+        assert not np.any(g)
+    g1 = oracle.bwd_gated(*args, x["w"], dU, 0, H, W)
+    assert np.allclose(g0[5], g1[5], rtol=1e-14, atol=0)
