@@ -64,11 +64,14 @@ KERNEL_SOURCES = {
     "wide": ("gla_wide.hip", "gla_kernel.hip") + _COMMON_SOURCES,
     "generic": ("gla_kernel.hip",) + _COMMON_SOURCES,
     "sswiglu": ("gla_sswiglu.hip",) + _COMMON_SOURCES,
-    "bwd": ("gla_bwd.hip", "gla_kernel.hip") + _COMMON_SOURCES,
+    "bwd": ("gla_bwd.hip", "gla_epi.h") + _COMMON_SOURCES,
+    "bwd_gated": ("gla_bwd.hip", "gla_epi.h") + _COMMON_SOURCES,
 }
 
 
 def kernel_family(spec):
+    if spec.get("kind") == "bwd" and spec.get("gated"):
+        return "bwd_gated"
     if spec.get("kind") in ("sswiglu", "bwd"):
         return spec["kind"]
     if spec["dtype"] == "f16" and spec["dk"] == 64 and spec["chunk"] == 64:
@@ -199,7 +202,10 @@ def cpu_baseline(spec, name, seconds):
         if spec.get("gate_proj"):
             z = oracle.gate_logits(x["x"], x["w1"], x["w2"], x["bias"], spec["NH"],
                                    threads=cores)
-        if spec.get("kind") == "bwd":
+        if spec.get("kind") == "bwd" and spec.get("gated"):
+            oracle.bwd_gated(x["q"], x["k"], x["v"], z, x["r"], x["w"], x["dout"],
+                             spec["dirs"][call], H, W, units=(u0, u1), threads=cores)
+        elif spec.get("kind") == "bwd":
             oracle.bwd(x["q"], x["k"], x["v"], z, x["dout"], spec["dirs"][call], H, W,
                        units=(u0, u1), threads=cores)
         else:
@@ -295,9 +301,13 @@ def bench_bwd(args, spec, name):
     dirs = spec["dirs"]
     es = 2 if spec["dtype"] == "f16" else 4
     th_call = B * NH * H * W
-    # q, k, v, dO read, dq, dk, dv written (storage type); z read, dz written (binary32)
-    bytes_call = th_call * (7 * es * d + 8 * d)
-    flops_call = th_call * algorithmic_flops_bwd_per_token_head(d, d, spec["chunk"])
+    gated = spec["gated"]
+    # q, k, v, dO read, dq, dk, dv written (storage type); z read, dz written
+    # (binary32); gated: r read and dr written as well, and o recomputed (the
+    # forward's flops counted: the gate's derivative needs o)
+    bytes_call = th_call * ((9 if gated else 7) * es * d + 8 * d)
+    flops_call = th_call * (algorithmic_flops_bwd_per_token_head(d, d, spec["chunk"]) +
+                            (algorithmic_flops_per_token_head(d, d, spec["chunk"]) if gated else 0))
     rotate = args.rotate or max(1, math.ceil(2 * MALL_BYTES / (bytes_call * len(dirs))))
     steps = args.steps if args.steps is not None else 100
     warmup = args.warmup if args.warmup is not None else 20
@@ -306,29 +316,38 @@ def bench_bwd(args, spec, name):
     print(f"[bench] {name}: {len(dirs)} calls/step, {bytes_call / 1e6:.2f} MB/call, "
           f"{rotate} input sets, steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
     opts = gla.make_opts(B, NH, d, d, gla.F16 if es == 2 else gla.F32)
-    ws_bytes = gla.bwd_workspace_size(dirs[0], H, W, opts)
+    ws_bytes = (gla.bwd_gated_workspace_size if gated else gla.bwd_workspace_size)(dirs[0], H, W, opts)
     sets = []
     for r in range(rotate):
         calls = []
         for c, dr in enumerate(dirs):
             x = make_bwd_inputs_device(B, NH, H, W, d, spec["dtype"], spec["z"],
-                                       seed=1000 * spec["index"] + 100 * r + c, device=dev)
+                                       seed=1000 * spec["index"] + 100 * r + c, device=dev,
+                                       gated=gated)
             grads = (torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"]),
                      torch.empty_like(x["z"]))
+            if gated:
+                grads += (torch.empty_like(x["r"]), torch.empty((d,), dtype=torch.float32, device=dev))
             ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
             calls.append((x, dr, grads, ws))
         sets.append(calls)
 
     def step(r):
         for x, dr, grads, ws in sets[r]:
-            gla.bwd(x["q"], x["k"], x["v"], x["z"], x["dout"], dr, H, W, grads=grads, workspace=ws)
+            if gated:
+                gla.bwd_gated(x["q"], x["k"], x["v"], x["z"], x["r"], x["dout"], dr, H, W,
+                              norm_weight=x["w"], grads=grads, workspace=ws)
+            else:
+                gla.bwd(x["q"], x["k"], x["v"], x["z"], x["dout"], dr, H, W, grads=grads,
+                        workspace=ws)
 
     ms_step, G, graphed = time_steps(step, rotate, steps, warmup, args, 10)
     us_call = 1e3 * ms_step / len(dirs)
     tflops = flops_call / (us_call * 1e-6) / 1e12
     gbs = bytes_call / (us_call * 1e-6) / 1e9
     result = {
-        "metric": "chunkwise GLA bwd: µs/call + Gtok·head/s at L=1600; % of MFMA (fp32) roofline",
+        "metric": ("chunkwise GLA bwd (output gate included)" if gated else "chunkwise GLA bwd") +
+                  ": µs/call + Gtok·head/s at L=1600; % of MFMA (fp32) roofline",
         "value": round(len(dirs) * th_call / (ms_step * 1e-3) / 1e9, 4), "unit": "Gtok·head/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
         "us_per_call": round(us_call, 3), "higher_is_better": True, "scaling": "weak",
@@ -338,13 +357,17 @@ def bench_bwd(args, spec, name):
                    "dirs": ",".join("L2R R2L T2B B2T".split()[x] for x in dirs),
                    "calls_per_step": len(dirs), "input_sets": rotate, "hip_graph": graphed,
                    "steps_per_graph": G, "workspace_bytes_per_call": ws_bytes,
-                   "accumulate": "f32", "mfma_operands": "f32"},
+                   "gated": gated, "accumulate": "f32", "mfma_operands": "f32"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
-                     "traffic": load_traffic(name, "bwd"),
-                     "kernel": "gla_chunk_kernel<aggregate> + gla_fold_kernel + gla_bwd_agg_kernel "
-                               "+ gla_bwd_fold_kernel + gla_bwd_chunk_kernel + gla_bwd_dz_kernel "
-                               "(six launches per call; figures for the whole call)",
+                     "traffic": load_traffic(name, kernel_family(spec)),
+                     "kernel": ("gla_bwd_states_kernel<local states> + gla_bwd_fold_kernel<forward> + "
+                                "gla_bwd_oepi_kernel (o and the output gate's backward) + "
+                                "gla_bwd_dw_kernel + gla_bwd_states_kernel<reverse> + "
+                                "gla_bwd_fold_kernel<reverse> + gla_bwd_chunk_kernel"
+                                if gated else
+                                "gla_bwd_states_kernel + gla_bwd_fold_kernel + gla_bwd_chunk_kernel") +
+                               " (figures for the whole call)",
                      "algorithmic_flops_per_call": flops_call,
                      "algorithmic_bytes_per_call": bytes_call,
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 4
+#define GLA_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define GLA_API __attribute__((visibility("default")))
@@ -240,6 +240,32 @@ GLA_API int gla_bwd(const void *q, const void *k, const void *v, const float *ga
 
 /* Bytes of workspace gla_bwd needs (0 for arguments it would reject). */
 GLA_API size_t gla_bwd_workspace_size(int dir, int H, int W, const gla_opts *opts);
+
+/*
+ * gla_bwd_gated -- gradients of the gated forward (gla_fwd with r; paper
+ * Section 2.1 output-gate paragraph): with dout = dL/du for
+ *     u = SiLU(r) (.) w (.) o / sqrt(mean_{d_v}(o^2) + eps),
+ * o the ungated output and rho = 1 / sqrt(mean(o^2) + eps), g = dout (.) SiLU(r) (.) w:
+ *     do = rho g - (rho^3 / d_v) o sum(g (.) o)
+ *     dr = dout (.) w (.) o rho (.) SiLU'(r)
+ *     dw = sum over every (batch, token, head) row of dout (.) SiLU(r) (.) o rho
+ * and dq, dk, dv, dz as gla_bwd for do.  o is recomputed by the three-pass
+ * forward (stored in the storage type, then used as is).
+ *   r, dout, dr [B, L, NH, dv] in opts->dtype; w = opts->norm_weight ([dv]
+ *   binary32, NULL selects ones) and opts->eps as in gla_fwd; dw [dv] binary32,
+ *   may be NULL (not computed); the rest as gla_bwd.
+ * The workspace must hold gla_bwd_gated_workspace_size() bytes (no
+ * initialisation).  16-byte aligned device pointers; outputs must not overlap
+ * each other, an input or the workspace.  Asynchronous on opts->stream;
+ * dw is the same for equal inputs (fixed summation order).  Returns a gla_status.
+ */
+GLA_API int gla_bwd_gated(const void *q, const void *k, const void *v, const float *gate_logits,
+                          const void *r, const void *dout, int dir, int H, int W, void *dq,
+                          void *dk, void *dv, float *dz, void *dr, float *dw,
+                          const gla_opts *opts);
+
+/* Bytes of workspace gla_bwd_gated needs (0 for arguments it would reject). */
+GLA_API size_t gla_bwd_gated_workspace_size(int dir, int H, int W, const gla_opts *opts);
 
 /* Static, NUL-terminated description of a gla_status value. */
 GLA_API const char *gla_status_str(int status);

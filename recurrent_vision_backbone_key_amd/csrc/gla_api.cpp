@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "gla.h"
+#include "gla_epi.h"
 #include "gla_launch.h"
 #include "gla_plan.h"
 
@@ -154,16 +155,14 @@ extern "C" int gla_spatial_swiglu(const void* gate, const void* value, int64_t l
                                channels, dtype, stream);
 }
 
-extern "C" int gla_bwd(const void* q, const void* k, const void* v, const float* gate_logits,
-                       const void* dout, int dir, int H, int W, void* dq, void* dk, void* dv,
-                       float* dz, const gla_opts* opts)
+namespace {
+
+// Launch parameters of the backward for validated arguments.
+void bwd_params(const void* q, const void* k, const void* v, const float* gate_logits,
+                const void* dout, int dir, int H, int W, void* dq, void* dk, void* dv, float* dz,
+                const gla_opts* opts, char* ws, int nchunks, size_t off_r, size_t off_s,
+                gla::Params& P, gla::BwdParams& Q)
 {
-    int nchunks = 0;
-    size_t off_r = 0, off_s = 0;
-    const int st = gla_validate_bwd(q, k, v, gate_logits, dout, dir, H, W, dq, dk, dv, dz, opts,
-                                    &nchunks, &off_r, &off_s);
-    if (st != GLA_OK) return st;
-    gla::Params P;
     P.q = q;
     P.k = k;
     P.v = v;
@@ -171,7 +170,6 @@ extern "C" int gla_bwd(const void* q, const void* k, const void* v, const float*
     P.r = nullptr;
     P.w = nullptr;
     P.out = nullptr;
-    char* ws = (char*)opts->workspace;
     P.ws = (float*)ws;
     P.B = opts->batch;
     P.NH = opts->heads;
@@ -190,7 +188,6 @@ extern "C" int gla_bwd(const void* q, const void* k, const void* v, const float*
     P.xcd_local = 0;
     P.xcd_tasks = 0;
     no_proj(P);
-    gla::BwdParams Q;
     Q.dout = dout;
     Q.dq = dq;
     Q.dk = dk;
@@ -199,6 +196,23 @@ extern "C" int gla_bwd(const void* q, const void* k, const void* v, const float*
     Q.ws_f = (float*)ws;
     Q.ws_r = (float*)(ws + off_r);
     Q.ws_s = (float*)(ws + off_s);
+}
+
+}  // namespace
+
+extern "C" int gla_bwd(const void* q, const void* k, const void* v, const float* gate_logits,
+                       const void* dout, int dir, int H, int W, void* dq, void* dk, void* dv,
+                       float* dz, const gla_opts* opts)
+{
+    int nchunks = 0;
+    size_t off_r = 0, off_s = 0;
+    const int st = gla_validate_bwd(q, k, v, gate_logits, dout, dir, H, W, dq, dk, dv, dz, opts,
+                                    &nchunks, &off_r, &off_s);
+    if (st != GLA_OK) return st;
+    gla::Params P;
+    gla::BwdParams Q;
+    bwd_params(q, k, v, gate_logits, dout, dir, H, W, dq, dk, dv, dz, opts, (char*)opts->workspace,
+               nchunks, off_r, off_s, P, Q);
     return gla::launch_bwd(P, Q, opts->dtype, opts->dk, opts->stream);
 }
 
@@ -208,6 +222,39 @@ extern "C" size_t gla_bwd_workspace_size(int dir, int H, int W, const gla_opts* 
     size_t off_r = 0, off_s = 0, bytes = 0;
     if (gla_plan_bwd(dir, H, W, opts, &nchunks, &off_r, &off_s, &bytes) != GLA_OK) return 0;
     return bytes;
+}
+
+extern "C" int gla_bwd_gated(const void* q, const void* k, const void* v,
+                             const float* gate_logits, const void* r, const void* dout, int dir,
+                             int H, int W, void* dq, void* dk, void* dv, float* dz, void* dr,
+                             float* dw, const gla_opts* opts)
+{
+    gla_bwd_gated_layout lay;
+    const int st = gla_validate_bwd_gated(q, k, v, gate_logits, r, dout, dir, H, W, dq, dk, dv,
+                                          dz, dr, dw, opts, &lay);
+    if (st != GLA_OK) return st;
+    char* ws = (char*)opts->workspace;
+    gla::Params P;
+    gla::BwdParams Q;
+    // dO (binary32) is produced inside the call, in the workspace
+    bwd_params(q, k, v, gate_logits, ws + lay.off_do, dir, H, W, dq, dk, dv, dz, opts, ws,
+               lay.nchunks, lay.off_r, lay.off_s, P, Q);
+    gla::GatedBwd G;
+    G.r = r;
+    G.du = dout;
+    G.w = opts->norm_weight;
+    G.dr = dr;
+    G.dwp = (float*)(ws + lay.off_dwp);
+    G.dw = dw;
+    G.eps = opts->eps;
+    return gla::launch_bwd_gated(P, Q, G, opts->dtype, opts->dk, opts->stream);
+}
+
+extern "C" size_t gla_bwd_gated_workspace_size(int dir, int H, int W, const gla_opts* opts)
+{
+    gla_bwd_gated_layout lay;
+    if (!opts || gla_plan_bwd_gated(dir, H, W, opts, &lay) != GLA_OK) return 0;
+    return lay.bytes;
 }
 
 extern "C" const char* gla_status_str(int status)

@@ -44,6 +44,7 @@
 
 #include "gla.h"
 #include "gla_device.h"
+#include "gla_epi.h"
 #include "gla_geometry.h"
 #include "gla_launch.h"
 
@@ -172,7 +173,10 @@ __device__ __forceinline__ void store1(T* base, size_t idx, float x)
 // Chunk states: slot c of ws_f <- (L_c, B_c) for c < nchunks - 1 and slot
 // c - 1 of ws_r <- (RA_c, B_c) for c >= 1.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+// T: storage type of q, k, v; TD: of dO (binary32 when it comes from the
+// output gate's backward).  FWD / REV select the local states / the reverse
+// aggregates (the gated backward needs the states before dO exists).
+template <typename T, typename TD, int D, bool FWD, bool REV>
 __global__ __launch_bounds__(NTS) void gla_bwd_states_kernel(Params P, BwdParams Q)
 {
     using Y = Lay<D>;
@@ -189,24 +193,29 @@ __global__ __launch_bounds__(NTS) void gla_bwd_states_kernel(Params P, BwdParams
     const int units = P.B * P.NH;
     const int unit = blockIdx.x % units;
     const int c = blockIdx.x / units;
-    const bool do_r = c >= 1, do_f = c < P.nchunks - 1;
+    const bool do_r = REV && c >= 1, do_f = FWD && c < P.nchunks - 1;
     for (int i = tid; i < C; i += NTS) sRows[i] = scan_row(P, unit, c * C + i);
     __syncthreads();
     // raw tiles (q, dO for the reverse aggregate, k, v for the local state;
     // all four are fetched, every load issued before the first conversion)
     constexpr int G8 = D / 8;
     constexpr int IT = (C * G8 + NTS - 1) / NTS;
-    Raw8<T> rq[IT], rd[IT], rk[IT], rv[IT];
+    Raw8<T> rq[IT], rk[IT], rv[IT];
+    Raw8<TD> rd[IT];
     int rows[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int i = tid + it * NTS;
         const int t = (i < C * G8 ? i : 0) / G8, c8 = 8 * (i % G8);
         rows[it] = sRows[t];
-        rq[it].load((const T*)P.q, rows[it], D, c8);
-        rd[it].load((const T*)Q.dout, rows[it], D, c8);
-        rk[it].load((const T*)P.k, rows[it], D, c8);
-        rv[it].load((const T*)P.v, rows[it], D, c8);
+        if (REV) {
+            rq[it].load((const T*)P.q, rows[it], D, c8);
+            rd[it].load((const TD*)Q.dout, rows[it], D, c8);
+        }
+        if (FWD) {
+            rk[it].load((const T*)P.k, rows[it], D, c8);
+            rv[it].load((const T*)P.v, rows[it], D, c8);
+        }
     }
     // the gate logits of thread (ch, i)'s 16 positions, in flight as well
     const bool gate_thread = tid < D * NS;
@@ -224,10 +233,14 @@ __global__ __launch_bounds__(NTS) void gla_bwd_states_kernel(Params P, BwdParams
             const bool ok = rows[it] >= 0;
             // 8 consecutive columns stay consecutive under the swizzle
             const int o = Y::sidx(t, c8);
-            rq[it].put(sQ + o, ok);
-            rd[it].put(sDO + o, ok);
-            rk[it].put(sK + o, ok);
-            rv[it].put(sV + o, ok);
+            if (REV) {
+                rq[it].put(sQ + o, ok);
+                rd[it].put(sDO + o, ok);
+            }
+            if (FWD) {
+                rk[it].put(sK + o, ok);
+                rv[it].put(sV + o, ok);
+            }
         }
     }
 
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(NTS) void gla_bwd_states_kernel(Params P, BwdParams
 //   carry:   ws_s[s][ch] = sum_j R_s[ch][j] S_in(s + 1)[ch][j]  (a row of D
 //            entries is D consecutive lanes of one wavefront).
 // Loads of a batch of slots are issued before the dependent multiply-adds.
-template <int D>
+template <int D, bool FWD, bool REV>
 __global__ __launch_bounds__(NTS) void gla_bwd_fold_kernel(Params P, BwdParams Q)
 {
     constexpr int ENTRIES = D * D;
@@ -322,7 +335,7 @@ __global__ __launch_bounds__(NTS) void gla_bwd_fold_kernel(Params P, BwdParams Q
     float* bf = Q.ws_f + (size_t)unit * nslot * slot_floats;
     float* br = Q.ws_r + (size_t)unit * nslot * slot_floats;
     float x = 0.f;
-    for (int s0 = 0; s0 < nslot; s0 += BATCH) {
+    for (int s0 = 0; FWD && s0 < nslot; s0 += BATCH) {
         float lv[BATCH], gv[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
@@ -340,7 +353,7 @@ __global__ __launch_bounds__(NTS) void gla_bwd_fold_kernel(Params P, BwdParams Q
         }
     }
     float y = 0.f;
-    for (int s0 = nslot - 1; s0 >= 0; s0 -= BATCH) {
+    for (int s0 = nslot - 1; REV && s0 >= 0; s0 -= BATCH) {
         float lv[BATCH], gv[BATCH], sv[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
@@ -448,12 +461,41 @@ __device__ __forceinline__ float4v diag_scores(const Params& P, const int* sRows
     return a;
 }
 
+// scores[t][tau] = s sum_ch q_t k_tau 2^{b_t - b_tau} for t = 16 si + l16 >=
+// tau = 16 si + 4 g + e (the layout of the output product's A operand).
+template <typename T, int D>
+__device__ __forceinline__ float4v diag_scores_out(const Params& P, const int* sRows, const float* sB,
+                                                   int si, int g, int l16)
+{
+    constexpr int SD = Lay<D>::SD;
+    const int t = 16 * si + l16;
+    const int rt = sRows[t];
+    float4v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int c8 = 0; c8 < D; c8 += 8) {
+        float qq[8];
+        load8<T>((const T*)P.q, rt, D, c8, qq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int u = 16 * si + 4 * g + e;
+            float kk[8];
+            load8<T>((const T*)P.k, sRows[u], D, c8, kk);
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+                a[e] += qq[x] * kk[x] * exp2_fast(fminf(sB[t * SD + c8 + x] - sB[u * SD + c8 + x], 0.f));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = (4 * g + e <= l16) ? P.scale * a[e] : 0.f;
+    return a;
+}
+
 // ---------------------------------------------------------------------------
 // Chunk kernel: dq, dk, dv and dz.  Wavefront w takes sub-chunk si = w / 2
 // and half h = w % 2 of the 16-channel column tiles (the two halves of a
 // sub-chunk sit on different SIMDs next to the halves of another sub-chunk).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, typename TD, int D>
 __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q)
 {
     using Y = Lay<D>;
@@ -514,7 +556,8 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
         }
         constexpr int G8 = D / 8;
         constexpr int IT = (C * G8 + NT - 1) / NT;
-        Raw8<T> rq[IT], rk[IT], rv[IT], rd[IT];
+        Raw8<T> rq[IT], rk[IT], rv[IT];
+        Raw8<TD> rd[IT];
         int rows[IT];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
@@ -524,7 +567,7 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             rq[it].load((const T*)P.q, rows[it], D, c8);
             rk[it].load((const T*)P.k, rows[it], D, c8);
             rv[it].load((const T*)P.v, rows[it], D, c8);
-            rd[it].load((const T*)Q.dout, rows[it], D, c8);
+            rd[it].load((const TD*)Q.dout, rows[it], D, c8);
         }
         if (gate_thread) {
 #pragma unroll
@@ -844,26 +887,358 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
     }
 }
 
+// ---------------------------------------------------------------------------
+// Gated backward, first half: the ungated output o of a chunk recomputed in
+// binary32 from the entering state (paper Sec. 2.1 recurrence, the forward's
+// chunkwise form with the same sub-chunk factors), then the output gate's
+// backward on it (u = SiLU(r) (.) w (.) o rho, rho = (mean(o^2) + eps)^-1/2):
+//     do = rho g - (rho^3 / d) o sum(g (.) o),  g = du (.) SiLU(r) (.) w
+//     dr = du (.) w (.) o rho (.) SiLU'(r),     dw partial = sum_rows du SiLU(r) o rho
+// do (binary32) feeds the reverse aggregates and the chunk kernel.  Same
+// geometry as the chunk kernel: wavefront (si, h) owns sub-chunk si and half
+// h of the column tiles; o of a block is sum_{j <= si} scores_ij V_j +
+// s Qh_si (2^{c_{si-1}} (.) S_in) with scores_ij = s Qh_i (Kh_j (.) E_ij)^T.
+// ---------------------------------------------------------------------------
 template <typename T, int D>
+__global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q, GatedBwd G)
+{
+    using Y = Lay<D>;
+    constexpr int SD = Y::SD, NTL = D / 16, KS = D / 4;
+    constexpr int CT = NTL >= 2 ? NTL / 2 : 1;
+    __shared__ __attribute__((aligned(16))) float lds[Y::WORDS];
+    float* sX = lds + Y::P;      // row sums of the two halves: [2 sums][2 halves][C]
+    float* sV = lds + Y::V;
+    float* sKT = lds + Y::KT;
+    float* sQH = lds + Y::QH;
+    float* sSS = lds + Y::SS;
+    float* sRed = lds + Y::RR;   // dw partial sums [NS][D]
+    float* sB = lds + Y::BB;
+    float* sCC = lds + Y::CC;
+    float* sE = lds + Y::EE;
+    float* sTot = lds + Y::TOT;
+    int* sRows = (int*)(lds + Y::ROWS);
+    int* sFlag = (int*)(lds + Y::FLAGS);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int units = P.B * P.NH;
+    const int unit = blockIdx.x % units;
+    const int c = blockIdx.x / units;
+    const int si = wave >> 1, h = wave & 1;
+    const int ct0 = h * CT;
+    const bool cols = ct0 < NTL;
+    const float s = P.scale;
+    const size_t slot_floats = (size_t)D * D + D;
+    const bool has_in = c > 0;
+    if (tid < NS) sFlag[tid] = 0;
+    auto E = [&](int x, int y, int ch) { return sE[(x * NS + y) * D + ch]; };
+
+    // ---- loads: S_in, raw q -> QH, k -> KT, v, the gate threads' logits
+    const bool gate_thread = tid < D * NS;
+    const int gch = tid % D, gi = tid / D;
+    float zz[16];
+    unsigned zok = 0;
+    {
+        constexpr int SQ4 = D * D / 4;
+        constexpr int SIT = (SQ4 + NT - 1) / NT;
+        float4v st_in[SIT];
+        const float4v* src_in = (const float4v*)(Q.ws_f + ((size_t)unit * (P.nchunks - 1) + (has_in ? c - 1 : 0)) * slot_floats);
+#pragma unroll
+        for (int it = 0; it < SIT; ++it) {
+            const int i = tid + it * NT;
+            if (has_in) st_in[it] = src_in[i < SQ4 ? i : 0];
+        }
+        constexpr int G8 = D / 8;
+        constexpr int IT = (C * G8 + NT - 1) / NT;
+        Raw8<T> rq[IT], rk[IT], rv[IT];
+        int rows[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int i = tid + it * NT;
+            const int t = (i < C * G8 ? i : 0) / G8, c8 = 8 * (i % G8);
+            rows[it] = scan_row(P, unit, c * C + t);
+            rq[it].load((const T*)P.q, rows[it], D, c8);
+            rk[it].load((const T*)P.k, rows[it], D, c8);
+            rv[it].load((const T*)P.v, rows[it], D, c8);
+        }
+        if (gate_thread) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int row = scan_row(P, unit, c * C + 16 * gi + u);
+                zok |= (row >= 0 ? 1u : 0u) << u;
+                zz[u] = ld1<float>(P.z, row, D, gch);
+            }
+        }
+        for (int i = tid; i < C; i += NT) sRows[i] = scan_row(P, unit, c * C + i);
+#pragma unroll
+        for (int it = 0; it < SIT; ++it) {
+            const int i = tid + it * NT;
+            if (i < SQ4 && has_in) {
+                const int r = (4 * i) / D, cc = 4 * i - r * D;
+                *(float4v*)(sSS + r * SD + cc) = st_in[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int i = tid + it * NT;
+            if (i < C * G8) {
+                const int o = (i / G8) * SD + 8 * (i % G8);
+                const bool ok = rows[it] >= 0;
+                rq[it].put(sQH + o, ok);
+                rk[it].put(sKT + o, ok);
+                rv[it].put(sV + o, ok);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- gate stage (as in the chunk kernel)
+    float br[16];
+    if (gate_thread) {
+        float run = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            run += ((zok >> u) & 1u) ? log2_decay(zz[u], P.inv_tau) : 0.f;
+            br[u] = run;
+        }
+        sTot[gi * D + gch] = run;
+        if (run < -kDiagSpan) sFlag[gi] = 1;
+    }
+    __syncthreads();
+    if (gate_thread) {
+        float cv[NS + 1];
+        cv[0] = 0.f;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) cv[m + 1] = cv[m] + sTot[m * D + gch];
+        const float off = cv[gi], ci = cv[gi + 1];
+        sCC[(gi + 1) * D + gch] = ci;
+        if (gi == 0) sCC[gch] = 0.f;
+#pragma unroll
+        for (int x = 0; x <= NS; ++x)
+            if (x >= gi) sE[(x * NS + gi) * D + gch] = exp2_fast(cv[x] - ci);
+        float xq[16], xk[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            xq[u] = sQH[(16 * gi + u) * SD + gch];
+            xk[u] = sKT[(16 * gi + u) * SD + gch];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int t = 16 * gi + u;
+            const float b = br[u] + off;
+            sQH[t * SD + gch] = xq[u] * exp2_fast(b - off);
+            sKT[t * SD + gch] = xk[u] * exp2_fast(ci - b);
+            sB[t * SD + gch] = b;
+        }
+    }
+    __syncthreads();
+    const bool pairwise = sFlag[si] != 0;
+
+    // ---- o of sub-chunk si: rows 16 si + 4g + e, columns 16 (ct0 + cl) + l16
+    float4v oacc[CT];
+#pragma unroll
+    for (int cl = 0; cl < CT; ++cl) oacc[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+    if (cols) {
+        for (int j = 0; j <= si; ++j) {
+            // scores[t = 16 si + l16][tau = 16 j + 4g + e], two chains
+            float4v a = {0.f, 0.f, 0.f, 0.f};
+            if (j == si && pairwise) {
+                a = diag_scores_out<T, D>(P, sRows, sB, si, g, l16);
+            } else {
+                float4v a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ks += 2) {
+                    const int ch = 4 * ks + g;
+                    a = mma(sKT[(16 * j + l16) * SD + ch] * E(si, j, ch), sQH[(16 * si + l16) * SD + ch], a);
+                    a1 = mma(sKT[(16 * j + l16) * SD + ch + 4] * E(si, j, ch + 4),
+                             sQH[(16 * si + l16) * SD + ch + 4], a1);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool keep = (j < si) || (4 * g + e <= l16);
+                    a[e] = keep ? s * (a[e] + a1[e]) : 0.f;
+                }
+            }
+            // o[t][col] += sum_tau scores[t][tau] v[tau][col]; k-slot g of step e is tau = 16 j + 4g + e
+#pragma unroll
+            for (int cl = 0; cl < CT; ++cl)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    oacc[cl] = mma(a[e], sV[(16 * j + 4 * g + e) * SD + 16 * (ct0 + cl) + l16], oacc[cl]);
+        }
+        if (has_in) {
+#pragma unroll 4
+            for (int ks = 0; ks < KS; ++ks) {
+                const int jj = 4 * ks + g;
+                const float a = sQH[(16 * si + l16) * SD + jj];
+                const float f = s * exp2_fast(sCC[si * D + jj]);
+#pragma unroll
+                for (int cl = 0; cl < CT; ++cl)
+                    oacc[cl] = mma(a, sSS[jj * SD + 16 * (ct0 + cl) + l16] * f, oacc[cl]);
+            }
+        }
+    }
+
+    // ---- output gate backward at (t = 16 si + 4g + e, col = 16 (ct0 + cl) + l16)
+    float rv[CT][4], uv[CT][4], wv[CT];
+    int rowe[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rowe[e] = sRows[16 * si + 4 * g + e];
+#pragma unroll
+    for (int cl = 0; cl < CT; ++cl) {
+        const int col = 16 * (ct0 + cl) + l16;
+        const int colc = cols ? col : 0;
+        wv[cl] = G.w ? G.w[colc] : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            rv[cl][e] = ld1<T>(G.r, cols ? rowe[e] : -1, D, colc);
+            uv[cl][e] = ld1<T>(G.du, cols ? rowe[e] : -1, D, colc);
+        }
+    }
+    float ss[4], dot[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        ss[e] = 0.f;
+        dot[e] = 0.f;
+#pragma unroll
+        for (int cl = 0; cl < CT; ++cl) {
+            const float o = oacc[cl][e];
+            ss[e] += o * o;
+            dot[e] += uv[cl][e] * silu(rv[cl][e]) * wv[cl] * o;
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+            ss[e] += __shfl_xor(ss[e], m);
+            dot[e] += __shfl_xor(dot[e], m);
+        }
+    }
+    if (l16 == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * si + 4 * g + e;
+            sX[(0 * 2 + h) * C + t] = ss[e];
+            sX[(1 * 2 + h) * C + t] = dot[e];
+        }
+    }
+    __syncthreads();
+    float dwl[CT];
+#pragma unroll
+    for (int cl = 0; cl < CT; ++cl) dwl[cl] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int t = 16 * si + 4 * g + e;
+        const float sst = sX[(0 * 2 + 0) * C + t] + sX[(0 * 2 + 1) * C + t];
+        const float dt = sX[(1 * 2 + 0) * C + t] + sX[(1 * 2 + 1) * C + t];
+        const float rho = rsq_fast(sst * (1.0f / D) + G.eps);
+        const float k3 = rho * rho * rho * (1.0f / D) * dt;
+#pragma unroll
+        for (int cl = 0; cl < CT; ++cl) {
+            const float o = oacc[cl][e], r = rv[cl][e], du = uv[cl][e];
+            const float sig = rcp_fast(1.0f + exp2_fast(-r * kLog2e));
+            const float sr = r * sig;
+            const float dov = rho * du * sr * wv[cl] - k3 * o;
+            const float drv = du * wv[cl] * o * rho * sig * (1.0f + r * (1.0f - sig));
+            dwl[cl] += du * sr * o * rho;
+            const int row = rowe[e];
+            if (cols && row >= 0) {
+                const size_t idx = (size_t)row * D + 16 * (ct0 + cl) + l16;
+                ((float*)Q.dout)[idx] = dov;
+                store1<T>((T*)G.dr, idx, drv);
+            }
+        }
+    }
+    // dw partial sums of this chunk: over the wavefront's rows (lanes g), then
+    // over the sub-chunks in order
+#pragma unroll
+    for (int cl = 0; cl < CT; ++cl) {
+        dwl[cl] += __shfl_xor(dwl[cl], 16);
+        dwl[cl] += __shfl_xor(dwl[cl], 32);
+        if (cols && g == 0) sRed[si * D + 16 * (ct0 + cl) + l16] = dwl[cl];
+    }
+    __syncthreads();
+    for (int col = tid; col < D; col += NT) {
+        float x = 0.f;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) x += sRed[m * D + col];
+        G.dwp[(size_t)blockIdx.x * D + col] = x;
+    }
+}
+
+// dw[c] = sum_b dwp[b][c] in a fixed order: part p of NDW / D parts adds the
+// blocks b = p (mod parts) in increasing order, eight loads in flight, then
+// the parts are added in order.
+constexpr int NDW = 1024;
+template <int D>
+__global__ __launch_bounds__(NDW) void gla_bwd_dw_kernel(const float* __restrict__ dwp,
+                                                         float* __restrict__ dw, int nblk)
+{
+    constexpr int PARTS = NDW / D;
+    __shared__ float part[PARTS][D];
+    const int c = threadIdx.x % D, p = threadIdx.x / D;
+    float x = 0.f;
+    for (int b0 = p; b0 < nblk; b0 += 8 * PARTS) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int b = b0 + u * PARTS;
+            v[u] = b < nblk ? dwp[(size_t)b * D + c] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x += v[u];
+    }
+    part[p][c] = x;
+    __syncthreads();
+    if (threadIdx.x < D) {
+        float y = 0.f;
+        for (int q = 0; q < PARTS; ++q) y += part[q][threadIdx.x];
+        dw[threadIdx.x] = y;
+    }
+}
+
+template <typename T, int D>
+static int run_bwd_gated(const Params& P, const BwdParams& Q, const GatedBwd& G, hipStream_t st)
+{
+    const unsigned units = (unsigned)(P.B * P.NH);
+    constexpr unsigned blks = D * D / NTS;
+    if (P.nchunks > 1) {
+        // entering states first (o needs them), the reverse aggregates once dO exists
+        hipLaunchKernelGGL((gla_bwd_states_kernel<T, float, D, true, false>), dim3(units * P.nchunks),
+                           dim3(NTS), 0, st, P, Q);
+        hipLaunchKernelGGL((gla_bwd_fold_kernel<D, true, false>), dim3(units * blks), dim3(NTS), 0, st, P, Q);
+    }
+    hipLaunchKernelGGL((gla_bwd_oepi_kernel<T, D>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q, G);
+    if (G.dw)
+        hipLaunchKernelGGL((gla_bwd_dw_kernel<D>), dim3(1), dim3(NDW), 0, st, G.dwp, G.dw,
+                           (int)(units * P.nchunks));
+    if (P.nchunks > 1) {
+        hipLaunchKernelGGL((gla_bwd_states_kernel<T, float, D, false, true>), dim3(units * P.nchunks),
+                           dim3(NTS), 0, st, P, Q);
+        hipLaunchKernelGGL((gla_bwd_fold_kernel<D, false, true>), dim3(units * blks), dim3(NTS), 0, st, P, Q);
+    }
+    hipLaunchKernelGGL((gla_bwd_chunk_kernel<T, float, D>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q);
+    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
+}
+
+template <typename T, typename TD, int D>
 static int run_bwd(const Params& P, const BwdParams& Q, hipStream_t st)
 {
     const unsigned units = (unsigned)(P.B * P.NH);
     if (P.nchunks > 1) {
-        hipLaunchKernelGGL((gla_bwd_states_kernel<T, D>), dim3(units * P.nchunks), dim3(NTS), 0, st, P, Q);
+        hipLaunchKernelGGL((gla_bwd_states_kernel<T, TD, D, true, true>), dim3(units * P.nchunks),
+                           dim3(NTS), 0, st, P, Q);
         constexpr unsigned blks = D * D / NTS;
-        hipLaunchKernelGGL((gla_bwd_fold_kernel<D>), dim3(units * blks), dim3(NTS), 0, st, P, Q);
+        hipLaunchKernelGGL((gla_bwd_fold_kernel<D, true, true>), dim3(units * blks), dim3(NTS), 0, st, P, Q);
     }
-    hipLaunchKernelGGL((gla_bwd_chunk_kernel<T, D>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q);
+    hipLaunchKernelGGL((gla_bwd_chunk_kernel<T, TD, D>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q);
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
 }
 
-template <typename T>
+template <typename T, typename TD>
 static int run_bwd_d(const Params& P, const BwdParams& Q, int d, hipStream_t st)
 {
     switch (d) {
-    case 16: return run_bwd<T, 16>(P, Q, st);
-    case 32: return run_bwd<T, 32>(P, Q, st);
-    case 64: return run_bwd<T, 64>(P, Q, st);
+    case 16: return run_bwd<T, TD, 16>(P, Q, st);
+    case 32: return run_bwd<T, TD, 32>(P, Q, st);
+    case 64: return run_bwd<T, TD, 64>(P, Q, st);
     default: return GLA_EUNSUPPORTED;
     }
 }
@@ -873,9 +1248,23 @@ static int run_bwd_d(const Params& P, const BwdParams& Q, int d, hipStream_t st)
 int launch_bwd(const Params& P, const BwdParams& Q, int dtype, int d, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
-    if (dtype == GLA_F16) return bwd::run_bwd_d<_Float16>(P, Q, d, st);
-    if (dtype == GLA_F32) return bwd::run_bwd_d<float>(P, Q, d, st);
+    if (dtype == GLA_F16) return bwd::run_bwd_d<_Float16, _Float16>(P, Q, d, st);
+    if (dtype == GLA_F32) return bwd::run_bwd_d<float, float>(P, Q, d, st);
     return GLA_EUNSUPPORTED;
+}
+
+int launch_bwd_gated(const Params& P, const BwdParams& Q, const GatedBwd& G, int dtype, int d,
+                     void* stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype != GLA_F16 && dtype != GLA_F32) return GLA_EUNSUPPORTED;
+    const bool h = dtype == GLA_F16;
+    switch (d) {
+    case 16: return h ? bwd::run_bwd_gated<_Float16, 16>(P, Q, G, st) : bwd::run_bwd_gated<float, 16>(P, Q, G, st);
+    case 32: return h ? bwd::run_bwd_gated<_Float16, 32>(P, Q, G, st) : bwd::run_bwd_gated<float, 32>(P, Q, G, st);
+    case 64: return h ? bwd::run_bwd_gated<_Float16, 64>(P, Q, G, st) : bwd::run_bwd_gated<float, 64>(P, Q, G, st);
+    default: return GLA_EUNSUPPORTED;
+    }
 }
 
 }  // namespace gla

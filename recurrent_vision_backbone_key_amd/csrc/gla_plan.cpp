@@ -351,3 +351,59 @@ extern "C" int gla_validate_bwd(const void* q, const void* k, const void* v, con
         if (overlaps(o->workspace, bytes, outs[i].p, outs[i].bytes)) return GLA_EINVAL;
     return GLA_OK;
 }
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+extern "C" int gla_plan_bwd_gated(int dir, int H, int W, const gla_opts* o, gla_bwd_gated_layout* lay)
+{
+    int nchunks = 0;
+    size_t off_r = 0, off_s = 0, bwd_bytes = 0;
+    const int st = gla_plan_bwd(dir, H, W, o, &nchunks, &off_r, &off_s, &bwd_bytes);
+    if (st != GLA_OK) return st;
+    if (isnan(o->eps) || isinf(o->eps) || o->eps < 0.0f) return GLA_EINVAL;
+    const size_t rows = (size_t)o->batch * H * W * o->heads;
+    const size_t units = (size_t)o->batch * o->heads;
+    lay->nchunks = nchunks;
+    lay->off_r = off_r;
+    lay->off_s = off_s;
+    lay->bwd_bytes = bwd_bytes;
+    lay->off_do = align256(bwd_bytes);
+    lay->off_dwp = align256(lay->off_do + rows * o->dk * 4);
+    lay->bytes = lay->off_dwp + units * nchunks * o->dk * 4;
+    return GLA_OK;
+}
+
+extern "C" int gla_validate_bwd_gated(const void* q, const void* k, const void* v, const float* z,
+                                      const void* r, const void* dout, int dir, int H, int W,
+                                      const void* dq, const void* dk, const void* dv, const float* dz,
+                                      const void* dr, const float* dw, const gla_opts* o,
+                                      gla_bwd_gated_layout* lay)
+{
+    if (!o || !q || !k || !v || !z || !r || !dout || !dq || !dk || !dv || !dz || !dr) return GLA_EINVAL;
+    const int st = gla_plan_bwd_gated(dir, H, W, o, lay);
+    if (st != GLA_OK) return st;
+    const size_t es = o->dtype == GLA_F16 ? 2 : 4;
+    const size_t n = (size_t)o->batch * H * W * o->heads * o->dk;
+    const size_t wb = (size_t)o->dk * 4;
+    const Operand ins[7] = {{q, n * es, 16},  {k, n * es, 16},    {v, n * es, 16},
+                            {z, n * 4, 16},   {r, n * es, 16},    {dout, n * es, 16},
+                            {o->norm_weight, wb, 16}};
+    const Operand outs[6] = {{dq, n * es, 16}, {dk, n * es, 16}, {dv, n * es, 16},
+                             {dz, n * 4, 16},  {dr, n * es, 16}, {dw, wb, 16}};
+    for (int i = 0; i < 7; ++i)
+        if (ins[i].p && !aligned(ins[i].p, 16)) return GLA_EINVAL;
+    for (int i = 0; i < 6; ++i) {
+        if (!outs[i].p) continue;
+        if (!aligned(outs[i].p, 16)) return GLA_EINVAL;
+        for (int j = 0; j < 7; ++j)
+            if (ins[j].p && overlaps(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes)) return GLA_EINVAL;
+        for (int j = 0; j < i; ++j)
+            if (outs[j].p && overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes)) return GLA_EINVAL;
+    }
+    if (!o->workspace || o->workspace_bytes < lay->bytes || !aligned(o->workspace, 16)) return GLA_EWORKSPACE;
+    for (int i = 0; i < 7; ++i)
+        if (ins[i].p && overlaps(o->workspace, lay->bytes, ins[i].p, ins[i].bytes)) return GLA_EINVAL;
+    for (int i = 0; i < 6; ++i)
+        if (outs[i].p && overlaps(o->workspace, lay->bytes, outs[i].p, outs[i].bytes)) return GLA_EINVAL;
+    return GLA_OK;
+}

@@ -63,6 +63,22 @@ int gla_validate_bwd(const void* q, const void* k, const void* v, const float* z
                      const float* dz, const gla_opts* opts, int* nchunks, size_t* off_r,
                      size_t* off_s);
 
+// Gated backward: workspace layout (bytes) -- the backward's own part at 0
+// (gla_plan_bwd), then dO (binary32, rows x d) and the dw partial sums
+// (units x nchunks x d binary32); total in bytes.
+typedef struct gla_bwd_gated_layout {
+    size_t bwd_bytes, off_r, off_s, off_do, off_dwp, bytes;
+    int nchunks;
+} gla_bwd_gated_layout;
+
+int gla_plan_bwd_gated(int dir, int H, int W, const gla_opts* opts, gla_bwd_gated_layout* lay);
+
+// Host check of every argument of gla_bwd_gated.
+int gla_validate_bwd_gated(const void* q, const void* k, const void* v, const float* z,
+                           const void* r, const void* dout, int dir, int H, int W, const void* dq,
+                           const void* dk, const void* dv, const float* dz, const void* dr,
+                           const float* dw, const gla_opts* opts, gla_bwd_gated_layout* lay);
+
 // Whether a (dtype, head dim, chunk) instantiation is built (shared-memory
 // footprint of one workgroup within the 160 KiB of a gfx950 CU).
 int gla_config_built(int dtype, int d, int chunk);

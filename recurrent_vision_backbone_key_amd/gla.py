@@ -18,7 +18,8 @@ ALGO_AUTO, ALGO_SINGLE_PASS, ALGO_THREE_PASS = 0, 1, 2
 STATUS = {0: "GLA_OK", 1: "GLA_EINVAL", 2: "GLA_EUNSUPPORTED", 3: "GLA_EWORKSPACE", 4: "GLA_EHIP"}
 EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_workspace_init", "gla_gate_logits",
            "gla_fwd_gate_proj", "gla_workspace_size_gate_proj", "gla_spatial_swiglu",
-           "gla_bwd", "gla_bwd_workspace_size", "gla_status_str", "gla_abi_version")
+           "gla_bwd", "gla_bwd_workspace_size", "gla_bwd_gated", "gla_bwd_gated_workspace_size",
+           "gla_status_str", "gla_abi_version")
 
 
 class GlaOpts(ctypes.Structure):
@@ -96,6 +97,11 @@ def lib():
             [ctypes.POINTER(GlaOpts)]
         h.gla_bwd_workspace_size.restype = ctypes.c_size_t
         h.gla_bwd_workspace_size.argtypes = [ctypes.c_int] * 3 + [ctypes.POINTER(GlaOpts)]
+        h.gla_bwd_gated.restype = ctypes.c_int
+        h.gla_bwd_gated.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 3 + \
+            [ctypes.c_void_p] * 6 + [ctypes.POINTER(GlaOpts)]
+        h.gla_bwd_gated_workspace_size.restype = ctypes.c_size_t
+        h.gla_bwd_gated_workspace_size.argtypes = [ctypes.c_int] * 3 + [ctypes.POINTER(GlaOpts)]
         h.gla_status_str.restype = ctypes.c_char_p
         h.gla_status_str.argtypes = [ctypes.c_int]
         h.gla_abi_version.restype = ctypes.c_int
@@ -246,6 +252,58 @@ def bwd(q, k, v, z, dout, direction, H, W, tau=16.0, scale=None, grads=None, wor
     if st != 0:
         raise GlaError(st, f"gla_bwd failed: {status_str(st)}")
     return dq, dk_, dv_, dz
+
+
+def bwd_gated_workspace_size(direction, H, W, opts: GlaOpts) -> int:
+    return lib().gla_bwd_gated_workspace_size(direction, H, W, ctypes.byref(opts))
+
+
+def bwd_gated(q, k, v, z, r, dout, direction, H, W, norm_weight=None, eps=1e-6, tau=16.0,
+              scale=None, grads=None, want_dw=True, workspace=None, stream=None):
+    """Gradients of the gated forward (include/gla.h: gla_bwd_gated) on CUDA
+    tensors: dout = dL/du for u = SiLU(r) * w * RMSNorm(o).  Returns
+    (dq, dk, dv, dz, dr, dw); dq, dk, dv, dr in q's dtype, dz float32, dw
+    float32 [dv] (None unless want_dw).  ``grads`` may supply the six outputs."""
+    torch = _torch()
+    B, L, NH, dk = q.shape
+    dv = v.shape[3]
+    if q.dtype == torch.float16:
+        dtype = F16
+    elif q.dtype == torch.float32:
+        dtype = F32
+    else:
+        raise TypeError("q must be float16 or float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("r", r), ("dout", dout),
+                    ("norm_weight", norm_weight)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if z.dtype != torch.float32 or (norm_weight is not None and norm_weight.dtype != torch.float32):
+        raise TypeError("gate logits and norm_weight must be float32")
+    for name, t in (("k", k), ("v", v), ("r", r), ("dout", dout)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty(z.shape, dtype=torch.float32, device=q.device), torch.empty_like(r),
+                 torch.empty((dv,), dtype=torch.float32, device=q.device) if want_dw else None)
+    dq, dk_, dv_, dz, dr, dw = grads
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = make_opts(B, NH, dk, dv, dtype, tau, scale, eps,
+                     norm_weight.data_ptr() if norm_weight is not None else 0, stream=stream)
+    need = bwd_gated_workspace_size(direction, H, W, opts)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().gla_bwd_gated(q.data_ptr(), k.data_ptr(), v.data_ptr(), z.data_ptr(), r.data_ptr(),
+                             dout.data_ptr(), direction, H, W, dq.data_ptr(), dk_.data_ptr(),
+                             dv_.data_ptr(), dz.data_ptr(), dr.data_ptr(),
+                             dw.data_ptr() if dw is not None else None, ctypes.byref(opts))
+    if st != 0:
+        raise GlaError(st, f"gla_bwd_gated failed: {status_str(st)}")
+    return dq, dk_, dv_, dz, dr, dw
 
 
 def make_gate(x, w1, w2, bias=None) -> GlaGateProj:

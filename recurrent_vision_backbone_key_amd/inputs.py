@@ -70,6 +70,10 @@ WORKLOADS.update(SWEEP)
 BWD = {
     "bwd640": dict(index=23, kind="bwd", B=8, NH=6, H=40, W=40, dk=64, dv=64, dtype="f16",
                    z=(0.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T), gated=False),
+    # the same through the output gate (the batch640_gated forward's backward)
+    "bwd640_gated": dict(index=24, kind="bwd", B=8, NH=6, H=40, W=40, dk=64, dv=64,
+                         dtype="f16", z=(0.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T),
+                         gated=True),
 }
 WORKLOADS.update(BWD)
 
@@ -107,22 +111,25 @@ def make_inputs(B, NH, H, W, dk, dv, dtype="f16", z=(0.0, 1.0), gated=False, see
     return dict(q=q, k=k, v=v, z=zz, r=r, w=w)
 
 
-def make_bwd_inputs(B, NH, H, W, d, dtype="f16", z=(0.0, 1.0), seed=0, dout_seed=None):
-    """Operands of the backward: q, k, v, z as :func:`make_inputs` (ungated)
-    with PCG64(seed), then dout ~ N(0, 1) [B, L, NH, d] rounded to ``dtype``
-    from PCG64(dout_seed), by default seed + 1."""
-    x = make_inputs(B, NH, H, W, d, d, dtype, z=z, gated=False, seed=seed)
+def make_bwd_inputs(B, NH, H, W, d, dtype="f16", z=(0.0, 1.0), seed=0, dout_seed=None,
+                    gated=False):
+    """Operands of the backward: q, k, v, z (and r, w if ``gated``) as
+    :func:`make_inputs` with PCG64(seed), then dout ~ N(0, 1) [B, L, NH, d]
+    rounded to ``dtype`` from PCG64(dout_seed), by default seed + 1 (dL/do,
+    or dL/du when gated)."""
+    x = make_inputs(B, NH, H, W, d, d, dtype, z=z, gated=gated, seed=seed)
     rng = np.random.default_rng(seed + 1 if dout_seed is None else dout_seed)
     x["dout"] = rng.standard_normal((B, H * W, NH, d)).astype(np_dtype(dtype))
     return x
 
 
-def make_bwd_inputs_device(B, NH, H, W, d, dtype="f16", z=(0.0, 1.0), seed=0, device="cuda"):
+def make_bwd_inputs_device(B, NH, H, W, d, dtype="f16", z=(0.0, 1.0), seed=0, device="cuda",
+                           gated=False):
     """Same distributions as :func:`make_bwd_inputs`, drawn on the device with
     seeded torch generators (timing inputs)."""
     import torch
 
-    x = make_inputs_device(B, NH, H, W, d, d, dtype, z=z, gated=False, seed=seed, device=device)
+    x = make_inputs_device(B, NH, H, W, d, d, dtype, z=z, gated=gated, seed=seed, device=device)
     gen = torch.Generator(device=device)
     gen.manual_seed(seed + 1)
     dt = {"f16": torch.float16, "f32": torch.float32}[dtype]
@@ -159,7 +166,8 @@ def workload_inputs(name: str, call: int = 0, **overrides):
         # output gradient from its own stream (seed + 500)
         return make_bwd_inputs(spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"],
                                spec["dtype"], spec["z"], seed=1000 * spec["index"] + call,
-                               dout_seed=1000 * spec["index"] + 500 + call)
+                               dout_seed=1000 * spec["index"] + 500 + call,
+                               gated=spec["gated"])
     x = make_inputs(spec["B"], spec["NH"], spec["H"], spec["W"], spec["dk"], spec["dv"],
                     spec["dtype"], spec["z"], spec["gated"], seed=1000 * spec["index"] + call)
     gp = spec.get("gate_proj")

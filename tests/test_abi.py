@@ -37,7 +37,7 @@ def test_only_declared_functions_are_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert gla.abi_version() == 4
+    assert gla.abi_version() == 5
     for s, name in gla.STATUS.items():
         assert gla.status_str(s).startswith(name)
     assert "unknown" in gla.status_str(99)

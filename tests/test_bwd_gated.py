@@ -1,0 +1,169 @@
+"""Backward of the gated forward (paper "GTR: Gated Token Recurrence for
+Efficient Dense Prediction", Section 2.1 output-gate paragraph: u = SiLU(r) *
+w * RMSNorm(o), differentiated, then the recurrence's backward).
+
+CPU part: argument checks and workspace sizes of gla_bwd_gated through the C
+ABI (fake addresses, every case rejected before any launch).
+GPU part: dq, dk, dv, dz, dr, dw against the fp64 oracle on the same seeded
+inputs: small shapes with and without a norm weight, every direction, the
+full gated batch shape element by element, and bitwise-repeatable dw.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from recurrent_vision_backbone_key_amd import gla
+from recurrent_vision_backbone_key_amd.inputs import WORKLOADS, make_bwd_inputs, workload_inputs
+
+A = 1 << 32
+MB = 1 << 26
+
+
+def _call(q=A, k=A + MB, v=A + 2 * MB, z=A + 3 * MB, r=A + 4 * MB, dout=A + 5 * MB, direction=0,
+          H=20, W=20, dq=A + 6 * MB, dk=A + 7 * MB, dv=A + 8 * MB, dz=A + 9 * MB, dr=A + 10 * MB,
+          dw=A + 11 * MB, opts=None):
+    opts = opts or gla.make_opts(1, 2, 64, 64, gla.F16)
+    return gla.lib().gla_bwd_gated(q, k, v, z, r, dout, direction, H, W, dq, dk, dv, dz, dr, dw,
+                                   ctypes.byref(opts))
+
+
+def _ok_opts(**kw):
+    o = gla.make_opts(1, 2, 64, 64, kw.pop("dtype", gla.F16), **kw)
+    o.workspace = A + 20 * MB
+    o.workspace_bytes = gla.bwd_gated_workspace_size(0, 20, 20, o)
+    return o
+
+
+def test_bwd_gated_workspace_sizes():
+    for B, NH, H, W, d in ((1, 1, 8, 8, 16), (2, 3, 10, 13, 32), (8, 6, 40, 40, 64)):
+        o = gla.make_opts(B, NH, d, d, gla.F16)
+        need = gla.bwd_gated_workspace_size(0, H, W, o)
+        # the backward's own part, then o and do in the storage type
+        assert need >= gla.bwd_workspace_size(0, H, W, o) + 2 * B * H * W * NH * d * 2
+    assert gla.bwd_gated_workspace_size(0, 20, 20, gla.make_opts(1, 2, 128, 128, gla.F16)) == 0
+    assert gla.bwd_gated_workspace_size(0, 20, 20, gla.make_opts(1, 2, 64, 32, gla.F16)) == 0
+    assert gla.bwd_gated_workspace_size(0, 20, 20, gla.make_opts(1, 2, 64, 64, gla.F16, eps=-1.0)) == 0
+
+
+def test_bwd_gated_argument_checks():
+    h = gla.lib()
+    assert h.gla_bwd_gated(A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, 0, 20, 20,
+                           A + 6 * MB, A + 7 * MB, A + 8 * MB, A + 9 * MB, A + 10 * MB,
+                           A + 11 * MB, None) == 1
+    for name in ("q", "k", "v", "z", "r", "dout", "dq", "dk", "dv", "dz", "dr"):
+        assert _call(**{name: None}, opts=_ok_opts()) == 1, name
+    assert _call(direction=4, opts=_ok_opts()) == 1
+    assert _call(opts=gla.make_opts(1, 2, 128, 128, gla.F16)) == 2
+    assert _call(r=A + 4 * MB + 8, opts=_ok_opts()) == 1        # r misaligned
+    assert _call(dr=A + 5 * MB + 64, opts=_ok_opts()) == 1      # dr over dout
+    assert _call(dw=A + 10 * MB + 1024, opts=_ok_opts()) == 1   # dw over dr
+    assert _call(dw=A + 4 * MB, opts=_ok_opts()) == 1           # dw over r
+    o = _ok_opts()
+    o.norm_weight = A + 9 * MB + 256                              # w under dz
+    assert _call(opts=o) == 1
+    assert _call(opts=gla.make_opts(1, 2, 64, 64, gla.F16)) == 3  # no workspace
+    o = _ok_opts()
+    o.workspace_bytes -= 16
+    assert _call(opts=o) == 3
+    o = _ok_opts()
+    o.workspace = A + 10 * MB + 4096                              # workspace over dr
+    assert _call(opts=o) == 1
+
+
+# ------------------------------------------------------------------- GPU
+
+def _dev(a, torch):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    return t
+
+
+NAMES = ("dq", "dk", "dv", "dz", "dr", "dw")
+TOL = {"f32": 2e-5, "f16": 2e-3}
+
+
+def _run(x, direction, H, W, with_w, torch):
+    d = {n: _dev(x[n], torch) for n in ("q", "k", "v", "z", "r", "dout")}
+    w = _dev(x["w"], torch) if with_w else None
+    nan = float("nan")
+    grads = (torch.full_like(d["q"], nan), torch.full_like(d["k"], nan),
+             torch.full_like(d["v"], nan),
+             torch.full(d["z"].shape, nan, dtype=torch.float32, device="cuda"),
+             torch.full_like(d["r"], nan),
+             torch.full((x["v"].shape[3],), nan, dtype=torch.float32, device="cuda"))
+    need = gla.bwd_gated_workspace_size(
+        direction, H, W, gla.make_opts(x["q"].shape[0], x["q"].shape[2], x["q"].shape[3],
+                                       x["q"].shape[3], gla.F16 if x["q"].dtype == np.float16
+                                       else gla.F32))
+    ws = torch.full((max(need, 16),), 0xA5, dtype=torch.uint8, device="cuda")
+    out = gla.bwd_gated(d["q"], d["k"], d["v"], d["z"], d["r"], d["dout"], direction, H, W,
+                        norm_weight=w, grads=grads, workspace=ws)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+def _check(name, x, direction, H, W, tol, torch, with_w=True):
+    B, L, NH, d = x["q"].shape
+    print(f"[case] bwd_gated {name} {x['q'].dtype} B={B} NH={NH} H={H} W={W} d={d} "
+          f"dir={direction} w={with_w}", flush=True)
+    got = _run(x, direction, H, W, with_w, torch)
+    ref = oracle.bwd_gated(x["q"], x["k"], x["v"], x["z"], x["r"], x["w"] if with_w else None,
+                           x["dout"], direction, H, W)
+    # dz's terms cancel; its rounding scales with |q (.) dq| / 16 (as for gla_bwd)
+    dz_floor = float(np.max(np.abs(x["q"].astype(np.float64) * ref[0]))) / 16.0
+    errs = {}
+    for n, g, r in zip(NAMES, got, ref):
+        assert np.all(np.isfinite(g)), f"{name}: {n} not finite"
+        den = float(np.max(np.abs(r)))
+        if n == "dz":
+            den = max(den, dz_floor)
+        errs[n] = float(np.max(np.abs(g.astype(np.float64) - r)) / den)
+    print(f"[parity] bwd_gated {name}: " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()),
+          flush=True)
+    for n, e in errs.items():
+        assert e <= tol, f"{name}: {n} {e:.3e} > {tol:.0e}"
+    return got
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("B,NH,H,W,d", [
+    (1, 1, 8, 8, 16),
+    (1, 2, 10, 13, 32),
+    (2, 3, 20, 20, 64),
+])
+@pytest.mark.parametrize("direction", (0, 1, 2, 3))
+def test_bwd_gated_small(torch, dtype, B, NH, H, W, d, direction):
+    x = make_bwd_inputs(B, NH, H, W, d, dtype, seed=3 * H + W + d, gated=True)
+    _check("small", x, direction, H, W, TOL[dtype], torch)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_bwd_gated_no_weight(torch, dtype):
+    x = make_bwd_inputs(2, 2, 12, 10, 64, dtype, seed=77, gated=True)
+    _check("no weight", x, 2, 12, 10, TOL[dtype], torch, with_w=False)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("call", range(4))
+def test_bwd640_gated(torch, call):
+    s = WORKLOADS["bwd640_gated"]
+    x = workload_inputs("bwd640_gated", call=call)
+    _check("bwd640_gated", x, s["dirs"][call], s["H"], s["W"], TOL[s["dtype"]], torch)
+
+
+@pytest.mark.gpu
+def test_bwd_gated_deterministic(torch):
+    x = make_bwd_inputs(2, 3, 20, 20, 64, "f16", seed=5, gated=True)
+    a = _run(x, 1, 20, 20, True, torch)
+    b = _run(x, 1, 20, 20, True, torch)
+    for n, u, w in zip(NAMES, a, b):
+        assert np.array_equal(u.view(np.uint8), w.view(np.uint8)), n
