@@ -362,9 +362,9 @@ def bench_bwd(args, spec, name):
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
                      "traffic": load_traffic(name, kernel_family(spec)),
                      "kernel": ("gla_bwd_states_kernel<local states> + gla_bwd_fold_kernel<forward> + "
-                                "gla_bwd_oepi_kernel (o and the output gate's backward) + "
-                                "gla_bwd_dw_kernel + gla_bwd_states_kernel<reverse> + "
-                                "gla_bwd_fold_kernel<reverse> + gla_bwd_chunk_kernel"
+                                "gla_bwd_oepi_kernel (o, the output gate's backward, reverse "
+                                "aggregates) + gla_bwd_dw_kernel + gla_bwd_fold_kernel<reverse> + "
+                                "gla_bwd_chunk_kernel"
                                 if gated else
                                 "gla_bwd_states_kernel + gla_bwd_fold_kernel + gla_bwd_chunk_kernel") +
                                " (figures for the whole call)",

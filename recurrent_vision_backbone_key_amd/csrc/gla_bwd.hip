@@ -906,12 +906,14 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
     constexpr int SD = Y::SD, NTL = D / 16, KS = D / 4;
     constexpr int CT = NTL >= 2 ? NTL / 2 : 1;
     __shared__ __attribute__((aligned(16))) float lds[Y::WORDS];
-    float* sX = lds + Y::P;      // row sums of the two halves: [2 sums][2 halves][C]
+    float* sQB = lds + Y::P;     // q (.) 2^b (b from the chunk start): the reverse aggregate's operand
+    float* sDO = lds + Y::DO;    // dO of the chunk (binary32)
     float* sV = lds + Y::V;
     float* sKT = lds + Y::KT;
     float* sQH = lds + Y::QH;
     float* sSS = lds + Y::SS;
     float* sRed = lds + Y::RR;   // dw partial sums [NS][D]
+    float* sX = sRed + NS * D;   // row sums of the two halves [2 sums][2 halves][C]
     float* sB = lds + Y::BB;
     float* sCC = lds + Y::CC;
     float* sE = lds + Y::EE;
@@ -1027,6 +1029,7 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
             const float b = br[u] + off;
             sQH[t * SD + gch] = xq[u] * exp2_fast(b - off);
             sKT[t * SD + gch] = xk[u] * exp2_fast(ci - b);
+            sQB[t * SD + gch] = xq[u] * exp2_fast(b);  // <= 1
             sB[t * SD + gch] = b;
         }
     }
@@ -1139,6 +1142,7 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
             const float drv = du * wv[cl] * o * rho * sig * (1.0f + r * (1.0f - sig));
             dwl[cl] += du * sr * o * rho;
             const int row = rowe[e];
+            if (cols) sDO[t * SD + 16 * (ct0 + cl) + l16] = dov;  // rows past the end: 0
             if (cols && row >= 0) {
                 const size_t idx = (size_t)row * D + 16 * (ct0 + cl) + l16;
                 ((float*)Q.dout)[idx] = dov;
@@ -1160,6 +1164,32 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
 #pragma unroll
         for (int m = 0; m < NS; ++m) x += sRed[m * D + col];
         G.dwp[(size_t)blockIdx.x * D + col] = x;
+    }
+    // reverse aggregate of this chunk from the dO just formed (the states
+    // kernel's other half): slot c - 1 of ws_r <- (s (q (.) 2^b)^T dO, B)
+    if (c >= 1) {
+        float* dst = Q.ws_r + ((size_t)unit * (P.nchunks - 1) + (c - 1)) * slot_floats;
+        if (tid < D) dst[D * D + tid] = sCC[NS * D + tid];  // c_3 = the chunk's decay
+        // wavefront w: key-channel tile a = w / 2, value tiles of half w % 2
+        constexpr int VT = NTL >= 2 ? NTL / 2 : 1;
+        const int a = wave >> 1, v0 = (wave & 1) * VT;
+        if (a < NTL && v0 < NTL) {
+            float4v acc[VT];
+#pragma unroll
+            for (int vb = 0; vb < VT; ++vb) acc[vb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int ks = 0; ks < C / 4; ++ks) {
+                const int u = 4 * ks + g;
+                const float x = sQB[u * SD + 16 * a + l16];
+#pragma unroll
+                for (int vb = 0; vb < VT; ++vb) acc[vb] = mma(x, sDO[u * SD + 16 * (v0 + vb) + l16], acc[vb]);
+            }
+#pragma unroll
+            for (int vb = 0; vb < VT; ++vb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[(size_t)(16 * a + 4 * g + e) * D + 16 * (v0 + vb) + l16] = s * acc[vb][e];
+        }
     }
 }
 
@@ -1200,7 +1230,8 @@ static int run_bwd_gated(const Params& P, const BwdParams& Q, const GatedBwd& G,
     const unsigned units = (unsigned)(P.B * P.NH);
     constexpr unsigned blks = D * D / NTS;
     if (P.nchunks > 1) {
-        // entering states first (o needs them), the reverse aggregates once dO exists
+        // entering states first (o needs them); the o kernel leaves the reverse
+        // aggregates (dO exists there)
         hipLaunchKernelGGL((gla_bwd_states_kernel<T, float, D, true, false>), dim3(units * P.nchunks),
                            dim3(NTS), 0, st, P, Q);
         hipLaunchKernelGGL((gla_bwd_fold_kernel<D, true, false>), dim3(units * blks), dim3(NTS), 0, st, P, Q);
@@ -1209,11 +1240,8 @@ static int run_bwd_gated(const Params& P, const BwdParams& Q, const GatedBwd& G,
     if (G.dw)
         hipLaunchKernelGGL((gla_bwd_dw_kernel<D>), dim3(1), dim3(NDW), 0, st, G.dwp, G.dw,
                            (int)(units * P.nchunks));
-    if (P.nchunks > 1) {
-        hipLaunchKernelGGL((gla_bwd_states_kernel<T, float, D, false, true>), dim3(units * P.nchunks),
-                           dim3(NTS), 0, st, P, Q);
+    if (P.nchunks > 1)
         hipLaunchKernelGGL((gla_bwd_fold_kernel<D, false, true>), dim3(units * blks), dim3(NTS), 0, st, P, Q);
-    }
     hipLaunchKernelGGL((gla_bwd_chunk_kernel<T, float, D>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q);
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
 }
