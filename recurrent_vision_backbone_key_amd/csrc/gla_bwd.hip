@@ -801,12 +801,17 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             if (j == si && pairwise) {
                 a = diag_scores<T, D>(P, sRows, sB, si, g, l16);
             } else {
+                // the block's B operands first (all factor loads in flight
+                // together), then the two MFMA chains
+                float kb[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) kb[ks] = kh[ks] * E(j, si, 4 * ks + g);
                 float4v a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ks += 2) {
                     const int ch = 4 * ks + g;
-                    a = mma(sQH[(16 * j + l16) * SD + ch], kh[ks] * E(j, si, ch), a);
-                    a1 = mma(sQH[(16 * j + l16) * SD + ch + 4], kh[ks + 1] * E(j, si, ch + 4), a1);
+                    a = mma(sQH[(16 * j + l16) * SD + ch], kb[ks], a);
+                    a1 = mma(sQH[(16 * j + l16) * SD + ch + 4], kb[ks + 1], a1);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1047,13 +1052,18 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
             if (j == si && pairwise) {
                 a = diag_scores_out<T, D>(P, sRows, sB, si, g, l16);
             } else {
+                // the block's A operands first (all loads in flight together),
+                // then the two MFMA chains
+                float ka[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    ka[ks] = sKT[(16 * j + l16) * SD + 4 * ks + g] * E(si, j, 4 * ks + g);
                 float4v a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ks += 2) {
                     const int ch = 4 * ks + g;
-                    a = mma(sKT[(16 * j + l16) * SD + ch] * E(si, j, ch), sQH[(16 * si + l16) * SD + ch], a);
-                    a1 = mma(sKT[(16 * j + l16) * SD + ch + 4] * E(si, j, ch + 4),
-                             sQH[(16 * si + l16) * SD + ch + 4], a1);
+                    a = mma(ka[ks], sQH[(16 * si + l16) * SD + ch], a);
+                    a1 = mma(ka[ks + 1], sQH[(16 * si + l16) * SD + ch + 4], a1);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
