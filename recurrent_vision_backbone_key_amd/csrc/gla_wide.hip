@@ -283,6 +283,12 @@ void gla_wide_kernel(Params P)
         // ================= row role: gate stage =================
         float bl[16];
         gate_prefix(raw, P.inv_tau, bl);
+        // The aggregate pass has too little work per chunk to hide a load
+        // issued late in it: each input of its next chunk is fetched as soon
+        // as this chunk's copy is consumed, from a row index of its own.
+        const bool pf = (c + 1 < c_end);
+        const int arow = (AGG && pf) ? scan_row(P, unit, (c + 1) * C + tl) : -1;
+        if (AGG && pf) load_part<PZ>(raw, P, arow, cb);
         if (l16 == 15) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -300,6 +306,7 @@ void gla_wide_kernel(Params P)
             *(u32x4*)(sV + tl * SH + cb + 32 * kb) = raw.v[kb];
             if (gated) *(u32x4*)(sR + tl * SH + cb + 32 * kb) = raw.r[kb];
         }
+        if (AGG && pf) load_part<PV>(raw, P, arow, cb);
 
         // ---- per-channel factors of this wave's sub-chunk, one channel per lane
         float* fac = sFac + wave * NFAC * 64;
@@ -404,14 +411,15 @@ void gla_wide_kernel(Params P)
                 if (lane == 0) sMisc[wave] = ww ? 1 : 0;
             }
         }
+        if (AGG && pf) load_part<PK>(raw, P, arow, cb);
         const int myrow = sRows[buf * C + tl];
         __syncthreads();  // (2) operands of every wave
 
-        // the next chunk's inputs (row table written after (1)) are fetched in
-        // parts spread over this chunk, so the loads stream while it computes
-        const bool pf = (c + 1 < c_end);
+        // output pass: the next chunk's inputs (row table written after (1))
+        // are fetched in parts spread over this chunk, so the loads stream
+        // while it computes
         const int nrow = pf ? sRows[(buf ^ 1) * C + tl] : -1;
-        if (pf) load_part<PZ>(raw, P, nrow, cb);
+        if (!AGG && pf) load_part<PZ>(raw, P, nrow, cb);
 
         // value fragments, shared by the value product and the state update:
         // lane (g, l16) holds v[32p + 8g + e][16 wave + l16]
@@ -540,10 +548,8 @@ void gla_wide_kernel(Params P)
         }
 
         // ================= state role: S = Diag(2^{chunk total}) S + k-hat^T v =================
-        if (AGG && pf) load_part<PK>(raw, P, nrow, cb);
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
-            if (AGG && pf && a == 4) load_part<PV>(raw, P, nrow, cb);
             const float4v dec = *(const float4v*)(sDec + 16 * a + 4 * g);
             S[a] = S[a] * dec;
 #pragma unroll
