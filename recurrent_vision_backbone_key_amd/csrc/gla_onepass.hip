@@ -124,6 +124,12 @@ __device__ __forceinline__ void st_u(unsigned* p, unsigned v)
 // across the per-XCD L2s); when every workgroup of a scan runs on one XCD
 // (LOCAL), the default policy, which leaves the line in that XCD's L2 where
 // the sc1 loads of the same XCD find it (about half the round-trip latency).
+// Segment aggregates are the exception: they are written through in both
+// modes.  Measured on MI355X, write-back aggregates kept the kernel running
+// 2-3 us after its last workgroup had ended (one 1600-token frame with 6
+// heads: 18.7 us per call, 16.6 us with write-through aggregates, though the
+// exchange inside the workgroups takes about 0.4 us longer); inclusive states
+// gain nothing from it and keep the local policy.
 template <bool LOCAL> struct Pol {
     static constexpr int kLoad = 16;
     static constexpr int kStore = LOCAL ? 0 : 16;
@@ -681,9 +687,10 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         const unsigned agg_bytes = (unsigned)(aggf * 4), st_bytes = (unsigned)(D * D * 4);
         if (seg > 0 && !last) {
             const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
-            st_x4<LOCAL>(r, off0, l0);
-            st_x4<LOCAL>(r, off1, l1);
-            if (tid < D / 4) st_x4<LOCAL>(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
+            // aggregates are written through in every mode (see Pol)
+            st_x4<false>(r, off0, l0);
+            st_x4<false>(r, off1, l1);
+            if (tid < D / 4) st_x4<false>(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
             wait_mem();
             __syncthreads();
             if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 1u);
