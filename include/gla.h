@@ -110,8 +110,8 @@ enum gla_algorithm { GLA_ALGO_AUTO = 0, GLA_ALGO_SINGLE_PASS = 1, GLA_ALGO_THREE
  *                out = o (no gate, no RMSNorm)
  *   opts         sizes, dtype, stream, workspace (must not be NULL)
  * The workspace must hold gla_workspace_size() bytes when that is nonzero.
- * It holds per-segment fp32 states and, for the single pass, a ticket
- * counter, per-scan counters and per-segment flags.  Before its first use
+ * It holds per-segment fp32 states and, for the single pass, ticket
+ * counters, an error word and per-segment flags.  Before its first use
  * (and after any call that did not complete) it must be cleared with
  * gla_workspace_init(); every completed call leaves the counters and flags
  * cleared again.  Calls that share a workspace must be ordered on one stream.

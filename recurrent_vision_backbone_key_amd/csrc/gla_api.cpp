@@ -33,7 +33,7 @@ int run_fwd(gla::Params& P, const void* q, const void* k, const void* v, int dir
     P.scale = plan.scale;
     P.inv_tau = 1.0f / plan.tau;
     P.eps = plan.eps;
-    P.ticket = P.err = P.done = P.flags = nullptr;
+    P.ticket = P.err = P.flags = nullptr;
     P.xcd_local = plan.xcd_local;
     P.xcd_tasks = plan.xcd_tasks;
     P.agg = P.incl = nullptr;
@@ -41,7 +41,6 @@ int run_fwd(gla::Params& P, const void* q, const void* k, const void* v, int dir
         char* ws = (char*)opts->workspace;
         P.ticket = (unsigned*)ws;
         P.err = (unsigned*)ws + 1;
-        P.done = (unsigned*)(ws + plan.off_done);
         P.flags = (unsigned*)(ws + plan.off_flags);
         P.agg = (float*)(ws + plan.off_agg);
         P.incl = (float*)(ws + plan.off_incl);
@@ -183,7 +182,7 @@ void bwd_params(const void* q, const void* k, const void* v, const float* gate_l
     P.scale = opts->scale > 0.0f ? opts->scale : (float)(1.0 / sqrt((double)opts->dk));
     P.inv_tau = 1.0f / (opts->tau > 0.0f ? opts->tau : 16.0f);
     P.eps = 0.0f;
-    P.ticket = P.err = P.done = P.flags = nullptr;
+    P.ticket = P.err = P.flags = nullptr;
     P.agg = P.incl = nullptr;
     P.xcd_local = 0;
     P.xcd_tasks = 0;

@@ -23,7 +23,6 @@ struct Params {
     // (scan, segment), segment aggregates and inclusive states
     unsigned* ticket;   // word 0: ticket counter; words 16 (1 + x): counter of XCD x
     unsigned* err;
-    unsigned* done;     // [units]: workgroups of the scan past their look-back
     unsigned* flags;    // [units][nseg]: 0 none, 1 aggregate, 2 inclusive
     float* agg;         // [units][nseg][DK*DV + DK]
     float* incl;        // [units][nseg][DK*DV]

@@ -18,7 +18,9 @@
 //           that fold, so the bits do not depend on which predecessor was
 //           found (deterministic).  Workgroups only wait on smaller tickets.
 //  phase 3  adds (q (.) 2^{b from segment start}) S_in to the kept partial
-//           outputs, applies the epilogue and stores every row.
+//           outputs, applies the epilogue and stores every row; the scan's
+//           last segment then waits until every earlier one has finished
+//           its exchange and clears the scan's flags for the next call.
 //
 // Work split inside a chunk: wavefront w handles the 16-token sub-chunk
 // i = w & 3 and the half h = w >> 2 of the channels.  A lane holds 8 channels
@@ -784,14 +786,6 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             __syncthreads();
             if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 2u);
         }
-        // the last workgroup of this scan to get here clears its flags
-        if (tid == 0) {
-            const unsigned done = atomicAdd(P.done + unit, 1u);
-            if (done == (unsigned)P.nseg - 1u) {
-                for (int s = 0; s < P.nseg; ++s) st_flag<LOCAL>(flags, P.nseg, s, 0u);
-                st_u(P.done + unit, 0u);
-            }
-        }
     }
     __syncthreads();
 
@@ -869,9 +863,31 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             if (t >= 0) *(half4*)((_Float16*)P.out + (size_t)t * D + 32 * h + 16 * m + 4 * g) = hv;
         }
     }
+
+    // The scan's last segment leaves its flags zero for the next call.  Every
+    // earlier segment sets its flag to 2 only after its look-back and fold
+    // have read all they need, so once every flag reads 2 the exchange is
+    // over; each lane then clears the one flag it read (the clear is ordered
+    // after the store it saw).  This runs after the outputs, where the other
+    // segments have long finished.
+    if (P.nseg > 1 && seg == P.nseg - 1 && wave == 0) {
+        unsigned* flags = P.flags + (size_t)unit * P.nseg;
+        const bool mine = lane < seg;  // segments 0 .. nseg-2 (at most 64)
+        unsigned spins = 0;
+        for (;;) {
+            const unsigned f = mine ? ld_flag<LOCAL>(flags, P.nseg, lane) : 2u;
+            if (__all(f == 2u)) break;
+            if (++spins > (1u << 22)) {
+                if (lane == 0) atomicOr(P.err, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (mine) st_flag<LOCAL>(flags, P.nseg, lane, 0u);
+    }
 }
 
-// Zero-fills the single-pass workspace header, counters and flags.
+// Zero-fills the single-pass workspace header and flags.
 __global__ __launch_bounds__(256) void gla_onepass_init(unsigned* words, size_t n)
 {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)

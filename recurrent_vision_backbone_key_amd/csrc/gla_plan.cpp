@@ -63,7 +63,7 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     plan->onepass = 0;
     plan->proj_fused = 0;
     plan->off_z = 0;
-    plan->off_done = plan->off_flags = plan->off_agg = plan->off_incl = 0;
+    plan->off_flags = plan->off_agg = plan->off_incl = 0;
 
     // Single pass: binary16, d = 64, 64-token chunks; segments of at most
     // kOnePassMaxChunks chunks, at most 65 segments per scan (one wavefront
@@ -107,8 +107,7 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
             plan->nseg = nseg;
             plan->xcd_local = local ? 1 : 0;
             plan->xcd_tasks = local ? (int)(upx * nseg) : 0;
-            plan->off_done = kOnePassHeader;
-            plan->off_flags = plan->off_done + (((size_t)units * 4 + 255) / 256) * 256;
+            plan->off_flags = kOnePassHeader;
             plan->off_agg = plan->off_flags + ((nflag * 4 + 255) / 256) * 256;
             plan->off_incl = plan->off_agg + nflag * ((size_t)64 * 64 + 64) * 4;
             plan->workspace_bytes = plan->off_incl + nflag * (size_t)64 * 64 * 4;

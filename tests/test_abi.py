@@ -137,13 +137,13 @@ def test_workspace_formula_three_pass():
 
 
 def test_workspace_formula_single_pass():
-    """1024-byte header (ticket counters, error word), one counter per scan and
-    one flag per (scan, segment), each rounded to 256 bytes, then an aggregate
-    (dk*dv + dk fp32) and an inclusive state (dk*dv fp32) per (scan, segment)."""
+    """1024-byte header (ticket counters, error word), one flag per (scan,
+    segment) rounded to 256 bytes, then an aggregate (dk*dv + dk fp32) and an
+    inclusive state (dk*dv fp32) per (scan, segment)."""
     o = _opts(batch=2, heads=3, segment_chunks=4, algorithm=gla.ALGO_SINGLE_PASS)
     nseg = -(-25 // 4)
     n = 6 * nseg
-    want = 1024 + 256 + -(-n * 4 // 256) * 256 + n * (64 * 64 + 64) * 4 + n * 64 * 64 * 4
+    want = 1024 + -(-n * 4 // 256) * 256 + n * (64 * 64 + 64) * 4 + n * 64 * 64 * 4
     assert gla.workspace_size(1, 40, 40, 64, o) == want
 
 
