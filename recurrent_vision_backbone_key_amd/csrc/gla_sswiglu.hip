@@ -42,8 +42,13 @@ template <typename T> struct V8;
 template <> struct V8<_Float16> {
     u32x4 x;
     static __device__ __forceinline__ V8 load(const _Float16* p) { return V8{*(const u32x4*)p}; }
+    static __device__ __forceinline__ V8 load_nt(const _Float16* p)
+    {
+        return V8{__builtin_nontemporal_load((const u32x4*)p)};
+    }
     static __device__ __forceinline__ V8 zero() { return V8{u32x4{0u, 0u, 0u, 0u}}; }
     __device__ __forceinline__ void store(_Float16* p) const { *(u32x4*)p = x; }
+    __device__ __forceinline__ void store_nt(_Float16* p) const { __builtin_nontemporal_store(x, (u32x4*)p); }
     __device__ __forceinline__ float get(int e) const { return (float)__builtin_bit_cast(half8, x)[e]; }
     static __device__ __forceinline__ V8 from(const float (&f)[8])
     {
@@ -59,11 +64,20 @@ template <> struct V8<float> {
     {
         return V8{*(const float4v*)p, *(const float4v*)(p + 4)};
     }
+    static __device__ __forceinline__ V8 load_nt(const float* p)
+    {
+        return V8{__builtin_nontemporal_load((const float4v*)p), __builtin_nontemporal_load((const float4v*)(p + 4))};
+    }
     static __device__ __forceinline__ V8 zero() { return V8{float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}}; }
     __device__ __forceinline__ void store(float* p) const
     {
         *(float4v*)p = x0;
         *(float4v*)(p + 4) = x1;
+    }
+    __device__ __forceinline__ void store_nt(float* p) const
+    {
+        __builtin_nontemporal_store(x0, (float4v*)p);
+        __builtin_nontemporal_store(x1, (float4v*)(p + 4));
     }
     __device__ __forceinline__ float get(int e) const { return e < 4 ? x0[e] : x1[e - 4]; }
     static __device__ __forceinline__ V8 from(const float (&f)[8])
@@ -111,8 +125,10 @@ __global__ __launch_bounds__(NT) void gla_sswiglu_kernel(const T* __restrict__ a
     const int gy = y0 + ty, gx = x0 + tx;
     const bool live = cc < C && gy < H && gx < W;  // C is a multiple of 8
     const size_t row = img + (size_t)(live ? gy * W + gx : 0);
-    // the gate of this thread's token, in flight during the staging
-    const V8<T> av = live ? V8<T>::load(a + row * ld_in + cc) : V8<T>::zero();
+    // the gate of this thread's token, in flight during the staging; the gate
+    // and the output are touched once, so both use the non-temporal (streaming)
+    // policy (measured: 36.3 -> 32.1 us on 8 x 40x40 tokens x 1536 channels)
+    const V8<T> av = live ? V8<T>::load_nt(a + row * ld_in + cc) : V8<T>::zero();
 
     // ---- stage v over the tile and its halo (zero outside the grid)
     for (int i = tid; i < HH * HW * CG; i += NT) {
@@ -153,7 +169,7 @@ __global__ __launch_bounds__(NT) void gla_sswiglu_kernel(const T* __restrict__ a
     float hv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) hv[e] = silu(av.get(e)) * acc[e];
-    V8<T>::from(hv).store(out + row * ld_out + cc);
+    V8<T>::from(hv).store_nt(out + row * ld_out + cc);
 }
 
 }  // namespace sswiglu
