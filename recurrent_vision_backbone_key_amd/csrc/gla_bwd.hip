@@ -163,10 +163,11 @@ template <> struct Raw8<float> {
     }
 };
 
+// Gradient outputs are written once and not read back: non-temporal stores.
 template <typename T>
 __device__ __forceinline__ void store1(T* base, size_t idx, float x)
 {
-    base[idx] = (T)x;
+    __builtin_nontemporal_store((T)x, base + idx);
 }
 
 // ---------------------------------------------------------------------------
@@ -887,7 +888,7 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             const int row = sRows[16 * gi + u];
             // 1 - sigmoid(z) as sigmoid(-z)
             const float nsig = rcp_fast(1.0f + exp2_fast(zz[u] * kLog2e));
-            if (row >= 0) Q.dz[(size_t)row * D + gch] = (br[u] + later) * nsig * P.inv_tau;
+            if (row >= 0) store1<float>(Q.dz, (size_t)row * D + gch, (br[u] + later) * nsig * P.inv_tau);
         }
     }
 }
