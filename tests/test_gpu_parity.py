@@ -326,6 +326,40 @@ def test_workspace_reused_across_shapes(torch):
         assert int(ws[4:8].cpu().numpy().view(np.uint32)[0]) == 0
 
 
+@pytest.mark.parametrize("B,NH,H,W,seg", [
+    (2, 3, 40, 40, 1),   # 25 one-chunk segments per scan
+    (1, 2, 65, 64, 1),   # 65 segments: the last clears 64 flags, one per lane
+    (3, 4, 30, 40, 2),   # two-chunk segments, ragged last segment
+])
+def test_single_pass_leaves_workspace_clear(torch, B, NH, H, W, seg):
+    """Every completed single-pass call leaves the ticket counters, the error
+    word and every segment flag at zero (the scan's last segment clears its
+    flags once every earlier segment has finished its exchange), so calls
+    back to back need no re-initialisation: checked word by word after each of
+    six calls on one workspace, with the outputs of the first four against the
+    oracle."""
+    from recurrent_vision_backbone_key_amd import gla
+    opts = gla.make_opts(B, NH, 64, 64, gla.F16, segment_chunks=seg,
+                         algorithm=gla.ALGO_SINGLE_PASS)
+    need = max(gla.workspace_size(d, H, W, 64, opts) for d in DIRS)
+    nseg = -(-(-(-(H * W) // 64)) // seg)
+    words = 1024 // 4 + B * NH * nseg  # header, then one flag per (scan, segment)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    gla.workspace_init(ws)
+    x = make_inputs(B, NH, H, W, 64, 64, "f16", (0.0, 1.0), True, seed=601 + H + seg)
+    t = _dev(x, torch)
+    for i in range(6):
+        d = DIRS[i % 4]
+        print(f"[case] clear B={B} NH={NH} {H}x{W} seg={seg} call {i} dir={d}", flush=True)
+        y = gla.fwd(t["q"], t["k"], t["v"], t["z"], d, H, W, r=t["r"], norm_weight=t["w"],
+                    segment_chunks=seg, workspace=ws, algorithm=gla.ALGO_SINGLE_PASS)
+        torch.cuda.synchronize()
+        w = ws[:4 * words].cpu().numpy().view(np.uint32)
+        assert not w.any(), f"call {i}: nonzero workspace words at {np.flatnonzero(w)[:8]}"
+        if i < 4:
+            assert rel_err(y.cpu().numpy(), run_oracle(x, d, H, W)) <= TOL["f16"]
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_non_finite_gate_logits_propagate(torch, d):
     """A NaN gate logit makes the outputs that depend on it NaN (as in the
