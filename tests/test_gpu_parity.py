@@ -84,6 +84,44 @@ def test_stack16k_gated_sampled_units(torch, call):
            units=(u0, u0 + 2))
 
 
+@pytest.mark.parametrize("case", ["single_pass", "d128"])
+def test_maximum_rows(torch, case):
+    """Close to the largest row count each kernel addresses with 32-bit buffer
+    offsets: the single pass (B*L*NH below 2^23; here 8.37 M rows of d = 64,
+    forced to 7-chunk segments: 18.9 K workgroups in 74 rounds) and the d = 128
+    passes (below 2^22; here 4.18 M rows), gated, 128x128 grids.  The oracle
+    checks the first and the last (batch, head) scans in full: their rows sit
+    at the lowest and the highest offsets."""
+    from recurrent_vision_backbone_key_amd import gla
+    from recurrent_vision_backbone_key_amd.inputs import make_inputs_device
+    B, NH, d = (73, 7, 64) if case == "single_pass" else (85, 3, 128)
+    H = W = 128
+    direction = 3 if case == "single_pass" else 2
+    rows = B * H * W * NH
+    assert rows < (1 << 23 if d == 64 else 1 << 22)
+    algo = gla.ALGO_SINGLE_PASS if case == "single_pass" else gla.ALGO_AUTO
+    seg = 7 if case == "single_pass" else 0
+    print(f"[case] maximum rows {case}: B={B} NH={NH} {H}x{W} d={d} rows={rows}", flush=True)
+    t = make_inputs_device(B, NH, H, W, d, d, "f16", (0.0, 1.0), True, seed=4242)
+    opts = gla.make_opts(B, NH, d, d, gla.F16, segment_chunks=seg, algorithm=algo)
+    ws = torch.zeros((max(gla.workspace_size(direction, H, W, 64, opts), 16),),
+                     dtype=torch.uint8, device="cuda")
+    gla.workspace_init(ws)
+    y = gla.fwd(t["q"], t["k"], t["v"], t["z"], direction, H, W, r=t["r"], norm_weight=t["w"],
+                segment_chunks=seg, workspace=ws, algorithm=algo)
+    torch.cuda.synchronize()
+    if case == "single_pass":
+        assert int(ws[4:8].cpu().numpy().view(np.uint32)[0]) == 0
+    for b, h in ((0, 0), (B - 1, NH - 1)):
+        x = {n: t[n][b:b + 1, :, h:h + 1, :].contiguous().cpu().numpy() for n in ("q", "k", "v", "z", "r")}
+        x["w"] = t["w"].cpu().numpy()
+        ref = run_oracle(x, direction, H, W)
+        err = rel_err(y[b:b + 1, :, h:h + 1, :].cpu().numpy(), ref)
+        print(f"[parity] maximum rows {case} unit ({b}, {h}): {err:.3e}", flush=True)
+        assert err <= TOL["f16"]
+    del t, y, ws
+
+
 @pytest.mark.parametrize("name", ["sweep16x16_b8", "sweep42x42_b1", "sweep128x128_b1"])
 def test_sweep_points(torch, name):
     """The length/batch sweep points (256, 1764 and 16384 tokens at d = 64,
