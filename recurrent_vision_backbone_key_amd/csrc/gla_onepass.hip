@@ -120,22 +120,23 @@ __device__ __forceinline__ void st_u(unsigned* p, unsigned v)
 }
 // Bulk exchange data moves 16 bytes per lane through buffer instructions whose
 // record count bounds every access.  Loads always use sc1, which misses the
-// CU's L1 and reads the XCD's L2 (or memory).  Stores: when the workgroups of
-// a scan may run on different XCDs, sc1 as well (write-through to memory: the
-// policy the compiler gives the relaxed agent-scope atomics above, coherent
-// across the per-XCD L2s); when every workgroup of a scan runs on one XCD
-// (LOCAL), the default policy, which leaves the line in that XCD's L2 where
-// the sc1 loads of the same XCD find it (about half the round-trip latency).
-// Segment aggregates are the exception: they are written through in both
-// modes.  Measured on MI355X, write-back aggregates kept the kernel running
-// 2-3 us after its last workgroup had ended (one 1600-token frame with 6
-// heads: 18.7 us per call, 16.6 us with write-through aggregates, though the
-// exchange inside the workgroups takes about 0.4 us longer); inclusive states
-// gain nothing from it and keep the local policy.
+// CU's L1 and reads the XCD's L2 (or memory).  Aggregates and inclusive states
+// are always stored with sc1 (write-through to memory: the policy the compiler
+// gives the relaxed agent-scope atomics above, coherent across the per-XCD
+// L2s).  Flags: sc1 as well when the workgroups of a scan may run on different
+// XCDs; when every workgroup of a scan runs on one XCD (LOCAL), the default
+// policy, which leaves the line in that XCD's L2 where the sc1 loads of the
+// same XCD find it (about half the round-trip latency).  Measured on MI355X,
+// write-back exchange data kept the kernel running 2-3 us after its last
+// workgroup had ended (one 1600-token frame with 6 heads: 18.7 us per call
+// with write-back aggregates and inclusive states, 15.6 us written through,
+// though the exchange inside the workgroups takes about 0.4 us longer), while
+// write-through flags slowed every look-back.
 template <bool LOCAL> struct Pol {
     static constexpr int kLoad = 16;
     static constexpr int kStore = LOCAL ? 0 : 16;
 };
+constexpr int kStoreThrough = 16;  // sc1
 template <bool LOCAL>
 __device__ __forceinline__ float4v ld_x4(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
@@ -146,10 +147,9 @@ __device__ __forceinline__ float ld_x1(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, Pol<LOCAL>::kLoad));
 }
-template <bool LOCAL>
 __device__ __forceinline__ void st_x4(__amdgpu_buffer_rsrc_t r, unsigned off, float4v v)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, Pol<LOCAL>::kStore);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kStoreThrough);
 }
 // Segment flags of one scan (0 none, 1 aggregate, 2 inclusive state).
 template <bool LOCAL>
@@ -689,10 +689,9 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         const unsigned agg_bytes = (unsigned)(aggf * 4), st_bytes = (unsigned)(D * D * 4);
         if (seg > 0 && !last) {
             const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
-            // aggregates are written through in every mode (see Pol)
-            st_x4<false>(r, off0, l0);
-            st_x4<false>(r, off1, l1);
-            if (tid < D / 4) st_x4<false>(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
+            st_x4(r, off0, l0);
+            st_x4(r, off1, l1);
+            if (tid < D / 4) st_x4(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
             wait_mem();
             __syncthreads();
             if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 1u);
@@ -772,14 +771,14 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                     i1[e] = fold_step(gm1, s1[e], l1[e]);
                 }
                 const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * D * D, st_bytes);
-                st_x4<LOCAL>(r, off0, i0);
-                st_x4<LOCAL>(r, off1, i1);
+                st_x4(r, off0, i0);
+                st_x4(r, off1, i1);
             }
         } else {
             // first segment: its local state is the inclusive state
             const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * D * D, st_bytes);
-            st_x4<LOCAL>(r, off0, l0);
-            st_x4<LOCAL>(r, off1, l1);
+            st_x4(r, off0, l0);
+            st_x4(r, off1, l1);
         }
         if (!last) {
             wait_mem();
