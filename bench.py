@@ -493,9 +493,9 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the forward shards across GPUs by batch/head with no communication; "
-              "see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward would shard across GPUs by batch/head with no communication)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -69,7 +69,7 @@ typedef struct gla_opts {
     int32_t batch;   /* B  >= 1 */
     int32_t heads;   /* NH >= 1 */
     int32_t dk;      /* key/query head dim; supported: 16, 32, 64, 128        */
-    int32_t dv;      /* value head dim; this build requires dv == dk           */
+    int32_t dv;      /* value head dim; must equal dk                          */
     int32_t dtype;   /* GLA_F16 or GLA_F32: storage of q, k, v, r and out      */
     float tau;       /* gate temperature; <= 0 selects 16 (paper Sec. 2.1)     */
     float scale;     /* output scale; <= 0 selects dk^-1/2 (paper Sec. 2.1)    */
@@ -227,7 +227,7 @@ GLA_API int gla_spatial_swiglu(const void *gate, const void *value, int64_t ld_i
  * along the scan order of `dir`, results at the original token positions.
  *   q, k, gate_logits, dq, dk, dz  [B, L, NH, dk]; v, dout, dv [B, L, NH, dv]
  *   q, k, v, dout, dq, dk, dv in opts->dtype; gate_logits and dz binary32
- * This build: dk == dv in {16, 32, 64}, binary16 or binary32 storage; 64-position
+ * Supported: dk == dv in {16, 32, 64}, binary16 or binary32 storage; 64-position
  * chunks.  opts->norm_weight, eps, segment_chunks and algorithm are ignored.
  * The workspace must hold gla_bwd_workspace_size() bytes (no initialisation:
  * every call rewrites what it reads).  All pointers are 16-byte aligned

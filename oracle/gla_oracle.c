@@ -17,7 +17,7 @@
  * result is written back at each token's original grid position (Sec. 2.1,
  * scan-direction paragraph and Figure 2).
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - token t = h*W + w (row-major grid); left-to-right is raster order,
  *     right-to-left is that order reversed, top-to-bottom is column-major
  *     order, bottom-to-top is column-major order reversed;
