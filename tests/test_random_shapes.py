@@ -1,15 +1,17 @@
 """Seeded random sweep of shapes against the fp64 oracle (paper "GTR: Gated
-Token Recurrence for Efficient Dense Prediction", Section 2.1 recurrence and
-output gate; its backward).
+Token Recurrence for Efficient Dense Prediction", Section 2.1 recurrence,
+output gate, low-rank retention-gate projection and Spatial SwiGLU paragraph;
+the recurrence's backward).
 
 The fixed parity cases pin the configurations that are timed; this sweep adds
 breadth: batch, heads and grid sides drawn from a seeded generator (sides
 from 1 to 50, so single tokens, single rows and columns, primes and ragged
 last chunks all occur), every head size and chunk the library takes, both
 storage types, each scan direction, with and without the output gate, and
-gate logits from strongly local to long retention.  Same bars as the other
-parity tests: 2e-3 of max |oracle| for binary16 storage, 1e-5 (forward) and
-2e-5 (backward) for binary32.
+gate logits from strongly local to long retention; the Spatial SwiGLU core and
+the gate projection over random grids, widths and ranks.  Same bars as the
+other parity tests: 2e-3 of max |oracle| for binary16 storage, 1e-5 (forward)
+and 2e-5 (backward) for binary32, the Spatial SwiGLU core's per-element bar.
 """
 import numpy as np
 import pytest
@@ -106,3 +108,42 @@ def test_random_backward(torch, c):
         err = float(np.max(np.abs(g - r))) / max(den, 1e-300)
         print(f"[parity] random backward {c['i']} {n}: {err:.3e}", flush=True)
         assert err <= BWD_TOL[c["dtype"]], f"{c}: {n} {err:.3e}"
+
+
+def _sswiglu_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    side = lambda: int(rng.choice([1, 2, 5, 8, 9, 15, 16, 23, 40]))
+    return [dict(i=i, B=int(rng.integers(1, 4)), H=side(), W=side(),
+                 C=int(8 * rng.integers(1, 40)), dtype="f16" if rng.random() < 0.7 else "f32",
+                 bias=bool(rng.random() < 0.7), packed=bool(rng.random() < 0.3))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("c", _sswiglu_cases(12, 20253), ids=lambda c: f"sswiglu{c['i']}")
+def test_random_sswiglu(torch, c):
+    # the Spatial SwiGLU core's own per-element bar (see tests/test_sswiglu.py)
+    from test_sswiglu import _check
+    _check(torch, c["B"], c["H"], c["W"], c["C"], c["dtype"], c["bias"], c["packed"], None,
+           seed=9000 + c["i"])
+
+
+def _proj_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    side = lambda: int(rng.choice([1, 3, 9, 16, 25, 40]))
+    cases = []
+    for i in range(n):
+        dk = int(rng.choice([64, 64, 32, 128]))
+        cases.append(dict(i=i, B=int(rng.integers(1, 3)), NH=int(rng.integers(1, 5)), H=side(),
+                          W=side(), dk=dk, d_model=int(8 * rng.integers(1, 65)),
+                          rank=int(rng.choice([16, 16, 8, 32])), dir=int(rng.integers(0, 4))))
+    return cases
+
+
+@pytest.mark.parametrize("c", _proj_cases(12, 20254), ids=lambda c: f"proj{c['i']}")
+def test_random_gate_projection(torch, c):
+    # rank 16 at d = 64 takes the fused expansion in the single pass when the
+    # plan allows it, every other case the staged logits kernel
+    from test_gate_proj import _check_proj, _proj_inputs
+    x = _proj_inputs(c["B"], c["NH"], c["H"], c["W"], c["dk"], c["d_model"], c["rank"],
+                     seed=9500 + c["i"])
+    _check_proj(f"random projection {c}", x, c["dir"], c["H"], c["W"], 64, TOL["f16"], torch)
