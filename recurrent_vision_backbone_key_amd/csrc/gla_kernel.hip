@@ -580,7 +580,9 @@ __global__ __launch_bounds__(kThreads) void gla_fold_kernel(Params P)
             const int s = s0 + u;
             if (s < nslot) {
                 x = exp2_fast(gv[u]) * x + lv[u];
-                base[(size_t)s * slot_floats + idx] = x;
+                // written through (agent scope): read by the next kernel
+                __hip_atomic_store(base + (size_t)s * slot_floats + idx, x, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }

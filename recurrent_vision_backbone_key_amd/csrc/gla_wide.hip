@@ -240,8 +240,11 @@ void gla_wide_kernel(Params P)
     const int cb = 64 * h + 8 * g;  // row role: channels cb + {0..7}, cb + 32 + {0..7}
 
     const int nunits = P.B * P.NH;
-    const int seg = blockIdx.x / nunits;
-    const int unit = blockIdx.x - seg * nunits;
+    // The output pass takes the segments in reverse order: its first round
+    // re-reads the inputs the aggregate pass read last, which the last-level
+    // cache still holds (about 1 % per call).
+    const int seg = AGG ? blockIdx.x / nunits : P.nseg - 1 - blockIdx.x / nunits;
+    const int unit = blockIdx.x % nunits;
     const int c_begin = seg * P.seg_chunks;
     const int c_end = min(P.nchunks, c_begin + P.seg_chunks);
     const bool gated = !AGG && P.r != nullptr;
@@ -598,13 +601,19 @@ void gla_wide_kernel(Params P)
     }
 
     if (AGG) {
-        // segment aggregate: local state from zero and total log2-decay
+        // segment aggregate: local state from zero and total log2-decay,
+        // written through to memory (agent-scope stores), where the fold
+        // kernel reads them
         float* dst = P.ws + ((size_t)unit * (P.nseg - 1) + seg) * slot_floats;
 #pragma unroll
         for (int a = 0; a < 8; ++a)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[(size_t)(16 * a + 4 * g + e) * D + 16 * wave + l16] = S[a][e];
-        if (si == 0) dst[(size_t)D * D + 64 * h + lane] = gacc;
+            for (int e = 0; e < 4; ++e)
+                __hip_atomic_store(dst + (size_t)(16 * a + 4 * g + e) * D + 16 * wave + l16, S[a][e],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (si == 0)
+            __hip_atomic_store(dst + (size_t)D * D + 64 * h + lane, gacc, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
