@@ -363,7 +363,7 @@ __device__ __forceinline__ void scores_values(const Params& P, const _Float16* s
     }
 }
 
-template <bool LOCAL, bool PROJ>
+template <bool LOCAL, bool PROJ, int NCHK>
 __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 {
     __shared__ __attribute__((aligned(16))) char lds[PROJ ? LDS_PROJ : LDS_TOTAL];
@@ -460,8 +460,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     }
     __syncthreads();
 
-    float4v okeep[NCH][2];
-    half8 qkeep[NCH];    // this lane's 8 channels of the segment-relative query
+    float4v okeep[NCHK][2];
+    half8 qkeep[NCHK];    // this lane's 8 channels of the segment-relative query
     float4v S[2];        // this wave's two 16x16 tiles of the local state
     S[0] = S[1] = float4v{0.f, 0.f, 0.f, 0.f};
     const int sa = wave >> 1;         // state tile row block (key channels)
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     float dseg = 0.f;                 // decay since segment start, channel 32*h + cht
 
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < NCHK; ++c) {
         if (c >= nch) break;
         float qv[8], kv[8], zv[8];
         const u32x4 raw_v = raw.v;
@@ -645,9 +645,9 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     // r of every chunk at this lane's output positions (token tl, value
     // channels 32h + 16m + 4g .. +3): loads issued now, in flight during the
     // exchange
-    half4 rreg[NCH][2];
+    half4 rreg[NCHK][2];
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
+    for (int cc = 0; cc < NCHK; ++cc) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) rreg[cc][m] = half4{0, 0, 0, 0};
         if (gated && cc < nch) {
@@ -793,12 +793,12 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     if (need_in) {
         // exchange the query-operand halves through the staging area
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc)
+        for (int cc = 0; cc < NCHK; ++cc)
             if (cc < nch) *(half8*)(sOut + (cc * C + tl) * SH + c0) = qkeep[cc];
         __syncthreads();
     }
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
+    for (int cc = 0; cc < NCHK; ++cc) {
         if (cc >= nch) break;
         float4v o0 = okeep[cc][0], o1 = okeep[cc][1];
         if (need_in) {
@@ -840,7 +840,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     // epilogue and stores straight from the output fragments: 8 bytes per lane
     // and value block (the two halves' stores of a row meet in the L2)
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
+    for (int cc = 0; cc < NCHK; ++cc) {
         if (cc >= nch) break;
         float inv = 1.f;
         if (gated) {
@@ -900,10 +900,20 @@ int launch_onepass(const Params& P, void* stream)
     hipStream_t st = (hipStream_t)stream;
     const dim3 grid(P.xcd_local ? 8 * P.xcd_tasks : P.B * P.NH * P.nseg);
     const bool proj = (P.ghp != nullptr);
-    void (*kern)(Params) = P.xcd_local ? (proj ? onepass::gla_onepass_kernel<true, true>
-                                                : onepass::gla_onepass_kernel<true, false>)
-                                       : (proj ? onepass::gla_onepass_kernel<false, true>
-                                               : onepass::gla_onepass_kernel<false, false>);
+    // one-chunk segments take an instance with a single chunk's registers and
+    // a straight-line body (a small code footprint for the cold instruction
+    // cache of workgroups that run it once)
+    void (*kern)(Params);
+    if (P.seg_chunks == 1)
+        kern = P.xcd_local ? (proj ? onepass::gla_onepass_kernel<true, true, 1>
+                                   : onepass::gla_onepass_kernel<true, false, 1>)
+                           : (proj ? onepass::gla_onepass_kernel<false, true, 1>
+                                   : onepass::gla_onepass_kernel<false, false, 1>);
+    else
+        kern = P.xcd_local ? (proj ? onepass::gla_onepass_kernel<true, true, onepass::NCH>
+                                   : onepass::gla_onepass_kernel<true, false, onepass::NCH>)
+                           : (proj ? onepass::gla_onepass_kernel<false, true, onepass::NCH>
+                                   : onepass::gla_onepass_kernel<false, false, onepass::NCH>);
     hipLaunchKernelGGL(kern, grid, dim3(onepass::NT), 0, st, P);
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
 }
