@@ -20,7 +20,7 @@ int run_fwd(gla::Params& P, const void* q, const void* k, const void* v, int dir
     P.r = r;
     P.w = r ? opts->norm_weight : nullptr;
     P.out = out;
-    P.ws = (float*)opts->workspace;
+    P.ws = plan.off_slots ? (float*)((char*)opts->workspace + plan.off_slots) : (float*)opts->workspace;
     P.B = opts->batch;
     P.NH = opts->heads;
     P.H = H;

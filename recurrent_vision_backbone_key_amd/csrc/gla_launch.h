@@ -20,12 +20,12 @@ struct Params {
     void* out;          // [B, L, NH, DV]
     float* ws;          // three-pass: segment slots [units][nseg-1][DK*DV + DK] fp32
     // single-pass exchange (workspace): ticket and error word, one flag per
-    // (scan, segment), segment aggregates and inclusive states
+    // (scan, segment), segment aggregates and group transfers
     unsigned* ticket;   // word 0: ticket counter; words 16 (1 + x): counter of XCD x
     unsigned* err;
-    unsigned* flags;    // [units][nseg]: 0 none, 1 aggregate, 2 inclusive
+    unsigned* flags;    // [units][nseg]: bits 1 aggregate, 2 group transfer, 4 done
     float* agg;         // [units][nseg][DK*DV + DK]
-    float* incl;        // [units][nseg][DK*DV]
+    float* incl;        // [units][nseg][DK*DV + DK]: group transfers (leaders' slots)
     int B, NH, H, W, L, dir;
     int nchunks;        // ceil(L / chunk)
     int seg_chunks;     // chunks per segment

@@ -10,13 +10,14 @@
 //           that starts at zero, keeping the partial outputs and the query
 //           operand relative to the segment start in registers.
 //  phase 2  it publishes its segment aggregate (local state, total decay),
-//           looks back over earlier segments of the same scan until every one
-//           has published, and folds forward from the latest inclusive state:
+//           waits until the earlier segments of the same scan have published
+//           and folds their transfers from zero, in segment order:
 //               S_in = fold_{i < seg} (S -> Diag(2^{G_i}) S + L_i),
-//           with the multipliers 2^{G_i} published as computed by segment i.
-//           The fold always runs in segment order from a state that is itself
-//           that fold, so the bits do not depend on which predecessor was
-//           found (deterministic).  Workgroups only wait on smaller tickets.
+//           with the multipliers 2^{G_i} published as computed by segment i;
+//           scans of many segments fold per-group combined transfers first
+//           (two levels, see the exchange).  The order is fixed, so the bits
+//           do not depend on timing (deterministic).  Workgroups only wait on
+//           smaller tickets.
 //  phase 3  adds (q (.) 2^{b from segment start}) S_in to the kept partial
 //           outputs, applies the epilogue and stores every row; the scan's
 //           last segment then waits until every earlier one has finished
@@ -150,6 +151,10 @@ __device__ __forceinline__ float ld_x1(__amdgpu_buffer_rsrc_t r, unsigned off)
 __device__ __forceinline__ void st_x4(__amdgpu_buffer_rsrc_t r, unsigned off, float4v v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kStoreThrough);
+}
+__device__ __forceinline__ void st_x1(__amdgpu_buffer_rsrc_t r, unsigned off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, kStoreThrough);
 }
 // Segment flags of one scan (0 none, 1 aggregate, 2 inclusive state).
 template <bool LOCAL>
@@ -687,103 +692,245 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         const float4v l0 = *(const float4v*)(sL + ch0 * D + cl0);
         const float4v l1 = *(const float4v*)(sL + (ch0 + 32) * D + cl0);
         const unsigned agg_bytes = (unsigned)(aggf * 4), st_bytes = (unsigned)(D * D * 4);
-        if (seg > 0 && !last) {
-            const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
-            st_x4(r, off0, l0);
-            st_x4(r, off1, l1);
-            if (tid < D / 4) st_x4(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
-            wait_mem();
-            __syncthreads();
-            if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 1u);
-        }
-        if (need_in) {
-            // look back: wait until every earlier segment has published, then
-            // start from the latest inclusive state
-            if (wave == 0) {
-                unsigned spins = 0;
-                int k = -1;
-                for (;;) {
-                    const int idx = seg - 1 - lane;
-                    const unsigned f = (idx >= 0) ? ld_flag<LOCAL>(flags, P.nseg, idx) : 2u;
-                    if (__all(f >= 1u)) {
-                        const unsigned long long inc = __ballot(idx >= 0 && f == 2u);
-                        // lowest lane with an inclusive state = latest segment
-                        // (segment 0 always publishes one, so inc != 0)
-                        k = inc ? seg - 1 - (int)__builtin_ctzll(inc) : -1;
-                        break;
-                    }
-                    if (++spins > (1u << 22)) {
-                        if (lane == 0) atomicOr(P.err, 1u);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                }
-                if (lane == 0) sMisc[1] = k;
+        // Plans whose workgroups all run in one round (every segment starts
+        // at the same time) fold published aggregates directly; plans of
+        // several rounds use inclusive states, which the segments of earlier
+        // rounds have published by the time later ones look back.
+        const bool one_round = LOCAL ? (P.xcd_tasks <= 32) : (nunits * P.nseg <= 256);
+        if (one_round) {
+            // Exchange.  Every segment but the last publishes its aggregate and
+            // segment j folds the aggregates of segments 0 .. j-1 from zero, in
+            // order.  Scans of many segments use two levels: the segments form
+            // groups of G = ceil(sqrt(nseg)); the last segment of a group that has
+            // segments after it (the group's leader) publishes the group's
+            // combined transfer (its aggregates folded from zero, multipliers
+            // multiplied) instead of its own aggregate, and segment j of group g
+            // folds the combined transfers of groups 0 .. g-1 and then the
+            // aggregates of its own group before it (about 2 sqrt(nseg) transfers
+            // instead of j).  The extra publish round trip of the leaders pays off
+            // from about two dozen segments on (measured: 28 one-chunk segments
+            // 16.7 -> 14.9 us per call, 5 segments 34.1 -> 35.7 us).  The fixed
+            // order makes the result independent of timing.  Flag bits: 1
+            // aggregate, 2 combined transfer, 4 done reading.
+            int G = P.nseg;
+            if (P.nseg >= 24) {
+                G = 1;
+                while (G * G < P.nseg) ++G;
             }
-            __syncthreads();
-            const int k = sMisc[1];
-            // forward fold from the inclusive state of segment k
-            float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-            if (k >= 0) {
-                const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + ((size_t)unit * P.nseg + k) * D * D, st_bytes);
-                s0 = ld_x4<LOCAL>(r, off0);
-                s1 = ld_x4<LOCAL>(r, off1);
-            }
-            constexpr int FW = 8;  // aggregates per round of loads
-            for (int sg0 = k + 1; sg0 < seg; sg0 += FW) {
-                // issue the loads of up to FW aggregates, then fold them in order
-                float4v a0[FW], a1[FW];
-                float g0[FW], g1[FW];
-#pragma unroll
-                for (int b = 0; b < FW; ++b) {
-                    const int sg = min(sg0 + b, seg - 1);
-                    const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + ((size_t)unit * P.nseg + sg) * aggf, agg_bytes);
-                    a0[b] = ld_x4<LOCAL>(r, off0);
-                    a1[b] = ld_x4<LOCAL>(r, off1);
-                    g0[b] = ld_x1<LOCAL>(r, st_bytes + 4u * ch0);
-                    g1[b] = ld_x1<LOCAL>(r, st_bytes + 4u * (ch0 + 32));
-                }
-#pragma unroll
-                for (int b = 0; b < FW; ++b)
-                    if (sg0 + b < seg) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            s0[e] = fold_step(g0[b], s0[e], a0[b][e]);
-                            s1[e] = fold_step(g1[b], s1[e], a1[b][e]);
+            const int grp = seg / G, gfirst = grp * G;
+            const bool leader = !last && seg == gfirst + G - 1;
+            auto leader_slot = [&](int gg) { return (size_t)unit * P.nseg + (size_t)(gg * G + G - 1); };
+            // wave 0 waits until groups 0 .. ng-1 have their combined transfers and
+            // segments first .. first+cnt-1 their aggregates (ng + cnt <= 64)
+            auto wait_for = [&](int ng, int first, int cnt) {
+                if (wave == 0) {
+                    unsigned spins = 0;
+                    for (;;) {
+                        bool ok = true;
+                        if (lane < ng) ok = (ld_flag<LOCAL>(flags, P.nseg, lane * G + G - 1) & 2u) != 0u;
+                        else if (lane < ng + cnt) ok = (ld_flag<LOCAL>(flags, P.nseg, first + lane - ng) & 1u) != 0u;
+                        if (__all(ok)) break;
+                        if (++spins > (1u << 22)) {
+                            if (lane == 0) atomicOr(P.err, 1u);
+                            break;
                         }
+                        __builtin_amdgcn_s_sleep(2);
                     }
-            }
-            // S_in^T (hi, lo) for phase 3; inclusive state for successors
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const _Float16 h0 = (_Float16)s0[e], h1 = (_Float16)s1[e];
-                sST[(cl0 + e) * SH + ch0] = h0;
-                if (kInLo) sSTL[(cl0 + e) * SH + ch0] = (_Float16)(s0[e] - (float)h0);
-                sST[(cl0 + e) * SH + ch0 + 32] = h1;
-                if (kInLo) sSTL[(cl0 + e) * SH + ch0 + 32] = (_Float16)(s1[e] - (float)h1);
-            }
-            if (!last) {
-                const float gm0 = sG[ch0], gm1 = sG[ch0 + 32];
-                float4v i0, i1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    i0[e] = fold_step(gm0, s0[e], l0[e]);
-                    i1[e] = fold_step(gm1, s1[e], l1[e]);
                 }
-                const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * D * D, st_bytes);
-                st_x4(r, off0, i0);
-                st_x4(r, off1, i1);
+                __syncthreads();
+            };
+            // fold, from (s0, s1), the combined transfers of groups 0 .. ng-1 and
+            // then the aggregates of segments first .. first+cnt-1, in that order;
+            // m0, m1 collect the product of the multipliers
+            auto fold = [&](float4v& s0, float4v& s1, float& m0, float& m1, int ng, int first, int cnt) {
+                constexpr int FW = 8;  // transfers per round of loads
+                const int n = ng + cnt;
+                for (int t0 = 0; t0 < n; t0 += FW) {
+                    float4v a0[FW], a1[FW];
+                    float g0[FW], g1[FW];
+    #pragma unroll
+                    for (int b = 0; b < FW; ++b) {
+                        const int t = min(t0 + b, n - 1);
+                        const float* base = t < ng ? P.incl + leader_slot(t) * aggf
+                                                   : P.agg + ((size_t)unit * P.nseg + first + t - ng) * aggf;
+                        const __amdgpu_buffer_rsrc_t r = xrsrc(base, agg_bytes);
+                        a0[b] = ld_x4<LOCAL>(r, off0);
+                        a1[b] = ld_x4<LOCAL>(r, off1);
+                        g0[b] = ld_x1<LOCAL>(r, st_bytes + 4u * ch0);
+                        g1[b] = ld_x1<LOCAL>(r, st_bytes + 4u * (ch0 + 32));
+                    }
+    #pragma unroll
+                    for (int b = 0; b < FW; ++b)
+                        if (t0 + b < n) {
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                s0[e] = fold_step(g0[b], s0[e], a0[b][e]);
+                                s1[e] = fold_step(g1[b], s1[e], a1[b][e]);
+                            }
+                            m0 *= g0[b];
+                            m1 *= g1[b];
+                        }
+                }
+            };
+            auto set_flag = [&](unsigned v) {
+                wait_mem();
+                __syncthreads();
+                if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, v);
+            };
+            if (!last && !leader) {
+                // aggregate: local state and multiplier 2^G
+                const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
+                st_x4(r, off0, l0);
+                st_x4(r, off1, l1);
+                if (tid < D / 4) st_x4(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
+                set_flag(need_in ? 1u : 5u);  // the first segment reads nothing
+            }
+            if (leader) {
+                // combined transfer of this group: its earlier aggregates, then this
+                // segment's own local state, folded from zero
+                wait_for(0, gfirst, seg - gfirst);
+                float4v c0v = {0.f, 0.f, 0.f, 0.f}, c1v = c0v;
+                float m0 = 1.f, m1 = 1.f;
+                fold(c0v, c1v, m0, m1, 0, gfirst, seg - gfirst);
+                const float gm0 = sG[ch0], gm1 = sG[ch0 + 32];
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    c0v[e] = fold_step(gm0, c0v[e], l0[e]);
+                    c1v[e] = fold_step(gm1, c1v[e], l1[e]);
+                }
+                m0 *= gm0;
+                m1 *= gm1;
+                const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * aggf, agg_bytes);
+                st_x4(r, off0, c0v);
+                st_x4(r, off1, c1v);
+                if ((tid & 15) == 0) {
+                    st_x1(r, st_bytes + 4u * ch0, m0);
+                    st_x1(r, st_bytes + 4u * (ch0 + 32), m1);
+                }
+                set_flag(2u);
+            }
+            if (need_in) {
+                wait_for(grp, gfirst, seg - gfirst);
+                float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+                float m0 = 1.f, m1 = 1.f;
+                fold(s0, s1, m0, m1, grp, gfirst, seg - gfirst);
+                // S_in^T (hi, lo) for phase 3
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const _Float16 h0 = (_Float16)s0[e], h1 = (_Float16)s1[e];
+                    sST[(cl0 + e) * SH + ch0] = h0;
+                    if (kInLo) sSTL[(cl0 + e) * SH + ch0] = (_Float16)(s0[e] - (float)h0);
+                    sST[(cl0 + e) * SH + ch0 + 32] = h1;
+                    if (kInLo) sSTL[(cl0 + e) * SH + ch0 + 32] = (_Float16)(s1[e] - (float)h1);
+                }
+                if (!last) set_flag(leader ? 6u : 5u);
             }
         } else {
-            // first segment: its local state is the inclusive state
-            const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * D * D, st_bytes);
-            st_x4(r, off0, l0);
-            st_x4(r, off1, l1);
-        }
-        if (!last) {
-            wait_mem();
-            __syncthreads();
-            if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 2u);
+            // Look back: each segment publishes its aggregate, waits until
+            // every earlier segment has published, starts from the latest
+            // inclusive state and folds the aggregates after it in segment
+            // order (each inclusive state is itself that left fold, so the
+            // result does not depend on which one was found), then publishes
+            // its own inclusive state.  Flag bits as above, 2 meaning an
+            // inclusive state.
+            if (seg > 0 && !last) {
+                const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
+                st_x4(r, off0, l0);
+                st_x4(r, off1, l1);
+                if (tid < D / 4) st_x4(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
+                wait_mem();
+                __syncthreads();
+                if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 1u);  // aggregate
+            }
+            if (need_in) {
+                // look back: wait until every earlier segment has published, then
+                // start from the latest inclusive state
+                if (wave == 0) {
+                    unsigned spins = 0;
+                    int k = -1;
+                    for (;;) {
+                        const int idx = seg - 1 - lane;
+                        const unsigned f = (idx >= 0) ? ld_flag<LOCAL>(flags, P.nseg, idx) : 2u;
+                        if (__all((f & 3u) != 0u)) {
+                            const unsigned long long inc = __ballot(idx >= 0 && (f & 2u) != 0u);
+                            // lowest lane with an inclusive state = latest segment
+                            // (segment 0 always publishes one, so inc != 0)
+                            k = inc ? seg - 1 - (int)__builtin_ctzll(inc) : -1;
+                            break;
+                        }
+                        if (++spins > (1u << 22)) {
+                            if (lane == 0) atomicOr(P.err, 1u);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                    if (lane == 0) sMisc[1] = k;
+                }
+                __syncthreads();
+                const int k = sMisc[1];
+                // forward fold from the inclusive state of segment k
+                float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+                if (k >= 0) {
+                    const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + ((size_t)unit * P.nseg + k) * aggf, st_bytes);
+                    s0 = ld_x4<LOCAL>(r, off0);
+                    s1 = ld_x4<LOCAL>(r, off1);
+                }
+                constexpr int FW = 8;  // aggregates per round of loads
+                for (int sg0 = k + 1; sg0 < seg; sg0 += FW) {
+                    // issue the loads of up to FW aggregates, then fold them in order
+                    float4v a0[FW], a1[FW];
+                    float g0[FW], g1[FW];
+    #pragma unroll
+                    for (int b = 0; b < FW; ++b) {
+                        const int sg = min(sg0 + b, seg - 1);
+                        const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + ((size_t)unit * P.nseg + sg) * aggf, agg_bytes);
+                        a0[b] = ld_x4<LOCAL>(r, off0);
+                        a1[b] = ld_x4<LOCAL>(r, off1);
+                        g0[b] = ld_x1<LOCAL>(r, st_bytes + 4u * ch0);
+                        g1[b] = ld_x1<LOCAL>(r, st_bytes + 4u * (ch0 + 32));
+                    }
+    #pragma unroll
+                    for (int b = 0; b < FW; ++b)
+                        if (sg0 + b < seg) {
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                s0[e] = fold_step(g0[b], s0[e], a0[b][e]);
+                                s1[e] = fold_step(g1[b], s1[e], a1[b][e]);
+                            }
+                        }
+                }
+                // S_in^T (hi, lo) for phase 3; inclusive state for successors
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const _Float16 h0 = (_Float16)s0[e], h1 = (_Float16)s1[e];
+                    sST[(cl0 + e) * SH + ch0] = h0;
+                    if (kInLo) sSTL[(cl0 + e) * SH + ch0] = (_Float16)(s0[e] - (float)h0);
+                    sST[(cl0 + e) * SH + ch0 + 32] = h1;
+                    if (kInLo) sSTL[(cl0 + e) * SH + ch0 + 32] = (_Float16)(s1[e] - (float)h1);
+                }
+                if (!last) {
+                    const float gm0 = sG[ch0], gm1 = sG[ch0 + 32];
+                    float4v i0, i1;
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        i0[e] = fold_step(gm0, s0[e], l0[e]);
+                        i1[e] = fold_step(gm1, s1[e], l1[e]);
+                    }
+                    const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * aggf, st_bytes);
+                    st_x4(r, off0, i0);
+                    st_x4(r, off1, i1);
+                }
+            } else {
+                // first segment: its local state is the inclusive state
+                const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * aggf, st_bytes);
+                st_x4(r, off0, l0);
+                st_x4(r, off1, l1);
+            }
+            if (!last) {
+                wait_mem();
+                __syncthreads();
+                if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, seg > 0 ? 7u : 6u);  // inclusive, done
+            }
         }
     }
     __syncthreads();
@@ -864,18 +1011,18 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     }
 
     // The scan's last segment leaves its flags zero for the next call.  Every
-    // earlier segment sets its flag to 2 only after its look-back and fold
-    // have read all they need, so once every flag reads 2 the exchange is
-    // over; each lane then clears the one flag it read (the clear is ordered
-    // after the store it saw).  This runs after the outputs, where the other
-    // segments have long finished.
+    // earlier segment sets flag bit 4 only after its look-back and folds have
+    // read all they need, so once every flag has it the exchange is over; each
+    // lane then clears the one flag it read (the clear is ordered after the
+    // store it saw).  This runs after the outputs, where the other segments
+    // have long finished.
     if (P.nseg > 1 && seg == P.nseg - 1 && wave == 0) {
         unsigned* flags = P.flags + (size_t)unit * P.nseg;
         const bool mine = lane < seg;  // segments 0 .. nseg-2 (at most 64)
         unsigned spins = 0;
         for (;;) {
-            const unsigned f = mine ? ld_flag<LOCAL>(flags, P.nseg, lane) : 2u;
-            if (__all(f == 2u)) break;
+            const unsigned f = mine ? ld_flag<LOCAL>(flags, P.nseg, lane) : 4u;
+            if (__all((f & 4u) != 0u)) break;
             if (++spins > (1u << 22)) {
                 if (lane == 0) atomicOr(P.err, 1u);
                 break;

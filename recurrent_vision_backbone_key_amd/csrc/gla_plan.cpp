@@ -17,6 +17,12 @@ constexpr int kCUsPerXcd = kCUs / kXcds;
 // Single-pass workspace header: word 0 ticket counter, word 1 error word,
 // word 16 (1 + x) ticket counter of XCD x.
 constexpr size_t kOnePassHeader = 1024;
+// Every forward layout starts with the same fixed prefix: the single pass's
+// header (ticket counters, error word) and room for kFlagWords segment flags.
+// Data never lands there, so a workspace reused across shapes or algorithms
+// never finds another call's data where its own flags must read zero.
+constexpr size_t kFlagWords = 32768;
+constexpr size_t kReserved = kOnePassHeader + kFlagWords * 4;
 constexpr int kTargetGroups = 2 * kCUs;
 
 bool is_pow2_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -63,7 +69,7 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     plan->onepass = 0;
     plan->proj_fused = 0;
     plan->off_z = 0;
-    plan->off_flags = plan->off_agg = plan->off_incl = 0;
+    plan->off_flags = plan->off_agg = plan->off_incl = plan->off_slots = 0;
 
     // Single pass: binary16, d = 64, 64-token chunks; segments of at most
     // kOnePassMaxChunks chunks, at most 65 segments per scan (one wavefront
@@ -99,18 +105,18 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
         const bool local = (seg > 0 || seg_l <= seg_g) &&
                            (tasks <= kCUsPerXcd || units % kXcds == 0);
         if (seg <= 0) seg = local ? seg_l : seg_g;
-        if (seg >= min_seg && seg <= gla::kOnePassMaxChunks) {
+        const size_t nflag = (size_t)units * ((nchunks + seg - 1) / (seg > 0 ? seg : 1));
+        if (seg >= min_seg && seg <= gla::kOnePassMaxChunks && nflag <= kFlagWords) {
             const int nseg = (nchunks + seg - 1) / seg;
-            const size_t nflag = (size_t)units * nseg;
             plan->onepass = 1;
             plan->seg_chunks = seg;
             plan->nseg = nseg;
             plan->xcd_local = local ? 1 : 0;
             plan->xcd_tasks = local ? (int)(upx * nseg) : 0;
             plan->off_flags = kOnePassHeader;
-            plan->off_agg = plan->off_flags + ((nflag * 4 + 255) / 256) * 256;
+            plan->off_agg = kReserved;
             plan->off_incl = plan->off_agg + nflag * ((size_t)64 * 64 + 64) * 4;
-            plan->workspace_bytes = plan->off_incl + nflag * (size_t)64 * 64 * 4;
+            plan->workspace_bytes = plan->off_incl + nflag * ((size_t)64 * 64 + 64) * 4;
         }
     }
     if (!plan->onepass) {
@@ -129,8 +135,9 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
         const int nseg = (nchunks + seg - 1) / seg;
         plan->seg_chunks = seg;
         plan->nseg = nseg;
+        plan->off_slots = nseg > 1 ? kReserved : 0;
         plan->workspace_bytes =
-            nseg > 1 ? (size_t)units * (nseg - 1) * ((size_t)o->dk * o->dv + o->dk) * 4 : 0;
+            nseg > 1 ? kReserved + (size_t)units * (nseg - 1) * ((size_t)o->dk * o->dv + o->dk) * 4 : 0;
     }
     plan->tau = o->tau > 0.0f ? o->tau : 16.0f;
     plan->scale = o->scale > 0.0f ? o->scale : (float)(1.0 / sqrt((double)o->dk));

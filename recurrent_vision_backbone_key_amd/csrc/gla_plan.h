@@ -16,6 +16,7 @@ typedef struct gla_plan {
     int xcd_tasks;               // single pass, xcd_local: workgroups per XCD
     size_t workspace_bytes;
     size_t off_flags, off_agg, off_incl;  // single-pass workspace layout (bytes)
+    size_t off_slots;                     // three-pass segment slots (bytes)
     int proj_fused;              // gate expansion (W2, b) inside the single pass
     size_t off_z;                // gate projection: x W1 (fused) or z staged here (bytes)
     float tau, scale, eps;

@@ -129,21 +129,22 @@ def test_workspace_size_and_errors():
 
 
 def test_workspace_formula_three_pass():
-    """(units) x (segments - 1) slots of (dk*dv + dk) fp32."""
+    """A fixed prefix (1024-byte header, 32768 flag words), then (units) x
+    (segments - 1) slots of (dk*dv + dk) fp32."""
     o = _opts(batch=2, heads=3, segment_chunks=4, algorithm=gla.ALGO_THREE_PASS)
     nchunks = -(-(40 * 40) // 64)
     nseg = -(-nchunks // 4)
-    assert gla.workspace_size(1, 40, 40, 64, o) == 6 * (nseg - 1) * (64 * 64 + 64) * 4
+    assert gla.workspace_size(1, 40, 40, 64, o) == 1024 + 32768 * 4 + 6 * (nseg - 1) * (64 * 64 + 64) * 4
 
 
 def test_workspace_formula_single_pass():
-    """1024-byte header (ticket counters, error word), one flag per (scan,
-    segment) rounded to 256 bytes, then an aggregate (dk*dv + dk fp32) and an
-    inclusive state (dk*dv fp32) per (scan, segment)."""
+    """1024-byte header (ticket counters, error word) and room for 32768
+    segment flags (the same prefix in every forward layout), then an aggregate
+    and a group transfer (dk*dv + dk fp32 each) per (scan, segment)."""
     o = _opts(batch=2, heads=3, segment_chunks=4, algorithm=gla.ALGO_SINGLE_PASS)
     nseg = -(-25 // 4)
     n = 6 * nseg
-    want = 1024 + -(-n * 4 // 256) * 256 + n * (64 * 64 + 64) * 4 + n * 64 * 64 * 4
+    want = 1024 + 32768 * 4 + 2 * n * (64 * 64 + 64) * 4
     assert gla.workspace_size(1, 40, 40, 64, o) == want
 
 
