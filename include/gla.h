@@ -110,8 +110,9 @@ enum gla_algorithm { GLA_ALGO_AUTO = 0, GLA_ALGO_SINGLE_PASS = 1, GLA_ALGO_THREE
  *                out = o (no gate, no RMSNorm)
  *   opts         sizes, dtype, stream, workspace (must not be NULL)
  * The workspace must hold gla_workspace_size() bytes when that is nonzero.
- * It holds per-segment fp32 states and, for the single pass, ticket
- * counters, an error word and per-segment flags.  Before its first use
+ * It starts with a fixed 1024 + 131072-byte prefix (the single pass's ticket
+ * counters, error word and per-segment flags; nothing else is ever written
+ * there), followed by per-segment fp32 states.  Before its first use
  * (and after any call that did not complete) it must be cleared with
  * gla_workspace_init(); every completed call leaves the counters and flags
  * cleared again.  Calls that share a workspace must be ordered on one stream.
