@@ -61,8 +61,9 @@ _COMMON_SOURCES = ("gla_device.h", "gla_launch.h", "gla_geometry.h")
 KERNEL_SOURCES = {
     "onepass": ("gla_onepass.hip",) + _COMMON_SOURCES,
     "onepass_proj": ("gla_onepass.hip", "gla_proj.hip") + _COMMON_SOURCES,
-    "wide": ("gla_wide.hip", "gla_kernel.hip") + _COMMON_SOURCES,
-    "generic": ("gla_kernel.hip",) + _COMMON_SOURCES,
+    "wide": ("gla_wide.hip", "gla_kernel.hip", "gla_chunk.h") + _COMMON_SOURCES,
+    "generic": ("gla_kernel.hip", "gla_chunk.h", "gla_chunk_f16.hip", "gla_chunk_f32.hip",
+                "gla_chunk_f16_mixed.hip", "gla_chunk_f32_mixed.hip") + _COMMON_SOURCES,
     "sswiglu": ("gla_sswiglu.hip",) + _COMMON_SOURCES,
     "bwd": ("gla_bwd.hip", "gla_epi.h") + _COMMON_SOURCES,
     "bwd_gated": ("gla_bwd.hip", "gla_epi.h") + _COMMON_SOURCES,
@@ -559,7 +560,9 @@ def main():
                                                     opts)
             else:
                 need = gla.workspace_size(d, H, W, chunk, opts)
-            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            if need:
+                gla.workspace_init(ws)
             calls.append((x, d, out, ws))
         sets.append(calls)
     opts_probe = gla.make_opts(B, NH, dk, dv, 0, segment_chunks=args.segment_chunks)

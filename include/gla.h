@@ -23,7 +23,8 @@
  * reordering is needed for any direction.
  *
  * Layout: q, k, gate_logits: [B, L, NH, d_k]; v, r, out: [B, L, NH, d_v];
- * all dense row-major, L = H*W.  q, k, v, r, out share one storage type
+ * all dense row-major, L = H*W.  d_k and d_v may differ (paper Section 2.1:
+ * W_Q, W_K of d x d_k, W_V of d x d_v).  q, k, v, r, out share one storage type
  * (opts->dtype); gate_logits and norm_weight are binary32.
  *
  * Memory and ownership: every tensor pointer is a DEVICE pointer owned by the
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 5
+#define GLA_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define GLA_API __attribute__((visibility("default")))
@@ -62,14 +63,28 @@ enum gla_status {
                              out overlapping an input                          */
     GLA_EUNSUPPORTED = 2, /* d_k, d_v, chunk, dtype or size outside the built set */
     GLA_EWORKSPACE = 3,   /* workspace missing or smaller than gla_workspace_size */
-    GLA_EHIP = 4          /* the HIP runtime reported an error at launch         */
+    GLA_EHIP = 4,         /* the HIP runtime reported an error at launch         */
+    GLA_EKERNEL = 5       /* a kernel reported a failure in the workspace's error
+                             word (gla_workspace_status)                        */
 };
+
+/* Bits of a workspace's error word (gla_workspace_status).  They are sticky:
+ * once one is set, every later single-pass call on that workspace writes NaN
+ * to all its outputs, until the workspace is initialised again.  Within a call,
+ * a failure poisons every segment downstream of it in its scan (NaN rows). */
+#define GLA_WS_ERR_WAIT 1u   /* a bounded wait for another workgroup's segment
+                                exchange gave up; the affected rows hold NaN    */
+#define GLA_WS_ERR_TICKET 2u /* a work ticket beyond the launch: the counters were
+                                not clear (an earlier call did not complete)     */
+#define GLA_WS_ERR_INIT 4u   /* the workspace was not initialised with
+                                gla_workspace_init; every output row holds NaN  */
 
 typedef struct gla_opts {
     int32_t batch;   /* B  >= 1 */
     int32_t heads;   /* NH >= 1 */
-    int32_t dk;      /* key/query head dim; supported: 16, 32, 64, 128        */
-    int32_t dv;      /* value head dim; must equal dk                          */
+    int32_t dk;      /* key/query head dim d_k; supported: 16, 32, 64, 128    */
+    int32_t dv;      /* value head dim d_v; supported: 16, 32, 64, 128; d_v !=
+                        d_k with 64-token chunks (three passes)                 */
     int32_t dtype;   /* GLA_F16 or GLA_F32: storage of q, k, v, r and out      */
     float tau;       /* gate temperature; <= 0 selects 16 (paper Sec. 2.1)     */
     float scale;     /* output scale; <= 0 selects dk^-1/2 (paper Sec. 2.1)    */
@@ -110,12 +125,19 @@ enum gla_algorithm { GLA_ALGO_AUTO = 0, GLA_ALGO_SINGLE_PASS = 1, GLA_ALGO_THREE
  *                out = o (no gate, no RMSNorm)
  *   opts         sizes, dtype, stream, workspace (must not be NULL)
  * The workspace must hold gla_workspace_size() bytes when that is nonzero.
- * It starts with a fixed 1024 + 131072-byte prefix (the single pass's ticket
- * counters, error word and per-segment flags; nothing else is ever written
- * there), followed by per-segment fp32 states.  Before its first use
- * (and after any call that did not complete) it must be cleared with
- * gla_workspace_init(); every completed call leaves the counters and flags
- * cleared again.  Calls that share a workspace must be ordered on one stream.
+ * It starts with a fixed 4096 + 131072-byte prefix (the single pass's ticket
+ * counters, error word, initialisation mark and per-segment flags; nothing
+ * else is ever written there), followed by per-segment fp32 states.  Before
+ * its first use it must be initialised with gla_workspace_init(); every
+ * completed call leaves the counters and flags cleared again, so calls and
+ * graph replays need no reset in between.  A single-pass call on a workspace
+ * that was not initialised writes NaN to every output row and sets
+ * GLA_WS_ERR_INIT; a wait that gives up (bounded spin) writes NaN to the rows
+ * it affects and sets GLA_WS_ERR_WAIT.  gla_workspace_status() reads these
+ * bits.  Calls that share a workspace must be ordered on one stream; calls
+ * that overlap on one workspace race.  The workspace size and the plan behind
+ * it depend on the device current on the calling thread (its compute units
+ * and XCDs; a host without a device plans for one MI355X).
  */
 GLA_API int gla_fwd(const void *q, const void *k, const void *v, const float *gate_logits,
             int dir, int H, int W, int chunk, void *out, const void *r,
@@ -126,13 +148,29 @@ GLA_API int gla_fwd(const void *q, const void *k, const void *v, const float *ga
 GLA_API size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla_opts *opts);
 
 /*
- * gla_workspace_init -- clears `bytes` bytes of a workspace (counters, flags)
- * on `stream` (hipStream_t, NULL selects the null stream) with a fill kernel.
- * Call once after allocating a workspace for gla_fwd.  workspace: device
- * pointer, 16-byte aligned; bytes: a multiple of 4 (0 does nothing).
+ * gla_workspace_init -- clears `bytes` bytes of a workspace (counters, flags,
+ * error word) and, when bytes >= 4096, writes the initialisation mark, on
+ * `stream` (hipStream_t, NULL selects the null stream) with a fill kernel.
+ * Call once after allocating a workspace for gla_fwd, and again after
+ * gla_workspace_status() reported an error.  workspace: device pointer,
+ * 16-byte aligned; bytes: a multiple of 4 (0 does nothing).
  * GLA_EINVAL on a bad pointer or size, GLA_EHIP on a launch failure.
  */
 GLA_API int gla_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/*
+ * gla_workspace_status -- waits for the work queued on `stream` (hipStream_t,
+ * NULL selects the null stream), then reads the error word of a workspace
+ * used by gla_fwd / gla_fwd_gate_proj (bytes >= 4096, 16-byte aligned device
+ * pointer) into *error_bits (GLA_WS_ERR_* bits; 0 when no kernel reported a
+ * failure).  Returns GLA_OK when the word is zero.  When it is not, the
+ * workspace is initialised again (gla_workspace_init over `bytes` bytes, on
+ * `stream`) so that it can be reused, and GLA_EKERNEL is returned.
+ * GLA_EINVAL on a bad pointer, size or a null error_bits, GLA_EHIP when the
+ * runtime reports an error (for example a fault of the queued work).
+ */
+GLA_API int gla_workspace_status(void *workspace, size_t bytes, void *stream,
+                                 uint32_t *error_bits);
 
 /*
  * Low-rank retention-gate projection (paper Section 2.1, definition of the
@@ -231,7 +269,9 @@ GLA_API int gla_spatial_swiglu(const void *gate, const void *value, int64_t ld_i
  * Supported: dk == dv in {16, 32, 64}, binary16 or binary32 storage; 64-position
  * chunks.  opts->norm_weight, eps, segment_chunks and algorithm are ignored.
  * The workspace must hold gla_bwd_workspace_size() bytes (no initialisation:
- * every call rewrites what it reads).  All pointers are 16-byte aligned
+ * every call rewrites what it reads).  Its data starts after the same fixed
+ * 4096 + 131072-byte prefix as gla_fwd's, which a backward never writes, so one
+ * workspace can serve both.  All pointers are 16-byte aligned
  * device pointers; the four outputs must not overlap each other, an input or
  * the workspace.  Asynchronous on opts->stream.  Returns a gla_status.
  */

@@ -30,12 +30,16 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-ar
              "-I" + INCLUDE, "-I" + CSRC]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra", "-I" + INCLUDE, "-I" + CSRC]
 
-# (source, compiler) -- the kernel file is split per dtype so the two halves
-# compile in parallel.
+# (source, compiler) -- the generic kernels are instantiated in four units
+# (storage type x square / mixed head sizes) that compile in parallel.
 UNITS = [
     ("gla_plan.cpp", "host", []),
     ("gla_api.cpp", "hip", []),
     ("gla_kernel.hip", "hip", []),
+    ("gla_chunk_f16.hip", "hip", []),
+    ("gla_chunk_f32.hip", "hip", []),
+    ("gla_chunk_f16_mixed.hip", "hip", []),
+    ("gla_chunk_f32_mixed.hip", "hip", []),
     ("gla_onepass.hip", "hip", []),
     ("gla_wide.hip", "hip", []),
     ("gla_proj.hip", "hip", []),

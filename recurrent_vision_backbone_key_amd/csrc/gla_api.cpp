@@ -3,12 +3,52 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gla.h"
 #include "gla_epi.h"
 #include "gla_launch.h"
 #include "gla_plan.h"
 
 namespace {
+
+// Geometry (compute units, XCDs) of the device `stream` belongs to (the
+// current device for the null stream), read from the runtime once per device
+// and kept: it never changes while the process runs.  A host with no device
+// plans for one MI355X (the plan then only sizes workspaces).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_geom[kMaxDevices];  // (cus << 8) | xcds, 0 until read
+
+gla_geom device_geom(void* stream)
+{
+    gla_geom g = {256, 8};
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) dev = -1;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        dev = -1;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return g;
+    }
+    int packed = g_geom[dev].load(std::memory_order_relaxed);
+    if (packed == 0) {
+        int cus = 0, xcds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+            xcds < 1 || xcds > 255)
+            xcds = 1;
+        (void)hipGetLastError();
+        packed = (cus << 8) | xcds;
+        g_geom[dev].store(packed, std::memory_order_relaxed);
+    }
+    g.cus = packed >> 8;
+    g.xcds = packed & 255;
+    return g;
+}
 
 // Launches the planned forward; P.z (or the fused projection operands) set.
 int run_fwd(gla::Params& P, const void* q, const void* k, const void* v, int dir, int H, int W,
@@ -36,17 +76,19 @@ int run_fwd(gla::Params& P, const void* q, const void* k, const void* v, int dir
     P.ticket = P.err = P.flags = nullptr;
     P.xcd_local = plan.xcd_local;
     P.xcd_tasks = plan.xcd_tasks;
+    P.xcds = plan.xcds;
+    P.one_round = plan.one_round;
     P.agg = P.incl = nullptr;
     if (plan.onepass) {
         char* ws = (char*)opts->workspace;
         P.ticket = (unsigned*)ws;
-        P.err = (unsigned*)ws + 1;
+        P.err = (unsigned*)ws + GLA_HDR_ERR;
         P.flags = (unsigned*)(ws + plan.off_flags);
         P.agg = (float*)(ws + plan.off_agg);
         P.incl = (float*)(ws + plan.off_incl);
         return gla::launch_onepass(P, opts->stream);
     }
-    return gla::launch_fwd(P, opts->dtype, opts->dk, chunk, opts->stream);
+    return gla::launch_fwd(P, opts->dtype, opts->dk, opts->dv, chunk, opts->stream);
 }
 
 gla::GateProj gate_of(const gla_gate_proj* g)
@@ -73,7 +115,8 @@ extern "C" int gla_fwd(const void* q, const void* k, const void* v, const float*
                        const gla_opts* opts)
 {
     gla_plan plan;
-    const int st = gla_validate(q, k, v, gate_logits, dir, H, W, chunk, out, r, opts, &plan);
+    const gla_geom geo = device_geom(opts ? opts->stream : nullptr);
+    const int st = gla_validate(q, k, v, gate_logits, dir, H, W, chunk, out, r, opts, &geo, &plan);
     if (st != GLA_OK) return st;
     gla::Params P;
     P.z = gate_logits;
@@ -86,7 +129,8 @@ extern "C" int gla_fwd_gate_proj(const void* q, const void* k, const void* v,
                                  void* out, const void* r, const gla_opts* opts)
 {
     gla_plan plan;
-    const int st = gla_validate_gate_proj(q, k, v, gate, dir, H, W, chunk, out, r, opts, &plan);
+    const gla_geom geo = device_geom(opts ? opts->stream : nullptr);
+    const int st = gla_validate_gate_proj(q, k, v, gate, dir, H, W, chunk, out, r, opts, &geo, &plan);
     if (st != GLA_OK) return st;
     gla::Params P;
     no_proj(P);
@@ -117,7 +161,8 @@ extern "C" size_t gla_workspace_size_gate_proj(int dir, int H, int W, int chunk,
                                                const gla_gate_proj* gate, const gla_opts* opts)
 {
     gla_plan plan;
-    if (gla_make_plan_gate_proj(dir, H, W, chunk, gate, opts, 0, &plan) != GLA_OK) return 0;
+    const gla_geom geo = device_geom(opts ? opts->stream : nullptr);
+    if (gla_make_plan_gate_proj(dir, H, W, chunk, gate, opts, 0, &geo, &plan) != GLA_OK) return 0;
     return plan.workspace_bytes;
 }
 
@@ -132,7 +177,8 @@ extern "C" int gla_gate_logits(const gla_gate_proj* gate, int batch, int tokens,
 extern "C" size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla_opts* opts)
 {
     gla_plan plan;
-    if (gla_make_plan(dir, H, W, chunk, opts, 0, &plan) != GLA_OK) return 0;
+    const gla_geom geo = device_geom(opts ? opts->stream : nullptr);
+    if (gla_make_plan(dir, H, W, chunk, opts, 0, &geo, &plan) != GLA_OK) return 0;
     return plan.workspace_bytes;
 }
 
@@ -141,6 +187,24 @@ extern "C" int gla_workspace_init(void* workspace, size_t bytes, void* stream)
     if (bytes == 0) return GLA_OK;
     if (!workspace || ((uintptr_t)workspace & 15u) != 0 || (bytes & 3u) != 0) return GLA_EINVAL;
     return gla::launch_workspace_init(workspace, bytes, stream);
+}
+
+extern "C" int gla_workspace_status(void* workspace, size_t bytes, void* stream,
+                                    uint32_t* error_bits)
+{
+    if (!error_bits || !workspace || ((uintptr_t)workspace & 15u) != 0 || bytes < GLA_HEADER_BYTES ||
+        (bytes & 3u) != 0)
+        return GLA_EINVAL;
+    *error_bits = 0;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, (const char*)workspace + 4 * GLA_HDR_ERR, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return GLA_EHIP;
+    *error_bits = word;
+    if (word == 0) return GLA_OK;
+    const int ls = gla::launch_workspace_init(workspace, bytes, stream);
+    return ls == GLA_OK ? GLA_EKERNEL : ls;
 }
 
 extern "C" int gla_spatial_swiglu(const void* gate, const void* value, int64_t ld_in,
@@ -159,8 +223,8 @@ namespace {
 // Launch parameters of the backward for validated arguments.
 void bwd_params(const void* q, const void* k, const void* v, const float* gate_logits,
                 const void* dout, int dir, int H, int W, void* dq, void* dk, void* dv, float* dz,
-                const gla_opts* opts, char* ws, int nchunks, size_t off_r, size_t off_s,
-                gla::Params& P, gla::BwdParams& Q)
+                const gla_opts* opts, char* ws, int nchunks, size_t off_f, size_t off_r,
+                size_t off_s, gla::Params& P, gla::BwdParams& Q)
 {
     P.q = q;
     P.k = k;
@@ -186,13 +250,15 @@ void bwd_params(const void* q, const void* k, const void* v, const float* gate_l
     P.agg = P.incl = nullptr;
     P.xcd_local = 0;
     P.xcd_tasks = 0;
+    P.xcds = 1;
+    P.one_round = 0;
     no_proj(P);
     Q.dout = dout;
     Q.dq = dq;
     Q.dk = dk;
     Q.dv = dv;
     Q.dz = dz;
-    Q.ws_f = (float*)ws;
+    Q.ws_f = (float*)(ws + off_f);
     Q.ws_r = (float*)(ws + off_r);
     Q.ws_s = (float*)(ws + off_s);
 }
@@ -204,22 +270,22 @@ extern "C" int gla_bwd(const void* q, const void* k, const void* v, const float*
                        float* dz, const gla_opts* opts)
 {
     int nchunks = 0;
-    size_t off_r = 0, off_s = 0;
+    size_t off_f = 0, off_r = 0, off_s = 0;
     const int st = gla_validate_bwd(q, k, v, gate_logits, dout, dir, H, W, dq, dk, dv, dz, opts,
-                                    &nchunks, &off_r, &off_s);
+                                    &nchunks, &off_f, &off_r, &off_s);
     if (st != GLA_OK) return st;
     gla::Params P;
     gla::BwdParams Q;
     bwd_params(q, k, v, gate_logits, dout, dir, H, W, dq, dk, dv, dz, opts, (char*)opts->workspace,
-               nchunks, off_r, off_s, P, Q);
+               nchunks, off_f, off_r, off_s, P, Q);
     return gla::launch_bwd(P, Q, opts->dtype, opts->dk, opts->stream);
 }
 
 extern "C" size_t gla_bwd_workspace_size(int dir, int H, int W, const gla_opts* opts)
 {
     int nchunks = 0;
-    size_t off_r = 0, off_s = 0, bytes = 0;
-    if (gla_plan_bwd(dir, H, W, opts, &nchunks, &off_r, &off_s, &bytes) != GLA_OK) return 0;
+    size_t off_f = 0, off_r = 0, off_s = 0, bytes = 0;
+    if (gla_plan_bwd(dir, H, W, opts, &nchunks, &off_f, &off_r, &off_s, &bytes) != GLA_OK) return 0;
     return bytes;
 }
 
@@ -237,7 +303,7 @@ extern "C" int gla_bwd_gated(const void* q, const void* k, const void* v,
     gla::BwdParams Q;
     // dO (binary32) is produced inside the call, in the workspace
     bwd_params(q, k, v, gate_logits, ws + lay.off_do, dir, H, W, dq, dk, dv, dz, opts, ws,
-               lay.nchunks, lay.off_r, lay.off_s, P, Q);
+               lay.nchunks, lay.off_f, lay.off_r, lay.off_s, P, Q);
     gla::GatedBwd G;
     G.r = r;
     G.du = dout;
@@ -264,6 +330,7 @@ extern "C" const char* gla_status_str(int status)
     case GLA_EUNSUPPORTED: return "GLA_EUNSUPPORTED: head dim, chunk, dtype or size outside the built set";
     case GLA_EWORKSPACE: return "GLA_EWORKSPACE: workspace missing, misaligned or smaller than gla_workspace_size()";
     case GLA_EHIP: return "GLA_EHIP: HIP runtime error at launch";
+    case GLA_EKERNEL: return "GLA_EKERNEL: a kernel reported a failure in the workspace error word";
     default: return "unknown gla status";
     }
 }

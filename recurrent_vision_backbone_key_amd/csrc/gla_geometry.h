@@ -24,7 +24,7 @@ constexpr int lds_bytes(int ts, int dk, int dv, int c)
            + 2 * c * 4;                   // row tables (double buffered)
 }
 
-constexpr bool config_fits(int ts, int d, int c) { return lds_bytes(ts, d, d, c) <= kLdsLimit; }
+constexpr bool config_fits(int ts, int dk, int dv, int c) { return lds_bytes(ts, dk, dv, c) <= kLdsLimit; }
 
 }  // namespace gla
 

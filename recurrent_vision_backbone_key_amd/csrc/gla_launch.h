@@ -19,10 +19,11 @@ struct Params {
     const float* w;     // [DV] RMSNorm weight, or null (ones)
     void* out;          // [B, L, NH, DV]
     float* ws;          // three-pass: segment slots [units][nseg-1][DK*DV + DK] fp32
-    // single-pass exchange (workspace): ticket and error word, one flag per
-    // (scan, segment), segment aggregates and group transfers
-    unsigned* ticket;   // word 0: ticket counter; words 16 (1 + x): counter of XCD x
-    unsigned* err;
+    // single-pass exchange (workspace): header words, one flag per (scan,
+    // segment), segment aggregates and group transfers
+    unsigned* ticket;   // workspace header (words GLA_HDR_* of gla_plan.h)
+    unsigned* err;      // header word GLA_HDR_ERR: sticky error bits (GLA_WS_ERR_*),
+                        // followed by the initialisation mark
     unsigned* flags;    // [units][nseg]: bits 1 aggregate, 2 group transfer, 4 done
     float* agg;         // [units][nseg][DK*DV + DK]
     float* incl;        // [units][nseg][DK*DV + DK]: group transfers (leaders' slots)
@@ -30,8 +31,10 @@ struct Params {
     int nchunks;        // ceil(L / chunk)
     int seg_chunks;     // chunks per segment
     int nseg;           // segments per scan
-    int xcd_local;      // single pass: scan u runs on XCD u mod 8 (exchange in that L2)
-    int xcd_tasks;      // single pass, xcd_local: workgroups per XCD (grid / 8)
+    int xcd_local;      // single pass: scan u runs on XCD u mod xcds (exchange in that L2)
+    int xcd_tasks;      // single pass, xcd_local: workgroups per XCD (grid / xcds)
+    int xcds;           // single pass: XCDs of the device
+    int one_round;      // single pass: every workgroup of the call is resident at once
     float scale;        // output scale
     float inv_tau;      // 1 / tau
     float eps;          // RMSNorm epsilon
@@ -56,7 +59,7 @@ constexpr int kFusedProjRank = 16;
 
 // Launches the aggregate, fold and output passes (or only the output pass
 // when nseg == 1) on `stream`.  Returns a gla_status value.
-int launch_fwd(const Params& P, int dtype, int d, int chunk, void* stream);
+int launch_fwd(const Params& P, int dtype, int dk, int dv, int chunk, void* stream);
 
 // Fold pass alone: turns the segment aggregates in P.ws into incoming states.
 int launch_fold(const Params& P, int d, void* stream);

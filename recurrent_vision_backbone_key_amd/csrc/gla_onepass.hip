@@ -46,6 +46,7 @@
 #include "gla_device.h"
 #include "gla_geometry.h"
 #include "gla_launch.h"
+#include "gla_plan.h"
 
 namespace gla {
 namespace onepass {
@@ -58,11 +59,6 @@ constexpr int NSUB = 4;   // 16-token sub-chunks per chunk
 constexpr int NCH = kOnePassMaxChunks;  // chunks per segment (upper bound)
 constexpr int SH = D + 8; // binary16 row stride (elements): 144-byte rows
 constexpr int SF = D + 4; // fp32 row stride (elements): 272-byte rows
-// The incoming state of a segment enters its outputs as binary16 hi + lo.
-#ifndef GLA_ONEPASS_IN_LO
-#define GLA_ONEPASS_IN_LO 0
-#endif
-constexpr bool kInLo = GLA_ONEPASS_IN_LO;
 // Per-wave factor table rows (sub-chunk i of the wave, 32 channels of its half):
 constexpr int FD = 0;     // 2^{-tot_i}                 diagonal query factor (>= 1)
 constexpr int FQ = 1;     // 2^{R_i}                    q (.) 2^b for the local inter-chunk term
@@ -100,7 +96,6 @@ static_assert(LDS_PROJ <= kLdsLimit, "LDS budget of one CU exceeded (fused gate 
 // phase-2/3 aliases
 constexpr int L_LSEG = L_PA;                  // segment local state [D][D] f32 (16 KiB)
 constexpr int L_GSEG = L_PA + D * D * 4;      // segment total decay [D] f32
-constexpr int L_STL = L_E;                    // S_in^T lo [D][SH] f16
 constexpr int L_OUT = L_PA;                   // output staging [NCH][C][SH] f16
 static_assert(L_GSEG + D * 4 <= L_TOT, "segment aggregate overlaps live buffers");
 static_assert(L_OUT + NCH * C * SH * 2 <= L_TOT, "output staging overlaps live buffers");
@@ -127,17 +122,17 @@ __device__ __forceinline__ void st_u(unsigned* p, unsigned v)
 // L2s).  Flags: sc1 as well when the workgroups of a scan may run on different
 // XCDs; when every workgroup of a scan runs on one XCD (LOCAL), the default
 // policy, which leaves the line in that XCD's L2 where the sc1 loads of the
-// same XCD find it (about half the round-trip latency).  Measured on MI355X,
-// write-back exchange data kept the kernel running 2-3 us after its last
-// workgroup had ended (one 1600-token frame with 6 heads: 18.7 us per call
-// with write-back aggregates and inclusive states, 15.6 us written through,
-// though the exchange inside the workgroups takes about 0.4 us longer), while
-// write-through flags slowed every look-back.
+// same XCD find it (about half the round-trip latency).  Measured on MI355X:
+// write-back aggregates and inclusive states kept the kernel running 2-3 us
+// after its last workgroup had ended (one 1600-token frame with 6 heads: 18.7
+// us per call against 15.6 us written through), while write-through flags in
+// LOCAL plans cost 1.4 us per call on that frame and 3.8 us on a batch of 8.
 template <bool LOCAL> struct Pol {
     static constexpr int kLoad = 16;
     static constexpr int kStore = LOCAL ? 0 : 16;
 };
 constexpr int kStoreThrough = 16;  // sc1
+constexpr unsigned kPoison = 8u;
 template <bool LOCAL>
 __device__ __forceinline__ float4v ld_x4(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
@@ -156,7 +151,8 @@ __device__ __forceinline__ void st_x1(__amdgpu_buffer_rsrc_t r, unsigned off, fl
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, kStoreThrough);
 }
-// Segment flags of one scan (0 none, 1 aggregate, 2 inclusive state).
+// Segment flags of one scan: bit 1 aggregate, bit 2 inclusive state or group
+// transfer, bit 4 done reading, kPoison published by a poisoned task.
 template <bool LOCAL>
 __device__ __forceinline__ unsigned ld_flag(const unsigned* flags, int nseg, int i)
 {
@@ -259,6 +255,21 @@ __device__ __forceinline__ void proj_logits(const float4v& hp, const float* sW2,
     for (int T = 0; T < 2; ++T)
 #pragma unroll
         for (int e = 0; e < 4; ++e) zv[4 * T + e] = acc[T][e];
+}
+
+// Writes NaN to every output row of the task (scan `unit`, segment `seg`):
+// the outputs of a task whose exchange could not complete are never left
+// holding stale data.
+__device__ __forceinline__ void nan_rows(const Params& P, int unit, int seg, int tid)
+{
+    const int c_begin = seg * P.seg_chunks;
+    const int n = (min(P.nchunks, c_begin + P.seg_chunks) - c_begin) * C;
+    const _Float16 qnan = __builtin_bit_cast(_Float16, (unsigned short)0x7e00u);
+    const half8 nan8 = {qnan, qnan, qnan, qnan, qnan, qnan, qnan, qnan};
+    for (int i = tid; i < n * (D / 8); i += NT) {
+        const int row = scan_row(P, unit, c_begin * C + i / (D / 8));
+        if (row >= 0) *(half8*)((_Float16*)P.out + (size_t)row * D + 8 * (i % (D / 8))) = nan8;
+    }
 }
 
 // Intra-chunk scores (M1, with the exchange of the two channel halves) and
@@ -402,38 +413,80 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     const int grid = nunits * P.nseg;
 
     // ---- ticket: logical (segment, scan) in start order.  LOCAL: scan u runs
-    //      on XCD u mod 8; the workgroups of an XCD number their tasks with the
-    //      XCD's own counter (the grid gives every XCD the same count).
+    //      on XCD u mod xcds; the workgroups of an XCD number their tasks with
+    //      the XCD's own counter.  The dispatcher hands workgroups to the XCDs
+    //      in turn (from whichever XCD it starts at), and the grid is a
+    //      multiple of xcds, so every XCD receives exactly xcd_tasks of them
+    //      and the one that takes an XCD's last ticket clears its counter.  A
+    //      dispatch that broke this would leave some list's tasks unrun: the
+    //      segments after them give up their bounded wait, report and write
+    //      NaN.  Beside the ticket, thread 0 reads the error word and the
+    //      initialisation mark.
     if (tid == 0) {
+        const unsigned long long em =
+            __hip_atomic_load((const unsigned long long*)P.err, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
         if (LOCAL) {
-            const unsigned x = __builtin_amdgcn_s_getreg(kXccIdReg) & 7u;
-            unsigned* ctr = P.ticket + 16 * (1 + x);
+            const unsigned x = (__builtin_amdgcn_s_getreg(kXccIdReg) & 15u) % (unsigned)P.xcds;
+            unsigned* ctr = P.ticket + GLA_HDR_XCD + 32 * x;
             const unsigned t = atomicAdd(ctr, 1u);
-            if (t == (unsigned)P.xcd_tasks - 1u) st_u(ctr, 0u);  // every ticket is taken
+            if (t == (unsigned)P.xcd_tasks - 1u) st_u(ctr, 0u);  // every ticket of this XCD is taken
             sMisc[0] = (int)t;
             sMisc[2] = (int)x;
         } else {
-            const unsigned t = atomicAdd(P.ticket, 1u);
-            if (t == (unsigned)grid - 1u) st_u(P.ticket, 0u);  // every ticket is taken
+            const unsigned t = atomicAdd(P.ticket + GLA_HDR_TICKET, 1u);
+            if (t == (unsigned)grid - 1u) st_u(P.ticket + GLA_HDR_TICKET, 0u);  // every ticket is taken
             sMisc[0] = (int)t;
         }
+        // (the word pair is consumed only here, after the ticket's round trip)
+        const bool mark_ok = (unsigned)(em >> 32) == GLA_WS_MARK;
+        sMisc[3] = (mark_ok ? 1 : 0) | ((unsigned)em != 0u ? 2 : 0);
     }
     __syncthreads();
     const int ticket = sMisc[0];
+    // poisoned: a failure upstream (a sticky error from an earlier call, a
+    // wait that gave up, a transfer folded from a poisoned segment): every
+    // store of this task writes NaN and every flag it publishes carries the
+    // poison bit, so no row downstream of a failure holds plausible data
+    bool poisoned = (sMisc[3] & 2) != 0;
     int seg, unit;
+    if (!(sMisc[3] & 1)) {
+        // the workspace was not initialised by gla_workspace_init (counters and
+        // flags untrusted): report and fill the rows of this block's task (one
+        // block per task) with NaN
+        if (tid == 0) atomicOr(P.err, GLA_WS_ERR_INIT);
+        const int b = blockIdx.x;
+        if (LOCAL) {
+            const int x = b % P.xcds, t = b / P.xcds;
+            const int units_x = (nunits - x + P.xcds - 1) / P.xcds;
+            if (x >= nunits || t >= units_x * P.nseg) return;
+            seg = t / units_x;
+            unit = x + P.xcds * (t - seg * units_x);
+        } else {
+            if (b >= grid) return;
+            seg = b / nunits;
+            unit = b - seg * nunits;
+        }
+        nan_rows(P, unit, seg, tid);
+        return;
+    }
     if (LOCAL) {
         const int x = sMisc[2];
-        if (ticket >= P.xcd_tasks) {  // workspace not initialised: report, do nothing
-            if (tid == 0) atomicOr(P.err, 2u);
+        const int units_x = (nunits - x + P.xcds - 1) / P.xcds;  // scans x, x + xcds, ... run here
+        if (ticket >= P.xcd_tasks) {  // counters not cleared: report, fill the task's rows with NaN
+            if (tid == 0) atomicOr(P.err, GLA_WS_ERR_TICKET);
+            const int t = ticket % P.xcd_tasks;
+            if (t < units_x * P.nseg) nan_rows(P, x + P.xcds * (t % units_x), t / units_x, tid);
             return;
         }
-        const int units_x = (nunits - x + 7) / 8;  // scans x, x + 8, ... run here
-        if (ticket >= units_x * P.nseg) return;     // spare workgroup of this XCD
+        if (ticket >= units_x * P.nseg) return;  // spare workgroup of this XCD
         seg = ticket / units_x;
-        unit = x + 8 * (ticket - seg * units_x);
+        unit = x + P.xcds * (ticket - seg * units_x);
     } else {
-        if (ticket >= grid) {  // workspace not initialised: report, do nothing
-            if (tid == 0) atomicOr(P.err, 2u);
+        if (ticket >= grid) {  // counters not cleared: report, fill the task's rows with NaN
+            if (tid == 0) atomicOr(P.err, GLA_WS_ERR_TICKET);
+            const int t = ticket % grid;
+            nan_rows(P, t % nunits, t / nunits, tid);
             return;
         }
         seg = ticket / nunits;
@@ -670,7 +723,6 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     const size_t slot = (size_t)unit * P.nseg + seg;
     float* sL = (float*)(lds + L_LSEG);
     float* sG = (float*)(lds + L_GSEG);
-    _Float16* sSTL = (_Float16*)(lds + L_STL);
     const bool need_in = (seg > 0);
     if (P.nseg > 1) {
         // local state and total decay into LDS, row-major [ch][dv]
@@ -696,7 +748,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         // at the same time) fold published aggregates directly; plans of
         // several rounds use inclusive states, which the segments of earlier
         // rounds have published by the time later ones look back.
-        const bool one_round = LOCAL ? (P.xcd_tasks <= 32) : (nunits * P.nseg <= 256);
+        const bool one_round = P.one_round != 0;
         if (one_round) {
             // Exchange.  Every segment but the last publishes its aggregate and
             // segment j folds the aggregates of segments 0 .. j-1 from zero, in
@@ -722,22 +774,37 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             auto leader_slot = [&](int gg) { return (size_t)unit * P.nseg + (size_t)(gg * G + G - 1); };
             // wave 0 waits until groups 0 .. ng-1 have their combined transfers and
             // segments first .. first+cnt-1 their aggregates (ng + cnt <= 64)
+            // (a poison bit on any of those flags, or a wait that gives up,
+            // poisons this task)
             auto wait_for = [&](int ng, int first, int cnt) {
                 if (wave == 0) {
                     unsigned spins = 0;
+                    bool bad = false;
                     for (;;) {
                         bool ok = true;
-                        if (lane < ng) ok = (ld_flag<LOCAL>(flags, P.nseg, lane * G + G - 1) & 2u) != 0u;
-                        else if (lane < ng + cnt) ok = (ld_flag<LOCAL>(flags, P.nseg, first + lane - ng) & 1u) != 0u;
-                        if (__all(ok)) break;
+                        unsigned f = 0u;
+                        if (lane < ng) {
+                            f = ld_flag<LOCAL>(flags, P.nseg, lane * G + G - 1);
+                            ok = (f & 2u) != 0u;
+                        } else if (lane < ng + cnt) {
+                            f = ld_flag<LOCAL>(flags, P.nseg, first + lane - ng);
+                            ok = (f & 1u) != 0u;
+                        }
+                        if (__all(ok)) {
+                            bad = __any((f & kPoison) != 0u);
+                            break;
+                        }
                         if (++spins > (1u << 22)) {
-                            if (lane == 0) atomicOr(P.err, 1u);
+                            if (lane == 0) atomicOr(P.err, GLA_WS_ERR_WAIT);
+                            bad = true;
                             break;
                         }
                         __builtin_amdgcn_s_sleep(2);
                     }
+                    if (lane == 0) sMisc[14] = bad ? 1 : 0;
                 }
                 __syncthreads();
+                poisoned |= sMisc[14] != 0;
             };
             // fold, from (s0, s1), the combined transfers of groups 0 .. ng-1 and
             // then the aggregates of segments first .. first+cnt-1, in that order;
@@ -775,7 +842,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             auto set_flag = [&](unsigned v) {
                 wait_mem();
                 __syncthreads();
-                if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, v);
+                if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, v | (poisoned ? kPoison : 0u));
             };
             if (!last && !leader) {
                 // aggregate: local state and multiplier 2^G
@@ -814,14 +881,12 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
                 float m0 = 1.f, m1 = 1.f;
                 fold(s0, s1, m0, m1, grp, gfirst, seg - gfirst);
-                // S_in^T (hi, lo) for phase 3
+                // S_in^T (binary16) for phase 3
     #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const _Float16 h0 = (_Float16)s0[e], h1 = (_Float16)s1[e];
                     sST[(cl0 + e) * SH + ch0] = h0;
-                    if (kInLo) sSTL[(cl0 + e) * SH + ch0] = (_Float16)(s0[e] - (float)h0);
                     sST[(cl0 + e) * SH + ch0 + 32] = h1;
-                    if (kInLo) sSTL[(cl0 + e) * SH + ch0 + 32] = (_Float16)(s1[e] - (float)h1);
                 }
                 if (!last) set_flag(leader ? 6u : 5u);
             }
@@ -840,14 +905,17 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 if (tid < D / 4) st_x4(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
                 wait_mem();
                 __syncthreads();
-                if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 1u);  // aggregate
+                if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, 1u | (poisoned ? kPoison : 0u));  // aggregate
             }
             if (need_in) {
                 // look back: wait until every earlier segment has published, then
                 // start from the latest inclusive state
+                // (a poison bit on any earlier flag, or a wait that gives up,
+                // poisons this task)
                 if (wave == 0) {
                     unsigned spins = 0;
                     int k = -1;
+                    bool bad = false;
                     for (;;) {
                         const int idx = seg - 1 - lane;
                         const unsigned f = (idx >= 0) ? ld_flag<LOCAL>(flags, P.nseg, idx) : 2u;
@@ -856,18 +924,24 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                             // lowest lane with an inclusive state = latest segment
                             // (segment 0 always publishes one, so inc != 0)
                             k = inc ? seg - 1 - (int)__builtin_ctzll(inc) : -1;
+                            bad = __any((f & kPoison) != 0u);
                             break;
                         }
                         if (++spins > (1u << 22)) {
-                            if (lane == 0) atomicOr(P.err, 1u);
+                            if (lane == 0) atomicOr(P.err, GLA_WS_ERR_WAIT);
+                            bad = true;
                             break;
                         }
                         __builtin_amdgcn_s_sleep(2);
                     }
-                    if (lane == 0) sMisc[1] = k;
+                    if (lane == 0) {
+                        sMisc[1] = k;
+                        sMisc[14] = bad ? 1 : 0;
+                    }
                 }
                 __syncthreads();
                 const int k = sMisc[1];
+                poisoned |= sMisc[14] != 0;
                 // forward fold from the inclusive state of segment k
                 float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
                 if (k >= 0) {
@@ -899,14 +973,12 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                             }
                         }
                 }
-                // S_in^T (hi, lo) for phase 3; inclusive state for successors
+                // S_in^T (binary16) for phase 3; inclusive state for successors
     #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const _Float16 h0 = (_Float16)s0[e], h1 = (_Float16)s1[e];
                     sST[(cl0 + e) * SH + ch0] = h0;
-                    if (kInLo) sSTL[(cl0 + e) * SH + ch0] = (_Float16)(s0[e] - (float)h0);
                     sST[(cl0 + e) * SH + ch0 + 32] = h1;
-                    if (kInLo) sSTL[(cl0 + e) * SH + ch0 + 32] = (_Float16)(s1[e] - (float)h1);
                 }
                 if (!last) {
                     const float gm0 = sG[ch0], gm1 = sG[ch0 + 32];
@@ -929,7 +1001,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             if (!last) {
                 wait_mem();
                 __syncthreads();
-                if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, seg > 0 ? 7u : 6u);  // inclusive, done
+                if (tid == 0)  // inclusive, done
+                    st_flag<LOCAL>(flags, P.nseg, seg, (seg > 0 ? 7u : 6u) | (poisoned ? kPoison : 0u));
             }
         }
     }
@@ -957,12 +1030,6 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 const half8 h1 = *(const half8*)(sST + (32 * h + 16 + l16) * SH + k0);
                 o0 = mma(h0, qf, o0);
                 o1 = mma(h1, qf, o1);
-                if (kInLo) {
-                    const half8 l0 = *(const half8*)(sSTL + (32 * h + l16) * SH + k0);
-                    const half8 l1 = *(const half8*)(sSTL + (32 * h + 16 + l16) * SH + k0);
-                    o0 = mma(l0, qf, o0);
-                    o1 = mma(l1, qf, o1);
-                }
             }
         }
         okeep[cc][0] = o0 * P.scale;
@@ -1006,6 +1073,10 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) hv[e] = (_Float16)okeep[cc][m][e];
             }
+            if (poisoned) {
+                const _Float16 qnan = __builtin_bit_cast(_Float16, (unsigned short)0x7e00u);
+                hv = half4{qnan, qnan, qnan, qnan};
+            }
             if (t >= 0) *(half4*)((_Float16*)P.out + (size_t)t * D + 32 * h + 16 * m + 4 * g) = hv;
         }
     }
@@ -1024,7 +1095,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             const unsigned f = mine ? ld_flag<LOCAL>(flags, P.nseg, lane) : 4u;
             if (__all((f & 4u) != 0u)) break;
             if (++spins > (1u << 22)) {
-                if (lane == 0) atomicOr(P.err, 1u);
+                if (lane == 0) atomicOr(P.err, GLA_WS_ERR_WAIT);
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
@@ -1033,11 +1104,13 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     }
 }
 
-// Zero-fills the single-pass workspace header and flags.
+// Zero-fills a workspace (header, flags) and writes the initialisation mark
+// into header word 2 when the header is complete.
 __global__ __launch_bounds__(256) void gla_onepass_init(unsigned* words, size_t n)
 {
+    const size_t header_words = GLA_HEADER_BYTES / 4;
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
-        words[i] = 0u;
+        words[i] = (i == GLA_HDR_MARK && n >= header_words) ? GLA_WS_MARK : 0u;
 }
 
 }  // namespace onepass
@@ -1045,7 +1118,7 @@ __global__ __launch_bounds__(256) void gla_onepass_init(unsigned* words, size_t 
 int launch_onepass(const Params& P, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
-    const dim3 grid(P.xcd_local ? 8 * P.xcd_tasks : P.B * P.NH * P.nseg);
+    const dim3 grid(P.xcd_local ? P.xcds * P.xcd_tasks : P.B * P.NH * P.nseg);
     const bool proj = (P.ghp != nullptr);
     // one-chunk segments take an instance with a single chunk's registers and
     // a straight-line body (a small code footprint for the cold instruction

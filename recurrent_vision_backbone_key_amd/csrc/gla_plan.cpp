@@ -11,19 +11,14 @@
 
 namespace {
 
-constexpr int kCUs = 256;          // compute units of one MI355X
-constexpr int kXcds = 8;           // accelerator dies (XCDs), each with its own L2
-constexpr int kCUsPerXcd = kCUs / kXcds;
-// Single-pass workspace header: word 0 ticket counter, word 1 error word,
-// word 16 (1 + x) ticket counter of XCD x.
-constexpr size_t kOnePassHeader = 1024;
-// Every forward layout starts with the same fixed prefix: the single pass's
-// header (ticket counters, error word) and room for kFlagWords segment flags.
-// Data never lands there, so a workspace reused across shapes or algorithms
-// never finds another call's data where its own flags must read zero.
-constexpr size_t kFlagWords = 32768;
-constexpr size_t kReserved = kOnePassHeader + kFlagWords * 4;
-constexpr int kTargetGroups = 2 * kCUs;
+// Default geometry: one MI355X in its single-partition mode.
+constexpr gla_geom kMi355x = {256, 8};
+constexpr size_t kFlagWords = GLA_FLAG_WORDS;
+// Every forward layout starts with the same fixed prefix (header and flag
+// room; see gla_plan.h).  Data never lands there, so a workspace reused
+// across shapes, algorithms or backward calls never finds another call's data
+// where its own counters, flags and mark must be.
+constexpr size_t kReserved = GLA_PREFIX_BYTES;
 
 bool is_pow2_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
@@ -36,24 +31,36 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// A usable geometry: the one given, else the default.
+gla_geom geometry(const gla_geom* geo)
+{
+    gla_geom g = geo ? *geo : kMi355x;
+    if (g.cus < 1) g.cus = kMi355x.cus;
+    if (g.xcds < 1 || g.xcds > g.cus) g.xcds = 1;
+    return g;
+}
+
 }  // namespace
 
-extern "C" int gla_config_built(int dtype, int d, int chunk)
+extern "C" int gla_config_built(int dtype, int dk, int dv, int chunk)
 {
     if (dtype != GLA_F16 && dtype != GLA_F32) return 0;
-    if (!is_pow2_dim(d) || !is_pow2_dim(chunk)) return 0;
-    return gla::config_fits(dtype == GLA_F16 ? 2 : 4, d, chunk) ? 1 : 0;
+    if (!is_pow2_dim(dk) || !is_pow2_dim(dv) || !is_pow2_dim(chunk)) return 0;
+    if (dk != dv && chunk != 64) return 0;
+    return gla::config_fits(dtype == GLA_F16 ? 2 : 4, dk, dv, chunk) ? 1 : 0;
 }
 
 extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o,
-                             int has_gate, gla_plan* plan)
+                             int has_gate, const gla_geom* geo, gla_plan* plan)
 {
     if (!o || !plan) return GLA_EINVAL;
     if (o->batch < 1 || o->heads < 1 || H < 1 || W < 1) return GLA_EINVAL;
     if (dir < GLA_L2R || dir > GLA_B2T) return GLA_EINVAL;
     if (o->dtype != GLA_F16 && o->dtype != GLA_F32) return GLA_EUNSUPPORTED;
-    if (!is_pow2_dim(o->dk) || !is_pow2_dim(o->dv) || o->dk != o->dv) return GLA_EUNSUPPORTED;
-    if (!is_pow2_dim(chunk) || !gla_config_built(o->dtype, o->dk, chunk)) return GLA_EUNSUPPORTED;
+    if (!is_pow2_dim(o->dk) || !is_pow2_dim(o->dv)) return GLA_EUNSUPPORTED;
+    if (!is_pow2_dim(chunk) || !gla_config_built(o->dtype, o->dk, o->dv, chunk)) return GLA_EUNSUPPORTED;
     const int64_t L = (int64_t)H * W;
     if (L >= (int64_t)1 << 24) return GLA_EUNSUPPORTED;
     const int64_t rows = (int64_t)o->batch * L * o->heads;  // kernel row index is int32
@@ -64,9 +71,13 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     const int nchunks = (int)((L + chunk - 1) / chunk);
     const int64_t units = (int64_t)o->batch * o->heads;
     if (o->algorithm < GLA_ALGO_AUTO || o->algorithm > GLA_ALGO_THREE_PASS) return GLA_EINVAL;
+    const gla_geom gm = geometry(geo);
+    const int cus = gm.cus, xcds = gm.xcds, cus_per_xcd = gm.cus / gm.xcds;
     plan->L = (int)L;
     plan->nchunks = nchunks;
     plan->onepass = 0;
+    plan->xcds = xcds;
+    plan->one_round = 0;
     plan->proj_fused = 0;
     plan->off_z = 0;
     plan->off_flags = plan->off_agg = plan->off_incl = plan->off_slots = 0;
@@ -74,8 +85,8 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     // Single pass: binary16, d = 64, 64-token chunks; segments of at most
     // kOnePassMaxChunks chunks, at most 65 segments per scan (one wavefront
     // of look-back), about one workgroup per compute unit.  When the scans
-    // spread over the 8 XCDs without costing a second round of workgroups on
-    // any of them (or divide evenly), scan u runs on XCD u mod 8 and the
+    // spread over the XCDs without costing a second round of workgroups on
+    // any of them (or divide evenly), scan u runs on XCD u mod xcds and the
     // segment exchange stays in that XCD's L2.
     // (the kernel addresses its inputs with 32-bit buffer offsets: the fp32
     // gate logits, 256 bytes per row, stay below 2^31 bytes)
@@ -85,7 +96,7 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     plan->xcd_tasks = 0;
     if (o->algorithm != GLA_ALGO_THREE_PASS && sp_shape) {
         const int min_seg = (nchunks + 64) / 65;
-        const int64_t upx = (units + kXcds - 1) / kXcds;  // scans per XCD (most)
+        const int64_t upx = (units + xcds - 1) / xcds;  // scans per XCD (most)
         const int max_seg = nchunks < gla::kOnePassMaxChunks ? nchunks : gla::kOnePassMaxChunks;
         // the shortest segment whose workgroups fit in `slots` at `per` scans
         // (the longest allowed when none does)
@@ -94,16 +105,16 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
                 if (per * ((nchunks + sg - 1) / sg) <= slots) return sg;
             return max_seg;
         };
-        const int seg_g = fit_seg(units, kCUs);
-        const int seg_l = fit_seg(upx, kCUsPerXcd);
+        const int seg_g = fit_seg(units, cus);
+        const int seg_l = fit_seg(upx, cus_per_xcd);
         int seg = o->segment_chunks;
         if (seg > nchunks) seg = nchunks;
         // XCD-local when it keeps segments as short as the chip-wide plan and
         // either fits one round per XCD or the scans divide evenly over XCDs
         const int seg_chk = seg > 0 ? seg : seg_l;
         const int64_t tasks = upx * ((nchunks + seg_chk - 1) / seg_chk);
-        const bool local = (seg > 0 || seg_l <= seg_g) &&
-                           (tasks <= kCUsPerXcd || units % kXcds == 0);
+        const bool local = xcds > 1 && xcds <= GLA_MAX_XCDS && (seg > 0 || seg_l <= seg_g) &&
+                           (tasks <= cus_per_xcd || units % xcds == 0);
         if (seg <= 0) seg = local ? seg_l : seg_g;
         const size_t nflag = (size_t)units * ((nchunks + seg - 1) / (seg > 0 ? seg : 1));
         if (seg >= min_seg && seg <= gla::kOnePassMaxChunks && nflag <= kFlagWords) {
@@ -113,7 +124,8 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
             plan->nseg = nseg;
             plan->xcd_local = local ? 1 : 0;
             plan->xcd_tasks = local ? (int)(upx * nseg) : 0;
-            plan->off_flags = kOnePassHeader;
+            plan->one_round = local ? (plan->xcd_tasks <= cus_per_xcd) : (units * nseg <= cus);
+            plan->off_flags = GLA_HEADER_BYTES;
             plan->off_agg = kReserved;
             plan->off_incl = plan->off_agg + nflag * ((size_t)64 * 64 + 64) * 4;
             plan->workspace_bytes = plan->off_incl + nflag * ((size_t)64 * 64 + 64) * 4;
@@ -124,8 +136,8 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
         // Three passes: segments of seg_chunks chunks, enough workgroups for
         // the chip (the d = 128 binary16 chunk-64 kernels hold one workgroup
         // per compute unit: three full rounds).
-        const bool wide = o->dtype == GLA_F16 && o->dk == 128 && chunk == 64;
-        const int64_t target = wide ? 3 * kCUs : kTargetGroups;
+        const bool wide = o->dtype == GLA_F16 && o->dk == 128 && o->dv == 128 && chunk == 64;
+        const int64_t target = wide ? 3 * (int64_t)cus : 2 * (int64_t)cus;
         int seg = o->segment_chunks;
         if (seg <= 0) {
             const int64_t want = (units * nchunks + target - 1) / target;
@@ -200,11 +212,11 @@ void gate_operands(const gla_gate_proj* gate, size_t tokens, int heads, int dk, 
 
 extern "C" int gla_validate(const void* q, const void* k, const void* v, const float* z,
                             int dir, int H, int W, int chunk, const void* out, const void* r,
-                            const gla_opts* o, gla_plan* plan)
+                            const gla_opts* o, const gla_geom* geo, gla_plan* plan)
 {
     if (!o || !plan) return GLA_EINVAL;
     if (!q || !k || !v || !z || !out) return GLA_EINVAL;
-    const int st = gla_make_plan(dir, H, W, chunk, o, r != nullptr, plan);
+    const int st = gla_make_plan(dir, H, W, chunk, o, r != nullptr, geo, plan);
     if (st != GLA_OK) return st;
 
     const size_t es = o->dtype == GLA_F16 ? 2 : 4;
@@ -216,15 +228,18 @@ extern "C" int gla_validate(const void* q, const void* k, const void* v, const f
 }
 
 extern "C" int gla_make_plan_gate_proj(int dir, int H, int W, int chunk, const gla_gate_proj* gate,
-                                       const gla_opts* o, int has_gate, gla_plan* plan)
+                                       const gla_opts* o, int has_gate, const gla_geom* geo,
+                                       gla_plan* plan)
 {
     int st = check_gate_sizes(gate);
     if (st != GLA_OK) return st;
-    st = gla_make_plan(dir, H, W, chunk, o, has_gate, plan);
+    st = gla_make_plan(dir, H, W, chunk, o, has_gate, geo, plan);
     if (st != GLA_OK) return st;
     // fused (single pass, rank 16): x W1 staged, 16 binary32 values per
-    // token; otherwise the logits themselves, NH*dk per token
-    plan->off_z = ((plan->workspace_bytes + 255) / 256) * 256;
+    // token; otherwise the logits themselves, NH*dk per token.  Either sits
+    // after the fixed prefix even when the forward itself needs no workspace,
+    // so it never overwrites the counters, flags or mark.
+    plan->off_z = align256(plan->workspace_bytes > kReserved ? plan->workspace_bytes : kReserved);
     const size_t tokens = (size_t)o->batch * plan->L;
     if (plan->onepass && gate->rank == gla::kFusedProjRank) {
         plan->proj_fused = 1;
@@ -238,11 +253,11 @@ extern "C" int gla_make_plan_gate_proj(int dir, int H, int W, int chunk, const g
 extern "C" int gla_validate_gate_proj(const void* q, const void* k, const void* v,
                                       const gla_gate_proj* gate, int dir, int H, int W, int chunk,
                                       const void* out, const void* r, const gla_opts* o,
-                                      gla_plan* plan)
+                                      const gla_geom* geo, gla_plan* plan)
 {
     if (!o || !plan || !gate) return GLA_EINVAL;
     if (!q || !k || !v || !out) return GLA_EINVAL;
-    const int st = gla_make_plan_gate_proj(dir, H, W, chunk, gate, o, r != nullptr, plan);
+    const int st = gla_make_plan_gate_proj(dir, H, W, chunk, gate, o, r != nullptr, geo, plan);
     if (st != GLA_OK) return st;
     const size_t es = o->dtype == GLA_F16 ? 2 : 4;
     const size_t tokens = (size_t)o->batch * plan->L;
@@ -303,8 +318,8 @@ extern "C" int gla_validate_sswiglu(const void* gate, const void* value, int64_t
     return GLA_OK;
 }
 
-extern "C" int gla_plan_bwd(int dir, int H, int W, const gla_opts* o, int* nchunks, size_t* off_r,
-                            size_t* off_s, size_t* bytes)
+extern "C" int gla_plan_bwd(int dir, int H, int W, const gla_opts* o, int* nchunks, size_t* off_f,
+                            size_t* off_r, size_t* off_s, size_t* bytes)
 {
     if (!o) return GLA_EINVAL;
     if (o->batch < 1 || o->heads < 1 || H < 1 || W < 1) return GLA_EINVAL;
@@ -321,8 +336,9 @@ extern "C" int gla_plan_bwd(int dir, int H, int W, const gla_opts* o, int* nchun
     const size_t slot = ((size_t)o->dk * o->dk + o->dk) * 4;
     const size_t part = (size_t)units * (nc - 1) * slot;
     *nchunks = (int)nc;
-    *off_r = ((part + 255) / 256) * 256;
-    *off_s = *off_r + ((part + 255) / 256) * 256;
+    *off_f = kReserved;
+    *off_r = *off_f + align256(part);
+    *off_s = *off_r + align256(part);
     *bytes = *off_s + (size_t)units * nc * o->dk * 4;
     return GLA_OK;
 }
@@ -330,11 +346,11 @@ extern "C" int gla_plan_bwd(int dir, int H, int W, const gla_opts* o, int* nchun
 extern "C" int gla_validate_bwd(const void* q, const void* k, const void* v, const float* z,
                                 const void* dout, int dir, int H, int W, const void* dq,
                                 const void* dk, const void* dv, const float* dz, const gla_opts* o,
-                                int* nchunks, size_t* off_r, size_t* off_s)
+                                int* nchunks, size_t* off_f, size_t* off_r, size_t* off_s)
 {
     if (!o || !q || !k || !v || !z || !dout || !dq || !dk || !dv || !dz) return GLA_EINVAL;
     size_t bytes = 0;
-    const int st = gla_plan_bwd(dir, H, W, o, nchunks, off_r, off_s, &bytes);
+    const int st = gla_plan_bwd(dir, H, W, o, nchunks, off_f, off_r, off_s, &bytes);
     if (st != GLA_OK) return st;
     const size_t es = o->dtype == GLA_F16 ? 2 : 4;
     const size_t n = (size_t)o->batch * H * W * o->heads * o->dk;
@@ -358,18 +374,17 @@ extern "C" int gla_validate_bwd(const void* q, const void* k, const void* v, con
     return GLA_OK;
 }
 
-static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
 extern "C" int gla_plan_bwd_gated(int dir, int H, int W, const gla_opts* o, gla_bwd_gated_layout* lay)
 {
     int nchunks = 0;
-    size_t off_r = 0, off_s = 0, bwd_bytes = 0;
-    const int st = gla_plan_bwd(dir, H, W, o, &nchunks, &off_r, &off_s, &bwd_bytes);
+    size_t off_f = 0, off_r = 0, off_s = 0, bwd_bytes = 0;
+    const int st = gla_plan_bwd(dir, H, W, o, &nchunks, &off_f, &off_r, &off_s, &bwd_bytes);
     if (st != GLA_OK) return st;
     if (isnan(o->eps) || isinf(o->eps) || o->eps < 0.0f) return GLA_EINVAL;
     const size_t rows = (size_t)o->batch * H * W * o->heads;
     const size_t units = (size_t)o->batch * o->heads;
     lay->nchunks = nchunks;
+    lay->off_f = off_f;
     lay->off_r = off_r;
     lay->off_s = off_s;
     lay->bwd_bytes = bwd_bytes;

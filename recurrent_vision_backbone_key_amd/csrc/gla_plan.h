@@ -9,11 +9,39 @@
 extern "C" {
 #endif
 
+// Compute units and accelerator dies (XCDs, each with its own L2) of the
+// device a call runs on.  A null pointer stands for one MI355X in its
+// single-partition mode: 256 compute units in 8 XCDs.
+typedef struct gla_geom {
+    int cus;
+    int xcds;
+} gla_geom;
+
+// Fixed prefix of every forward workspace: a 4096-byte header and room for
+// GLA_FLAG_WORDS segment flags.  Header words (4 bytes each), every group on a
+// 128-byte cache line of its own so that the loads of one never wait behind
+// the atomics of another: the chip-wide ticket counter, the sticky error word
+// with the initialisation mark beside it (read together), and the ticket
+// counter of XCD x at GLA_HDR_XCD + 32 x.
+#define GLA_HEADER_BYTES 4096
+#define GLA_FLAG_WORDS 32768
+#define GLA_PREFIX_BYTES (GLA_HEADER_BYTES + GLA_FLAG_WORDS * 4)
+#define GLA_HDR_TICKET 0
+#define GLA_HDR_ERR 32
+#define GLA_HDR_MARK 33
+#define GLA_HDR_XCD 128
+// Initialisation mark gla_workspace_init writes at header word GLA_HDR_MARK.
+#define GLA_WS_MARK 0x474c4131u
+// Most XCDs the header's per-XCD ticket counters serve.
+#define GLA_MAX_XCDS 16
+
 typedef struct gla_plan {
     int L, nchunks, seg_chunks, nseg;
     int onepass;                 // 1: single-pass kernel, 0: three passes
-    int xcd_local;               // single pass: every scan on one XCD (u mod 8)
+    int xcd_local;               // single pass: every scan on one XCD (u mod xcds)
     int xcd_tasks;               // single pass, xcd_local: workgroups per XCD
+    int xcds;                    // single pass: XCDs of the device
+    int one_round;               // single pass: every workgroup of the call resident at once
     size_t workspace_bytes;
     size_t off_flags, off_agg, off_incl;  // single-pass workspace layout (bytes)
     size_t off_slots;                     // three-pass segment slots (bytes)
@@ -22,27 +50,29 @@ typedef struct gla_plan {
     float tau, scale, eps;
 } gla_plan;
 
-// Size-only checks and the work plan (segments, workspace bytes).
+// Size-only checks and the work plan (segments, workspace bytes) for a
+// device of geometry `geo` (null: the MI355X default).
 int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* opts, int has_gate,
-                  gla_plan* plan);
+                  const gla_geom* geo, gla_plan* plan);
 
 // Pure host check of every argument of gla_fwd (pointers are compared, never
 // dereferenced).  Fills *plan on success.  Returns a gla_status.
 int gla_validate(const void* q, const void* k, const void* v, const float* gate_logits,
                  int dir, int H, int W, int chunk, const void* out, const void* r,
-                 const gla_opts* opts, gla_plan* plan);
+                 const gla_opts* opts, const gla_geom* geo, gla_plan* plan);
 
 // Plan of gla_fwd_gate_proj: the plan of gla_fwd plus whether the expansion
 // by W2 and b is fused into the single pass.  The workspace grows by the
 // staged x W1 (B*L*16 binary32 words, fused) or the staged logits
 // (B*L*NH*dk binary32 words) at off_z (included in workspace_bytes).
 int gla_make_plan_gate_proj(int dir, int H, int W, int chunk, const gla_gate_proj* gate,
-                            const gla_opts* opts, int has_gate, gla_plan* plan);
+                            const gla_opts* opts, int has_gate, const gla_geom* geo,
+                            gla_plan* plan);
 
 // Host check of every argument of gla_fwd_gate_proj.  Fills *plan on success.
 int gla_validate_gate_proj(const void* q, const void* k, const void* v, const gla_gate_proj* gate,
                            int dir, int H, int W, int chunk, const void* out, const void* r,
-                           const gla_opts* opts, gla_plan* plan);
+                           const gla_opts* opts, const gla_geom* geo, gla_plan* plan);
 
 // Host check of every argument of gla_gate_logits.
 int gla_validate_gate_logits(const gla_gate_proj* gate, int batch, int tokens, int heads, int dk,
@@ -53,22 +83,24 @@ int gla_validate_sswiglu(const void* gate, const void* value, int64_t ld_in, con
                          const float* conv_b, int batch, int H, int W, int channels, int dtype,
                          const void* out, int64_t ld_out);
 
-// Backward: sizes checks, workspace layout (bytes): forward states at 0,
-// reverse states at *off_r, chunk sums at *off_s, total *bytes.
-int gla_plan_bwd(int dir, int H, int W, const gla_opts* opts, int* nchunks, size_t* off_r,
-                 size_t* off_s, size_t* bytes);
+// Backward: sizes checks, workspace layout (bytes): forward states at
+// *off_f (after the fixed forward prefix, which a backward never writes, so a
+// workspace shared with gla_fwd keeps its counters, flags and mark), reverse
+// states at *off_r, chunk sums at *off_s, total *bytes.
+int gla_plan_bwd(int dir, int H, int W, const gla_opts* opts, int* nchunks, size_t* off_f,
+                 size_t* off_r, size_t* off_s, size_t* bytes);
 
 // Host check of every argument of gla_bwd.
 int gla_validate_bwd(const void* q, const void* k, const void* v, const float* z, const void* dout,
                      int dir, int H, int W, const void* dq, const void* dk, const void* dv,
-                     const float* dz, const gla_opts* opts, int* nchunks, size_t* off_r,
-                     size_t* off_s);
+                     const float* dz, const gla_opts* opts, int* nchunks, size_t* off_f,
+                     size_t* off_r, size_t* off_s);
 
 // Gated backward: workspace layout (bytes) -- the backward's own part at 0
 // (gla_plan_bwd), then dO (binary32, rows x d) and the dw partial sums
 // (units x nchunks x d binary32); total in bytes.
 typedef struct gla_bwd_gated_layout {
-    size_t bwd_bytes, off_r, off_s, off_do, off_dwp, bytes;
+    size_t bwd_bytes, off_f, off_r, off_s, off_do, off_dwp, bytes;
     int nchunks;
 } gla_bwd_gated_layout;
 
@@ -80,9 +112,10 @@ int gla_validate_bwd_gated(const void* q, const void* k, const void* v, const fl
                            const void* dk, const void* dv, const float* dz, const void* dr,
                            const float* dw, const gla_opts* opts, gla_bwd_gated_layout* lay);
 
-// Whether a (dtype, head dim, chunk) instantiation is built (shared-memory
-// footprint of one workgroup within the 160 KiB of a gfx950 CU).
-int gla_config_built(int dtype, int d, int chunk);
+// Whether a (dtype, d_k, d_v, chunk) instantiation is built (shared-memory
+// footprint of one workgroup within the 160 KiB of a gfx950 CU; d_k != d_v
+// with 64-token chunks only).
+int gla_config_built(int dtype, int dk, int dv, int chunk);
 
 #ifdef __cplusplus
 }

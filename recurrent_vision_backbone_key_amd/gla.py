@@ -15,8 +15,12 @@ LIB_PATH = os.path.join(PKG, "_lib", "libgla.so")
 L2R, R2L, T2B, B2T = 0, 1, 2, 3
 F16, F32 = 0, 1
 ALGO_AUTO, ALGO_SINGLE_PASS, ALGO_THREE_PASS = 0, 1, 2
-STATUS = {0: "GLA_OK", 1: "GLA_EINVAL", 2: "GLA_EUNSUPPORTED", 3: "GLA_EWORKSPACE", 4: "GLA_EHIP"}
-EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_workspace_init", "gla_gate_logits",
+STATUS = {0: "GLA_OK", 1: "GLA_EINVAL", 2: "GLA_EUNSUPPORTED", 3: "GLA_EWORKSPACE", 4: "GLA_EHIP",
+          5: "GLA_EKERNEL"}
+# error-word bits (include/gla.h: GLA_WS_ERR_*)
+WS_ERR_WAIT, WS_ERR_TICKET, WS_ERR_INIT = 1, 2, 4
+EXPORTS = ("gla_fwd", "gla_workspace_size", "gla_workspace_init", "gla_workspace_status",
+           "gla_gate_logits",
            "gla_fwd_gate_proj", "gla_workspace_size_gate_proj", "gla_spatial_swiglu",
            "gla_bwd", "gla_bwd_workspace_size", "gla_bwd_gated", "gla_bwd_gated_workspace_size",
            "gla_status_str", "gla_abi_version")
@@ -79,6 +83,9 @@ def lib():
         h.gla_workspace_size.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(GlaOpts)]
         h.gla_workspace_init.restype = ctypes.c_int
         h.gla_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        h.gla_workspace_status.restype = ctypes.c_int
+        h.gla_workspace_status.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_uint32)]
         h.gla_gate_logits.restype = ctypes.c_int
         h.gla_gate_logits.argtypes = [ctypes.POINTER(GlaGateProj)] + [ctypes.c_int] * 5 + \
             [ctypes.c_void_p, ctypes.c_void_p]
@@ -132,7 +139,7 @@ def workspace_size(direction, H, W, chunk, opts: GlaOpts) -> int:
 
 
 def workspace_init(workspace, stream=None):
-    """Clear a device workspace tensor (include/gla.h: gla_workspace_init)."""
+    """Initialise a device workspace tensor (include/gla.h: gla_workspace_init)."""
     torch = _torch()
     if stream is None:
         stream = torch.cuda.current_stream(workspace.device).cuda_stream
@@ -142,13 +149,50 @@ def workspace_init(workspace, stream=None):
         raise GlaError(st, f"gla_workspace_init failed: {status_str(st)}")
 
 
+def workspace_status(workspace, stream=None) -> int:
+    """Error bits a kernel left in a forward workspace (include/gla.h:
+    gla_workspace_status; waits for the stream).  Returns 0 when none; a
+    nonzero word means the library has re-initialised the workspace."""
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    nbytes = workspace.numel() * workspace.element_size()
+    bits = ctypes.c_uint32(0)
+    st = lib().gla_workspace_status(workspace.data_ptr(), nbytes & ~3, stream, ctypes.byref(bits))
+    if st not in (0, 5):
+        raise GlaError(st, f"gla_workspace_status failed: {status_str(st)}")
+    return int(bits.value)
+
+
 def new_workspace(direction, H, W, chunk, opts: GlaOpts, device):
-    """A cleared workspace tensor sized for these arguments (or None)."""
+    """An initialised workspace tensor sized for these arguments (or None)."""
     torch = _torch()
     need = workspace_size(direction, H, W, chunk, opts)
     if not need:
         return None
-    return torch.zeros(need, dtype=torch.uint8, device=device)
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    workspace_init(ws)
+    return ws
+
+
+# Workspaces the binding keeps for calls that pass none: one per (device,
+# stream), grown when a call needs more and initialised once when allocated;
+# every completed call leaves it ready for the next, so a call allocates
+# nothing once the workspace is large enough.  Calls on one stream are ordered,
+# so they may share it.
+_ws_cache = {}
+
+
+def cached_workspace(need, device, stream):
+    """An initialised workspace of at least `need` bytes for (device, stream)."""
+    torch = _torch()
+    key = (str(device), int(stream or 0))
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        workspace_init(ws, stream)
+        _ws_cache[key] = ws
+    return ws
 
 
 def _torch():
@@ -190,10 +234,10 @@ def fwd(q, k, v, z, direction, H, W, chunk=64, r=None, norm_weight=None, eps=1e-
                      stream=stream, segment_chunks=segment_chunks, algorithm=algorithm)
     need = workspace_size(direction, H, W, chunk, opts)
     if need:
-        # a workspace passed in must have been cleared once (workspace_init);
-        # one allocated here starts cleared
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        # a workspace passed in must have been initialised once
+        # (workspace_init); without one the binding's own is used
+        if workspace is None:
+            workspace = cached_workspace(need, q.device, stream)
         opts.workspace = workspace.data_ptr()
         opts.workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib().gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), z.data_ptr(), direction, H, W,
@@ -242,8 +286,8 @@ def bwd(q, k, v, z, dout, direction, H, W, tau=16.0, scale=None, grads=None, wor
     opts = make_opts(B, NH, dk, dv, dtype, tau, scale, stream=stream)
     need = bwd_workspace_size(direction, H, W, opts)
     if need:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is None:
+            workspace = cached_workspace(need, q.device, stream)
         opts.workspace = workspace.data_ptr()
         opts.workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib().gla_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), z.data_ptr(), dout.data_ptr(),
@@ -293,8 +337,8 @@ def bwd_gated(q, k, v, z, r, dout, direction, H, W, norm_weight=None, eps=1e-6, 
                      norm_weight.data_ptr() if norm_weight is not None else 0, stream=stream)
     need = bwd_gated_workspace_size(direction, H, W, opts)
     if need:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is None:
+            workspace = cached_workspace(need, q.device, stream)
         opts.workspace = workspace.data_ptr()
         opts.workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib().gla_bwd_gated(q.data_ptr(), k.data_ptr(), v.data_ptr(), z.data_ptr(), r.data_ptr(),
@@ -386,8 +430,8 @@ def fwd_gate_proj(q, k, v, x, w1, w2, bias, direction, H, W, chunk=64, r=None,
                      stream=stream, segment_chunks=segment_chunks, algorithm=algorithm)
     need = workspace_size_gate_proj(direction, H, W, chunk, gate, opts)
     if need:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        if workspace is None:
+            workspace = cached_workspace(need, q.device, stream)
         opts.workspace = workspace.data_ptr()
         opts.workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib().gla_fwd_gate_proj(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(gate),

@@ -31,11 +31,11 @@ def run_gpu(x, direction, H, W, chunk, torch, eps=1e-6, segment_chunks=0, out=No
                 norm_weight=d["w"], eps=eps, out=out, tau=tau, segment_chunks=segment_chunks,
                 workspace=ws, algorithm=algorithm)
     torch.cuda.synchronize()
-    # single pass: word 1 of the workspace is the error word (sticky until the
-    # next init), set only if a look-back wait gave up or a ticket was bad
-    if algorithm == gla.ALGO_SINGLE_PASS:
-        err = int(ws[4:8].cpu().numpy().view(np.uint32)[0])
-        assert err == 0, f"look-back error flag set: {err:#x}"
+    # the workspace's error word (sticky until the next init) through the
+    # library's own status call, whichever algorithm the plan picked
+    if need:
+        err = gla.workspace_status(ws)
+        assert err == 0, f"kernel error bits set in the workspace: {err:#x}"
     return y.cpu().numpy()
 
 

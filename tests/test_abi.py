@@ -37,7 +37,7 @@ def test_only_declared_functions_are_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert gla.abi_version() == 5
+    assert gla.abi_version() == 6
     for s, name in gla.STATUS.items():
         assert gla.status_str(s).startswith(name)
     assert "unknown" in gla.status_str(99)
@@ -64,12 +64,26 @@ def test_null_pointers():
 
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, 1), ("heads", 0, 1), ("dtype", 7, 2), ("dk", 48, 2), ("dv", 96, 2),
-    ("dk", 32, 2),  # dk != dv
 ])
 def test_bad_sizes(field, value, status):
     o = _opts(segment_chunks=1000)
     setattr(o, field, value)
     assert _call(opts=o) == status
+
+
+def test_dk_dv_differ_only_with_64_token_chunks():
+    """d_k != d_v is built for 64-token chunks (three passes); other chunks,
+    and forcing the single pass, are GLA_EUNSUPPORTED.  (No call here passes
+    validation: the addresses are fake.)"""
+    for chunk in (16, 32, 128):
+        assert _call(chunk=chunk, opts=_opts(dk=32, dv=64, segment_chunks=1000)) == 2
+    assert _call(opts=_opts(dk=64, dv=128, algorithm=gla.ALGO_SINGLE_PASS)) == 2
+    # sizes are planned for them (three passes, slots of d_k d_v + d_k fp32)
+    o = _opts(batch=2, heads=3, dk=32, dv=128, segment_chunks=4, algorithm=gla.ALGO_THREE_PASS)
+    nseg = -(-25 // 4)
+    assert gla.workspace_size(0, 40, 40, 64, o) == 4096 + 32768 * 4 + 6 * (nseg - 1) * (32 * 128 + 32) * 4
+    # binary32 with d_k = 128, d_v = 64 exceeds one CU's shared memory
+    assert gla.workspace_size(0, 40, 40, 64, _opts(dk=128, dv=64, dtype=gla.F32)) == 0
 
 
 def test_bad_grid_direction_chunk():
@@ -129,22 +143,22 @@ def test_workspace_size_and_errors():
 
 
 def test_workspace_formula_three_pass():
-    """A fixed prefix (1024-byte header, 32768 flag words), then (units) x
+    """A fixed prefix (4096-byte header, 32768 flag words), then (units) x
     (segments - 1) slots of (dk*dv + dk) fp32."""
     o = _opts(batch=2, heads=3, segment_chunks=4, algorithm=gla.ALGO_THREE_PASS)
     nchunks = -(-(40 * 40) // 64)
     nseg = -(-nchunks // 4)
-    assert gla.workspace_size(1, 40, 40, 64, o) == 1024 + 32768 * 4 + 6 * (nseg - 1) * (64 * 64 + 64) * 4
+    assert gla.workspace_size(1, 40, 40, 64, o) == 4096 + 32768 * 4 + 6 * (nseg - 1) * (64 * 64 + 64) * 4
 
 
 def test_workspace_formula_single_pass():
-    """1024-byte header (ticket counters, error word) and room for 32768
+    """4096-byte header (ticket counters, error word) and room for 32768
     segment flags (the same prefix in every forward layout), then an aggregate
     and a group transfer (dk*dv + dk fp32 each) per (scan, segment)."""
     o = _opts(batch=2, heads=3, segment_chunks=4, algorithm=gla.ALGO_SINGLE_PASS)
     nseg = -(-25 // 4)
     n = 6 * nseg
-    want = 1024 + 32768 * 4 + 2 * n * (64 * 64 + 64) * 4
+    want = 4096 + 32768 * 4 + 2 * n * (64 * 64 + 64) * 4
     assert gla.workspace_size(1, 40, 40, 64, o) == want
 
 
@@ -154,6 +168,46 @@ def test_workspace_init_argument_checks():
     assert h.gla_workspace_init(None, 256, None) == 1
     assert h.gla_workspace_init(A + 8, 256, None) == 1
     assert h.gla_workspace_init(A, 254, None) == 1
+
+
+def test_workspace_status_argument_checks():
+    """Bad arguments are rejected before anything touches the device."""
+    h = gla.lib()
+    bits = ctypes.c_uint32(7)
+    assert h.gla_workspace_status(A, 4096, None, None) == 1
+    assert h.gla_workspace_status(None, 4096, None, ctypes.byref(bits)) == 1
+    assert h.gla_workspace_status(A + 8, 4096, None, ctypes.byref(bits)) == 1
+    assert h.gla_workspace_status(A, 4092, None, ctypes.byref(bits)) == 1  # no whole header
+    assert h.gla_workspace_status(A, 4098, None, ctypes.byref(bits)) == 1
+
+
+def test_gate_projection_staging_after_the_prefix():
+    """Staged logits (or x W1) never land in the fixed prefix, even when the
+    forward itself needs no workspace (one segment per scan)."""
+    prefix = 4096 + 32768 * 4
+    for dk, H, W, seg in ((32, 8, 8, 0), (64, 40, 40, 1000), (16, 3, 5, 0)):
+        o = _opts(batch=2, heads=3, dk=dk, dv=dk, segment_chunks=seg)
+        gate = gla.GlaGateProj(A, A + MB, A + 2 * MB, None, 64, 16)
+        fwd_ws = gla.workspace_size(0, H, W, 64, o)
+        need = gla.workspace_size_gate_proj(0, H, W, 64, gate, o)
+        tokens = 2 * H * W
+        z_bytes = tokens * 16 * 4 if (dk == 64 and fwd_ws) else tokens * 3 * dk * 4
+        start = -(-max(fwd_ws, prefix) // 256) * 256
+        assert need == start + z_bytes, (dk, H, W, need, fwd_ws)
+
+
+def test_backward_workspace_after_the_prefix():
+    """The backward lays its slots out after the same fixed prefix, so one
+    workspace can serve gla_fwd and gla_bwd in turn."""
+    prefix = 4096 + 32768 * 4
+    o = _opts(batch=2, heads=3, dk=64, dv=64)
+    nc = 25
+    part = 6 * (nc - 1) * (64 * 64 + 64) * 4
+    a256 = lambda x: -(-x // 256) * 256
+    assert gla.bwd_workspace_size(0, 40, 40, o) == prefix + 2 * a256(part) + 6 * nc * 64 * 4
+    g = gla.bwd_gated_workspace_size(0, 40, 40, o)
+    base = prefix + 2 * a256(part) + 6 * nc * 64 * 4
+    assert g == a256(a256(base) + 6 * 1600 * 64 * 4) + 6 * nc * 64 * 4
 
 
 def test_algorithm_selection():

@@ -23,10 +23,12 @@ MB = 1 << 26
 
 
 def _ws_bytes(B, NH, L, d):
+    """The forward's fixed prefix (4096-byte header, 32768 flag words, never
+    written by a backward), then two slot arrays and the chunk sums."""
     nc = (L + 63) // 64
     part = B * NH * (nc - 1) * (d * d + d) * 4
     al = ((part + 255) // 256) * 256
-    return 2 * al + B * NH * nc * d * 4
+    return 4096 + 32768 * 4 + 2 * al + B * NH * nc * d * 4
 
 
 def _call(q=A, k=A + MB, v=A + 2 * MB, z=A + 3 * MB, dout=A + 4 * MB, direction=0, H=20, W=20,
