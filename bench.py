@@ -218,7 +218,7 @@ def cpu_baseline(spec, name, seconds):
             break
     dt = time.perf_counter() - t0
     return {"value": done_th / dt / 1e9, "unit": "Gtok·head/s", "cores": cores,
-            "kind": "oracle",
+            "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"{calls} oracle {'backward ' if spec.get('kind') == 'bwd' else ''}calls "
                       f"of {name} ({spec['H']}x{spec['W']}, d={spec['dk']}), "
                       + ("gate logits of every token projected per call, "
@@ -271,14 +271,40 @@ def time_steps(step, rotate, steps, warmup, args, steps_per_graph):
     for i in range(warmup // G):
         run(i)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(steps // G):
+    # one event before every replay (or eager step) and one after the last:
+    # the whole bracket gives the mean, consecutive pairs give each replay's
+    # time for the median and minimum (the pages compare latencies on the
+    # median of repeated runs and report minimum and mean beside it)
+    n = steps // G
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    for i in range(n):
+        evs[i].record(stream)
         run(warmup // G + i)
-    ev1.record(stream)
+    evs[n].record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps, G, graphs is not None
+    per_replay = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+    return evs[0].elapsed_time(evs[n]) / steps, G, graphs is not None, per_replay
+
+
+def latency_stats(per_replay_ms, steps_per_replay, calls_per_step):
+    """Median, minimum and mean microseconds per call over the timed replays."""
+    import statistics
+    per_call = [1e3 * t / (steps_per_replay * calls_per_step) for t in per_replay_ms]
+    return {"median": round(statistics.median(per_call), 3), "min": round(min(per_call), 3),
+            "mean": round(statistics.fmean(per_call), 3), "replays": len(per_call),
+            "calls_per_replay": steps_per_replay * calls_per_step}
+
+
+def host_cpu_model():
+    """Model name of the host CPU (/proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def algorithmic_flops_bwd_per_token_head(dk, dv, chunk):
@@ -342,7 +368,7 @@ def bench_bwd(args, spec, name):
                 gla.bwd(x["q"], x["k"], x["v"], x["z"], x["dout"], dr, H, W, grads=grads,
                         workspace=ws)
 
-    ms_step, G, graphed = time_steps(step, rotate, steps, warmup, args, 10)
+    ms_step, G, graphed, per_replay = time_steps(step, rotate, steps, warmup, args, 10)
     us_call = 1e3 * ms_step / len(dirs)
     tflops = flops_call / (us_call * 1e-6) / 1e12
     gbs = bytes_call / (us_call * 1e-6) / 1e9
@@ -351,7 +377,9 @@ def bench_bwd(args, spec, name):
                   ": µs/call + Gtok·head/s at L=1600; % of MFMA (fp32) roofline",
         "value": round(len(dirs) * th_call / (ms_step * 1e-3) / 1e9, 4), "unit": "Gtok·head/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
-        "us_per_call": round(us_call, 3), "higher_is_better": True, "scaling": "weak",
+        "us_per_call": round(us_call, 3),
+        "latency_us_per_call": latency_stats(per_replay, G, len(dirs)),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
         "config": {"workload": name, "B": B, "heads": NH, "grid": f"{H}x{W}", "L": H * W,
                    "dk": d, "dv": d, "chunk": spec["chunk"],
@@ -411,13 +439,15 @@ def bench_sswiglu(args, spec, name):
         a, v, w, b, o = sets[r]
         gla.spatial_swiglu(a, v, H, W, w, b, out=o)
 
-    ms_step, G, graphed = time_steps(step, rotate, steps, warmup, args, 10)
+    ms_step, G, graphed, per_replay = time_steps(step, rotate, steps, warmup, args, 10)
     achieved = bytes_call / (ms_step * 1e-3) / 1e9
     result = {
         "metric": "Spatial SwiGLU core: µs/call; % of HBM roofline",
         "value": round(tokens * C / (ms_step * 1e-3) / 1e9, 3), "unit": "Gtok·channel/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
-        "us_per_call": round(1e3 * ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "us_per_call": round(1e3 * ms_step, 3),
+        "latency_us_per_call": latency_stats(per_replay, G, 1),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
         "config": {"workload": name, "B": B, "grid": f"{H}x{W}", "L": H * W, "channels": C,
                    "input_sets": rotate, "hip_graph": graphed, "steps_per_graph": G,
@@ -443,7 +473,7 @@ def bench_sswiglu(args, spec, name):
         dt_s = time.perf_counter() - t0
         result["cpu_baseline"] = {
             "value": round(n * H * W * C / dt_s / 1e9, 5), "unit": "Gtok·channel/s", "cores": 1,
-            "kind": "oracle",
+            "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"{n} oracle calls on one image ({H}x{W}, {C} channels) in {dt_s:.1f} s"}
     print(json.dumps(result), flush=True)
 
@@ -581,7 +611,8 @@ def main():
                     norm_weight=x["w"], eps=1e-6, out=out, segment_chunks=args.segment_chunks,
                     workspace=ws)
 
-    ms_step, G, graphed = time_steps(step, rotate, steps, warmup, args, 1 if big else 10)
+    ms_step, G, graphed, per_replay = time_steps(step, rotate, steps, warmup, args,
+                                                 1 if big else 10)
     us_call = 1e3 * ms_step / calls_per_step
     value = calls_per_step * th_call / (ms_step * 1e-3) / 1e9
 
@@ -597,7 +628,9 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 4), "unit": "Gtok·head/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
-        "us_per_call": round(us_call, 3), "higher_is_better": True, "scaling": "weak",
+        "us_per_call": round(us_call, 3),
+        "latency_us_per_call": latency_stats(per_replay, G, calls_per_step),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
         "config": {"workload": name, "B": B, "heads": NH, "grid": f"{H}x{W}", "L": H * W,
                    "dk": dk, "dv": dv, "chunk": chunk,

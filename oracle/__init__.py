@@ -4,7 +4,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP
 implementation in ``recurrent_vision_backbone_key_amd`` and never imports it.
 
-Two independent references of the same definition ("GTR: Gated Token
+Six references, each written from its definition ("GTR: Gated Token
 Recurrence for Efficient Dense Prediction", paper Section 2.1):
 
 * :func:`fwd` -- the token-by-token fp64 recurrence in plain C
@@ -16,6 +16,9 @@ Recurrence for Efficient Dense Prediction", paper Section 2.1):
   (same section), numpy fp64 shifted sums;
 * :func:`bwd` -- the gradients of q, k, v, z of the ungated forward (the
   recurrence differentiated, run backwards along the scan), fp64 C;
+* :func:`bwd_gated` -- the same through the output gate (dr, dw and the
+  gradient entering the ungated backward, from the epilogue's derivative),
+  fp64 C;
 * :func:`closed_form_fwd` -- the O(L^2) unrolled sum
   ``o_t = scale * sum_{s<=t} (q_t (.) prod_{j=s+1..t} gamma_j (.) k_s) v_s``
   in numpy fp64 with explicit per-pair gate sums, for tiny inputs.  Its scan

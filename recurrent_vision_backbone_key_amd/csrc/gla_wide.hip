@@ -60,11 +60,6 @@ constexpr int F1 = 3;   // 2^{tot_{i-1}}              query factor for key sub-c
 constexpr int F2 = 4;   // 2^{tot_{i-1} + tot_{i-2}}  query factor for key sub-chunk i-3
 constexpr int NFAC = 5;
 constexpr int NPA = 10; // partial score tiles exchanged per chunk
-// The state enters the inter-chunk product as binary16 hi + lo parts.
-#ifndef GLA_WIDE_STATE_LO
-#define GLA_WIDE_STATE_LO 0
-#endif
-constexpr bool kStateLo = GLA_WIDE_STATE_LO;
 
 // LDS layout (bytes)
 constexpr int L_E = 0;                          // E hi            [C][SH] f16
@@ -477,13 +472,12 @@ void gla_wide_kernel(Params P)
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     // k-slots 8g + e: channel 32p + 4g + e (e < 4), 32p + 16 + 4g + e - 4
-                    half8 ah, al;
+                    // (the state enters as its binary16 high part)
+                    half8 ah;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         ah[e] = (_Float16)S[2 * p][e];
                         ah[4 + e] = (_Float16)S[2 * p + 1][e];
-                        al[e] = lo_part(S[2 * p][e]);
-                        al[4 + e] = lo_part(S[2 * p + 1][e]);
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -492,7 +486,6 @@ void gla_wide_kernel(Params P)
                         const half4 b1 = *(const half4*)(qrow + 16);
                         const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
                         o[i] = mma(ah, bq, o[i]);
-                        if (kStateLo) o[i] = mma(al, bq, o[i]);
                     }
                 }
             }
