@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 6
+#define GLA_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define GLA_API __attribute__((visibility("default")))
@@ -64,8 +64,10 @@ enum gla_status {
     GLA_EUNSUPPORTED = 2, /* d_k, d_v, chunk, dtype or size outside the built set */
     GLA_EWORKSPACE = 3,   /* workspace missing or smaller than gla_workspace_size */
     GLA_EHIP = 4,         /* the HIP runtime reported an error at launch         */
-    GLA_EKERNEL = 5       /* a kernel reported a failure in the workspace's error
+    GLA_EKERNEL = 5,      /* a kernel reported a failure in the workspace's error
                              word (gla_workspace_status)                        */
+    GLA_ESCRATCH = 6      /* gla_fwd_noalloc: the call needs more scratch than the
+                             library's fixed array holds                        */
 };
 
 /* Bits of a workspace's error word (gla_workspace_status).  They are sticky:
@@ -142,6 +144,28 @@ enum gla_algorithm { GLA_ALGO_AUTO = 0, GLA_ALGO_SINGLE_PASS = 1, GLA_ALGO_THREE
 GLA_API int gla_fwd(const void *q, const void *k, const void *v, const float *gate_logits,
             int dir, int H, int W, int chunk, void *out, const void *r,
             const gla_opts *opts);
+
+/*
+ * gla_fwd_noalloc -- gla_fwd for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and kernels, with opts->workspace and
+ * opts->workspace_bytes ignored.  The exchange area lives in a library-owned
+ * device array of GLA_NOALLOC_SCRATCH_BYTES per GPU (allocated when the code
+ * object loads, held until the process ends); a call whose
+ * gla_workspace_size() exceeds it returns GLA_ESCRATCH and launches nothing.
+ * Nothing is allocated per call.  The first call on a device looks the array
+ * up and initialises it on opts->stream, ahead of its own kernels; every
+ * completed call leaves it ready for the next.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams, no
+ * ordering between them) race and must not be issued.  gla_workspace_status
+ * does not apply (the array is not addressable by the caller); a failure
+ * still writes NaN to the affected rows.  Arguments, layout and the other
+ * statuses as for gla_fwd.
+ */
+#define GLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+GLA_API int gla_fwd_noalloc(const void *q, const void *k, const void *v, const float *gate_logits,
+                            int dir, int H, int W, int chunk, void *out, const void *r,
+                            const gla_opts *opts);
 
 /* Bytes of workspace gla_fwd needs for these arguments (0: none needed).
  * Returns 0 as well for arguments gla_fwd would reject. */

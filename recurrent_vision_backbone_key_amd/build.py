@@ -45,6 +45,7 @@ UNITS = [
     ("gla_proj.hip", "hip", []),
     ("gla_sswiglu.hip", "hip", []),
     ("gla_bwd.hip", "hip", []),
+    ("gla_noalloc.hip", "hip", []),
 ]
 
 

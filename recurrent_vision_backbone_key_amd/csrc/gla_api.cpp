@@ -19,15 +19,22 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_geom[kMaxDevices];  // (cus << 8) | xcds, 0 until read
 
-gla_geom device_geom(void* stream)
+// Device `stream` belongs to (the current device for the null stream), or -1.
+int stream_device(void* stream)
 {
-    gla_geom g = {256, 8};
     int dev = -1;
     if (stream) {
         if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) dev = -1;
     } else if (hipGetDevice(&dev) != hipSuccess) {
         dev = -1;
     }
+    return dev;
+}
+
+gla_geom device_geom(void* stream)
+{
+    gla_geom g = {256, 8};
+    const int dev = stream_device(stream);
     if (dev < 0 || dev >= kMaxDevices) {
         (void)hipGetLastError();
         return g;
@@ -122,6 +129,34 @@ extern "C" int gla_fwd(const void* q, const void* k, const void* v, const float*
     P.z = gate_logits;
     no_proj(P);
     return run_fwd(P, q, k, v, dir, H, W, chunk, out, r, opts, plan);
+}
+
+extern "C" int gla_fwd_noalloc(const void* q, const void* k, const void* v,
+                               const float* gate_logits, int dir, int H, int W, int chunk,
+                               void* out, const void* r, const gla_opts* opts)
+{
+    if (!opts) return GLA_EINVAL;
+    const gla_geom geo = device_geom(opts->stream);
+    gla_opts o = *opts;
+    o.workspace = nullptr;
+    o.workspace_bytes = 0;
+    gla_plan plan;
+    int st = gla_make_plan(dir, H, W, chunk, &o, r != nullptr, &geo, &plan);
+    if (st != GLA_OK) return st;
+    if (plan.workspace_bytes > gla::kScratchBytes) return GLA_ESCRATCH;
+    if (plan.workspace_bytes) {
+        void* ptr = nullptr;
+        st = gla::scratch_for_device(stream_device(opts->stream), opts->stream, &ptr);
+        if (st != GLA_OK) return st;
+        o.workspace = ptr;
+        o.workspace_bytes = gla::kScratchBytes;
+    }
+    st = gla_validate(q, k, v, gate_logits, dir, H, W, chunk, out, r, &o, &geo, &plan);
+    if (st != GLA_OK) return st;
+    gla::Params P;
+    P.z = gate_logits;
+    no_proj(P);
+    return run_fwd(P, q, k, v, dir, H, W, chunk, out, r, &o, plan);
 }
 
 extern "C" int gla_fwd_gate_proj(const void* q, const void* k, const void* v,
@@ -331,6 +366,7 @@ extern "C" const char* gla_status_str(int status)
     case GLA_EWORKSPACE: return "GLA_EWORKSPACE: workspace missing, misaligned or smaller than gla_workspace_size()";
     case GLA_EHIP: return "GLA_EHIP: HIP runtime error at launch";
     case GLA_EKERNEL: return "GLA_EKERNEL: a kernel reported a failure in the workspace error word";
+    case GLA_ESCRATCH: return "GLA_ESCRATCH: the call needs more scratch than gla_fwd_noalloc's fixed 64 MiB array (use gla_fwd with a workspace of gla_workspace_size() bytes)";
     default: return "unknown gla status";
     }
 }

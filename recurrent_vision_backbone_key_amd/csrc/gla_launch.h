@@ -4,6 +4,8 @@
 
 #include <stddef.h>
 
+#include "gla.h"
+
 namespace gla {
 
 // Largest segment (in chunks) the single-pass kernel keeps on chip.
@@ -99,6 +101,13 @@ int launch_bwd(const Params& P, const BwdParams& Q, int dtype, int d, void* stre
 
 // Zero-fills a workspace (counters, flags) on `stream`.
 int launch_workspace_init(void* ws, size_t bytes, void* stream);
+
+// Size of the library-owned scratch array of gla_fwd_noalloc (per device).
+constexpr size_t kScratchBytes = GLA_NOALLOC_SCRATCH_BYTES;
+
+// Device address of the scratch array on device `dev`, looked up (with `dev`
+// current) and initialised on `stream` at the first call for that device.
+int scratch_for_device(int dev, void* stream, void** ptr);
 
 }  // namespace gla
 

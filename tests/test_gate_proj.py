@@ -35,7 +35,7 @@ def _fwdp(gate=None, q=A, k=A + MB, v=A + 2 * MB, out=A + 5 * MB, r=None, direct
 
 
 def test_abi_version():
-    assert gla.abi_version() == 6
+    assert gla.abi_version() == 7
 
 
 def test_fwd_gate_proj_argument_checks():
