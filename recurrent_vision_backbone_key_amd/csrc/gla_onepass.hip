@@ -67,38 +67,43 @@ constexpr int FK = 3;     // 2^{total - R_i - tot_i}    k-hat from E
 constexpr int F1 = 4;     // 2^{tot_{i-1}}              query factor for key sub-chunk i-2
 constexpr int F2 = 5;     // 2^{tot_{i-1} + tot_{i-2}}  query factor for key sub-chunk i-3
 
-// LDS layout (bytes)
-constexpr int L_E = 0;                        // E hi          [C][SH] f16 ([token][ch])
-constexpr int L_EL = L_E + C * SH * 2;        // E lo          [C][SH] f16
-constexpr int L_KT = L_EL + C * SH * 2;       // k-hat         [C][SH] f16 ([token][ch]), read transposed
-constexpr int L_VT = L_KT + C * SH * 2;       // v             [C][SH] f16 ([token][dv]), read transposed
-constexpr int L_ST = L_VT + C * SH * 2;       // S^T           [D][SH] f16 ([dv][ch])
-constexpr int L_QH = L_ST + D * SH * 2;       // q (.) 2^b     [C][SH] f16 ([token][ch])
-constexpr int L_PA = L_QH + C * SH * 2;       // partial scores [NW][NSUB][64 lanes][4] f32
-constexpr int L_FQ = L_PA + NW * NSUB * 64 * 16;  // raw q      [C][SH] f16 (pairwise fallback)
-constexpr int L_FK = L_FQ + C * SH * 2;       // raw k         [C][SH] f16 (pairwise fallback)
-constexpr int L_FB = L_FK + C * SH * 2;       // bl            [C][SF] f32 (pairwise fallback)
-constexpr int L_TOT = L_FB + C * SF * 4;      // sub-chunk totals [NSUB][D] f32
-constexpr int L_DEC = L_TOT + NSUB * D * 4;   // 2^{chunk total} [D] f32
-constexpr int L_FAC = L_DEC + D * 4;         // per-wave factors [NW][NFAC][32] f32
-constexpr int L_ROWS = L_FAC + NW * 8 * 32 * 4;  // row tables  [NCH][C] i32
-constexpr int L_SS = L_ROWS + NCH * C * 4;    // RMS partials   [NCH][2][C] f32
-constexpr int L_MISC = L_SS + NCH * 2 * C * 4;  // ticket, wide flags, look-back result
-constexpr int LDS_TOTAL = L_MISC + 64;
-static_assert(LDS_TOTAL <= kLdsLimit, "LDS budget of one CU exceeded");
-// fused gate expansion (z = hp W2 + b with hp = x W1 of rank 16 read per
-// token): this head's W2 rows and bias
-constexpr int L_W2 = LDS_TOTAL;               // W2^T of the head [D][16] f32
-constexpr int L_GB = L_W2 + D * 16 * 4;       // gate bias of the head [D] f32
-constexpr int LDS_PROJ = L_GB + D * 4;
+// LDS layout (bytes) of the instance that keeps up to NCHK chunks per
+// segment.  Chunk loop: E (keys relative to their sub-chunk end), k-hat and v
+// (read transposed), the partial score tiles of the two channel halves,
+// sub-chunk totals, chunk decay, per-wave factor tables; with more than one
+// chunk also the local state S^T and q (.) 2^b for the local inter-chunk term.
+// Phase 3 keeps only S_in^T, the row tables, the RMS partials and the
+// staging of the query halves, which reuses the loop's dead buffers (the
+// one-chunk instance holds about 70 KB).
+template <int NCHK> struct Lay {
+    static constexpr bool kMulti = NCHK > 1;
+    static constexpr int ST = 0;                                   // S^T [D][SH] f16 ([dv][ch])
+    static constexpr int QH = kMulti ? ST + D * SH * 2 : ST;       // q (.) 2^b [C][SH] f16
+    static constexpr int E = kMulti ? QH + C * SH * 2 : 0;         // E [C][SH] f16 ([token][ch])
+    static constexpr int KT = E + C * SH * 2;                      // k-hat [C][SH] f16, read transposed
+    static constexpr int VT = KT + C * SH * 2;                     // v [C][SH] f16, read transposed
+    static constexpr int PA = VT + C * SH * 2;                     // partial scores [NW][NSUB][64][4] f32
+    static constexpr int TOT = PA + NW * NSUB * 64 * 16;           // sub-chunk totals [NSUB][D] f32
+    static constexpr int DEC = TOT + NSUB * D * 4;                 // 2^{chunk total} [D] f32
+    static constexpr int FAC = DEC + D * 4;                        // per-wave factors [NW][8][32] f32
+    static constexpr int ROWS = FAC + NW * 8 * 32 * 4;             // row tables [NCHK][C] i32
+    static constexpr int SS = ROWS + NCHK * C * 4;                 // RMS partials [NCHK][2][C] f32
+    static constexpr int MISC = SS + NCHK * 2 * C * 4;             // ticket, look-back result, ...
+    static constexpr int TOTAL = MISC + 64;
+    // fused gate expansion: this head's W2 rows and bias
+    static constexpr int W2 = TOTAL;                               // W2^T of the head [D][16] f32
+    static constexpr int GB = W2 + D * 16 * 4;                     // gate bias of the head [D] f32
+    static constexpr int TOTAL_PROJ = GB + D * 4;
+    // phase-2/3 aliases (the loop's buffers are dead by then; with one chunk,
+    // S_in^T takes the place of E, with several the place of the local S^T)
+    static constexpr int LSEG = PA;                                // segment local state [D][D] f32
+    static constexpr int GSEG = PA + D * D * 4;                    // segment total decay [D] f32
+    static constexpr int OUT = kMulti ? QH : KT;                   // query staging [NCHK][C][SH] f16
+    static_assert(TOTAL_PROJ <= kLdsLimit, "LDS budget of one CU exceeded");
+    static_assert(GSEG + D * 4 <= TOT, "segment aggregate overlaps live buffers");
+    static_assert(OUT + NCHK * C * SH * 2 <= ROWS, "output staging overlaps live buffers");
+};
 static_assert(kFusedProjRank == 16, "the fused gate expansion is built for rank 16");
-static_assert(LDS_PROJ <= kLdsLimit, "LDS budget of one CU exceeded (fused gate expansion)");
-// phase-2/3 aliases
-constexpr int L_LSEG = L_PA;                  // segment local state [D][D] f32 (16 KiB)
-constexpr int L_GSEG = L_PA + D * D * 4;      // segment total decay [D] f32
-constexpr int L_OUT = L_PA;                   // output staging [NCH][C][SH] f16
-static_assert(L_GSEG + D * 4 <= L_TOT, "segment aggregate overlaps live buffers");
-static_assert(L_OUT + NCH * C * SH * 2 <= L_TOT, "output staging overlaps live buffers");
 
 // Exchange through device memory.  Every exchanged word (states, decays,
 // flags, counters) is accessed with agent-scope atomics, which on gfx950
@@ -275,18 +280,18 @@ __device__ __forceinline__ void nan_rows(const Params& P, int unit, int seg, int
 // Intra-chunk scores (M1, with the exchange of the two channel halves) and
 // scores times values (M2) for query sub-chunk SI: a compile-time sub-chunk
 // keeps every tile selection out of the control flow, so no register array is
-// merged across branches.
+// merged across branches.  The diagonal tile's key operand is the lane's own
+// E (hi, lo) row; when the wave's sub-chunk is too wide for that factorised
+// form (wide_w), its diagonal partial is already in sPA, evaluated pairwise.
 template <int SI>
-__device__ __forceinline__ void scores_values(const Params& P, const _Float16* sE, const _Float16* sEL,
-                                              const _Float16* sVT, float* sPA, const int* sMisc,
-                                              const _Float16* sFQ, const _Float16* sFK, const float* sFB,
-                                              int wave, int lane, int g, int l16, int h, int c0, int tl,
+__device__ __forceinline__ void scores_values(const _Float16* sE, const _Float16* sVT, float* sPA,
+                                              int wave, int lane, int g, int l16, int h, int c0,
+                                              bool wide_w, const half8& eh, const half8& el,
                                               const half8& qa, const half8& qo1, const half8& qo2,
                                               const half8& qd_h, const half8& qd_l, float4v (&o)[2])
 {
     // ---- M1 partial scores over this wave's 32 channels, tiles j <= SI
     //      (j < SI off the diagonal; the diagonal tile separately)
-    const bool wide_i = (sMisc[4 + SI] | sMisc[4 + SI + 4]) != 0;
     float4v part[NSUB];
 #pragma unroll
     for (int j = 0; j < NSUB - 1; ++j) {
@@ -298,31 +303,15 @@ __device__ __forceinline__ void scores_values(const Params& P, const _Float16* s
         *(float4v*)(sPA + ((wave * NSUB + j) * 64 + lane) * 4) = part[j];
     }
     float4v pd = float4v{0.f, 0.f, 0.f, 0.f};
-    if (!wide_i) {
-        const half8 ek = *(const half8*)(sE + tl * SH + c0);
-        const half8 ekl = *(const half8*)(sEL + tl * SH + c0);
-        pd = mma(ek, qd_h, pd);
-        pd = mma(ekl, qd_h, pd);
-        pd = mma(ek, qd_l, pd);
-    } else {
-        // exact pairwise over this wave's channels: q_t k_s 2^{bl_t - bl_s}
-        // (rare: a sub-chunk whose decay span is too wide for binary16)
-#pragma unroll 1
-        for (int e = 0; e < 4; ++e) {
-            const int sl = 4 * g + e;
-            float acc = 0.f;
-            if (sl <= l16) {
-                const int ts = 16 * SI + sl;
-#pragma unroll 1
-                for (int cc = 32 * h; cc < 32 * h + 32; ++cc)
-                    acc += (float)sFQ[tl * SH + cc] * (float)sFK[ts * SH + cc] *
-                           exp2_fast(sFB[tl * SF + cc] - sFB[ts * SF + cc]);
-            }
-            pd[e] = acc;
-        }
+    float* const dslot = sPA + ((wave * NSUB + SI) * 64 + lane) * 4;
+    if (!wide_w) {
+        pd = mma(eh, qd_h, pd);
+        pd = mma(el, qd_h, pd);
+        pd = mma(eh, qd_l, pd);
+        *(float4v*)dslot = pd;
     }
-    *(float4v*)(sPA + ((wave * NSUB + SI) * 64 + lane) * 4) = pd;
     __syncthreads();  // (3) partial scores of both halves
+    if (wide_w) pd = *(const float4v*)dslot;
     float4v at[NSUB];
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) {
@@ -338,7 +327,6 @@ __device__ __forceinline__ void scores_values(const Params& P, const _Float16* s
                 if (4 * g + e > l16) at[j][e] = 0.f;
         }
     }
-
     // ---- M2: O^T[dv][t] += V^T A^T, this wave's 32 value channels
     o[0] = o[1] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -379,26 +367,63 @@ __device__ __forceinline__ void scores_values(const Params& P, const _Float16* s
     }
 }
 
+// One chunk's operands as the lane loaded them (q, k, v: 8 binary16 channels
+// of one token) and the cumulative log2-decay bl along the 16 tokens of the
+// lane's sub-chunk, from the gate stage to the operand forms.
+struct Cur {
+    u32x4 q, k, v;
+    float bl[8];
+};
+
+// Gate stage of one chunk: per-token log2-decay (from the logits, or from the
+// rank values through the fused expansion), inclusive prefix along the 16
+// tokens of the sub-chunk by DPP row scans, and the sub-chunk totals into
+// sTot for the factor tables.  Tokens past the end of the scan (zero q, k, v,
+// only in its last chunk) keep their finite decay: it enters only quantities
+// after every valid token (sub-chunk totals that cancel in the scores, the
+// state after the last chunk, which is never published).
+template <bool PROJ>
+__device__ __forceinline__ void gate_stage(const Raw& raw, Cur& cur, float* sTot, const float* sW2,
+                                           const float* sGB, float inv_tau, int si, int h, int g,
+                                           int l16, int c0)
+{
+    cur.q = raw.q;
+    cur.k = raw.k;
+    cur.v = raw.v;
+    float zv[8];
+    {
+        const float4v z0 = __builtin_bit_cast(float4v, raw.z0);
+        const float4v z1 = __builtin_bit_cast(float4v, raw.z1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zv[e] = e < 4 ? z0[e] : z1[e - 4];
+    }
+    if (PROJ) proj_logits(__builtin_bit_cast(float4v, raw.z0), sW2, sGB, h, g, l16, zv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cur.bl[e] = log2_decay(zv[e], inv_tau);
+    row_scan_n(cur.bl);
+    if (l16 == 15) {
+        *(float4v*)(sTot + si * D + c0) = float4v{cur.bl[0], cur.bl[1], cur.bl[2], cur.bl[3]};
+        *(float4v*)(sTot + si * D + c0 + 4) = float4v{cur.bl[4], cur.bl[5], cur.bl[6], cur.bl[7]};
+    }
+}
+
 template <bool LOCAL, bool PROJ, int NCHK>
 __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 {
-    __shared__ __attribute__((aligned(16))) char lds[PROJ ? LDS_PROJ : LDS_TOTAL];
-    _Float16* sE = (_Float16*)(lds + L_E);
-    _Float16* sEL = (_Float16*)(lds + L_EL);
-    _Float16* sKT = (_Float16*)(lds + L_KT);
-    _Float16* sVT = (_Float16*)(lds + L_VT);
-    _Float16* sST = (_Float16*)(lds + L_ST);
-    _Float16* sQH = (_Float16*)(lds + L_QH);
-    float* sPA = (float*)(lds + L_PA);
-    _Float16* sFQ = (_Float16*)(lds + L_FQ);
-    _Float16* sFK = (_Float16*)(lds + L_FK);
-    float* sFB = (float*)(lds + L_FB);
-    float* sTot = (float*)(lds + L_TOT);
-    float* sDec = (float*)(lds + L_DEC);
-    float* sFac = (float*)(lds + L_FAC);
-    int* sRows = (int*)(lds + L_ROWS);
-    float* sSS = (float*)(lds + L_SS);
-    int* sMisc = (int*)(lds + L_MISC);
+    typedef Lay<NCHK> LY;
+    __shared__ __attribute__((aligned(16))) char lds[PROJ ? LY::TOTAL_PROJ : LY::TOTAL];
+    _Float16* sE = (_Float16*)(lds + LY::E);
+    _Float16* sKT = (_Float16*)(lds + LY::KT);
+    _Float16* sVT = (_Float16*)(lds + LY::VT);
+    _Float16* sST = (_Float16*)(lds + LY::ST);
+    _Float16* sQH = (_Float16*)(lds + LY::QH);
+    float* sPA = (float*)(lds + LY::PA);
+    float* sTot = (float*)(lds + LY::TOT);
+    float* sDec = (float*)(lds + LY::DEC);
+    float* sFac = (float*)(lds + LY::FAC);
+    int* sRows = (int*)(lds + LY::ROWS);
+    float* sSS = (float*)(lds + LY::SS);
+    int* sMisc = (int*)(lds + LY::MISC);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -503,8 +528,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 
     // ---- row tables of every chunk of the segment
     for (int i = tid; i < nch * C; i += NT) sRows[i] = scan_row(P, unit, c_begin * C + i);
-    float* sW2 = (float*)(lds + L_W2);
-    float* sGB = (float*)(lds + L_GB);
+    float* sW2 = (float*)(lds + LY::W2);
+    float* sGB = (float*)(lds + LY::GB);
     if (PROJ) {
         // this head's W2^T rows (D x 16) and bias: one 16-byte load per thread
         const int hd = unit % P.NH;
@@ -529,42 +554,24 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 #pragma unroll
     for (int c = 0; c < NCHK; ++c) {
         if (c >= nch) break;
-        float qv[8], kv[8], zv[8];
+        float qv[8], kv[8];
+        Cur cur;  // this chunk's operands and log2-decay prefix
         const u32x4 raw_v = raw.v;
         {
             const half8 qh = __builtin_bit_cast(half8, raw.q);
             const half8 kh8 = __builtin_bit_cast(half8, raw.k);
-            const float4v z0 = __builtin_bit_cast(float4v, raw.z0);
-            const float4v z1 = __builtin_bit_cast(float4v, raw.z1);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 qv[e] = (float)qh[e];
                 kv[e] = (float)kh8[e];
-                zv[e] = e < 4 ? z0[e] : z1[e - 4];
             }
-            // raw copies for the pairwise fallback of a wide diagonal block
-            *(u32x4*)(sFQ + tl * SH + c0) = raw.q;
-            *(u32x4*)(sFK + tl * SH + c0) = raw.k;
         }
-        if (PROJ) proj_logits(__builtin_bit_cast(float4v, raw.z0), sW2, sGB, h, g, l16, zv);
+        gate_stage<PROJ>(raw, cur, sTot, sW2, sGB, P.inv_tau, si, h, g, l16, c0);
         if (c + 1 < nch) load_raw<PROJ>(raw, src, P, sRows[(c + 1) * C + tl], c0, g);
-
-        // ---- gate stage: log2-decay, prefix along the 16 tokens of the sub-chunk.
-        //      Tokens past the end of the scan (zero q, k, v, only in its last
-        //      chunk) keep their finite decay: it enters only quantities after
-        //      every valid token (sub-chunk totals that cancel in the scores,
-        //      the state after the last chunk, which is never published).
+        __syncthreads();  // (1) sub-chunk totals
         float bl[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bl[e] = log2_decay(zv[e], P.inv_tau);
-        row_scan_n(bl);
-        if (l16 == 15) {
-            *(float4v*)(sTot + si * D + c0) = float4v{bl[0], bl[1], bl[2], bl[3]};
-            *(float4v*)(sTot + si * D + c0 + 4) = float4v{bl[4], bl[5], bl[6], bl[7]};
-        }
-        *(float4v*)(sFB + tl * SF + c0) = float4v{bl[0], bl[1], bl[2], bl[3]};
-        *(float4v*)(sFB + tl * SF + c0 + 4) = float4v{bl[4], bl[5], bl[6], bl[7]};
-        __syncthreads();  // (1) sub-chunk totals
+        for (int e = 0; e < 8; ++e) bl[e] = cur.bl[e];
 
         // ---- per-channel factors of this wave's sub-chunk and channel half,
         //      computed once per channel (table layout) and read back per lane
@@ -630,13 +637,38 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         // (a NaN also takes the pairwise path, which propagates it)
         wide |= !(maxqd <= Fmt<_Float16>::kMaxOperand);
         *(half8*)(sE + tl * SH + c0) = eh;
-        *(half8*)(sEL + tl * SH + c0) = el;
-        *(half8*)(sQH + tl * SH + c0) = qhat;
+        if (LY::kMulti) *(half8*)(sQH + tl * SH + c0) = qhat;
         *(half8*)(sKT + tl * SH + c0) = kt8;
         *(u32x4*)(sVT + tl * SH + c0) = raw_v;
-        {
-            const bool ww = __any(wide);
-            if (lane == 0) sMisc[4 + wave] = ww ? 1 : 0;
+        // A sub-chunk whose decay span is too wide for the factorised diagonal
+        // block (rare: it takes per-token decays far below any workload's)
+        // evaluates this half's diagonal partial pairwise, exactly,
+        //     q_t k_s 2^{bl_t - bl_s}  summed over the half's 32 channels, s <= t,
+        // from the registers of its own tokens: lane (t, g) holds channels
+        // c0 .. c0 + 7 of token t; the 16 lanes of its row hold the same
+        // channels of every token of the sub-chunk.  The partial lands in the
+        // wave's diagonal slot of the score exchange.
+        const bool wide_w = __any(wide);
+        if (wide_w) {
+            float pdv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int sk = 0; sk < kSub; ++sk) {
+                const int src = (lane & 0x30) | sk;
+                float pp = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float ks = __shfl(kv[e], src);
+                    const float bs = __shfl(bl[e], src);
+                    pp += qv[e] * ks * exp2_fast(bl[e] - bs);
+                }
+                if (sk > l16) pp = 0.f;
+                pp += __shfl_xor(pp, 16);
+                pp += __shfl_xor(pp, 32);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (sk == 4 * g + e) pdv[e] = pp;
+            }
+            *(float4v*)(sPA + ((wave * NSUB + si) * 64 + lane) * 4) = float4v{pdv[0], pdv[1], pdv[2], pdv[3]};
         }
         qkeep[c] = qs;
         // off-diagonal query operands for key sub-chunks i-2 and i-3
@@ -657,10 +689,10 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 
         float4v o[2];
         switch (si) {
-        case 0: scores_values<0>(P, sE, sEL, sVT, sPA, sMisc, sFQ, sFK, sFB, wave, lane, g, l16, h, c0, tl, qa, qo1, qo2, qd_h, qd_l, o); break;
-        case 1: scores_values<1>(P, sE, sEL, sVT, sPA, sMisc, sFQ, sFK, sFB, wave, lane, g, l16, h, c0, tl, qa, qo1, qo2, qd_h, qd_l, o); break;
-        case 2: scores_values<2>(P, sE, sEL, sVT, sPA, sMisc, sFQ, sFK, sFB, wave, lane, g, l16, h, c0, tl, qa, qo1, qo2, qd_h, qd_l, o); break;
-        default: scores_values<3>(P, sE, sEL, sVT, sPA, sMisc, sFQ, sFK, sFB, wave, lane, g, l16, h, c0, tl, qa, qo1, qo2, qd_h, qd_l, o); break;
+        case 0: scores_values<0>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, eh, el, qa, qo1, qo2, qd_h, qd_l, o); break;
+        case 1: scores_values<1>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, eh, el, qa, qo1, qo2, qd_h, qd_l, o); break;
+        case 2: scores_values<2>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, eh, el, qa, qo1, qo2, qd_h, qd_l, o); break;
+        default: scores_values<3>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, eh, el, qa, qo1, qo2, qd_h, qd_l, o); break;
         }
         // ---- M3: O^T += S_loc^T (q (.) 2^b)^T, local state from the segment start
         if (c > 0) {
@@ -691,12 +723,15 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             }
         }
         __syncthreads();  // (4) all readers of this chunk's buffers are done
+        if (LY::kMulti && c + 1 < nch) {
+            // the local state's binary16 copy for the next chunk's inter-chunk term
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int bb = sb0 + jj;
+            for (int jj = 0; jj < 2; ++jj) {
+                const int bb = sb0 + jj;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sST[(16 * bb + l16) * SH + 16 * sa + 4 * g + e] = (_Float16)S[jj][e];
+                for (int e = 0; e < 4; ++e)
+                    sST[(16 * bb + l16) * SH + 16 * sa + 4 * g + e] = (_Float16)S[jj][e];
+            }
         }
     }
 
@@ -721,8 +756,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     // ================= phase 2: segment exchange =================
     const size_t aggf = (size_t)D * D + D;
     const size_t slot = (size_t)unit * P.nseg + seg;
-    float* sL = (float*)(lds + L_LSEG);
-    float* sG = (float*)(lds + L_GSEG);
+    float* sL = (float*)(lds + LY::LSEG);
+    float* sG = (float*)(lds + LY::GSEG);
     const bool need_in = (seg > 0);
     if (P.nseg > 1) {
         // local state and total decay into LDS, row-major [ch][dv]
@@ -1009,7 +1044,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     __syncthreads();
 
     // ================= phase 3: incoming state, epilogue, stores =================
-    _Float16* sOut = (_Float16*)(lds + L_OUT);
+    _Float16* sOut = (_Float16*)(lds + LY::OUT);
     if (need_in) {
         // exchange the query-operand halves through the staging area
 #pragma unroll

@@ -98,11 +98,15 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
         const int min_seg = (nchunks + 64) / 65;
         const int64_t upx = (units + xcds - 1) / xcds;  // scans per XCD (most)
         const int max_seg = nchunks < gla::kOnePassMaxChunks ? nchunks : gla::kOnePassMaxChunks;
-        // the shortest segment whose workgroups fit in `slots` at `per` scans
-        // (the longest allowed when none does)
-        auto fit_seg = [&](int64_t per, int64_t slots) {
+        // the shortest segment whose workgroups fit in one round, one per
+        // compute unit, on `cu` compute units at `per` scans (the longest
+        // allowed when none does).  (The one-chunk instance could hold two
+        // workgroups per CU, but plans that used them measured slower: a
+        // 1.6K-token frame with 12 heads in one-chunk segments two per CU
+        // took 19.3 us per call against 16.1 us in two-chunk segments.)
+        auto fit_seg = [&](int64_t per, int64_t cu) {
             for (int sg = min_seg; sg <= max_seg; ++sg)
-                if (per * ((nchunks + sg - 1) / sg) <= slots) return sg;
+                if (per * ((nchunks + sg - 1) / sg) <= cu) return sg;
             return max_seg;
         };
         const int seg_g = fit_seg(units, cus);

@@ -90,7 +90,7 @@ def test_stack16k_gated(torch, call):
 def test_maximum_rows(torch, case):
     """Close to the largest row count each kernel addresses with 32-bit buffer
     offsets: the single pass (B*L*NH below 2^23; here 8.37 M rows of d = 64,
-    forced to 7-chunk segments: 18.9 K workgroups in 74 rounds) and the d = 128
+    forced to 5-chunk segments: 26.6 K workgroups in 104 rounds) and the d = 128
     passes (below 2^22; here 4.18 M rows), gated, 128x128 grids.  The oracle
     checks the first and the last (batch, head) scans in full: their rows sit
     at the lowest and the highest offsets."""
@@ -102,7 +102,7 @@ def test_maximum_rows(torch, case):
     rows = B * H * W * NH
     assert rows < (1 << 23 if d == 64 else 1 << 22)
     algo = gla.ALGO_SINGLE_PASS if case == "single_pass" else gla.ALGO_AUTO
-    seg = 7 if case == "single_pass" else 0
+    seg = 5 if case == "single_pass" else 0
     print(f"[case] maximum rows {case}: B={B} NH={NH} {H}x{W} d={d} rows={rows}", flush=True)
     t = make_inputs_device(B, NH, H, W, d, d, "f16", (0.0, 1.0), True, seed=4242)
     opts = gla.make_opts(B, NH, d, d, gla.F16, segment_chunks=seg, algorithm=algo)
@@ -153,7 +153,7 @@ def test_segment_split_invariance_three_pass(torch, seg):
         _check(f"seg{seg}", x, d, 24, 40, 64, "f16", torch, segment_chunks=seg, algorithm=2)
 
 
-@pytest.mark.parametrize("seg", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("seg", [1, 2, 3, 4, 5])
 def test_segment_split_invariance_single_pass(torch, seg):
     """Single pass with every segment length it supports (look-back over up to
     15 segments per scan, ragged last segment)."""

@@ -67,6 +67,11 @@ def test_default_geometry_is_mi355x(planner):
         (1, 1, 25, 1, 25, 1)
 
 
+def capacity(seg, cus):
+    """Workgroups resident at once: one per compute unit."""
+    return cus
+
+
 def test_four_xcd_geometry(planner):
     """128 compute units in 4 XCDs (32 each): the 1.6K-token frame with 6 heads
     needs two-chunk segments to fit one round, two scans per XCD."""
@@ -76,8 +81,8 @@ def test_four_xcd_geometry(planner):
     assert workgroups(p, 1, 6) == 4 * 26
     # 8 images: 48 scans do not fit one round; scans divide evenly over 4 XCDs
     q = plan(planner, (128, 4), 8, 6, 40, 40)
-    assert q.onepass == 1 and q.seg_chunks == 7 and q.xcd_local == 1
-    assert q.xcd_tasks == 12 * 4 and q.one_round == 0
+    assert q.onepass == 1 and q.seg_chunks == 5 and q.xcd_local == 1
+    assert q.xcd_tasks == 12 * 5 and q.one_round == 0
     # the same batch on an MI355X: five-chunk segments in one round
     r = plan(planner, (256, 8), 8, 6, 40, 40)
     assert (r.seg_chunks, r.nseg, r.one_round) == (5, 5, 1)
@@ -87,7 +92,7 @@ def test_single_xcd_geometry_is_chip_wide(planner):
     """One XCD (a partitioned device): no XCD-local placement."""
     p = plan(planner, (32, 1), 1, 6, 40, 40)
     assert p.onepass == 1 and p.xcd_local == 0 and p.xcds == 1
-    assert p.one_round == (6 * p.nseg <= 32)
+    assert p.one_round == (6 * p.nseg <= capacity(p.seg_chunks, 32))
     assert workgroups(p, 1, 6) == 6 * p.nseg
 
 
@@ -103,8 +108,8 @@ def test_one_round_matches_the_grid(planner):
             if not p.onepass:
                 continue
             if p.xcd_local:
-                assert p.one_round == (p.xcd_tasks <= cus // xcds)
+                assert p.one_round == (p.xcd_tasks <= capacity(p.seg_chunks, cus // xcds))
                 units_x = -(-B * NH // xcds)
                 assert p.xcd_tasks == units_x * p.nseg
             else:
-                assert p.one_round == (B * NH * p.nseg <= cus)
+                assert p.one_round == (B * NH * p.nseg <= capacity(p.seg_chunks, cus))
