@@ -280,15 +280,18 @@ __device__ __forceinline__ void nan_rows(const Params& P, int unit, int seg, int
 // Intra-chunk scores (M1, with the exchange of the two channel halves) and
 // scores times values (M2) for query sub-chunk SI: a compile-time sub-chunk
 // keeps every tile selection out of the control flow, so no register array is
-// merged across branches.  The diagonal tile's key operand is the lane's own
-// E (hi, lo) row; when the wave's sub-chunk is too wide for that factorised
-// form (wide_w), its diagonal partial is already in sPA, evaluated pairwise.
+// merged across branches.  The diagonal tile runs on the binary32 matrix
+// cores from the lane's own binary32 operands: at step s the lane supplies
+// key operand E[token][8g + s] and query operand q 2^{b - tot}[token][8g + s]
+// (its own channels, the same order on both sides), eight 16x16x4 steps over
+// the half's 32 channels.  When the wave's sub-chunk is too wide even for that
+// (wide_w), its diagonal partial is already in sPA, evaluated pairwise.
 template <int SI>
 __device__ __forceinline__ void scores_values(const _Float16* sE, const _Float16* sVT, float* sPA,
                                               int wave, int lane, int g, int l16, int h, int c0,
-                                              bool wide_w, const half8& eh, const half8& el,
+                                              bool wide_w, const float (&ef)[8], const float (&qd)[8],
                                               const half8& qa, const half8& qo1, const half8& qo2,
-                                              const half8& qd_h, const half8& qd_l, float4v (&o)[2])
+                                              float4v (&o)[2])
 {
     // ---- M1 partial scores over this wave's 32 channels, tiles j <= SI
     //      (j < SI off the diagonal; the diagonal tile separately)
@@ -305,9 +308,8 @@ __device__ __forceinline__ void scores_values(const _Float16* sE, const _Float16
     float4v pd = float4v{0.f, 0.f, 0.f, 0.f};
     float* const dslot = sPA + ((wave * NSUB + SI) * 64 + lane) * 4;
     if (!wide_w) {
-        pd = mma(eh, qd_h, pd);
-        pd = mma(el, qd_h, pd);
-        pd = mma(eh, qd_l, pd);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) pd = mma(ef[st], qd[st], pd);
         *(float4v*)dslot = pd;
     }
     __syncthreads();  // (3) partial scores of both halves
@@ -595,7 +597,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 fac[FD * 32 + cht] = exp2_fast(-ti);
                 fac[FQ * 32 + cht] = exp2_fast(rr);
                 fac[FS * 32 + cht] = exp2_fast(rr + dseg);
-                wide = !(-ti <= Fmt<_Float16>::kSpan);
+                wide = !(-ti <= Fmt<float>::kSpan);
                 if (si == 0) sDec[ch] = exp2_fast(all);
             } else {
                 fac[FK * 32 + cht] = exp2_fast(all - rr - ti);
@@ -616,26 +618,24 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         ld8f(fac + FS * 32 + 8 * g, fs);
         ld8f(fac + FK * 32 + 8 * g, fk);
         float qb[8];
-        half8 eh, el, kt8, qd_h, qd_l, qhat, qs, qa;
+        half8 eh, kt8, qhat, qs, qa;
+        float ef[8], qd[8];
         float maxqd = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             qb[e] = qv[e] * exp2_fast(bl[e]);
-            const float ef = kv[e] * exp2_fast(ti8[e] - bl[e]);
-            eh[e] = (_Float16)ef;
-            el[e] = (_Float16)(ef - (float)eh[e]);
-            kt8[e] = (_Float16)(ef * fk[e]);
-            const float qd = qb[e] * fd[e];
-            maxqd = fmaxf(maxqd, fabsf(qd));
-            qd_h[e] = (_Float16)qd;
-            qd_l[e] = (_Float16)(qd - (float)qd_h[e]);
+            ef[e] = kv[e] * exp2_fast(ti8[e] - bl[e]);
+            eh[e] = (_Float16)ef[e];
+            kt8[e] = (_Float16)(ef[e] * fk[e]);
+            qd[e] = qb[e] * fd[e];
+            maxqd = fmaxf(maxqd, fabsf(qd[e]));
             qhat[e] = (_Float16)(qb[e] * fq[e]);
             qs[e] = (_Float16)(qb[e] * fs[e]);
             qa[e] = (_Float16)qb[e];
         }
-        // the amplified diagonal query operand must stay in binary16 range
-        // (a NaN also takes the pairwise path, which propagates it)
-        wide |= !(maxqd <= Fmt<_Float16>::kMaxOperand);
+        // the amplified diagonal query operand must stay far inside binary32
+        // range (a NaN also takes the pairwise path, which propagates it)
+        wide |= !(maxqd <= Fmt<float>::kMaxOperand);
         *(half8*)(sE + tl * SH + c0) = eh;
         if (LY::kMulti) *(half8*)(sQH + tl * SH + c0) = qhat;
         *(half8*)(sKT + tl * SH + c0) = kt8;
@@ -689,10 +689,10 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
 
         float4v o[2];
         switch (si) {
-        case 0: scores_values<0>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, eh, el, qa, qo1, qo2, qd_h, qd_l, o); break;
-        case 1: scores_values<1>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, eh, el, qa, qo1, qo2, qd_h, qd_l, o); break;
-        case 2: scores_values<2>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, eh, el, qa, qo1, qo2, qd_h, qd_l, o); break;
-        default: scores_values<3>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, eh, el, qa, qo1, qo2, qd_h, qd_l, o); break;
+        case 0: scores_values<0>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, ef, qd, qa, qo1, qo2, o); break;
+        case 1: scores_values<1>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, ef, qd, qa, qo1, qo2, o); break;
+        case 2: scores_values<2>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, ef, qd, qa, qo1, qo2, o); break;
+        default: scores_values<3>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, ef, qd, qa, qo1, qo2, o); break;
         }
         // ---- M3: O^T += S_loc^T (q (.) 2^b)^T, local state from the segment start
         if (c > 0) {
