@@ -385,6 +385,25 @@ __global__ __launch_bounds__(NTS) void gla_bwd_fold_kernel(Params P, BwdParams Q
 // 2^{min(b_u - b_t, 0)}: pairs outside the causal triangle meet a zero score.
 // ---------------------------------------------------------------------------
 
+// E_{x, y} = 2^{c_{x-1} - c_y} for x = y .. NS (c_m the decay from the chunk
+// start to the end of sub-chunk m): 2^{-tot_y} for x = y, then the running
+// sums of the totals of the sub-chunks strictly between y and x, so each
+// exponent is a short sum and never a difference of two large cumulative
+// decays.
+template <int D>
+__device__ __forceinline__ void write_e_factors(float* sE, const float* sTot, int y, int ch)
+{
+    sE[(y * NS + y) * D + ch] = exp2_fast(-sTot[y * D + ch]);
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 1; x <= NS; ++x) {
+        if (x > y) {
+            sE[(x * NS + y) * D + ch] = exp2_fast(acc);
+            if (x < NS) acc += sTot[x * D + ch];
+        }
+    }
+}
+
 // dq_t += sum_{tau <= t, same sub-chunk} P[t][tau] k_tau 2^{b_t - b_tau}
 // for t = 16 si + 4 g + e, channel ch.
 template <typename T, int D>
@@ -623,26 +642,28 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
         cv[0] = 0.f;
 #pragma unroll
         for (int m = 0; m < NS; ++m) cv[m + 1] = cv[m] + sTot[m * D + gch];
-        const float off = cv[gi], ci = cv[gi + 1];
+        const float ci = cv[gi + 1], tot = br[15];
         sCC[(gi + 1) * D + gch] = ci;
         if (gi == 0) sCC[gch] = 0.f;
-        // E_{x, gi} for x = gi .. NS
-#pragma unroll
-        for (int x = 0; x <= NS; ++x)
-            if (x >= gi) sE[(x * NS + gi) * D + gch] = exp2_fast(cv[x] - ci);
+        // E_{x, gi} = 2^{c_{x-1} - c_gi} for x = gi .. NS, from the short sums
+        // of the sub-chunk totals between them (no differences of the large
+        // cumulative decays, whose rounding would dominate when decays are
+        // strong)
+        write_e_factors<D>(sE, sTot, gi, gch);
         float xq[16], xk[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             xq[u] = sQH[(16 * gi + u) * SD + gch];
             xk[u] = sKT[(16 * gi + u) * SD + gch];
         }
+        // b is kept relative to the sub-chunk start: pairwise factors and the
+        // per-position scalings take differences of these short sums only
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int t = 16 * gi + u;
-            const float b = br[u] + off;  // cumulative from the chunk start
-            sQH[t * SD + gch] = xq[u] * exp2_fast(b - off);  // <= 1
-            sKT[t * SD + gch] = xk[u] * exp2_fast(ci - b);   // <= 1
-            sB[t * SD + gch] = b;
+            sQH[t * SD + gch] = xq[u] * exp2_fast(br[u]);        // <= 1
+            sKT[t * SD + gch] = xk[u] * exp2_fast(tot - br[u]);  // <= 1
+            sB[t * SD + gch] = br[u];
         }
     }
     __syncthreads();
@@ -715,13 +736,12 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
 #pragma unroll
             for (int cl = 0; cl < CT; ++cl) {
                 const int ch = 16 * (ct0 + cl) + l16;
-                const float cim1 = sCC[si * D + ch];
                 float dg[4] = {0.f, 0.f, 0.f, 0.f};
                 if (pairwise) diag_dq<T, D>(P, sRows, sP, sB, si, g, ch, dg);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * si + 4 * g + e;
-                    dqv[cl][e] = acc[cl][e] * exp2_fast(sB[t * SD + ch] - cim1) + dg[e];
+                    dqv[cl][e] = acc[cl][e] * exp2_fast(sB[t * SD + ch]) + dg[e];
                     const int row = sRows[t];
                     if (row >= 0) store1<T>((T*)Q.dq, (size_t)row * D + ch, dqv[cl][e]);
                 }
@@ -776,11 +796,11 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
                 const int ch = 16 * (ct0 + cl) + l16;
                 float dg[4] = {0.f, 0.f, 0.f, 0.f};
                 if (pairwise) diag_dk<T, D>(P, sRows, sP, sB, si, g, ch, dg);
-                const float cic = sCC[(si + 1) * D + ch];
+                const float tot = sTot[si * D + ch];  // this sub-chunk's decay
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * si + 4 * g + e;
-                    dkv[cl][e] = acc[cl][e] * exp2_fast(cic - sB[t * SD + ch]) + dg[e];
+                    dkv[cl][e] = acc[cl][e] * exp2_fast(tot - sB[t * SD + ch]) + dg[e];
                     const int row = sRows[t];
                     if (row >= 0) store1<T>((T*)Q.dk, (size_t)row * D + ch, dkv[cl][e]);
                 }
@@ -1017,26 +1037,24 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
         cv[0] = 0.f;
 #pragma unroll
         for (int m = 0; m < NS; ++m) cv[m + 1] = cv[m] + sTot[m * D + gch];
-        const float off = cv[gi], ci = cv[gi + 1];
+        const float off = cv[gi], ci = cv[gi + 1], tot = br[15];
         sCC[(gi + 1) * D + gch] = ci;
         if (gi == 0) sCC[gch] = 0.f;
-#pragma unroll
-        for (int x = 0; x <= NS; ++x)
-            if (x >= gi) sE[(x * NS + gi) * D + gch] = exp2_fast(cv[x] - ci);
+        write_e_factors<D>(sE, sTot, gi, gch);
         float xq[16], xk[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             xq[u] = sQH[(16 * gi + u) * SD + gch];
             xk[u] = sKT[(16 * gi + u) * SD + gch];
         }
+        // b relative to the sub-chunk start, as in the chunk kernel
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int t = 16 * gi + u;
-            const float b = br[u] + off;
-            sQH[t * SD + gch] = xq[u] * exp2_fast(b - off);
-            sKT[t * SD + gch] = xk[u] * exp2_fast(ci - b);
-            sQB[t * SD + gch] = xq[u] * exp2_fast(b);  // <= 1
-            sB[t * SD + gch] = b;
+            sQH[t * SD + gch] = xq[u] * exp2_fast(br[u]);
+            sKT[t * SD + gch] = xk[u] * exp2_fast(tot - br[u]);
+            sQB[t * SD + gch] = xq[u] * exp2_fast(br[u] + off);  // <= 1, from the chunk start
+            sB[t * SD + gch] = br[u];
         }
     }
     __syncthreads();

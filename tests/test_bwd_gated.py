@@ -170,12 +170,84 @@ def test_bwd_gated_deterministic(torch):
 
 
 # Binary32 bar of the strongly local case z ~ N(-60, 5) (per-token decay about
-# 2^-5.4): o_t is then about s (q_t . k_t) v_t, a 64-term dot product that can
-# cancel, and RMSNorm's 1/rms(o) (up to 200 here) magnifies its binary32
-# evaluation error into dO.  Evaluating o alone in plain binary32 (numpy, same
-# inputs, everything else exact) moves dq and dk by 1.8-2.2e-5 of their max, so
-# no binary32 implementation meets 2e-5 there; the bar is ten times that.
-TOL_STRONG_F32 = 2e-4
+# 2^-5.4): o_t is then about s (q_t . k_t) v_t plus a few quickly decaying
+# neighbours, a dot product that can cancel, and RMSNorm's 1/rms(o) (up to 200
+# here) magnifies its evaluation error into dO, more in the direction whose
+# worst token has the smaller rms (B2T: 203 against L2R: 107).  The bar comes
+# from a model of the least any binary32 implementation can do:
+# binary32_o_model evaluates o alone in binary32 (exact pair factors rounded to
+# binary32, every product and sum in binary32), then everything after it
+# exactly, and measures the gradients against the oracle.  The kernel must stay
+# within 1.5 times that (it measures within 1 % of it: pair factors come from
+# short sums of per-position decays, never from differences of large
+# cumulative ones).
+
+
+def binary32_o_model(x, direction, H, W, reach=24):
+    """o [B, L, NH, D] evaluated in binary32: for each token the pairs with the
+    `reach` positions before it along the scan (the rest weigh below 2^-120 in
+    the strongly local case), each pair's decay factor computed exactly and
+    rounded to binary32, products and channel sums (sequential) and the sum
+    over pairs in binary32."""
+    f32 = np.float32
+    q, k, v, z = x["q"], x["k"], x["v"], x["z"]
+    B, L, NH, D = q.shape
+
+    def scan(a):
+        return np.moveaxis(oracle.to_scan_order(np.moveaxis(a, 1, 0), direction, H, W), 0, 1)
+
+    Q, K, V = (scan(a).astype(f32) for a in (q, k, v))
+    zs = scan(z).astype(np.float64)
+    a = -np.log1p(np.exp(-zs)) / 16.0  # natural-log decay per position
+    cum = np.cumsum(a, axis=1)
+    o = np.zeros((B, L, NH, D), f32)
+    for dl in range(min(reach + 1, L)):
+        fac = np.exp(cum[:, dl:] - cum[:, :L - dl]).astype(f32)
+        prod = (Q[:, dl:] * K[:, :L - dl]).astype(f32) * fac
+        sc = np.cumsum(prod.astype(f32), axis=-1, dtype=f32)[..., -1] * f32(1 / np.sqrt(D))
+        o[:, dl:] = (o[:, dl:] + sc.astype(f32)[..., None] * V[:, :L - dl]).astype(f32)
+    return np.moveaxis(oracle.from_scan_order(np.moveaxis(o, 1, 0), direction, H, W), 0, 1)
+
+
+def gate_backward_binary32(o, r, w, du, eps=1e-6):
+    """dO = rho g - (rho^3 / d) o sum(g (.) o), g = du (.) SiLU(r) (.) w, in binary32."""
+    f32 = np.float32
+    D = o.shape[-1]
+    o, r, du, w = (a.astype(f32) for a in (o, r, du, w))
+    sr = (r * (f32(1) / (f32(1) + np.exp(-r))).astype(f32)).astype(f32)
+    ss = np.sum(o * o, axis=-1, dtype=f32, keepdims=True)
+    dot = np.sum(du * sr * w * o, axis=-1, dtype=f32, keepdims=True)
+    rho = (f32(1) / np.sqrt(ss / f32(D) + f32(eps))).astype(f32)
+    return (rho * du * sr * w - (rho * rho * rho / f32(D) * dot).astype(f32) * o).astype(f32)
+
+
+def binary32_o_errors(x, direction, H, W, o=None):
+    """Errors (relative to max |oracle|) of dq, dk, dv, dz when o comes from
+    `o` (default: binary32_o_model) and everything after it is exact."""
+    ref = oracle.bwd_gated(x["q"], x["k"], x["v"], x["z"], x["r"], x["w"], x["dout"], direction,
+                           H, W)
+    if o is None:
+        o = binary32_o_model(x, direction, H, W)
+    dO = gate_backward_binary32(o, x["r"], x["w"], x["dout"])
+    got = oracle.bwd(x["q"], x["k"], x["v"], x["z"], dO, direction, H, W)
+    return {n: float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
+            for n, g, r in zip(("dq", "dk", "dv", "dz"), got, ref[:4])}
+
+
+def test_binary32_o_model_pins():
+    """The model's own pins: with the fp64 o of the oracle everything after o
+    adds almost nothing (the binary32 gate backward alone: < 1e-6), and the
+    modelled o differs from the oracle's by binary32 rounding only."""
+    x = make_bwd_inputs(2, 2, 16, 20, 64, "f32", z=(-60.0, 5.0), seed=13, gated=True)
+    for d in (0, 3):
+        o64 = oracle.fwd(x["q"], x["k"], x["v"], x["z"], d, 16, 20)
+        e = binary32_o_errors(x, d, 16, 20, o=o64)
+        assert max(e.values()) < 1e-6, e
+        om = binary32_o_model(x, d, 16, 20)
+        assert np.max(np.abs(om - o64)) / np.max(np.abs(o64)) < 1e-6
+        # o in binary32 costs dq and dk a few 1e-5 here (the kernel's floor)
+        e = binary32_o_errors(x, d, 16, 20)
+        assert 1e-5 < e["dq"] < 5e-5 and 1e-5 < e["dk"] < 5e-5, e
 
 
 @pytest.mark.gpu
@@ -185,6 +257,10 @@ def test_bwd_gated_strong_decay(torch, dtype, z):
     # sub-chunks whose decay spans more than 2^60 take the pairwise diagonal
     # blocks, in the o kernel as in the chunk kernel; (-12, 12) mixes both paths
     x = make_bwd_inputs(2, 2, 16, 20, 64, dtype, z=z, seed=13, gated=True)
-    tol = TOL_STRONG_F32 if (dtype == "f32" and z[0] == -60.0) else TOL[dtype]
     for direction in (0, 3):
+        tol = TOL[dtype]
+        if dtype == "f32" and z[0] == -60.0:
+            model = binary32_o_errors(x, direction, 16, 20)
+            tol = max(tol, 1.5 * max(model.values()))
+            print(f"[bar] strong binary32 dir={direction}: model {model} -> {tol:.2e}", flush=True)
         _check(f"strong z={z}", x, direction, 16, 20, tol, torch)
