@@ -290,8 +290,11 @@ GLA_API int gla_spatial_swiglu(const void *gate, const void *value, int64_t ld_i
  * along the scan order of `dir`, results at the original token positions.
  *   q, k, gate_logits, dq, dk, dz  [B, L, NH, dk]; v, dout, dv [B, L, NH, dv]
  *   q, k, v, dout, dq, dk, dv in opts->dtype; gate_logits and dz binary32
- * Supported: dk == dv in {16, 32, 64}, binary16 or binary32 storage; 64-position
- * chunks.  opts->norm_weight, eps, segment_chunks and algorithm are ignored.
+ * Supported: dk == dv in {16, 32, 64, 128}, binary16 or binary32 storage;
+ * 64-position chunks.  d = 128 runs as four d = 64 quarters (key half x value
+ * half: the decay acts on each key channel alone and o is linear in v) whose
+ * gradients add up in binary32 in the workspace.  opts->norm_weight, eps,
+ * segment_chunks and algorithm are ignored.
  * The workspace must hold gla_bwd_workspace_size() bytes (no initialisation:
  * every call rewrites what it reads).  Its data starts after the same fixed
  * 4096 + 131072-byte prefix as gla_fwd's, which a backward never writes, so one
@@ -314,8 +317,9 @@ GLA_API size_t gla_bwd_workspace_size(int dir, int H, int W, const gla_opts *opt
  *     do = rho g - (rho^3 / d_v) o sum(g (.) o)
  *     dr = dout (.) w (.) o rho (.) SiLU'(r)
  *     dw = sum over every (batch, token, head) row of dout (.) SiLU(r) (.) o rho
- * and dq, dk, dv, dz as gla_bwd for do.  o is recomputed by the three-pass
- * forward (stored in the storage type, then used as is).
+ * and dq, dk, dv, dz as gla_bwd for do.  o is recomputed chunk by chunk in
+ * binary32 (never rounded to the storage type) and do stays binary32 in the
+ * workspace; the same head sizes as gla_bwd.
  *   r, dout, dr [B, L, NH, dv] in opts->dtype; w = opts->norm_weight ([dv]
  *   binary32, NULL selects ones) and opts->eps as in gla_fwd; dw [dv] binary32,
  *   may be NULL (not computed); the rest as gla_bwd.

@@ -259,7 +259,7 @@ namespace {
 void bwd_params(const void* q, const void* k, const void* v, const float* gate_logits,
                 const void* dout, int dir, int H, int W, void* dq, void* dk, void* dv, float* dz,
                 const gla_opts* opts, char* ws, int nchunks, size_t off_f, size_t off_r,
-                size_t off_s, gla::Params& P, gla::BwdParams& Q)
+                size_t off_s, size_t off_p, gla::Params& P, gla::BwdParams& Q)
 {
     P.q = q;
     P.k = k;
@@ -296,6 +296,15 @@ void bwd_params(const void* q, const void* k, const void* v, const float* gate_l
     Q.ws_f = (float*)(ws + off_f);
     Q.ws_r = (float*)(ws + off_r);
     Q.ws_s = (float*)(ws + off_s);
+    Q.ld = opts->dk;
+    // d = 128: binary32 partial sums of the d = 64 quarters (dq, dk of one key
+    // half, dv of both value halves)
+    const size_t rows = (size_t)opts->batch * H * W * opts->heads;
+    Q.ldp = 64;
+    Q.pq = off_p ? (float*)(ws + off_p) : nullptr;
+    Q.pk = off_p ? Q.pq + rows * 64 : nullptr;
+    Q.pv = off_p ? Q.pk + rows * 64 : nullptr;
+    Q.mode_qk = Q.mode_v = 0;
 }
 
 }  // namespace
@@ -305,22 +314,23 @@ extern "C" int gla_bwd(const void* q, const void* k, const void* v, const float*
                        float* dz, const gla_opts* opts)
 {
     int nchunks = 0;
-    size_t off_f = 0, off_r = 0, off_s = 0;
+    size_t off_f = 0, off_r = 0, off_s = 0, off_p = 0;
     const int st = gla_validate_bwd(q, k, v, gate_logits, dout, dir, H, W, dq, dk, dv, dz, opts,
-                                    &nchunks, &off_f, &off_r, &off_s);
+                                    &nchunks, &off_f, &off_r, &off_s, &off_p);
     if (st != GLA_OK) return st;
     gla::Params P;
     gla::BwdParams Q;
     bwd_params(q, k, v, gate_logits, dout, dir, H, W, dq, dk, dv, dz, opts, (char*)opts->workspace,
-               nchunks, off_f, off_r, off_s, P, Q);
+               nchunks, off_f, off_r, off_s, off_p, P, Q);
     return gla::launch_bwd(P, Q, opts->dtype, opts->dk, opts->stream);
 }
 
 extern "C" size_t gla_bwd_workspace_size(int dir, int H, int W, const gla_opts* opts)
 {
     int nchunks = 0;
-    size_t off_f = 0, off_r = 0, off_s = 0, bytes = 0;
-    if (gla_plan_bwd(dir, H, W, opts, &nchunks, &off_f, &off_r, &off_s, &bytes) != GLA_OK) return 0;
+    size_t off_f = 0, off_r = 0, off_s = 0, off_p = 0, bytes = 0;
+    if (gla_plan_bwd(dir, H, W, opts, &nchunks, &off_f, &off_r, &off_s, &off_p, &bytes) != GLA_OK)
+        return 0;
     return bytes;
 }
 
@@ -338,7 +348,7 @@ extern "C" int gla_bwd_gated(const void* q, const void* k, const void* v,
     gla::BwdParams Q;
     // dO (binary32) is produced inside the call, in the workspace
     bwd_params(q, k, v, gate_logits, ws + lay.off_do, dir, H, W, dq, dk, dv, dz, opts, ws,
-               lay.nchunks, lay.off_f, lay.off_r, lay.off_s, P, Q);
+               lay.nchunks, lay.off_f, lay.off_r, lay.off_s, lay.off_p, P, Q);
     gla::GatedBwd G;
     G.r = r;
     G.du = dout;
@@ -347,6 +357,8 @@ extern "C" int gla_bwd_gated(const void* q, const void* k, const void* v,
     G.dwp = (float*)(ws + lay.off_dwp);
     G.dw = dw;
     G.eps = opts->eps;
+    G.o_out = nullptr;
+    G.o_acc = 0;
     return gla::launch_bwd_gated(P, Q, G, opts->dtype, opts->dk, opts->stream);
 }
 

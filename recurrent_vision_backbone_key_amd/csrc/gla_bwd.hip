@@ -170,6 +170,20 @@ __device__ __forceinline__ void store1(T* base, size_t idx, float x)
     __builtin_nontemporal_store((T)x, base + idx);
 }
 
+// One gradient element: stored (mode 0); or, in a quarter of a d = 128 call,
+// kept as a binary32 partial sum (mode 1) or added to the partial sum the
+// other quarter left and stored (mode 2).
+template <typename T>
+__device__ __forceinline__ void put_grad(T* fin, size_t fi, float* part, size_t pi, int mode, float x)
+{
+    if (mode == 1) {
+        part[pi] = x;
+        return;
+    }
+    if (mode == 2) x += part[pi];
+    store1<T>(fin, fi, x);
+}
+
 // ---------------------------------------------------------------------------
 // Chunk states: slot c of ws_f <- (L_c, B_c) for c < nchunks - 1 and slot
 // c - 1 of ws_r <- (RA_c, B_c) for c >= 1.
@@ -210,12 +224,12 @@ __global__ __launch_bounds__(NTS) void gla_bwd_states_kernel(Params P, BwdParams
         const int t = (i < C * G8 ? i : 0) / G8, c8 = 8 * (i % G8);
         rows[it] = sRows[t];
         if (REV) {
-            rq[it].load((const T*)P.q, rows[it], D, c8);
-            rd[it].load((const TD*)Q.dout, rows[it], D, c8);
+            rq[it].load((const T*)P.q, rows[it], Q.ld, c8);
+            rd[it].load((const TD*)Q.dout, rows[it], Q.ld, c8);
         }
         if (FWD) {
-            rk[it].load((const T*)P.k, rows[it], D, c8);
-            rv[it].load((const T*)P.v, rows[it], D, c8);
+            rk[it].load((const T*)P.k, rows[it], Q.ld, c8);
+            rv[it].load((const T*)P.v, rows[it], Q.ld, c8);
         }
     }
     // the gate logits of thread (ch, i)'s 16 positions, in flight as well
@@ -224,7 +238,7 @@ __global__ __launch_bounds__(NTS) void gla_bwd_states_kernel(Params P, BwdParams
     float br[16];
     if (gate_thread) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) br[u] = ld1<float>(P.z, sRows[16 * gi + u], D, gch);
+        for (int u = 0; u < 16; ++u) br[u] = ld1<float>(P.z, sRows[16 * gi + u], Q.ld, gch);
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -407,14 +421,14 @@ __device__ __forceinline__ void write_e_factors(float* sE, const float* sTot, in
 // dq_t += sum_{tau <= t, same sub-chunk} P[t][tau] k_tau 2^{b_t - b_tau}
 // for t = 16 si + 4 g + e, channel ch.
 template <typename T, int D>
-__device__ __forceinline__ void diag_dq(const Params& P, const int* sRows, const float* sP,
+__device__ __forceinline__ void diag_dq(const Params& P, int ld, const int* sRows, const float* sP,
                                         const float* sB, int si, int g, int ch, float (&out)[4])
 {
     constexpr int SD = Lay<D>::SD, SC = Lay<D>::SC;
     float kr[16], bk[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-        kr[x] = ld1<T>(P.k, sRows[16 * si + x], D, ch);
+        kr[x] = ld1<T>(P.k, sRows[16 * si + x], ld, ch);
         bk[x] = sB[(16 * si + x) * SD + ch];
     }
 #pragma unroll
@@ -431,14 +445,14 @@ __device__ __forceinline__ void diag_dq(const Params& P, const int* sRows, const
 
 // dk_t += sum_{u >= t, same sub-chunk} P[u][t] q_u 2^{b_u - b_t}.
 template <typename T, int D>
-__device__ __forceinline__ void diag_dk(const Params& P, const int* sRows, const float* sP,
+__device__ __forceinline__ void diag_dk(const Params& P, int ld, const int* sRows, const float* sP,
                                         const float* sB, int si, int g, int ch, float (&out)[4])
 {
     constexpr int SD = Lay<D>::SD, SC = Lay<D>::SC;
     float qr[16], bq[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-        qr[x] = ld1<T>(P.q, sRows[16 * si + x], D, ch);
+        qr[x] = ld1<T>(P.q, sRows[16 * si + x], ld, ch);
         bq[x] = sB[(16 * si + x) * SD + ch];
     }
 #pragma unroll
@@ -455,7 +469,7 @@ __device__ __forceinline__ void diag_dk(const Params& P, const int* sRows, const
 
 // A[u][t] = s sum_ch q_u k_t 2^{b_u - b_t} for u = 16 si + 4 g + e >= t = 16 si + l16.
 template <typename T, int D>
-__device__ __forceinline__ float4v diag_scores(const Params& P, const int* sRows, const float* sB,
+__device__ __forceinline__ float4v diag_scores(const Params& P, int ld, const int* sRows, const float* sB,
                                                int si, int g, int l16)
 {
     constexpr int SD = Lay<D>::SD;
@@ -465,12 +479,12 @@ __device__ __forceinline__ float4v diag_scores(const Params& P, const int* sRows
 #pragma unroll 1
     for (int c8 = 0; c8 < D; c8 += 8) {
         float kk[8];
-        load8<T>((const T*)P.k, rt, D, c8, kk);
+        load8<T>((const T*)P.k, rt, ld, c8, kk);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int u = 16 * si + 4 * g + e;
             float qq[8];
-            load8<T>((const T*)P.q, sRows[u], D, c8, qq);
+            load8<T>((const T*)P.q, sRows[u], ld, c8, qq);
 #pragma unroll
             for (int x = 0; x < 8; ++x)
                 a[e] += qq[x] * kk[x] * exp2_fast(fminf(sB[u * SD + c8 + x] - sB[t * SD + c8 + x], 0.f));
@@ -484,7 +498,7 @@ __device__ __forceinline__ float4v diag_scores(const Params& P, const int* sRows
 // scores[t][tau] = s sum_ch q_t k_tau 2^{b_t - b_tau} for t = 16 si + l16 >=
 // tau = 16 si + 4 g + e (the layout of the output product's A operand).
 template <typename T, int D>
-__device__ __forceinline__ float4v diag_scores_out(const Params& P, const int* sRows, const float* sB,
+__device__ __forceinline__ float4v diag_scores_out(const Params& P, int ld, const int* sRows, const float* sB,
                                                    int si, int g, int l16)
 {
     constexpr int SD = Lay<D>::SD;
@@ -494,12 +508,12 @@ __device__ __forceinline__ float4v diag_scores_out(const Params& P, const int* s
 #pragma unroll 1
     for (int c8 = 0; c8 < D; c8 += 8) {
         float qq[8];
-        load8<T>((const T*)P.q, rt, D, c8, qq);
+        load8<T>((const T*)P.q, rt, ld, c8, qq);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int u = 16 * si + 4 * g + e;
             float kk[8];
-            load8<T>((const T*)P.k, sRows[u], D, c8, kk);
+            load8<T>((const T*)P.k, sRows[u], ld, c8, kk);
 #pragma unroll
             for (int x = 0; x < 8; ++x)
                 a[e] += qq[x] * kk[x] * exp2_fast(fminf(sB[t * SD + c8 + x] - sB[u * SD + c8 + x], 0.f));
@@ -584,17 +598,17 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             const int i = tid + it * NT;
             const int t = (i < C * G8 ? i : 0) / G8, c8 = 8 * (i % G8);
             rows[it] = scan_row(P, unit, c * C + t);
-            rq[it].load((const T*)P.q, rows[it], D, c8);
-            rk[it].load((const T*)P.k, rows[it], D, c8);
-            rv[it].load((const T*)P.v, rows[it], D, c8);
-            rd[it].load((const TD*)Q.dout, rows[it], D, c8);
+            rq[it].load((const T*)P.q, rows[it], Q.ld, c8);
+            rk[it].load((const T*)P.k, rows[it], Q.ld, c8);
+            rv[it].load((const T*)P.v, rows[it], Q.ld, c8);
+            rd[it].load((const TD*)Q.dout, rows[it], Q.ld, c8);
         }
         if (gate_thread) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int row = scan_row(P, unit, c * C + 16 * gi + u);
                 zok |= (row >= 0 ? 1u : 0u) << u;
-                zz[u] = ld1<float>(P.z, row, D, gch);
+                zz[u] = ld1<float>(P.z, row, Q.ld, gch);
             }
             later_c = has_r ? Q.ws_s[((size_t)unit * P.nchunks + c) * D + gch] : 0.f;
         }
@@ -737,13 +751,13 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             for (int cl = 0; cl < CT; ++cl) {
                 const int ch = 16 * (ct0 + cl) + l16;
                 float dg[4] = {0.f, 0.f, 0.f, 0.f};
-                if (pairwise) diag_dq<T, D>(P, sRows, sP, sB, si, g, ch, dg);
+                if (pairwise) diag_dq<T, D>(P, Q.ld, sRows, sP, sB, si, g, ch, dg);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * si + 4 * g + e;
                     dqv[cl][e] = acc[cl][e] * exp2_fast(sB[t * SD + ch]) + dg[e];
                     const int row = sRows[t];
-                    if (row >= 0) store1<T>((T*)Q.dq, (size_t)row * D + ch, dqv[cl][e]);
+                    if (row >= 0) put_grad<T>((T*)Q.dq, (size_t)row * Q.ld + ch, Q.pq, (size_t)row * Q.ldp + ch, Q.mode_qk, dqv[cl][e]);
                 }
             }
         }
@@ -795,14 +809,14 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             for (int cl = 0; cl < CT; ++cl) {
                 const int ch = 16 * (ct0 + cl) + l16;
                 float dg[4] = {0.f, 0.f, 0.f, 0.f};
-                if (pairwise) diag_dk<T, D>(P, sRows, sP, sB, si, g, ch, dg);
+                if (pairwise) diag_dk<T, D>(P, Q.ld, sRows, sP, sB, si, g, ch, dg);
                 const float tot = sTot[si * D + ch];  // this sub-chunk's decay
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * si + 4 * g + e;
                     dkv[cl][e] = acc[cl][e] * exp2_fast(tot - sB[t * SD + ch]) + dg[e];
                     const int row = sRows[t];
-                    if (row >= 0) store1<T>((T*)Q.dk, (size_t)row * D + ch, dkv[cl][e]);
+                    if (row >= 0) put_grad<T>((T*)Q.dk, (size_t)row * Q.ld + ch, Q.pk, (size_t)row * Q.ldp + ch, Q.mode_qk, dkv[cl][e]);
                 }
             }
         }
@@ -820,7 +834,7 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             // even and odd k-steps on two independent chains
             float4v a = {0.f, 0.f, 0.f, 0.f};
             if (j == si && pairwise) {
-                a = diag_scores<T, D>(P, sRows, sB, si, g, l16);
+                a = diag_scores<T, D>(P, Q.ld, sRows, sB, si, g, l16);
             } else {
                 // the block's B operands first (all factor loads in flight
                 // together), then the two MFMA chains
@@ -862,7 +876,8 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = sRows[16 * si + 4 * g + e];
-                if (row >= 0) store1<T>((T*)Q.dv, (size_t)row * D + 16 * (ct0 + cl) + l16, dvacc[cl][e]);
+                const size_t idx = (size_t)row * Q.ld + 16 * (ct0 + cl) + l16;
+                if (row >= 0) put_grad<T>((T*)Q.dv, idx, Q.pv, idx, Q.mode_v, dvacc[cl][e]);
             }
     }
     __syncthreads();  // every reader of P is done: reuse it
@@ -876,8 +891,8 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = sRows[16 * si + 4 * g + e], ch = 16 * (ct0 + cl) + l16;
-                qv[cl][e] = ld1<T>(P.q, row, D, ch);
-                kv[cl][e] = ld1<T>(P.k, row, D, ch);
+                qv[cl][e] = ld1<T>(P.q, row, Q.ld, ch);
+                kv[cl][e] = ld1<T>(P.k, row, Q.ld, ch);
             }
 #pragma unroll
         for (int cl = 0; cl < CT; ++cl)
@@ -908,7 +923,8 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
             const int row = sRows[16 * gi + u];
             // 1 - sigmoid(z) as sigmoid(-z)
             const float nsig = rcp_fast(1.0f + exp2_fast(zz[u] * kLog2e));
-            if (row >= 0) store1<float>(Q.dz, (size_t)row * D + gch, (br[u] + later) * nsig * P.inv_tau);
+            const size_t idx = (size_t)row * Q.ld + gch;
+            if (row >= 0) put_grad<float>(Q.dz, idx, Q.dz, idx, Q.mode_qk, (br[u] + later) * nsig * P.inv_tau);
         }
     }
 }
@@ -925,7 +941,8 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
 // h of the column tiles; o of a block is sum_{j <= si} scores_ij V_j +
 // s Qh_si (2^{c_{si-1}} (.) S_in) with scores_ij = s Qh_i (Kh_j (.) E_ij)^T.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+// OONLY: o alone (a quarter of a d = 128 call), added to G.o_out.
+template <typename T, int D, bool OONLY>
 __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q, GatedBwd G)
 {
     using Y = Lay<D>;
@@ -984,16 +1001,16 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
             const int i = tid + it * NT;
             const int t = (i < C * G8 ? i : 0) / G8, c8 = 8 * (i % G8);
             rows[it] = scan_row(P, unit, c * C + t);
-            rq[it].load((const T*)P.q, rows[it], D, c8);
-            rk[it].load((const T*)P.k, rows[it], D, c8);
-            rv[it].load((const T*)P.v, rows[it], D, c8);
+            rq[it].load((const T*)P.q, rows[it], Q.ld, c8);
+            rk[it].load((const T*)P.k, rows[it], Q.ld, c8);
+            rv[it].load((const T*)P.v, rows[it], Q.ld, c8);
         }
         if (gate_thread) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int row = scan_row(P, unit, c * C + 16 * gi + u);
                 zok |= (row >= 0 ? 1u : 0u) << u;
-                zz[u] = ld1<float>(P.z, row, D, gch);
+                zz[u] = ld1<float>(P.z, row, Q.ld, gch);
             }
         }
         for (int i = tid; i < C; i += NT) sRows[i] = scan_row(P, unit, c * C + i);
@@ -1069,7 +1086,7 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
             // scores[t = 16 si + l16][tau = 16 j + 4g + e], two chains
             float4v a = {0.f, 0.f, 0.f, 0.f};
             if (j == si && pairwise) {
-                a = diag_scores_out<T, D>(P, sRows, sB, si, g, l16);
+                a = diag_scores_out<T, D>(P, Q.ld, sRows, sB, si, g, l16);
             } else {
                 // the block's A operands first (all loads in flight together),
                 // then the two MFMA chains
@@ -1110,11 +1127,25 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
         }
     }
 
-    // ---- output gate backward at (t = 16 si + 4g + e, col = 16 (ct0 + cl) + l16)
-    float rv[CT][4], uv[CT][4], wv[CT];
     int rowe[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) rowe[e] = sRows[16 * si + 4 * g + e];
+    if constexpr (OONLY) {
+        if (cols) {
+#pragma unroll
+            for (int cl = 0; cl < CT; ++cl)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (rowe[e] < 0) continue;
+                    const size_t idx = (size_t)rowe[e] * Q.ld + 16 * (ct0 + cl) + l16;
+                    G.o_out[idx] = G.o_acc ? G.o_out[idx] + oacc[cl][e] : oacc[cl][e];
+                }
+        }
+        return;
+    }
+
+    // ---- output gate backward at (t = 16 si + 4g + e, col = 16 (ct0 + cl) + l16)
+    float rv[CT][4], uv[CT][4], wv[CT];
 #pragma unroll
     for (int cl = 0; cl < CT; ++cl) {
         const int col = 16 * (ct0 + cl) + l16;
@@ -1122,8 +1153,8 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
         wv[cl] = G.w ? G.w[colc] : 1.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            rv[cl][e] = ld1<T>(G.r, cols ? rowe[e] : -1, D, colc);
-            uv[cl][e] = ld1<T>(G.du, cols ? rowe[e] : -1, D, colc);
+            rv[cl][e] = ld1<T>(G.r, cols ? rowe[e] : -1, Q.ld, colc);
+            uv[cl][e] = ld1<T>(G.du, cols ? rowe[e] : -1, Q.ld, colc);
         }
     }
     float ss[4], dot[4];
@@ -1173,7 +1204,7 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
             const int row = rowe[e];
             if (cols) sDO[t * SD + 16 * (ct0 + cl) + l16] = dov;  // rows past the end: 0
             if (cols && row >= 0) {
-                const size_t idx = (size_t)row * D + 16 * (ct0 + cl) + l16;
+                const size_t idx = (size_t)row * Q.ld + 16 * (ct0 + cl) + l16;
                 ((float*)Q.dout)[idx] = dov;
                 store1<T>((T*)G.dr, idx, drv);
             }
@@ -1222,6 +1253,71 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
     }
 }
 
+// Output gate backward row by row, for a d = 128 call whose o (binary32,
+// complete) sits in `od` (row stride d): dO replaces o there, dr is stored,
+// and block b leaves its rows' dw partial sums in dwp[b] (the formulas of the
+// o kernel's epilogue; fixed summation order).  Block b takes rows
+// [64 b, 64 b + 64), 16 per wavefront; lane l the columns l + 64 p.
+constexpr int NER = 256;
+template <typename T, int D>
+__global__ __launch_bounds__(NER) void gla_bwd_epi_rows_kernel(float* __restrict__ od, GatedBwd G,
+                                                              int rows)
+{
+    constexpr int PER = D / 64;
+    __shared__ float sRed[NER / 64][D];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float wv[PER], dwl[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        wv[p] = G.w ? G.w[lane + 64 * p] : 1.0f;
+        dwl[p] = 0.f;
+    }
+    const int row0 = blockIdx.x * 64 + wave * 16;
+    for (int i = 0; i < 16 && row0 + i < rows; ++i) {
+        const size_t base = (size_t)(row0 + i) * D;
+        float o[PER], rr[PER], uu[PER];
+        float ss = 0.f, dot = 0.f;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const size_t idx = base + lane + 64 * p;
+            o[p] = od[idx];
+            rr[p] = (float)((const T*)G.r)[idx];
+            uu[p] = (float)((const T*)G.du)[idx];
+        }
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            ss += o[p] * o[p];
+            dot += uu[p] * silu(rr[p]) * wv[p] * o[p];
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            ss += __shfl_xor(ss, m);
+            dot += __shfl_xor(dot, m);
+        }
+        const float rho = rsq_fast(ss * (1.0f / D) + G.eps);
+        const float k3 = rho * rho * rho * (1.0f / D) * dot;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const size_t idx = base + lane + 64 * p;
+            const float r = rr[p], du = uu[p];
+            const float sig = rcp_fast(1.0f + exp2_fast(-r * kLog2e));
+            const float sr = r * sig;
+            od[idx] = rho * du * sr * wv[p] - k3 * o[p];
+            store1<T>((T*)G.dr, idx, du * wv[p] * o[p] * rho * sig * (1.0f + r * (1.0f - sig)));
+            dwl[p] += du * sr * o[p] * rho;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) sRed[wave][lane + 64 * p] = dwl[p];
+    __syncthreads();
+    for (int col = threadIdx.x; col < D; col += NER) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < NER / 64; ++w) x += sRed[w][col];
+        G.dwp[(size_t)blockIdx.x * D + col] = x;
+    }
+}
+
 // dw[c] = sum_b dwp[b][c] in a fixed order: part p of NDW / D parts adds the
 // blocks b = p (mod parts) in increasing order, eight loads in flight, then
 // the parts are added in order.
@@ -1265,7 +1361,7 @@ static int run_bwd_gated(const Params& P, const BwdParams& Q, const GatedBwd& G,
                            dim3(NTS), 0, st, P, Q);
         hipLaunchKernelGGL((gla_bwd_fold_kernel<D, true, false>), dim3(units * blks), dim3(NTS), 0, st, P, Q);
     }
-    hipLaunchKernelGGL((gla_bwd_oepi_kernel<T, D>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q, G);
+    hipLaunchKernelGGL((gla_bwd_oepi_kernel<T, D, false>), dim3(units * P.nchunks), dim3(NT), 0, st, P, Q, G);
     if (G.dw)
         hipLaunchKernelGGL((gla_bwd_dw_kernel<D>), dim3(1), dim3(NDW), 0, st, G.dwp, G.dw,
                            (int)(units * P.nchunks));
@@ -1289,6 +1385,83 @@ static int run_bwd(const Params& P, const BwdParams& Q, hipStream_t st)
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
 }
 
+// d = 128 as four d = 64 quarters.  The decay acts on each key channel alone
+// and o is linear in v, so with key half a and value half cv the quarter's
+// state is the block S[a][cv] of the full state, and the quarter (a, cv) is
+// the d = 64 problem on the columns [64 a, 64 a + 64) of q, k, z and
+// [64 cv, 64 cv + 64) of v and dO, at the full problem's scale.  dq, dk and
+// dz of key half a are the sums over cv of the quarters' gradients, dv of
+// value half cv the sum over a.  In the order (0,0), (0,1), (1,0), (1,1)
+// the first quarter of each output half keeps a binary32 partial sum (dz its
+// own buffer) and the second adds it and stores.
+template <typename T, typename TD>
+static Params quarter(const Params& P0, BwdParams& Q, const BwdParams& Q0, int a, int cv)
+{
+    Params P = P0;
+    P.q = (const T*)P0.q + 64 * a;
+    P.k = (const T*)P0.k + 64 * a;
+    P.z = P0.z + 64 * a;
+    P.v = (const T*)P0.v + 64 * cv;
+    Q = Q0;
+    Q.dout = (const TD*)Q0.dout + 64 * cv;
+    Q.dq = (T*)Q0.dq + 64 * a;
+    Q.dk = (T*)Q0.dk + 64 * a;
+    Q.dz = Q0.dz + 64 * a;
+    Q.dv = (T*)Q0.dv + 64 * cv;
+    Q.pv = Q0.pv + 64 * cv;
+    Q.mode_qk = cv == 0 ? 1 : 2;
+    Q.mode_v = a == 0 ? 1 : 2;
+    return P;
+}
+
+template <typename T, typename TD>
+static int run_bwd_quarters(const Params& P0, const BwdParams& Q0, hipStream_t st)
+{
+    for (int a = 0; a < 2; ++a)
+        for (int cv = 0; cv < 2; ++cv) {
+            BwdParams Q;
+            const Params P = quarter<T, TD>(P0, Q, Q0, a, cv);
+            const int rc = run_bwd<T, TD, 64>(P, Q, st);
+            if (rc != GLA_OK) return rc;
+        }
+    return GLA_OK;
+}
+
+// Gated d = 128: o (binary32) of the quarters added up in the dO area, the
+// output gate's backward row by row (dO in place of o), then the quarters'
+// gradients from dO.
+template <typename T>
+static int run_bwd_gated_quarters(const Params& P0, const BwdParams& Q0, const GatedBwd& G0,
+                                  hipStream_t st)
+{
+    const unsigned units = (unsigned)(P0.B * P0.NH);
+    constexpr unsigned blks = 64 * 64 / NTS;
+    float* od = (float*)Q0.dout;
+    for (int a = 0; a < 2; ++a)
+        for (int cv = 0; cv < 2; ++cv) {
+            BwdParams Q;
+            const Params P = quarter<T, float>(P0, Q, Q0, a, cv);
+            if (P.nchunks > 1) {
+                hipLaunchKernelGGL((gla_bwd_states_kernel<T, float, 64, true, false>),
+                                   dim3(units * P.nchunks), dim3(NTS), 0, st, P, Q);
+                hipLaunchKernelGGL((gla_bwd_fold_kernel<64, true, false>), dim3(units * blks), dim3(NTS),
+                                   0, st, P, Q);
+            }
+            GatedBwd G = G0;
+            G.o_out = od + 64 * cv;
+            G.o_acc = a;
+            hipLaunchKernelGGL((gla_bwd_oepi_kernel<T, 64, true>), dim3(units * P.nchunks), dim3(NT), 0,
+                               st, P, Q, G);
+        }
+    const int rows = P0.B * P0.L * P0.NH;
+    const int nblk = (rows + 63) / 64;
+    hipLaunchKernelGGL((gla_bwd_epi_rows_kernel<T, 128>), dim3(nblk), dim3(NER), 0, st, od, G0, rows);
+    if (G0.dw)
+        hipLaunchKernelGGL((gla_bwd_dw_kernel<128>), dim3(1), dim3(NDW), 0, st, G0.dwp, G0.dw, nblk);
+    if (hipGetLastError() != hipSuccess) return GLA_EHIP;
+    return run_bwd_quarters<T, float>(P0, Q0, st);
+}
+
 template <typename T, typename TD>
 static int run_bwd_d(const Params& P, const BwdParams& Q, int d, hipStream_t st)
 {
@@ -1296,6 +1469,7 @@ static int run_bwd_d(const Params& P, const BwdParams& Q, int d, hipStream_t st)
     case 16: return run_bwd<T, TD, 16>(P, Q, st);
     case 32: return run_bwd<T, TD, 32>(P, Q, st);
     case 64: return run_bwd<T, TD, 64>(P, Q, st);
+    case 128: return run_bwd_quarters<T, TD>(P, Q, st);
     default: return GLA_EUNSUPPORTED;
     }
 }
@@ -1320,6 +1494,7 @@ int launch_bwd_gated(const Params& P, const BwdParams& Q, const GatedBwd& G, int
     case 16: return h ? bwd::run_bwd_gated<_Float16, 16>(P, Q, G, st) : bwd::run_bwd_gated<float, 16>(P, Q, G, st);
     case 32: return h ? bwd::run_bwd_gated<_Float16, 32>(P, Q, G, st) : bwd::run_bwd_gated<float, 32>(P, Q, G, st);
     case 64: return h ? bwd::run_bwd_gated<_Float16, 64>(P, Q, G, st) : bwd::run_bwd_gated<float, 64>(P, Q, G, st);
+    case 128: return h ? bwd::run_bwd_gated_quarters<_Float16>(P, Q, G, st) : bwd::run_bwd_gated_quarters<float>(P, Q, G, st);
     default: return GLA_EUNSUPPORTED;
     }
 }

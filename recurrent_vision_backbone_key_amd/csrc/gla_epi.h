@@ -21,6 +21,10 @@ struct GatedBwd {
     float* dwp;       // [units * nchunks][d]
     float* dw;        // [d] or null
     float eps;
+    // d = 128 (quarters): o of one quarter alone, added in binary32 to o_out
+    // (row stride BwdParams::ld) unless it is the first of its value half
+    float* o_out;
+    int o_acc;
 };
 
 // Gated backward: entering states, o and the output gate's backward (dO into

@@ -94,6 +94,15 @@ struct BwdParams {
     float* ws_f;        // chunk local states, then the entering states [units][nchunks-1][D*D + D]
     float* ws_r;        // reverse aggregates, then the entering gradients [units][nchunks-1][D*D + D]
     float* ws_s;        // later chunks' part of dz per chunk [units][nchunks][D]
+    int ld;             // row stride (elements) of q, k, v, z, dout and the gradients
+    // A d = 128 call runs as four d = 64 quarters (key half x value half) whose
+    // gradients add up in binary32 (mode 0: the quarter is the whole problem)
+    float* pq;          // [rows][ldp] dq of one key half
+    float* pk;          // [rows][ldp] dk of one key half
+    float* pv;          // dv partials, row stride ld (at the value half's columns)
+    int ldp;            // row stride of pq and pk
+    int mode_qk;        // dq, dk, dz: 0 store, 1 keep as partial, 2 add the partial and store
+    int mode_v;         // dv: the same
 };
 
 // Chunkwise backward, 64-position chunks (P describes the forward call).

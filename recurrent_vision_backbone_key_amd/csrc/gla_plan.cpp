@@ -323,13 +323,14 @@ extern "C" int gla_validate_sswiglu(const void* gate, const void* value, int64_t
 }
 
 extern "C" int gla_plan_bwd(int dir, int H, int W, const gla_opts* o, int* nchunks, size_t* off_f,
-                            size_t* off_r, size_t* off_s, size_t* bytes)
+                            size_t* off_r, size_t* off_s, size_t* off_p, size_t* bytes)
 {
     if (!o) return GLA_EINVAL;
     if (o->batch < 1 || o->heads < 1 || H < 1 || W < 1) return GLA_EINVAL;
     if (dir < GLA_L2R || dir > GLA_B2T) return GLA_EINVAL;
     if (o->dtype != GLA_F16 && o->dtype != GLA_F32) return GLA_EUNSUPPORTED;
-    if (o->dk != o->dv || (o->dk != 16 && o->dk != 32 && o->dk != 64)) return GLA_EUNSUPPORTED;
+    if (o->dk != o->dv || (o->dk != 16 && o->dk != 32 && o->dk != 64 && o->dk != 128))
+        return GLA_EUNSUPPORTED;
     const int64_t L = (int64_t)H * W;
     if (L >= (int64_t)1 << 24) return GLA_EUNSUPPORTED;
     const int64_t rows = (int64_t)o->batch * L * o->heads;
@@ -337,24 +338,31 @@ extern "C" int gla_plan_bwd(int dir, int H, int W, const gla_opts* o, int* nchun
     if (isnan(o->tau) || isnan(o->scale) || isinf(o->tau) || isinf(o->scale)) return GLA_EINVAL;
     const int64_t nc = (L + 63) / 64;
     const int64_t units = (int64_t)o->batch * o->heads;
-    const size_t slot = ((size_t)o->dk * o->dk + o->dk) * 4;
+    const int dq = o->dk == 128 ? 64 : o->dk;  // d = 128 runs as four d = 64 quarters
+    const size_t slot = ((size_t)dq * dq + dq) * 4;
     const size_t part = (size_t)units * (nc - 1) * slot;
     *nchunks = (int)nc;
     *off_f = kReserved;
     *off_r = *off_f + align256(part);
     *off_s = *off_r + align256(part);
-    *bytes = *off_s + (size_t)units * nc * o->dk * 4;
+    *bytes = *off_s + (size_t)units * nc * dq * 4;
+    *off_p = 0;
+    if (o->dk == 128) {
+        *off_p = align256(*bytes);
+        *bytes = *off_p + (size_t)rows * 256 * 4;
+    }
     return GLA_OK;
 }
 
 extern "C" int gla_validate_bwd(const void* q, const void* k, const void* v, const float* z,
                                 const void* dout, int dir, int H, int W, const void* dq,
                                 const void* dk, const void* dv, const float* dz, const gla_opts* o,
-                                int* nchunks, size_t* off_f, size_t* off_r, size_t* off_s)
+                                int* nchunks, size_t* off_f, size_t* off_r, size_t* off_s,
+                                size_t* off_p)
 {
     if (!o || !q || !k || !v || !z || !dout || !dq || !dk || !dv || !dz) return GLA_EINVAL;
     size_t bytes = 0;
-    const int st = gla_plan_bwd(dir, H, W, o, nchunks, off_f, off_r, off_s, &bytes);
+    const int st = gla_plan_bwd(dir, H, W, o, nchunks, off_f, off_r, off_s, off_p, &bytes);
     if (st != GLA_OK) return st;
     const size_t es = o->dtype == GLA_F16 ? 2 : 4;
     const size_t n = (size_t)o->batch * H * W * o->heads * o->dk;
@@ -381,8 +389,8 @@ extern "C" int gla_validate_bwd(const void* q, const void* k, const void* v, con
 extern "C" int gla_plan_bwd_gated(int dir, int H, int W, const gla_opts* o, gla_bwd_gated_layout* lay)
 {
     int nchunks = 0;
-    size_t off_f = 0, off_r = 0, off_s = 0, bwd_bytes = 0;
-    const int st = gla_plan_bwd(dir, H, W, o, &nchunks, &off_f, &off_r, &off_s, &bwd_bytes);
+    size_t off_f = 0, off_r = 0, off_s = 0, off_p = 0, bwd_bytes = 0;
+    const int st = gla_plan_bwd(dir, H, W, o, &nchunks, &off_f, &off_r, &off_s, &off_p, &bwd_bytes);
     if (st != GLA_OK) return st;
     if (isnan(o->eps) || isinf(o->eps) || o->eps < 0.0f) return GLA_EINVAL;
     const size_t rows = (size_t)o->batch * H * W * o->heads;
@@ -391,6 +399,7 @@ extern "C" int gla_plan_bwd_gated(int dir, int H, int W, const gla_opts* o, gla_
     lay->off_f = off_f;
     lay->off_r = off_r;
     lay->off_s = off_s;
+    lay->off_p = off_p;
     lay->bwd_bytes = bwd_bytes;
     lay->off_do = align256(bwd_bytes);
     lay->off_dwp = align256(lay->off_do + rows * o->dk * 4);

@@ -86,21 +86,23 @@ int gla_validate_sswiglu(const void* gate, const void* value, int64_t ld_in, con
 // Backward: sizes checks, workspace layout (bytes): forward states at
 // *off_f (after the fixed forward prefix, which a backward never writes, so a
 // workspace shared with gla_fwd keeps its counters, flags and mark), reverse
-// states at *off_r, chunk sums at *off_s, total *bytes.
+// states at *off_r, chunk sums at *off_s, for d = 128 the binary32 partial
+// sums of its d = 64 quarters at *off_p (rows x 256 floats; else 0), total
+// *bytes.  The state slots are those of the (quarter's) head size.
 int gla_plan_bwd(int dir, int H, int W, const gla_opts* opts, int* nchunks, size_t* off_f,
-                 size_t* off_r, size_t* off_s, size_t* bytes);
+                 size_t* off_r, size_t* off_s, size_t* off_p, size_t* bytes);
 
 // Host check of every argument of gla_bwd.
 int gla_validate_bwd(const void* q, const void* k, const void* v, const float* z, const void* dout,
                      int dir, int H, int W, const void* dq, const void* dk, const void* dv,
                      const float* dz, const gla_opts* opts, int* nchunks, size_t* off_f,
-                     size_t* off_r, size_t* off_s);
+                     size_t* off_r, size_t* off_s, size_t* off_p);
 
 // Gated backward: workspace layout (bytes) -- the backward's own part at 0
 // (gla_plan_bwd), then dO (binary32, rows x d) and the dw partial sums
 // (units x nchunks x d binary32); total in bytes.
 typedef struct gla_bwd_gated_layout {
-    size_t bwd_bytes, off_f, off_r, off_s, off_do, off_dwp, bytes;
+    size_t bwd_bytes, off_f, off_r, off_s, off_p, off_do, off_dwp, bytes;
     int nchunks;
 } gla_bwd_gated_layout;
 

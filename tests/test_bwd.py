@@ -22,13 +22,21 @@ A = 1 << 32
 MB = 1 << 26
 
 
+def _al(x):
+    return ((x + 255) // 256) * 256
+
+
 def _ws_bytes(B, NH, L, d):
     """The forward's fixed prefix (4096-byte header, 32768 flag words, never
-    written by a backward), then two slot arrays and the chunk sums."""
+    written by a backward), then two slot arrays and the chunk sums; d = 128
+    runs as four d = 64 quarters (slots of d = 64) and adds their binary32
+    partial sums (dq and dk of a key half, dv of both value halves: 256
+    floats per row)."""
     nc = (L + 63) // 64
-    part = B * NH * (nc - 1) * (d * d + d) * 4
-    al = ((part + 255) // 256) * 256
-    return 4096 + 32768 * 4 + 2 * al + B * NH * nc * d * 4
+    dq = 64 if d == 128 else d
+    part = B * NH * (nc - 1) * (dq * dq + dq) * 4
+    end = 4096 + 32768 * 4 + 2 * _al(part) + B * NH * nc * dq * 4
+    return _al(end) + B * L * NH * 256 * 4 if d == 128 else end
 
 
 def _call(q=A, k=A + MB, v=A + 2 * MB, z=A + 3 * MB, dout=A + 4 * MB, direction=0, H=20, W=20,
@@ -40,13 +48,15 @@ def _call(q=A, k=A + MB, v=A + 2 * MB, z=A + 3 * MB, dout=A + 4 * MB, direction=
 
 def test_bwd_workspace_sizes():
     for B, NH, H, W, d in ((1, 1, 8, 8, 16), (2, 3, 10, 13, 32), (8, 6, 40, 40, 64),
-                           (1, 1, 1, 1, 64), (1, 2, 3, 50, 64)):
+                           (1, 1, 1, 1, 64), (1, 2, 3, 50, 64), (1, 2, 10, 13, 128),
+                           (2, 12, 128, 128, 128)):
         o = gla.make_opts(B, NH, d, d, gla.F16)
         for direction in range(4):
             assert gla.bwd_workspace_size(direction, H, W, o) == _ws_bytes(B, NH, H * W, d)
     # rejected arguments give 0
     assert gla.bwd_workspace_size(0, 20, 20, gla.make_opts(1, 2, 64, 32, gla.F16)) == 0
-    assert gla.bwd_workspace_size(0, 20, 20, gla.make_opts(1, 2, 128, 128, gla.F16)) == 0
+    assert gla.bwd_workspace_size(0, 20, 20, gla.make_opts(1, 2, 96, 96, gla.F16)) == 0
+    assert gla.bwd_workspace_size(0, 20, 20, gla.make_opts(1, 2, 128, 64, gla.F16)) == 0
     assert gla.bwd_workspace_size(4, 20, 20, gla.make_opts(1, 2, 64, 64, gla.F16)) == 0
     assert gla.bwd_workspace_size(0, 0, 20, gla.make_opts(1, 2, 64, 64, gla.F16)) == 0
 
@@ -72,8 +82,10 @@ def test_bwd_argument_checks():
     assert _call(opts=o) == 1
     # dk != dv, unsupported head size, storage type
     assert _call(opts=gla.make_opts(1, 2, 64, 32, gla.F16)) == 2
-    assert _call(opts=gla.make_opts(1, 2, 128, 128, gla.F16)) == 2
+    assert _call(opts=gla.make_opts(1, 2, 96, 96, gla.F16)) == 2
     assert _call(opts=gla.make_opts(1, 2, 48, 48, gla.F16)) == 2
+    # d = 128 is supported: without a workspace the call stops there
+    assert _call(opts=gla.make_opts(1, 2, 128, 128, gla.F16)) == 3
     assert _call(opts=gla.make_opts(1, 2, 64, 64, 7)) == 2
     # alignment
     assert _call(q=A + 8, opts=_ok_opts()) == 1
@@ -169,6 +181,8 @@ TOL = {"f32": 2e-5, "f16": 2e-3}
     (1, 2, 10, 13, 32),    # 3 chunks, ragged tail of 2
     (2, 3, 20, 20, 64),    # 7 chunks, tail of 16
     (1, 2, 3, 50, 64),     # non-square grid, column-major orders differ
+    (1, 1, 8, 8, 128),     # d = 128 (four d = 64 quarters): one chunk
+    (1, 2, 10, 13, 128),   # d = 128, 3 chunks, ragged tail
 ])
 @pytest.mark.parametrize("direction", (0, 1, 2, 3))
 def test_bwd_small(torch, dtype, B, NH, H, W, d, direction):
@@ -196,8 +210,27 @@ def test_bwd640(torch, call):
 
 
 @pytest.mark.gpu
-def test_bwd_deterministic(torch):
-    x = make_bwd_inputs(2, 3, 20, 20, 64, "f16", seed=5)
+@pytest.mark.parametrize("dtype,z", [("f32", (-12.0, 12.0)), ("f16", (-60.0, 5.0))])
+def test_bwd_strong_decay_d128(torch, dtype, z):
+    x = make_bwd_inputs(1, 2, 16, 20, 128, dtype, z=z, seed=12)
+    for direction in (1, 2):
+        _check(f"strong d=128 z={z}", x, direction, 16, 20, TOL[dtype], torch)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("direction", (0, 1, 2, 3))
+def test_bwd_stack16k_shape(torch, direction):
+    """The 12-block stack's shape: B = 2, 12 heads, 128 x 128 grid (L = 16384),
+    d = 128, binary16, long retention (z ~ N(2, 1)); every (batch, head) scan
+    against the oracle, element by element."""
+    x = make_bwd_inputs(2, 12, 128, 128, 128, "f16", z=(2.0, 1.0), seed=5000 + direction)
+    _check("stack16k shape", x, direction, 128, 128, TOL["f16"], torch)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d", (64, 128))
+def test_bwd_deterministic(torch, d):
+    x = make_bwd_inputs(2, 3, 20, 20, d, "f16", seed=5)
     a = _run_bwd(x, 2, 20, 20, torch)
     b = _run_bwd(x, 2, 20, 20, torch)
     for n, u, w in zip(NAMES, a, b):

@@ -42,7 +42,11 @@ def test_bwd_gated_workspace_sizes():
         need = gla.bwd_gated_workspace_size(0, H, W, o)
         # the backward's own part, then o and do in the storage type
         assert need >= gla.bwd_workspace_size(0, H, W, o) + 2 * B * H * W * NH * d * 2
-    assert gla.bwd_gated_workspace_size(0, 20, 20, gla.make_opts(1, 2, 128, 128, gla.F16)) == 0
+    # d = 128: the backward's part (with the quarters' partial sums), then o / do in binary32
+    o = gla.make_opts(2, 3, 128, 128, gla.F16)
+    assert gla.bwd_gated_workspace_size(0, 10, 13, o) >= \
+        gla.bwd_workspace_size(0, 10, 13, o) + 2 * 130 * 3 * 128 * 4
+    assert gla.bwd_gated_workspace_size(0, 20, 20, gla.make_opts(1, 2, 96, 96, gla.F16)) == 0
     assert gla.bwd_gated_workspace_size(0, 20, 20, gla.make_opts(1, 2, 64, 32, gla.F16)) == 0
     assert gla.bwd_gated_workspace_size(0, 20, 20, gla.make_opts(1, 2, 64, 64, gla.F16, eps=-1.0)) == 0
 
@@ -55,7 +59,8 @@ def test_bwd_gated_argument_checks():
     for name in ("q", "k", "v", "z", "r", "dout", "dq", "dk", "dv", "dz", "dr"):
         assert _call(**{name: None}, opts=_ok_opts()) == 1, name
     assert _call(direction=4, opts=_ok_opts()) == 1
-    assert _call(opts=gla.make_opts(1, 2, 128, 128, gla.F16)) == 2
+    assert _call(opts=gla.make_opts(1, 2, 96, 96, gla.F16)) == 2
+    assert _call(opts=gla.make_opts(1, 2, 128, 128, gla.F16)) == 3  # supported; no workspace
     assert _call(r=A + 4 * MB + 8, opts=_ok_opts()) == 1        # r misaligned
     assert _call(dr=A + 5 * MB + 64, opts=_ok_opts()) == 1      # dr over dout
     assert _call(dw=A + 10 * MB + 1024, opts=_ok_opts()) == 1   # dw over dr
@@ -138,6 +143,7 @@ def _check(name, x, direction, H, W, tol, torch, with_w=True):
     (1, 1, 8, 8, 16),
     (1, 2, 10, 13, 32),
     (2, 3, 20, 20, 64),
+    (1, 2, 10, 13, 128),   # d = 128: o of four d = 64 quarters, the gate row by row
 ])
 @pytest.mark.parametrize("direction", (0, 1, 2, 3))
 def test_bwd_gated_small(torch, dtype, B, NH, H, W, d, direction):
@@ -161,8 +167,20 @@ def test_bwd640_gated(torch, call):
 
 
 @pytest.mark.gpu
-def test_bwd_gated_deterministic(torch):
-    x = make_bwd_inputs(2, 3, 20, 20, 64, "f16", seed=5, gated=True)
+@pytest.mark.parametrize("direction", (0, 1, 2, 3))
+def test_bwd_gated_stack16k_shape(torch, direction):
+    """The 12-block stack's shape with the output gate: B = 2, 12 heads,
+    128 x 128 grid, d = 128, binary16, z ~ N(2, 1); every scan element by
+    element against the oracle."""
+    x = make_bwd_inputs(2, 12, 128, 128, 128, "f16", z=(2.0, 1.0), seed=6000 + direction,
+                        gated=True)
+    _check("stack16k shape", x, direction, 128, 128, TOL["f16"], torch)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d", (64, 128))
+def test_bwd_gated_deterministic(torch, d):
+    x = make_bwd_inputs(2, 3, 20, 20, d, "f16", seed=5, gated=True)
     a = _run(x, 1, 20, 20, True, torch)
     b = _run(x, 1, 20, 20, True, torch)
     for n, u, w in zip(NAMES, a, b):
