@@ -374,7 +374,7 @@ def bench_bwd(args, spec, name):
     gbs = bytes_call / (us_call * 1e-6) / 1e9
     result = {
         "metric": ("chunkwise GLA bwd (output gate included)" if gated else "chunkwise GLA bwd") +
-                  ": µs/call + Gtok·head/s at L=1600; % of MFMA (fp32) roofline",
+                  f": µs/call + Gtok·head/s at L={H * W}; % of MFMA (fp32) roofline",
         "value": round(len(dirs) * th_call / (ms_step * 1e-3) / 1e9, 4), "unit": "Gtok·head/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
         "us_per_call": round(us_call, 3),

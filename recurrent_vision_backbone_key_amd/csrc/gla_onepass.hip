@@ -34,10 +34,11 @@
 //     E_s     = k_s (.) 2^{tot_j - bl_s}           (<= |k|, key relative to its sub-chunk end)
 //     A(t, s) = (Qbase_t (.) 2^{R_i - R_j - tot_j}) . E_s   for s in sub-chunk j <= i
 // The factor is 1 for adjacent sub-chunks and <= 1 for earlier ones; on the
-// diagonal it is 2^{-tot_i} >= 1, so that block uses split binary16
-// operands and falls back to an exact pairwise fp32 evaluation when the
-// sub-chunk's decay span exceeds 2^8.  The two wavefronts of a sub-chunk each
-// contract their own 32 channels and exchange the partial score tiles.
+// diagonal it is 2^{-tot_i} >= 1, so that block runs on the binary32 matrix
+// cores from binary32 operands and falls back to an exact pairwise fp32
+// evaluation when the sub-chunk's decay span exceeds 2^60.  The two wavefronts
+// of a sub-chunk each contract their own 32 channels and exchange the partial
+// score tiles.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -74,6 +74,11 @@ BWD = {
     "bwd640_gated": dict(index=24, kind="bwd", B=8, NH=6, H=40, W=40, dk=64, dv=64,
                          dtype="f16", z=(0.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T),
                          gated=True),
+    # the 12-block stack's shape through the output gate (d = 128: four d = 64
+    # quarters per call)
+    "bwd16k_gated": dict(index=25, kind="bwd", B=2, NH=12, H=128, W=128, dk=128, dv=128,
+                         dtype="f16", z=(2.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T),
+                         gated=True),
 }
 WORKLOADS.update(BWD)
 
