@@ -554,6 +554,65 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     const int sb0 = 2 * (wave & 1);   // first state tile column block (value channels)
     float dseg = 0.f;                 // decay since segment start, channel 32*h + cht
 
+    // One-chunk segments in one-round plans of at least 8 segments per scan:
+    // the segments whose aggregate another segment reads (all but the last
+    // and the group leaders, which publish a combined transfer instead)
+    // publish it as soon as their local state is complete, right after the
+    // chunk's state update and before its intra-chunk products, which then
+    // overlap the other segments' exchange (1600-token frame, 25 segments:
+    // 14.9 -> 14.2 us per call).  Everywhere else the aggregate goes out after
+    // the loop: with 5 segments the exchange is short and the wait for the
+    // stores' acknowledgement in front of the products cost more than it hid,
+    // in plans of several rounds later segments start from a recent inclusive
+    // state, and compiled into the five-chunk instance the early path alone
+    // (11 more VGPRs) slowed its other plans by 2-3 %.
+    const bool last = (seg == P.nseg - 1);
+    const bool one_round = P.one_round != 0;
+    int G = P.nseg;  // one round: group size of the two-level exchange
+    if (P.nseg >= 24) {
+        G = 1;
+        while (G * G < P.nseg) ++G;
+    }
+    const int grp = seg / G, gfirst = grp * G;
+    const bool leader = !last && seg == gfirst + G - 1;
+    const bool early = NCHK == 1 && one_round && P.nseg >= 8 && !last && !leader;
+    const size_t aggf = (size_t)D * D + D;
+    const size_t slot = (size_t)unit * P.nseg + seg;
+    const unsigned agg_bytes = (unsigned)(aggf * 4), st_bytes = (unsigned)(D * D * 4);
+    unsigned* flags = P.flags + (size_t)unit * P.nseg;
+    // M4: local state update S = Diag(2^{chunk total}) S + k-hat^T v
+    auto state_update = [&]() {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int bb = sb0 + jj;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[jj][e] *= sDec[16 * sa + 4 * g + e];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const half8 kf = tr_frag_s<SH>(sKT, 32 * kb + 8 * g, 16 * sa, l16);
+                const half8 vf = tr_frag_s<SH>(sVT, 32 * kb + 8 * g, 16 * bb, l16);
+                S[jj] = mma(kf, vf, S[jj]);
+            }
+        }
+    };
+    // the segment aggregate (local state [ch][dv] straight from the state
+    // tiles, and the multiplier 2^{segment decay}), then its flag once every
+    // wave's stores are acknowledged
+    auto publish_aggregate = [&]() {
+        const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st_x1(r, 4u * (unsigned)((16 * sa + 4 * g + e) * D + 16 * (sb0 + jj) + l16), S[jj][e]);
+        if (si == 0 && ht == 0) st_x1(r, st_bytes + 4u * (unsigned)(32 * h + cht), exp2_fast(dseg));
+        wait_mem();
+        __syncthreads();
+        // one round, first segment: it reads nothing, so it is done as well
+        const unsigned v = (one_round && seg == 0) ? 5u : 1u;
+        if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, v | (poisoned ? kPoison : 0u));
+    };
+
 #pragma unroll
     for (int c = 0; c < NCHK; ++c) {
         if (c >= nch) break;
@@ -688,6 +747,11 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         }
         __syncthreads();  // (2) operands of every wave
 
+        const bool pub_now = early && (c == nch - 1);
+        if (pub_now) {
+            state_update();
+            publish_aggregate();
+        }
         float4v o[2];
         switch (si) {
         case 0: scores_values<0>(sE, sVT, sPA, wave, lane, g, l16, h, c0, wide_w, ef, qd, qa, qo1, qo2, o); break;
@@ -710,19 +774,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         okeep[c][0] = o[0];
         okeep[c][1] = o[1];
 
-        // ---- M4: local state update S = Diag(2^{chunk total}) S + k-hat^T v
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int bb = sb0 + jj;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S[jj][e] *= sDec[16 * sa + 4 * g + e];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const half8 kf = tr_frag_s<SH>(sKT, 32 * kb + 8 * g, 16 * sa, l16);
-                const half8 vf = tr_frag_s<SH>(sVT, 32 * kb + 8 * g, 16 * bb, l16);
-                S[jj] = mma(kf, vf, S[jj]);
-            }
-        }
+        if (!pub_now) state_update();
         __syncthreads();  // (4) all readers of this chunk's buffers are done
         if (LY::kMulti && c + 1 < nch) {
             // the local state's binary16 copy for the next chunk's inter-chunk term
@@ -755,8 +807,6 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     }
 
     // ================= phase 2: segment exchange =================
-    const size_t aggf = (size_t)D * D + D;
-    const size_t slot = (size_t)unit * P.nseg + seg;
     float* sL = (float*)(lds + LY::LSEG);
     float* sG = (float*)(lds + LY::GSEG);
     const bool need_in = (seg > 0);
@@ -771,20 +821,16 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         // total decay of the segment as the factor 2^G (the fold's multiplier)
         if (si == 0 && ht == 0) sG[32 * h + cht] = exp2_fast(dseg);
         __syncthreads();
-        const bool last = (seg == P.nseg - 1);
-        unsigned* flags = P.flags + (size_t)unit * P.nseg;
         // this thread's 8 state entries: rows ch0 = tid / 16 and ch0 + 32,
         // columns 4 (tid % 16) .. +3 (16 contiguous bytes in each row)
         const int ch0 = tid >> 4, cl0 = 4 * (tid & 15);
         const unsigned off0 = 16u * tid, off1 = off0 + 16u * NT;  // bytes
         const float4v l0 = *(const float4v*)(sL + ch0 * D + cl0);
         const float4v l1 = *(const float4v*)(sL + (ch0 + 32) * D + cl0);
-        const unsigned agg_bytes = (unsigned)(aggf * 4), st_bytes = (unsigned)(D * D * 4);
         // Plans whose workgroups all run in one round (every segment starts
         // at the same time) fold published aggregates directly; plans of
         // several rounds use inclusive states, which the segments of earlier
         // rounds have published by the time later ones look back.
-        const bool one_round = P.one_round != 0;
         if (one_round) {
             // Exchange.  Every segment but the last publishes its aggregate and
             // segment j folds the aggregates of segments 0 .. j-1 from zero, in
@@ -800,13 +846,6 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             // 16.7 -> 14.9 us per call, 5 segments 34.1 -> 35.7 us).  The fixed
             // order makes the result independent of timing.  Flag bits: 1
             // aggregate, 2 combined transfer, 4 done reading.
-            int G = P.nseg;
-            if (P.nseg >= 24) {
-                G = 1;
-                while (G * G < P.nseg) ++G;
-            }
-            const int grp = seg / G, gfirst = grp * G;
-            const bool leader = !last && seg == gfirst + G - 1;
             auto leader_slot = [&](int gg) { return (size_t)unit * P.nseg + (size_t)(gg * G + G - 1); };
             // wave 0 waits until groups 0 .. ng-1 have their combined transfers and
             // segments first .. first+cnt-1 their aggregates (ng + cnt <= 64)
@@ -880,7 +919,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 __syncthreads();
                 if (tid == 0) st_flag<LOCAL>(flags, P.nseg, seg, v | (poisoned ? kPoison : 0u));
             };
-            if (!last && !leader) {
+            if (!last && !leader && !early) {
                 // aggregate: local state and multiplier 2^G
                 const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + slot * aggf, agg_bytes);
                 st_x4(r, off0, l0);
