@@ -67,13 +67,14 @@ KERNEL_SOURCES = {
     "sswiglu": ("gla_sswiglu.hip",) + _COMMON_SOURCES,
     "bwd": ("gla_bwd.hip", "gla_epi.h") + _COMMON_SOURCES,
     "bwd_gated": ("gla_bwd.hip", "gla_epi.h") + _COMMON_SOURCES,
+    "proj_bwd": ("gla_proj_bwd.hip", "gla_proj.hip") + _COMMON_SOURCES,
 }
 
 
 def kernel_family(spec):
     if spec.get("kind") == "bwd" and spec.get("gated"):
         return "bwd_gated"
-    if spec.get("kind") in ("sswiglu", "bwd"):
+    if spec.get("kind") in ("sswiglu", "bwd", "proj_bwd"):
         return spec["kind"]
     if spec["dtype"] == "f16" and spec["dk"] == 64 and spec["chunk"] == 64:
         return "onepass_proj" if spec.get("gate_proj") else "onepass"
@@ -407,6 +408,90 @@ def bench_bwd(args, spec, name):
     print(json.dumps(result), flush=True)
 
 
+def bench_proj_bwd(args, spec, name):
+    """One step = one gla_gate_proj_bwd call over every token of the batch;
+    same timing method as the forward."""
+    import torch
+
+    from recurrent_vision_backbone_key_amd import gla
+
+    B, L, NH, dk = spec["B"], spec["H"] * spec["W"], spec["NH"], spec["dk"]
+    dm, rank = spec["d_model"], spec["rank"]
+    es = 2 if spec["dtype"] == "f16" else 4
+    dt = torch.float16 if es == 2 else torch.float32
+    T, nout = B * L, NH * dk
+    # dz read, x read, dx written; the weights read and their gradients written
+    bytes_call = 4 * T * nout + 2 * es * T * dm + es * rank * dm + 4 * nout * rank + \
+        4 * (rank * dm + nout * rank + nout)
+    # hp = x W1, dhp = dz W2^T, dx, dW1, dW2 (2 flops per multiply-add), db
+    flops_call = 2 * T * rank * (3 * dm + 2 * nout) + T * nout
+    rotate = args.rotate or max(1, math.ceil(2 * MALL_BYTES / bytes_call))
+    steps = args.steps if args.steps is not None else 200
+    warmup = args.warmup if args.warmup is not None else 50
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    sets = []
+    for r in range(rotate):
+        gen.manual_seed(1000 * spec["index"] + r)
+        x = torch.randn((B, L, dm), generator=gen, device=dev).to(dt)
+        w1 = (torch.randn((rank, dm), generator=gen, device=dev) / math.sqrt(dm)).to(dt)
+        w2 = torch.randn((nout, rank), generator=gen, device=dev) / math.sqrt(rank)
+        dz = torch.randn((B, L, NH, dk), generator=gen, device=dev)
+        grads = (torch.empty_like(x), torch.empty((rank, dm), dtype=torch.float32, device=dev),
+                 torch.empty((nout, rank), dtype=torch.float32, device=dev),
+                 torch.empty((nout,), dtype=torch.float32, device=dev))
+        need = gla.gate_proj_bwd_workspace_size(gla.make_gate(x, w1, w2, None), T, nout)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        sets.append((x, w1, w2, dz, grads, ws))
+
+    def step(r):
+        x, w1, w2, dz, grads, ws = sets[r]
+        gla.gate_proj_bwd(x, w1, w2, dz, grads=grads, workspace=ws)
+
+    ms_step, G, graphed, per_replay = time_steps(step, rotate, steps, warmup, args, 10)
+    achieved = bytes_call / (ms_step * 1e-3) / 1e9
+    tflops = flops_call / (ms_step * 1e-3) / 1e12
+    result = {
+        "metric": f"gate projection backward: µs/call at {T} tokens; % of HBM roofline",
+        "value": round(T / (ms_step * 1e-3) / 1e9, 4), "unit": "Gtok/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
+        "us_per_call": round(1e3 * ms_step, 3),
+        "latency_us_per_call": latency_stats(per_replay, G, 1),
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
+        "config": {"workload": name, "tokens": T, "d_model": dm, "rank": rank, "nout": nout,
+                   "input_sets": rotate, "hip_graph": graphed, "steps_per_graph": G,
+                   "accumulate": "f32", "mfma_operands": "f32"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gla_gate_rank_kernel + 5 gla_pbwd_gemm_kernel + 3 "
+                               "gla_pbwd_reduce_kernel (figures for the whole call)",
+                     "algorithmic_bytes_per_call": bytes_call,
+                     "algorithmic_flops_per_call": flops_call,
+                     "mfma_f32_frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        import numpy as np
+
+        import oracle
+        from recurrent_vision_backbone_key_amd.inputs import make_gate_proj_inputs
+        x = make_gate_proj_inputs(1, L, NH, dk, dm, rank, spec["dtype"], seed=1)
+        dz = np.random.default_rng(2).standard_normal((1, L, nout)).astype(np.float32)
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.gate_proj_bwd(x["x"], x["w1"], x["w2"], dz)
+            n += 1
+        dt_s = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(n * L / dt_s / 1e9, 6), "unit": "Gtok/s", "cores": os.cpu_count(),
+            "cpu_model": host_cpu_model(), "kind": "oracle",
+            "sample": f"{n} oracle calls on one image ({L} tokens) in {dt_s:.1f} s (numpy)"}
+    print(json.dumps(result), flush=True)
+
+
 def bench_sswiglu(args, spec, name):
     """One step = one gla_spatial_swiglu call over the whole batch; same
     timing method as the forward (resident inputs rotating past the last-level
@@ -542,6 +627,9 @@ def main():
         return
     if spec.get("kind") == "bwd":
         bench_bwd(args, spec, name)
+        return
+    if spec.get("kind") == "proj_bwd":
+        bench_proj_bwd(args, spec, name)
         return
     chunk = args.chunk or spec["chunk"]
     dirs = spec["dirs"]

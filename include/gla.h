@@ -230,6 +230,36 @@ GLA_API int gla_gate_logits(const gla_gate_proj *gate, int batch, int tokens, in
                             int dtype, float *z, void *stream);
 
 /*
+ * gla_gate_proj_bwd -- gradients of the projection above (chain rule of
+ * z = x W1 W2 + b) for dz = dL/dz, written on the stored arrays (w1 [rank,
+ * d_model], w2 [nout, rank]) with hp[t][j] = sum_m x[t][m] w1[j][m] (the rank
+ * values of token t) and dhp[t][j] = sum_n dz[t][n] w2[n][j]:
+ *     dx[t][m]  = sum_j dhp[t][j] w1[j][m]   [tokens, d_model]  storage dtype
+ *     dw1[j][m] = sum_t dhp[t][j] x[t][m]    [rank, d_model]    binary32
+ *     dw2[n][j] = sum_t dz[t][n] hp[t][j]    [nout, rank]       binary32
+ *     db[n]     = sum_t dz[t][n]             [nout]             binary32
+ * tokens = batch * sequence length and nout = heads * dk; dz [tokens, nout]
+ * binary32 is the layout gla_bwd writes dz in ([B, L, NH, dk]).  x, w1 and
+ * w2 are read from `gate` (bias unused); dtype: GLA_F16 or GLA_F32, the
+ * storage of x, w1 and dx.  Accumulation in binary32; the sums over tokens
+ * are formed per block of 64 tokens and the blocks added in order, so equal
+ * inputs give equal bits.  The workspace (device, 16-byte aligned, no
+ * initialisation) must hold gla_gate_proj_bwd_workspace_size() bytes; the
+ * outputs must not overlap each other, an input or the workspace.
+ * Asynchronous on `stream` (hipStream_t, NULL: the null stream).
+ * GLA_EINVAL on a bad pointer, size or overlap, GLA_EUNSUPPORTED on a dtype
+ * or size outside the built set (tokens <= 2^26, nout <= 65536),
+ * GLA_EWORKSPACE on a missing or small workspace, GLA_EHIP on a launch
+ * failure.
+ */
+GLA_API int gla_gate_proj_bwd(const gla_gate_proj *gate, int tokens, int nout, int dtype,
+                              const float *dz, void *dx, float *dw1, float *dw2, float *db,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace gla_gate_proj_bwd needs (0 for arguments it would reject). */
+GLA_API size_t gla_gate_proj_bwd_workspace_size(const gla_gate_proj *gate, int tokens, int nout);
+
+/*
  * gla_fwd_gate_proj -- gla_fwd with the gate logits computed from the block
  * input by the low-rank projection above instead of read from memory.
  * Arguments as for gla_fwd, with `gate` in place of gate_logits (x and w1

@@ -4,13 +4,15 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP
 implementation in ``recurrent_vision_backbone_key_amd`` and never imports it.
 
-Six references, each written from its definition ("GTR: Gated Token
+Seven references, each written from its definition ("GTR: Gated Token
 Recurrence for Efficient Dense Prediction", paper Section 2.1):
 
 * :func:`fwd` -- the token-by-token fp64 recurrence in plain C
   (``gla_oracle.c``), OpenMP over the (batch, head) units;
 * :func:`gate_logits` -- the low-rank gate logits z = (x W1) W2 + b of
   the retention gate (same section), plain C loops in fp64;
+* :func:`gate_proj_bwd` -- the gradients of x, W1, W2, b of those logits
+  (the chain rule of a product of matrices), numpy fp64 matrix products;
 * :func:`spatial_swiglu` (with :func:`dwconv3x3`, :func:`silu`) -- the
   Spatial SwiGLU core SiLU(a) (.) (3x3 depthwise convolution of v + b)
   (same section), numpy fp64 shifted sums;
@@ -292,6 +294,35 @@ def gate_logits(x, w1, w2, bias, heads, threads=None):
     if rc != 0:
         raise RuntimeError(f"gla_oracle_gate_logits failed with status {rc}")
     return z
+
+
+def gate_proj_bwd(x, w1, w2, dz):
+    """Gradients of the gate logits z = (x W1) W2 + b (paper Section 2.1,
+    retention gate; storage as in :func:`gate_logits`: w1 [rank, d_model] is
+    W1 transposed, w2 [nout, rank] is W2 transposed) for dz = dL/dz, in fp64.
+    x: [B, L, d_model] or [tokens, d_model]; dz: [B, L, heads, dk] or
+    [tokens, nout].  With hp = x W1 (rank values per token) and
+    dhp = dz W2^T, the chain rule of the two products gives, on the stored
+    arrays: dx = dhp w1, dw1 = dhp^T x, dw2 = dz^T hp, db = sum_t dz.
+    Returns (dx shaped like x, dw1 [rank, d_model], dw2 [nout, rank],
+    db [nout]), all float64."""
+    x64 = np.asarray(x, dtype=np.float64)
+    shape = x64.shape
+    d_model = shape[-1]
+    x64 = x64.reshape(-1, d_model)
+    w1_64 = np.asarray(w1, dtype=np.float64)
+    w2_64 = np.asarray(w2, dtype=np.float64)
+    nout, rank = w2_64.shape
+    dz64 = np.asarray(dz, dtype=np.float64).reshape(x64.shape[0], nout)
+    if w1_64.shape != (rank, d_model):
+        raise ValueError("shape mismatch")
+    hp = x64 @ w1_64.T          # [tokens, rank]
+    dhp = dz64 @ w2_64          # [tokens, rank]
+    dx = dhp @ w1_64            # [tokens, d_model]
+    dw1 = dhp.T @ x64           # [rank, d_model]
+    dw2 = dz64.T @ hp           # [nout, rank]
+    db = dz64.sum(axis=0)       # [nout]
+    return dx.reshape(shape), dw1, dw2, db
 
 
 # ---------------------------------------------------------------------------

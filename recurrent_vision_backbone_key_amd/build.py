@@ -43,6 +43,7 @@ UNITS = [
     ("gla_onepass.hip", "hip", []),
     ("gla_wide.hip", "hip", []),
     ("gla_proj.hip", "hip", []),
+    ("gla_proj_bwd.hip", "hip", []),
     ("gla_sswiglu.hip", "hip", []),
     ("gla_bwd.hip", "hip", []),
     ("gla_noalloc.hip", "hip", []),

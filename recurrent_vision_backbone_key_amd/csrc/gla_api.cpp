@@ -209,6 +209,32 @@ extern "C" int gla_gate_logits(const gla_gate_proj* gate, int batch, int tokens,
     return gla::launch_gate_logits(gate_of(gate), dtype, batch * tokens, heads * dk, z, stream);
 }
 
+extern "C" int gla_gate_proj_bwd(const gla_gate_proj* gate, int tokens, int nout, int dtype,
+                                 const float* dz, void* dx, float* dw1, float* dw2, float* db,
+                                 void* workspace, size_t workspace_bytes, void* stream)
+{
+    gla_proj_bwd_layout lay;
+    const int st = gla_validate_gate_proj_bwd(gate, tokens, nout, dtype, dz, dx, dw1, dw2, db,
+                                              workspace, workspace_bytes, &lay);
+    if (st != GLA_OK) return st;
+    char* ws = (char*)workspace;
+    gla::ProjBwdWs W;
+    W.hp = (float*)(ws + lay.off_hp);
+    W.dhp = (float*)(ws + lay.off_dhp);
+    W.p1 = (float*)(ws + lay.off_p1);
+    W.p2 = (float*)(ws + lay.off_p2);
+    W.pb = (float*)(ws + lay.off_pb);
+    return gla::launch_gate_proj_bwd(gate_of(gate), dtype, tokens, nout, dz, dx, dw1, dw2, db, W,
+                                     stream);
+}
+
+extern "C" size_t gla_gate_proj_bwd_workspace_size(const gla_gate_proj* gate, int tokens, int nout)
+{
+    gla_proj_bwd_layout lay;
+    if (gla_plan_gate_proj_bwd(gate, tokens, nout, &lay) != GLA_OK) return 0;
+    return lay.bytes;
+}
+
 extern "C" size_t gla_workspace_size(int dir, int H, int W, int chunk, const gla_opts* opts)
 {
     gla_plan plan;

@@ -79,6 +79,26 @@ int launch_gate_logits(const GateProj& G, int dtype, int tokens, int nout, float
 // First factor alone: hp = x W1, [tokens, 16 ceil(rank / 16)] binary32.
 int launch_gate_rank(const GateProj& G, int dtype, int tokens, float* hp, void* stream);
 
+// Tokens per partial product of the gate projection's backward (its products
+// over the tokens are added up block by block in this order).
+constexpr int kProjBwdSplit = 64;
+
+// Workspace parts of the gate projection's backward (binary32): hp [tokens][16
+// ceil(rank/16)], dhp [tokens][rank], and the per-block partial sums of dW1
+// [nsplit][rank][d_model], dW2 [nsplit][nout][rank] and db [nsplit][nout].
+struct ProjBwdWs {
+    float* hp;
+    float* dhp;
+    float* p1;
+    float* p2;
+    float* pb;
+};
+
+// Gradients of the gate projection (include/gla.h, gla_gate_proj_bwd),
+// arguments checked.
+int launch_gate_proj_bwd(const GateProj& G, int dtype, int tokens, int nout, const float* dz, void* dx,
+                         float* dw1, float* dw2, float* db, const ProjBwdWs& W, void* stream);
+
 // Spatial SwiGLU core (include/gla.h, gla_spatial_swiglu), arguments checked.
 int launch_sswiglu(const void* a, const void* v, long long ld_in, const float* w, const float* bias,
                    void* out, long long ld_out, int B, int H, int W, int C, int dtype, void* stream);

@@ -295,6 +295,68 @@ extern "C" int gla_validate_gate_logits(const gla_gate_proj* gate, int batch, in
     return GLA_OK;
 }
 
+extern "C" int gla_plan_gate_proj_bwd(const gla_gate_proj* gate, int tokens, int nout,
+                                      gla_proj_bwd_layout* lay)
+{
+    const int st = check_gate_sizes(gate);
+    if (st != GLA_OK) return st;
+    if (!lay || tokens < 1 || nout < 1) return GLA_EINVAL;
+    if (tokens > (1 << 26) || nout > (1 << 16)) return GLA_EUNSUPPORTED;
+    const int64_t R = gate->rank, RP = 16 * ((R + 15) / 16), DM = gate->d_model;
+    const int64_t ns = ((int64_t)tokens + gla::kProjBwdSplit - 1) / gla::kProjBwdSplit;
+    // grids: one wavefront per 16 x 16 output tile (and per token block for
+    // the sums over tokens), four per workgroup, below 2^31 workgroups
+    const int64_t lim = (int64_t)1 << 33, rt = RP / 16;
+    if (((int64_t)tokens + 15) / 16 * ((DM + 15) / 16) >= lim) return GLA_EUNSUPPORTED;
+    if (rt * ((DM + 15) / 16) * ns >= lim || ((int64_t)nout + 15) / 16 * rt * ns >= lim)
+        return GLA_EUNSUPPORTED;
+    lay->nsplit = (int)ns;
+    lay->off_hp = 0;
+    lay->off_dhp = align256(lay->off_hp + (size_t)tokens * RP * 4);
+    lay->off_p1 = align256(lay->off_dhp + (size_t)tokens * R * 4);
+    lay->off_p2 = align256(lay->off_p1 + (size_t)ns * R * DM * 4);
+    lay->off_pb = align256(lay->off_p2 + (size_t)ns * nout * R * 4);
+    lay->bytes = lay->off_pb + (size_t)ns * nout * 4;
+    return GLA_OK;
+}
+
+extern "C" int gla_validate_gate_proj_bwd(const gla_gate_proj* gate, int tokens, int nout, int dtype,
+                                          const float* dz, const void* dx, const float* dw1,
+                                          const float* dw2, const float* db, const void* workspace,
+                                          size_t workspace_bytes, gla_proj_bwd_layout* lay)
+{
+    const int st = gla_plan_gate_proj_bwd(gate, tokens, nout, lay);
+    if (st != GLA_OK) return st;
+    if (!dz || !dx || !dw1 || !dw2 || !db) return GLA_EINVAL;
+    if (dtype != GLA_F16 && dtype != GLA_F32) return GLA_EUNSUPPORTED;
+    const size_t es = dtype == GLA_F16 ? 2 : 4;
+    const size_t R = gate->rank, DM = gate->d_model;
+    const Operand ins[5] = {{gate->x, (size_t)tokens * DM * es, 16},
+                            {gate->w1, R * DM * es, 16},
+                            {gate->w2, (size_t)nout * R * 4, 16},
+                            {gate->bias, (size_t)nout * 4, 16},
+                            {dz, (size_t)tokens * nout * 4, 16}};
+    const Operand outs[4] = {{dx, (size_t)tokens * DM * es, 16},
+                             {dw1, R * DM * 4, 16},
+                             {dw2, (size_t)nout * R * 4, 16},
+                             {db, (size_t)nout * 4, 16}};
+    for (int i = 0; i < 5; ++i)
+        if (ins[i].p && !aligned(ins[i].p, 16)) return GLA_EINVAL;
+    for (int i = 0; i < 4; ++i) {
+        if (!aligned(outs[i].p, 16)) return GLA_EINVAL;
+        for (int j = 0; j < 5; ++j)
+            if (ins[j].p && overlaps(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes)) return GLA_EINVAL;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes)) return GLA_EINVAL;
+    }
+    if (!workspace || workspace_bytes < lay->bytes || !aligned(workspace, 16)) return GLA_EWORKSPACE;
+    for (int i = 0; i < 5; ++i)
+        if (ins[i].p && overlaps(workspace, lay->bytes, ins[i].p, ins[i].bytes)) return GLA_EINVAL;
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(workspace, lay->bytes, outs[i].p, outs[i].bytes)) return GLA_EINVAL;
+    return GLA_OK;
+}
+
 extern "C" int gla_validate_sswiglu(const void* gate, const void* value, int64_t ld_in,
                                     const float* conv_w, const float* conv_b, int batch, int H,
                                     int W, int channels, int dtype, const void* out, int64_t ld_out)

@@ -114,6 +114,23 @@ int gla_validate_bwd_gated(const void* q, const void* k, const void* v, const fl
                            const void* dk, const void* dv, const float* dz, const void* dr,
                            const float* dw, const gla_opts* opts, gla_bwd_gated_layout* lay);
 
+// Gate projection backward: workspace layout (bytes, each part 256-byte
+// aligned): hp [tokens][16 ceil(rank/16)], dhp [tokens][rank], then the
+// partial sums of dW1 [nsplit][rank][d_model], dW2 [nsplit][nout][rank] and
+// db [nsplit][nout] (binary32), nsplit = ceil(tokens / 64).
+typedef struct gla_proj_bwd_layout {
+    size_t off_hp, off_dhp, off_p1, off_p2, off_pb, bytes;
+    int nsplit;
+} gla_proj_bwd_layout;
+
+int gla_plan_gate_proj_bwd(const gla_gate_proj* gate, int tokens, int nout, gla_proj_bwd_layout* lay);
+
+// Host check of every argument of gla_gate_proj_bwd.
+int gla_validate_gate_proj_bwd(const gla_gate_proj* gate, int tokens, int nout, int dtype,
+                               const float* dz, const void* dx, const float* dw1, const float* dw2,
+                               const float* db, const void* workspace, size_t workspace_bytes,
+                               gla_proj_bwd_layout* lay);
+
 // Whether a (dtype, d_k, d_v, chunk) instantiation is built (shared-memory
 // footprint of one workgroup within the 160 KiB of a gfx950 CU; d_k != d_v
 // with 64-token chunks only).

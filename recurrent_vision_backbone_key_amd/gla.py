@@ -21,7 +21,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # include/gla.h: GLA_NOALLOC_SCRATCH_BYTES
 # error-word bits (include/gla.h: GLA_WS_ERR_*)
 WS_ERR_WAIT, WS_ERR_TICKET, WS_ERR_INIT = 1, 2, 4
 EXPORTS = ("gla_fwd", "gla_fwd_noalloc", "gla_workspace_size", "gla_workspace_init", "gla_workspace_status",
-           "gla_gate_logits",
+           "gla_gate_logits", "gla_gate_proj_bwd", "gla_gate_proj_bwd_workspace_size",
            "gla_fwd_gate_proj", "gla_workspace_size_gate_proj", "gla_spatial_swiglu",
            "gla_bwd", "gla_bwd_workspace_size", "gla_bwd_gated", "gla_bwd_gated_workspace_size",
            "gla_status_str", "gla_abi_version")
@@ -97,6 +97,12 @@ def lib():
         h.gla_gate_logits.restype = ctypes.c_int
         h.gla_gate_logits.argtypes = [ctypes.POINTER(GlaGateProj)] + [ctypes.c_int] * 5 + \
             [ctypes.c_void_p, ctypes.c_void_p]
+        h.gla_gate_proj_bwd.restype = ctypes.c_int
+        h.gla_gate_proj_bwd.argtypes = [ctypes.POINTER(GlaGateProj)] + [ctypes.c_int] * 3 + \
+            [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
+        h.gla_gate_proj_bwd_workspace_size.restype = ctypes.c_size_t
+        h.gla_gate_proj_bwd_workspace_size.argtypes = [ctypes.POINTER(GlaGateProj), ctypes.c_int,
+                                                       ctypes.c_int]
         h.gla_fwd_gate_proj.restype = ctypes.c_int
         h.gla_fwd_gate_proj.argtypes = [ctypes.c_void_p] * 3 + [ctypes.POINTER(GlaGateProj)] + \
             [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(GlaOpts)]
@@ -432,6 +438,46 @@ def gate_logits(x, w1, w2, bias, heads, out=None, stream=None):
     if st != 0:
         raise GlaError(st, f"gla_gate_logits failed: {status_str(st)}")
     return out
+
+
+def gate_proj_bwd_workspace_size(gate: GlaGateProj, tokens, nout) -> int:
+    return lib().gla_gate_proj_bwd_workspace_size(ctypes.byref(gate), tokens, nout)
+
+
+def gate_proj_bwd(x, w1, w2, dz, grads=None, workspace=None, stream=None):
+    """Gradients of the gate projection (include/gla.h: gla_gate_proj_bwd).
+    x: [B, L, d_model] float16/float32, w1 [rank, d_model] (x's dtype),
+    w2 [nout, rank] float32, dz: [B, L, heads, dk] or [B, L, nout] float32.
+    Returns (dx like x, dw1 [rank, d_model] float32, dw2 [nout, rank] float32,
+    db [nout] float32)."""
+    torch = _torch()
+    B, L, d_model = x.shape
+    nout = w2.shape[0]
+    if dz.dtype != torch.float32 or dz.numel() != B * L * nout:
+        raise ValueError("dz must be float32 with B * L * nout elements")
+    dtype = F16 if x.dtype == torch.float16 else F32 if x.dtype == torch.float32 else None
+    if dtype is None:
+        raise TypeError("x must be float16 or float32")
+    for name, t in (("x", x), ("w1", w1), ("w2", w2), ("dz", dz)):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    gate = make_gate(x, w1, w2, None)
+    if grads is None:
+        grads = (torch.empty_like(x), torch.empty(w1.shape, dtype=torch.float32, device=x.device),
+                 torch.empty(w2.shape, dtype=torch.float32, device=x.device),
+                 torch.empty((nout,), dtype=torch.float32, device=x.device))
+    dx, dw1, dw2, db = grads
+    need = gate_proj_bwd_workspace_size(gate, B * L, nout)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = lib().gla_gate_proj_bwd(ctypes.byref(gate), B * L, nout, dtype, dz.data_ptr(), dx.data_ptr(),
+                                 dw1.data_ptr(), dw2.data_ptr(), db.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel(), stream)
+    if st != 0:
+        raise GlaError(st, f"gla_gate_proj_bwd failed: {status_str(st)}")
+    return dx, dw1, dw2, db
 
 
 def workspace_size_gate_proj(direction, H, W, chunk, gate: GlaGateProj, opts: GlaOpts) -> int:

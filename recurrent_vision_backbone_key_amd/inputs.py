@@ -79,6 +79,10 @@ BWD = {
     "bwd16k_gated": dict(index=25, kind="bwd", B=2, NH=12, H=128, W=128, dk=128, dv=128,
                          dtype="f16", z=(2.0, 1.0), chunk=64, dirs=(L2R, R2L, T2B, B2T),
                          gated=True),
+    # the gate projection's backward at the gated batch's shapes (12800 tokens,
+    # d_model 384, 6 heads of 64, rank 16)
+    "gateproj_bwd640": dict(index=26, kind="proj_bwd", B=8, NH=6, H=40, W=40, dk=64, dv=64,
+                            dtype="f16", d_model=384, rank=16),
 }
 WORKLOADS.update(BWD)
 

@@ -1,0 +1,230 @@
+"""Backward of the low-rank gate projection (paper "GTR: Gated Token Recurrence
+for Efficient Dense Prediction", Section 2.1, retention gate: z = x W1 W2 + b,
+differentiated).
+
+CPU part: the oracle's gradients pinned without their own formulas -- z is
+linear in each of x, W1, W2 and b separately, so a central difference of the
+fp64 C forward oracle (`oracle.gate_logits`) over any one stored entry is the
+exact partial derivative (up to fp64 rounding), whatever the step; a worked
+example; argument checks and workspace sizes through the C ABI (fake
+addresses, every case rejected before any launch).
+GPU part: dx, dW1, dW2, db of gla_gate_proj_bwd against the oracle on the same
+seeded inputs: ragged token counts around the 64-token partial sums, ranks
+1 .. 64, the gated batch's projection (8 x 1600 tokens, d_model 384, 6 x 64
+logits) in both storage types and the 16K-token stack's (2 x 16384 tokens,
+d_model 1536, 12 x 128 logits), and bitwise repeatability.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from recurrent_vision_backbone_key_amd import gla
+from recurrent_vision_backbone_key_amd.inputs import make_gate_proj_inputs
+
+A = 1 << 32
+MB = 1 << 26
+
+
+def _dz(B, L, nout, seed):
+    return np.random.default_rng(seed).standard_normal((B, L, nout)).astype(np.float32)
+
+
+# ------------------------------------------------------------------- CPU pins
+
+def _loss(x, w1, w2, b, dz, heads):
+    z = oracle.gate_logits(x, w1, w2, b, heads)
+    return float(np.sum(z.reshape(dz.shape) * dz.astype(np.float64)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("B,L,heads,dk,d_model,rank", [(1, 5, 2, 2, 8, 3), (2, 3, 1, 8, 16, 5)])
+def test_oracle_matches_exact_differences(dtype, B, L, heads, dk, d_model, rank):
+    """Every entry of every gradient against (L(theta+) - L(theta-)) /
+    (theta+ - theta-), theta+- the stored entry moved by 0.25 and rounded to
+    its storage type (the division uses the stored values, so the quotient
+    is exact for a linear dependence)."""
+    x = make_gate_proj_inputs(B, L, heads, dk, d_model, rank, dtype, seed=3)
+    dz = _dz(B, L, heads * dk, 4)
+    dx, dw1, dw2, db = oracle.gate_proj_bwd(x["x"], x["w1"], x["w2"], dz)
+    grads = {"x": dx, "w1": dw1, "w2": dw2, "bias": db}
+    for name in ("x", "w1", "w2", "bias"):
+        base = x[name]
+        for idx in np.ndindex(base.shape):
+            vals = []
+            for sgn in (1, -1):
+                arg = {k: v.copy() for k, v in x.items()}
+                arg[name][idx] = arg[name][idx] + base.dtype.type(sgn * 0.25)
+                vals.append((_loss(arg["x"], arg["w1"], arg["w2"], arg["bias"], dz, heads),
+                             float(arg[name][idx])))
+            d = (vals[0][0] - vals[1][0]) / (vals[0][1] - vals[1][1])
+            g = float(grads[name][idx])
+            assert abs(d - g) <= 1e-9 * max(1.0, abs(g)), (name, idx, d, g)
+
+
+def test_oracle_worked_example():
+    """One token, x = e0 + 2 e1, w1 = [[1, -1, 0 ...]] (rank 1, so hp = -1),
+    w2 = [[3], [4]], dz = [1, 10]: dhp = 3 + 40 = 43, dx = 43 w1,
+    dw1 = 43 x, dw2 = dz^T hp = [[-1], [-10]], db = dz."""
+    x = np.zeros((1, 1, 8), np.float32)
+    x[0, 0, :2] = (1, 2)
+    w1 = np.zeros((1, 8), np.float32)
+    w1[0, :2] = (1, -1)
+    w2 = np.array([[3.0], [4.0]], np.float32)
+    dz = np.array([[[1.0, 10.0]]], np.float32)
+    dx, dw1, dw2, db = oracle.gate_proj_bwd(x, w1, w2, dz)
+    assert np.array_equal(dx[0, 0], 43 * w1[0])
+    assert np.array_equal(dw1, 43 * x[0])
+    assert np.array_equal(dw2, np.array([[-1.0], [-10.0]]))
+    assert np.array_equal(db, np.array([1.0, 10.0]))
+
+
+# ------------------------------------------------------------------- ABI checks
+
+def _gate(x=A, w1=A + MB, w2=A + 2 * MB, bias=None, d_model=384, rank=16):
+    return gla.GlaGateProj(x, w1, w2, bias, d_model, rank)
+
+
+def _ws_bytes(tokens, nout, d_model, rank):
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    rp = 16 * ((rank + 15) // 16)
+    ns = (tokens + 63) // 64
+    off = al(tokens * rp * 4)
+    off = al(off + tokens * rank * 4)
+    off = al(off + ns * rank * d_model * 4)
+    off = al(off + ns * nout * rank * 4)
+    return off + ns * nout * 4
+
+
+def _call(gate=None, tokens=1000, nout=384, dtype=gla.F16, dz=A + 3 * MB, dx=A + 4 * MB,
+          dw1=A + 5 * MB, dw2=A + 6 * MB, db=A + 7 * MB, ws=A + 8 * MB, ws_bytes=None):
+    gate = gate or _gate()
+    if ws_bytes is None:
+        ws_bytes = _ws_bytes(tokens, nout, gate.d_model, gate.rank)
+    return gla.lib().gla_gate_proj_bwd(ctypes.byref(gate), tokens, nout, dtype, dz, dx, dw1, dw2, db,
+                                       ws, ws_bytes, None)
+
+
+def test_workspace_sizes():
+    for tokens, nout, d_model, rank in ((1, 16, 8, 1), (300, 384, 384, 16), (12800, 384, 384, 16),
+                                        (32768, 1536, 1536, 16), (77, 40, 24, 64)):
+        g = _gate(d_model=d_model, rank=rank)
+        assert gla.gate_proj_bwd_workspace_size(g, tokens, nout) == _ws_bytes(tokens, nout, d_model,
+                                                                             rank)
+    assert gla.gate_proj_bwd_workspace_size(_gate(rank=65), 100, 16) == 0
+    assert gla.gate_proj_bwd_workspace_size(_gate(d_model=12), 100, 16) == 0
+    assert gla.gate_proj_bwd_workspace_size(_gate(), 0, 16) == 0
+    assert gla.gate_proj_bwd_workspace_size(_gate(), 100, 0) == 0
+
+
+def test_argument_checks():
+    h = gla.lib()
+    assert h.gla_gate_proj_bwd(None, 100, 384, gla.F16, A, A, A, A, A, A, 1 << 30, None) == 1
+    for name in ("dz", "dx", "dw1", "dw2", "db"):
+        assert _call(**{name: None}) == 1, name
+    assert _call(gate=_gate(x=None)) == 1
+    assert _call(gate=_gate(rank=0)) == 1
+    assert _call(tokens=0) == 1
+    assert _call(nout=0) == 1
+    assert _call(dtype=7) == 2
+    assert _call(tokens=(1 << 26) + 1) == 2
+    assert _call(dz=A + 3 * MB + 8) == 1                 # misaligned
+    assert _call(dx=A + 16) == 1                          # dx over x
+    assert _call(dw2=A + 5 * MB + 64) == 1                # dw2 over dw1
+    assert _call(db=A + 3 * MB + 1024) == 1               # db over dz
+    assert _call(ws=None) == 3
+    assert _call(ws_bytes=_ws_bytes(1000, 384, 384, 16) - 4) == 3
+    assert _call(ws=A + 8 * MB + 8) == 3                  # misaligned workspace
+    assert _call(ws=A + 7 * MB) == 1                      # workspace over db
+    assert _call(gate=_gate(bias=A + 2 * MB + 8)) == 1    # bias (unused) misaligned
+    assert _call(db=A + 9 * MB, gate=_gate(bias=A + 9 * MB)) == 1  # db over bias
+
+
+# ------------------------------------------------------------------- GPU
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    return t
+
+
+NAMES = ("dx", "dw1", "dw2", "db")
+# binary32 accumulation throughout (sums over up to 32768 tokens in blocks of
+# 64, random signs: the rounding grows like sqrt(tokens) 2^-24, well below
+# 2e-5 of the largest magnitude); binary16 dx is rounded to its storage
+# (2^-11 relative)
+TOL = {"f32": {"dx": 2e-5, "dw1": 2e-5, "dw2": 2e-5, "db": 2e-5},
+       "f16": {"dx": 2e-3, "dw1": 2e-5, "dw2": 2e-5, "db": 2e-5}}
+
+
+def _run(x, dz, torch):
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+    dzd = torch.from_numpy(dz).cuda()
+    nan = float("nan")
+    grads = (torch.full_like(dev["x"], nan),
+             torch.full(dev["w1"].shape, nan, dtype=torch.float32, device="cuda"),
+             torch.full(dev["w2"].shape, nan, dtype=torch.float32, device="cuda"),
+             torch.full((dev["w2"].shape[0],), nan, dtype=torch.float32, device="cuda"))
+    gate = gla.make_gate(dev["x"], dev["w1"], dev["w2"], None)
+    B, L, _ = dev["x"].shape
+    need = gla.gate_proj_bwd_workspace_size(gate, B * L, dev["w2"].shape[0])
+    ws = torch.full((max(need, 16),), 0xA5, dtype=torch.uint8, device="cuda")  # no initialisation
+    out = gla.gate_proj_bwd(dev["x"], dev["w1"], dev["w2"], dzd, grads=grads, workspace=ws)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+def _check(name, B, L, heads, dk, d_model, rank, dtype, seed, torch):
+    print(f"[case] gate_proj_bwd {name} {dtype} tokens={B * L} d_model={d_model} rank={rank} "
+          f"nout={heads * dk}", flush=True)
+    x = make_gate_proj_inputs(B, L, heads, dk, d_model, rank, dtype, seed=seed)
+    dz = _dz(B, L, heads * dk, seed + 1)
+    got = _run(x, dz, torch)
+    ref = oracle.gate_proj_bwd(x["x"], x["w1"], x["w2"], dz)
+    errs = {}
+    for n, g, r in zip(NAMES, got, ref):
+        assert np.all(np.isfinite(g)), f"{name}: {n} not finite"
+        errs[n] = float(np.max(np.abs(g.astype(np.float64) - r)) / max(np.max(np.abs(r)), 1e-30))
+    print(f"[parity] gate_proj_bwd {name}: " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()),
+          flush=True)
+    for n, e in errs.items():
+        assert e <= TOL[dtype][n], f"{name}: {n} {e:.3e} > {TOL[dtype][n]:.0e}"
+    return got
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("B,L,heads,dk,d_model,rank", [
+    (1, 1, 1, 16, 8, 1),        # one token, rank 1
+    (1, 37, 6, 16, 24, 5),      # ragged tiles everywhere
+    (1, 300, 6, 64, 384, 16),   # five 64-token partial blocks, the last short
+    (3, 171, 2, 64, 64, 40),    # 513 tokens, three rank tiles
+    (1, 260, 1, 32, 16, 64),    # rank 64 (four rank tiles)
+])
+def test_small(torch, dtype, B, L, heads, dk, d_model, rank):
+    _check("small", B, L, heads, dk, d_model, rank, dtype, 31 * L + rank, torch)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_batch640_projection(torch, dtype):
+    """The gated batch's projection: 8 x 1600 tokens, d_model 384, 6 heads of 64."""
+    _check("batch640", 8, 1600, 6, 64, 384, 16, dtype, 700, torch)
+
+
+@pytest.mark.gpu
+def test_stack16k_projection(torch):
+    """The 16K-token stack's: 2 x 16384 tokens, d_model 1536, 12 heads of 128."""
+    _check("stack16k", 2, 16384, 12, 128, 1536, 16, "f16", 800, torch)
+
+
+@pytest.mark.gpu
+def test_deterministic(torch):
+    x = make_gate_proj_inputs(2, 700, 6, 64, 384, 16, "f16", seed=5)
+    dz = _dz(2, 700, 384, 6)
+    a = _run(x, dz, torch)
+    b = _run(x, dz, torch)
+    for n, u, w in zip(NAMES, a, b):
+        assert np.array_equal(u.view(np.uint8), w.view(np.uint8)), n
