@@ -143,6 +143,7 @@ def _check(name, x, direction, H, W, tol, torch, with_w=True):
     (1, 1, 8, 8, 16),
     (1, 2, 10, 13, 32),
     (2, 3, 20, 20, 64),
+    (1, 1, 8, 8, 128),     # d = 128, one chunk (no entering state)
     (1, 2, 10, 13, 128),   # d = 128: o of four d = 64 quarters, the gate row by row
 ])
 @pytest.mark.parametrize("direction", (0, 1, 2, 3))
