@@ -385,6 +385,8 @@ extern "C" int gla_bwd_gated(const void* q, const void* k, const void* v,
     G.eps = opts->eps;
     G.o_out = nullptr;
     G.o_acc = 0;
+    G.fq = lay.off_fq ? (float*)(ws + lay.off_fq) : nullptr;
+    G.fq_floats = lay.fq_bytes / 4;
     return gla::launch_bwd_gated(P, Q, G, opts->dtype, opts->dk, opts->stream);
 }
 

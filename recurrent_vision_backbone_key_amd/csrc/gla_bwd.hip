@@ -1429,7 +1429,9 @@ static int run_bwd_quarters(const Params& P0, const BwdParams& Q0, hipStream_t s
 
 // Gated d = 128: o (binary32) of the quarters added up in the dO area, the
 // output gate's backward row by row (dO in place of o), then the quarters'
-// gradients from dO.
+// gradients from dO.  Each quarter keeps the entering states of its o phase
+// (its own workspace array), so its gradient phase runs only the reverse
+// halves of the states and fold kernels.
 template <typename T>
 static int run_bwd_gated_quarters(const Params& P0, const BwdParams& Q0, const GatedBwd& G0,
                                   hipStream_t st)
@@ -1437,10 +1439,15 @@ static int run_bwd_gated_quarters(const Params& P0, const BwdParams& Q0, const G
     const unsigned units = (unsigned)(P0.B * P0.NH);
     constexpr unsigned blks = 64 * 64 / NTS;
     float* od = (float*)Q0.dout;
+    auto states_of = [&](int a, int cv) {
+        const int q = 2 * a + cv;
+        return q == 0 ? Q0.ws_f : G0.fq + (size_t)(q - 1) * G0.fq_floats;
+    };
     for (int a = 0; a < 2; ++a)
         for (int cv = 0; cv < 2; ++cv) {
             BwdParams Q;
             const Params P = quarter<T, float>(P0, Q, Q0, a, cv);
+            Q.ws_f = states_of(a, cv);
             if (P.nchunks > 1) {
                 hipLaunchKernelGGL((gla_bwd_states_kernel<T, float, 64, true, false>),
                                    dim3(units * P.nchunks), dim3(NTS), 0, st, P, Q);
@@ -1458,8 +1465,21 @@ static int run_bwd_gated_quarters(const Params& P0, const BwdParams& Q0, const G
     hipLaunchKernelGGL((gla_bwd_epi_rows_kernel<T, 128>), dim3(nblk), dim3(NER), 0, st, od, G0, rows);
     if (G0.dw)
         hipLaunchKernelGGL((gla_bwd_dw_kernel<128>), dim3(1), dim3(NDW), 0, st, G0.dwp, G0.dw, nblk);
-    if (hipGetLastError() != hipSuccess) return GLA_EHIP;
-    return run_bwd_quarters<T, float>(P0, Q0, st);
+    for (int a = 0; a < 2; ++a)
+        for (int cv = 0; cv < 2; ++cv) {
+            BwdParams Q;
+            const Params P = quarter<T, float>(P0, Q, Q0, a, cv);
+            Q.ws_f = states_of(a, cv);
+            if (P.nchunks > 1) {
+                hipLaunchKernelGGL((gla_bwd_states_kernel<T, float, 64, false, true>),
+                                   dim3(units * P.nchunks), dim3(NTS), 0, st, P, Q);
+                hipLaunchKernelGGL((gla_bwd_fold_kernel<64, false, true>), dim3(units * blks), dim3(NTS),
+                                   0, st, P, Q);
+            }
+            hipLaunchKernelGGL((gla_bwd_chunk_kernel<T, float, 64>), dim3(units * P.nchunks), dim3(NT), 0, st,
+                               P, Q);
+        }
+    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_EHIP;
 }
 
 template <typename T, typename TD>

@@ -25,6 +25,10 @@ struct GatedBwd {
     // (row stride BwdParams::ld) unless it is the first of its value half
     float* o_out;
     int o_acc;
+    // d = 128: entering states of quarters 1 .. 3 (quarter 0: BwdParams::ws_f),
+    // fq_floats apart
+    float* fq;
+    size_t fq_floats;
 };
 
 // Gated backward: entering states, o and the output gate's backward (dO into

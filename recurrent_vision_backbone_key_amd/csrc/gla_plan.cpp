@@ -466,6 +466,14 @@ extern "C" int gla_plan_bwd_gated(int dir, int H, int W, const gla_opts* o, gla_
     lay->off_do = align256(bwd_bytes);
     lay->off_dwp = align256(lay->off_do + rows * o->dk * 4);
     lay->bytes = lay->off_dwp + units * nchunks * o->dk * 4;
+    // d = 128: each quarter keeps its entering states from the o phase for
+    // the gradient phase (three more arrays of the off_f part's size)
+    lay->off_fq = 0;
+    lay->fq_bytes = off_r - off_f;
+    if (o->dk == 128) {
+        lay->off_fq = align256(lay->bytes);
+        lay->bytes = lay->off_fq + 3 * lay->fq_bytes;
+    }
     return GLA_OK;
 }
 

@@ -99,10 +99,12 @@ int gla_validate_bwd(const void* q, const void* k, const void* v, const float* z
                      size_t* off_r, size_t* off_s, size_t* off_p);
 
 // Gated backward: workspace layout (bytes) -- the backward's own part at 0
-// (gla_plan_bwd), then dO (binary32, rows x d) and the dw partial sums
-// (units x nchunks x d binary32); total in bytes.
+// (gla_plan_bwd), then dO (binary32, rows x d), the dw partial sums
+// (units x nchunks x d binary32) and, for d = 128, the entering states of
+// quarters 1 .. 3 at off_fq, fq_bytes apart (quarter 0 keeps off_f); total in
+// bytes.
 typedef struct gla_bwd_gated_layout {
-    size_t bwd_bytes, off_f, off_r, off_s, off_p, off_do, off_dwp, bytes;
+    size_t bwd_bytes, off_f, off_r, off_s, off_p, off_do, off_dwp, off_fq, fq_bytes, bytes;
     int nchunks;
 } gla_bwd_gated_layout;
 
