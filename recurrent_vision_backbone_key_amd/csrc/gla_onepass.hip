@@ -157,6 +157,19 @@ __device__ __forceinline__ void st_x1(__amdgpu_buffer_rsrc_t r, unsigned off, fl
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, kStoreThrough);
 }
+// The flags' policy: a group's combined transfer (a few per scan, read only by
+// later segments of the same scan) stays in the XCD's L2 when the scan is
+// XCD-local, so its publication waits for the L2's acknowledgement only.
+template <bool LOCAL>
+__device__ __forceinline__ void st_x4_pol(__amdgpu_buffer_rsrc_t r, unsigned off, float4v v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, Pol<LOCAL>::kStore);
+}
+template <bool LOCAL>
+__device__ __forceinline__ void st_x1_pol(__amdgpu_buffer_rsrc_t r, unsigned off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, Pol<LOCAL>::kStore);
+}
 // Segment flags of one scan: bit 1 aggregate, bit 2 inclusive state or group
 // transfer, bit 4 done reading, kPoison published by a poisoned task.
 template <bool LOCAL>
@@ -943,11 +956,11 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 m0 *= gm0;
                 m1 *= gm1;
                 const __amdgpu_buffer_rsrc_t r = xrsrc(P.incl + slot * aggf, agg_bytes);
-                st_x4(r, off0, c0v);
-                st_x4(r, off1, c1v);
+                st_x4_pol<LOCAL>(r, off0, c0v);
+                st_x4_pol<LOCAL>(r, off1, c1v);
                 if ((tid & 15) == 0) {
-                    st_x1(r, st_bytes + 4u * ch0, m0);
-                    st_x1(r, st_bytes + 4u * (ch0 + 32), m1);
+                    st_x1_pol<LOCAL>(r, st_bytes + 4u * ch0, m0);
+                    st_x1_pol<LOCAL>(r, st_bytes + 4u * (ch0 + 32), m1);
                 }
                 set_flag(2u);
             }
