@@ -104,7 +104,7 @@ typedef struct gla_opts {
 } gla_opts;
 
 /* Algorithms.  SINGLE_PASS (binary16, d_k = d_v = 64, chunk 64, segments of
- * at most 5 chunks, at most 65 segments per scan) reads every input once: one
+ * at most 8 chunks, at most 65 segments per scan) reads every input once: one
  * workgroup per segment, segments exchange states through the workspace.
  * THREE_PASS (every built configuration) runs an aggregate pass, a fold pass
  * and an output pass.  AUTO picks SINGLE_PASS whenever it applies. */

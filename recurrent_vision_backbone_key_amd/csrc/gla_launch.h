@@ -8,8 +8,11 @@
 
 namespace gla {
 
-// Largest segment (in chunks) the single-pass kernel keeps on chip.
-constexpr int kOnePassMaxChunks = 5;
+// Largest segment (in chunks) the single-pass kernel keeps on chip, and the
+// largest one its mid-size instance takes (fewer registers: segments of up to
+// kOnePassMidChunks chunks run there, longer ones in the eight-chunk instance).
+constexpr int kOnePassMaxChunks = 8;
+constexpr int kOnePassMidChunks = 5;
 
 // Arguments of one forward call, already validated.
 struct Params {

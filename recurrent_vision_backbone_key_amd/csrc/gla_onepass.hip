@@ -1217,6 +1217,11 @@ int launch_onepass(const Params& P, void* stream)
                                    : onepass::gla_onepass_kernel<true, false, 1>)
                            : (proj ? onepass::gla_onepass_kernel<false, true, 1>
                                    : onepass::gla_onepass_kernel<false, false, 1>);
+    else if (P.seg_chunks <= kOnePassMidChunks)
+        kern = P.xcd_local ? (proj ? onepass::gla_onepass_kernel<true, true, kOnePassMidChunks>
+                                   : onepass::gla_onepass_kernel<true, false, kOnePassMidChunks>)
+                           : (proj ? onepass::gla_onepass_kernel<false, true, kOnePassMidChunks>
+                                   : onepass::gla_onepass_kernel<false, false, kOnePassMidChunks>);
     else
         kern = P.xcd_local ? (proj ? onepass::gla_onepass_kernel<true, true, onepass::NCH>
                                    : onepass::gla_onepass_kernel<true, false, onepass::NCH>)

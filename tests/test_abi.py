@@ -212,14 +212,14 @@ def test_backward_workspace_after_the_prefix():
 
 def test_algorithm_selection():
     """The single pass applies to binary16, d = 64, chunk 64 with segments of
-    at most 5 chunks and at most 65 segments per scan; forcing it elsewhere
+    at most 8 chunks and at most 65 segments per scan; forcing it elsewhere
     is GLA_EUNSUPPORTED; an unknown algorithm is GLA_EINVAL."""
     ok = _opts(algorithm=gla.ALGO_SINGLE_PASS)
     assert gla.workspace_size(0, 40, 40, 64, ok) > 0
     assert _call(chunk=32, opts=_opts(algorithm=gla.ALGO_SINGLE_PASS)) == 2
     assert _call(opts=_opts(dk=32, dv=32, algorithm=gla.ALGO_SINGLE_PASS)) == 2
     assert _call(opts=_opts(dtype=gla.F32, algorithm=gla.ALGO_SINGLE_PASS)) == 2
-    assert _call(opts=_opts(segment_chunks=6, algorithm=gla.ALGO_SINGLE_PASS)) == 2
+    assert _call(opts=_opts(segment_chunks=9, algorithm=gla.ALGO_SINGLE_PASS)) == 2
     # 157 chunks in 2-chunk segments: 79 segments exceed the look-back window
     assert _call(H=100, W=100, opts=_opts(segment_chunks=2, algorithm=gla.ALGO_SINGLE_PASS)) == 2
     assert _call(opts=_opts(algorithm=7)) == 1

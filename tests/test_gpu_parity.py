@@ -153,10 +153,11 @@ def test_segment_split_invariance_three_pass(torch, seg):
         _check(f"seg{seg}", x, d, 24, 40, 64, "f16", torch, segment_chunks=seg, algorithm=2)
 
 
-@pytest.mark.parametrize("seg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("seg", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_segment_split_invariance_single_pass(torch, seg):
-    """Single pass with every segment length it supports (look-back over up to
-    15 segments per scan, ragged last segment)."""
+    """Single pass with every segment length it supports, in its three
+    instances (one chunk, up to five, up to eight; look-back over up to 15
+    segments per scan, ragged last segment)."""
     x = make_inputs(1, 4, 24, 40, 64, 64, "f16", (0.5, 1.0), True, seed=103)
     for d in DIRS:
         _check(f"sp-seg{seg}", x, d, 24, 40, 64, "f16", torch, segment_chunks=seg, algorithm=1)

@@ -79,13 +79,29 @@ def test_four_xcd_geometry(planner):
     assert (p.onepass, p.seg_chunks, p.nseg, p.xcds) == (1, 2, 13, 4)
     assert p.xcd_local == 1 and p.xcd_tasks == 2 * 13 and p.one_round == 1
     assert workgroups(p, 1, 6) == 4 * 26
-    # 8 images: 48 scans do not fit one round; scans divide evenly over 4 XCDs
+    # 8 images: 48 scans do not fit one round even in eight-chunk segments
+    # (the longest, fewest workgroups); scans divide evenly over 4 XCDs
     q = plan(planner, (128, 4), 8, 6, 40, 40)
-    assert q.onepass == 1 and q.seg_chunks == 5 and q.xcd_local == 1
-    assert q.xcd_tasks == 12 * 5 and q.one_round == 0
+    assert q.onepass == 1 and q.seg_chunks == 8 and q.xcd_local == 1
+    assert q.xcd_tasks == 12 * 4 and q.one_round == 0
     # the same batch on an MI355X: five-chunk segments in one round
     r = plan(planner, (256, 8), 8, 6, 40, 40)
     assert (r.seg_chunks, r.nseg, r.one_round) == (5, 5, 1)
+
+
+def test_segments_longer_than_five_chunks(planner):
+    """Segments of six to eight chunks (the eight-chunk instance) when shorter
+    ones would need a second round: the shortest that fits one round, else
+    eight chunks."""
+    # 8 x 6 scans of 28 chunks: 6-chunk segments, 30 workgroups per XCD
+    p = plan(planner, (256, 8), 8, 6, 42, 42)
+    assert (p.seg_chunks, p.nseg, p.xcd_local, p.xcd_tasks, p.one_round) == (6, 5, 1, 30, 1)
+    # 6 scans of 256 chunks: 7-chunk segments, 222 workgroups chip-wide
+    p = plan(planner, (256, 8), 1, 6, 128, 128)
+    assert (p.seg_chunks, p.nseg, p.xcd_local, p.one_round) == (7, 37, 0, 1)
+    # 48 scans of 256 chunks fit no single round: eight-chunk segments
+    p = plan(planner, (256, 8), 8, 6, 128, 128)
+    assert (p.seg_chunks, p.nseg, p.one_round) == (8, 32, 0)
 
 
 def test_single_xcd_geometry_is_chip_wide(planner):
