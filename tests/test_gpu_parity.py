@@ -287,10 +287,13 @@ def test_d128_ragged_grids(torch, H, W):
                out=torch.full((1, H * W, 2, 128), float("nan"), dtype=torch.float16, device="cuda"))
 
 
-@pytest.mark.parametrize("zval,label", [(40.0, "gamma=1"), (-1000.0, "gamma->0"), (None, "wide")])
+@pytest.mark.parametrize("zval,label", [(40.0, "gamma=1"), (-1000.0, "gamma->0"), (-34.7, "span50"),
+                                        (None, "wide")])
 def test_d128_extreme_gates(torch, zval, label):
-    """d = 128 with gamma == 1, gamma -> 0 (pairwise diagonal blocks) and logits
-    ~ N(0, 8) mixing both regimes."""
+    """d = 128 with gamma == 1, gamma -> 0 (decay span of a 16-token sub-chunk
+    about 2^923), a span of about 2^50 (both past the factorised diagonal
+    block's 2^8: pairwise diagonal blocks) and logits ~ N(0, 8) mixing the
+    regimes (spans up to about 2^12, some sub-chunks over 2^8)."""
     x = make_inputs(1, 2, 16, 20, 128, 128, "f16", (0.0, 1.0), True, seed=163)
     if zval is None:
         rng = np.random.default_rng(7)
