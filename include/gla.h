@@ -248,7 +248,8 @@ GLA_API int gla_gate_logits(const gla_gate_proj *gate, int batch, int tokens, in
  * outputs must not overlap each other, an input or the workspace.
  * Asynchronous on `stream` (hipStream_t, NULL: the null stream).
  * GLA_EINVAL on a bad pointer, size or overlap, GLA_EUNSUPPORTED on a dtype
- * or size outside the built set (tokens <= 2^26, nout <= 65536),
+ * or size outside the built set (tokens <= 2^26, nout <= 65536, tokens *
+ * nout and tokens * d_model below 2^29),
  * GLA_EWORKSPACE on a missing or small workspace, GLA_EHIP on a launch
  * failure.
  */

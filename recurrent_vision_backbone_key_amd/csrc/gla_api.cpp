@@ -220,7 +220,6 @@ extern "C" int gla_gate_proj_bwd(const gla_gate_proj* gate, int tokens, int nout
     char* ws = (char*)workspace;
     gla::ProjBwdWs W;
     W.hp = (float*)(ws + lay.off_hp);
-    W.dhp = (float*)(ws + lay.off_dhp);
     W.p1 = (float*)(ws + lay.off_p1);
     W.p2 = (float*)(ws + lay.off_p2);
     W.pb = (float*)(ws + lay.off_pb);

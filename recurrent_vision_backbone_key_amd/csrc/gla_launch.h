@@ -87,11 +87,10 @@ int launch_gate_rank(const GateProj& G, int dtype, int tokens, float* hp, void* 
 constexpr int kProjBwdSplit = 64;
 
 // Workspace parts of the gate projection's backward (binary32): hp [tokens][16
-// ceil(rank/16)], dhp [tokens][rank], and the per-block partial sums of dW1
-// [nsplit][rank][d_model], dW2 [nsplit][nout][rank] and db [nsplit][nout].
+// ceil(rank/16)] and the per-block partial sums of dW1 [nsplit][rank][d_model],
+// dW2 [nsplit][nout][rank] and db [nsplit][nout].
 struct ProjBwdWs {
     float* hp;
-    float* dhp;
     float* p1;
     float* p2;
     float* pb;

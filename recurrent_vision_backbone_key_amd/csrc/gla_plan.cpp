@@ -306,16 +306,14 @@ extern "C" int gla_plan_gate_proj_bwd(const gla_gate_proj* gate, int tokens, int
     if (tokens > (1 << 26) || nout > (1 << 16)) return GLA_EUNSUPPORTED;
     const int64_t R = gate->rank, RP = 16 * ((R + 15) / 16), DM = gate->d_model;
     const int64_t ns = ((int64_t)tokens + gla::kProjBwdSplit - 1) / gla::kProjBwdSplit;
-    // grids: one wavefront per 16 x 16 output tile (and per token block for
-    // the sums over tokens), four per workgroup, below 2^31 workgroups
-    const int64_t lim = (int64_t)1 << 33, rt = RP / 16;
-    if (((int64_t)tokens + 15) / 16 * ((DM + 15) / 16) >= lim) return GLA_EUNSUPPORTED;
-    if (rt * ((DM + 15) / 16) * ns >= lim || ((int64_t)nout + 15) / 16 * rt * ns >= lim)
+    // the fused kernel addresses dz and x with 32-bit buffer offsets
+    if ((int64_t)tokens * nout * 4 >= ((int64_t)1 << 31) || (int64_t)tokens * DM * 4 >= ((int64_t)1 << 31))
         return GLA_EUNSUPPORTED;
+    // one workgroup per token block; the reduction's grid (64 outputs per
+    // workgroup over the three arrays) stays far below 2^31 at these bounds
     lay->nsplit = (int)ns;
     lay->off_hp = 0;
-    lay->off_dhp = align256(lay->off_hp + (size_t)tokens * RP * 4);
-    lay->off_p1 = align256(lay->off_dhp + (size_t)tokens * R * 4);
+    lay->off_p1 = align256(lay->off_hp + (size_t)tokens * RP * 4);
     lay->off_p2 = align256(lay->off_p1 + (size_t)ns * R * DM * 4);
     lay->off_pb = align256(lay->off_p2 + (size_t)ns * nout * R * 4);
     lay->bytes = lay->off_pb + (size_t)ns * nout * 4;

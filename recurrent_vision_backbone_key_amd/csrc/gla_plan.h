@@ -117,11 +117,11 @@ int gla_validate_bwd_gated(const void* q, const void* k, const void* v, const fl
                            const float* dw, const gla_opts* opts, gla_bwd_gated_layout* lay);
 
 // Gate projection backward: workspace layout (bytes, each part 256-byte
-// aligned): hp [tokens][16 ceil(rank/16)], dhp [tokens][rank], then the
-// partial sums of dW1 [nsplit][rank][d_model], dW2 [nsplit][nout][rank] and
-// db [nsplit][nout] (binary32), nsplit = ceil(tokens / 64).
+// aligned): hp [tokens][16 ceil(rank/16)], then the partial sums of dW1
+// [nsplit][rank][d_model], dW2 [nsplit][nout][rank] and db [nsplit][nout]
+// (binary32), nsplit = ceil(tokens / 64).
 typedef struct gla_proj_bwd_layout {
-    size_t off_hp, off_dhp, off_p1, off_p2, off_pb, bytes;
+    size_t off_hp, off_p1, off_p2, off_pb, bytes;
     int nsplit;
 } gla_proj_bwd_layout;
 

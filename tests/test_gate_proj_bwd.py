@@ -91,7 +91,6 @@ def _ws_bytes(tokens, nout, d_model, rank):
     rp = 16 * ((rank + 15) // 16)
     ns = (tokens + 63) // 64
     off = al(tokens * rp * 4)
-    off = al(off + tokens * rank * 4)
     off = al(off + ns * rank * d_model * 4)
     off = al(off + ns * nout * rank * 4)
     return off + ns * nout * 4
@@ -129,6 +128,8 @@ def test_argument_checks():
     assert _call(nout=0) == 1
     assert _call(dtype=7) == 2
     assert _call(tokens=(1 << 26) + 1) == 2
+    assert _call(tokens=1 << 20, nout=512) == 2          # dz of 2 GiB: past 32-bit offsets
+    assert _call(tokens=1 << 21, gate=_gate(d_model=256)) == 2  # x rows past 2^31 bytes (fp32 bound)
     assert _call(dz=A + 3 * MB + 8) == 1                 # misaligned
     assert _call(dx=A + 16) == 1                          # dx over x
     assert _call(dw2=A + 5 * MB + 64) == 1                # dw2 over dw1
@@ -202,6 +203,8 @@ def _check(name, B, L, heads, dk, d_model, rank, dtype, seed, torch):
     (1, 300, 6, 64, 384, 16),   # five 64-token partial blocks, the last short
     (3, 171, 2, 64, 64, 40),    # 513 tokens, three rank tiles
     (1, 260, 1, 32, 16, 64),    # rank 64 (four rank tiles)
+    (1, 70, 5, 2, 200, 24),     # 10 logits (not a multiple of 4), d_model 200 (ragged 64-column chunk)
+    (2, 45, 3, 1, 72, 17),      # 3 logits, two rank tiles, d_model past one chunk by 8
 ])
 def test_small(torch, dtype, B, L, heads, dk, d_model, rank):
     _check("small", B, L, heads, dk, d_model, rank, dtype, 31 * L + rank, torch)
