@@ -70,6 +70,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const void* base, unsign
 }
 // Offset past every record (the tensors it is used on stay below 2^31 bytes).
 constexpr unsigned kPastEnd = 0x80000000u;
+// Cache-policy operand of buffer instructions: non-temporal (streaming).
+constexpr int kNonTemporal = 2;
 __device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, unsigned off)
 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));

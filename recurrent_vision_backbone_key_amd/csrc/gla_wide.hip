@@ -116,7 +116,8 @@ __device__ __forceinline__ void load_part(Raw& x, const Params& P, int row, int 
     const unsigned es = PART == PZ ? 4u : 2u;
     const void* base = PART == PZ ? (const void*)P.z : PART == PK ? P.k : PART == PQ ? P.q
                      : PART == PV ? P.v : P.r;
-    const __amdgpu_buffer_rsrc_t rs = xrsrc(base, rows * D * es);
+    // without an output gate r has no records: its loads read zero
+    const __amdgpu_buffer_rsrc_t rs = xrsrc(base, (PART == PR && !P.r) ? 0u : rows * D * es);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const unsigned off = row >= 0 ? (unsigned)(row * D + cb + 32 * kb) * es : kPastEnd;
@@ -139,9 +140,7 @@ __device__ __forceinline__ void load_raw(Raw& x, const Params& P, int row, int c
     load_part<PV>(x, P, row, cb);
     if (!AGG) {
         load_part<PQ>(x, P, row, cb);
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        x.r[0] = x.r[1] = zero;
-        if (gated) load_part<PR>(x, P, row, cb);
+        load_part<PR>(x, P, row, cb);
     }
 }
 
@@ -286,7 +285,7 @@ void gla_wide_kernel(Params P)
         // as this chunk's copy is consumed, from a row index of its own.
         const bool pf = (c + 1 < c_end);
         const int arow = (AGG && pf) ? scan_row(P, unit, (c + 1) * C + tl) : -1;
-        if (AGG && pf) load_part<PZ>(raw, P, arow, cb);
+        if (AGG) load_part<PZ>(raw, P, arow, cb);
         if (l16 == 15) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -304,7 +303,7 @@ void gla_wide_kernel(Params P)
             *(u32x4*)(sV + tl * SH + cb + 32 * kb) = raw.v[kb];
             if (gated) *(u32x4*)(sR + tl * SH + cb + 32 * kb) = raw.r[kb];
         }
-        if (AGG && pf) load_part<PV>(raw, P, arow, cb);
+        if (AGG) load_part<PV>(raw, P, arow, cb);
 
         // ---- per-channel factors of this wave's sub-chunk, one channel per lane
         float* fac = sFac + wave * NFAC * 64;
@@ -409,7 +408,7 @@ void gla_wide_kernel(Params P)
                 if (lane == 0) sMisc[wave] = ww ? 1 : 0;
             }
         }
-        if (AGG && pf) load_part<PK>(raw, P, arow, cb);
+        if (AGG) load_part<PK>(raw, P, arow, cb);
         const int myrow = sRows[buf * C + tl];
         __syncthreads();  // (2) operands of every wave
 
@@ -417,7 +416,7 @@ void gla_wide_kernel(Params P)
         // are fetched in parts spread over this chunk, so the loads stream
         // while it computes
         const int nrow = pf ? sRows[(buf ^ 1) * C + tl] : -1;
-        if (!AGG && pf) load_part<PZ>(raw, P, nrow, cb);
+        if (!AGG) load_part<PZ>(raw, P, nrow, cb);
 
         // value fragments, shared by the value product and the state update:
         // lane (g, l16) holds v[32p + 8g + e][16 wave + l16]
@@ -463,7 +462,7 @@ void gla_wide_kernel(Params P)
                     if (j < si) *(float4v*)(sPA + ((4 + tri + j) * 64 + lane) * 4) = part[j];
             }
 
-            if (pf) load_part<PK>(raw, P, nrow, cb);
+            load_part<PK>(raw, P, nrow, cb);
             // ================= state role: inter-chunk term =================
             // o^T[16 wave + 4g + e][16 i + l16] = sum_c S[c][dv] (q (.) 2^b)[t][c]
 #pragma unroll
@@ -490,7 +489,7 @@ void gla_wide_kernel(Params P)
                 }
             }
             __syncthreads();  // (3) partial scores
-            if (pf) load_part<PQ>(raw, P, nrow, cb);
+            load_part<PQ>(raw, P, nrow, cb);
 
             // ---- row role: full scores of sub-chunk si into the score matrix
             if (h == 0) {
@@ -516,7 +515,7 @@ void gla_wide_kernel(Params P)
                 *(half4*)(sAL + tl * SAL + 4 * g) = lo;
             }
             __syncthreads();  // (4) scores
-            if (pf) load_part<PV>(raw, P, nrow, cb);
+            load_part<PV>(raw, P, nrow, cb);
 
             // ================= state role: scores times values =================
 #pragma unroll
@@ -555,7 +554,7 @@ void gla_wide_kernel(Params P)
 
         if (!AGG) {
             if (gated) __syncthreads();  // (5) sums of squares
-            if (pf && gated) load_part<PR>(raw, P, nrow, cb);
+            load_part<PR>(raw, P, nrow, cb);
             // epilogue, part 2: u = SiLU(r) (.) w (.) o / rms(o), staged over r
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -581,14 +580,17 @@ void gla_wide_kernel(Params P)
             // (written once; measured 324 -> 315 us per call on the 16K-token
             // 12-block stack)
             const int* rows = sRows + buf * C;
+            const __amdgpu_buffer_rsrc_t ro = xrsrc(P.out, (unsigned)(P.B * P.L * P.NH) * D * 2u);
 #pragma unroll
             for (int p = 0; p < C * 16 / NT; ++p) {
                 const int idx = tid + p * NT;
                 const int row = idx >> 4, piece = idx & 15;
                 const int t = rows[row];
-                if (t >= 0)
-                    __builtin_nontemporal_store(*(const u32x4*)((const char*)(sR + row * SH) + piece * 16),
-                                                (u32x4*)((char*)P.out + (size_t)t * D * 2 + piece * 16));
+                // rows past the end of the scan take an offset past every record
+                // (the store is dropped), so no store sits behind a branch
+                const unsigned off = t >= 0 ? (unsigned)t * D * 2u + 16u * piece : kPastEnd;
+                __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)((const char*)(sR + row * SH) + piece * 16),
+                                                       ro, (int)off, 0, kNonTemporal);
             }
         }
     }
