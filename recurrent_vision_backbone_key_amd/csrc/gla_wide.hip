@@ -468,8 +468,25 @@ void gla_wide_kernel(Params P)
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = float4v{0.f, 0.f, 0.f, 0.f};
             if (have_state) {
+                // the query operands of step p + 1 are read before step p's
+                // products, so the LDS latency overlaps them
+                auto qop = [&](int p, int i) {
+                    const _Float16* qrow = sQH + (16 * i + l16) * SH + 32 * p + 4 * g;
+                    const half4 b0 = *(const half4*)qrow;
+                    const half4 b1 = *(const half4*)(qrow + 16);
+                    return half8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                };
+                half8 bq[2][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bq[0][i] = qop(0, i);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
+                    if (p + 1 < 4) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) bq[(p + 1) & 1][i] = qop(p + 1, i);
+                    }
+                    // keep those reads ahead of this step's products
+                    __builtin_amdgcn_sched_barrier(0);
                     // k-slots 8g + e: channel 32p + 4g + e (e < 4), 32p + 16 + 4g + e - 4
                     // (the state enters as its binary16 high part)
                     half8 ah;
@@ -479,13 +496,7 @@ void gla_wide_kernel(Params P)
                         ah[4 + e] = (_Float16)S[2 * p + 1][e];
                     }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const _Float16* qrow = sQH + (16 * i + l16) * SH + 32 * p + 4 * g;
-                        const half4 b0 = *(const half4*)qrow;
-                        const half4 b1 = *(const half4*)(qrow + 16);
-                        const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-                        o[i] = mma(ah, bq, o[i]);
-                    }
+                    for (int i = 0; i < 4; ++i) o[i] = mma(ah, bq[p & 1][i], o[i]);
                 }
             }
             __syncthreads();  // (3) partial scores
@@ -543,12 +554,21 @@ void gla_wide_kernel(Params P)
         }
 
         // ================= state role: S = Diag(2^{chunk total}) S + k-hat^T v =================
+        // k-hat fragments of tile a + 1 read before tile a's products
+        half8 kf[2][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) kf[0][p] = tr_frag(sKH, 32 * p + 8 * g, 0, l16);
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
+            if (a + 1 < 8) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) kf[(a + 1) & 1][p] = tr_frag(sKH, 32 * p + 8 * g, 16 * (a + 1), l16);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this tile's products
             const float4v dec = *(const float4v*)(sDec + 16 * a + 4 * g);
             S[a] = S[a] * dec;
 #pragma unroll
-            for (int p = 0; p < 2; ++p) S[a] = mma(tr_frag(sKH, 32 * p + 8 * g, 16 * a, l16), vf[p], S[a]);
+            for (int p = 0; p < 2; ++p) S[a] = mma(kf[a & 1][p], vf[p], S[a]);
         }
         have_state = true;
 
