@@ -310,13 +310,17 @@ __device__ __forceinline__ void scores_values(const _Float16* sE, const _Float16
     // ---- M1 partial scores over this wave's 32 channels, tiles j <= SI
     //      (j < SI off the diagonal; the diagonal tile separately)
     float4v part[NSUB];
+    half8 ek[NSUB - 1];  // the key operands, read before the first product
+#pragma unroll
+    for (int j = 0; j < NSUB - 1; ++j)
+        if (j < SI) ek[j] = *(const half8*)(sE + (16 * j + l16) * SH + c0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NSUB - 1; ++j) {
         part[j] = float4v{0.f, 0.f, 0.f, 0.f};
         if (j >= SI) continue;
-        const half8 ek = *(const half8*)(sE + (16 * j + l16) * SH + c0);
         const half8 qf = (j == SI - 1) ? qa : (j == SI - 2) ? qo1 : qo2;
-        part[j] = mma(ek, qf, part[j]);
+        part[j] = mma(ek[j], qf, part[j]);
         *(float4v*)(sPA + ((wave * NSUB + j) * 64 + lane) * 4) = part[j];
     }
     float4v pd = float4v{0.f, 0.f, 0.f, 0.f};
@@ -343,8 +347,22 @@ __device__ __forceinline__ void scores_values(const _Float16* sE, const _Float16
                 if (4 * g + e > l16) at[j][e] = 0.f;
         }
     }
-    // ---- M2: O^T[dv][t] += V^T A^T, this wave's 32 value channels
+    // ---- M2: O^T[dv][t] += V^T A^T, this wave's 32 value channels (the
+    //      value fragments read before the first product)
     o[0] = o[1] = float4v{0.f, 0.f, 0.f, 0.f};
+    half4 vt[NSUB / 2][2][2];
+#pragma unroll
+    for (int p = 0; p < NSUB / 2; ++p) {
+        if (2 * p > SI) continue;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            // value rows 32p + 4g + e and 32p + 16 + 4g + e of column 32h + 16m + l16
+            vt[p][m][0] = ld_tr(tr_addr<SH>(sVT, 32 * p + 4 * g, 32 * h + 16 * m, l16));
+            vt[p][m][1] = half4{0, 0, 0, 0};
+            if (2 * p + 1 <= SI) vt[p][m][1] = ld_tr(tr_addr<SH>(sVT, 32 * p + 16 + 4 * g, 32 * h + 16 * m, l16));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < NSUB / 2; ++p) {
         if (2 * p > SI) continue;
@@ -367,10 +385,8 @@ __device__ __forceinline__ void scores_values(const _Float16* sE, const _Float16
         const bool has_diag = (2 * p == SI) || (2 * p + 1 == SI);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            // value rows 32p + 4g + e and 32p + 16 + 4g + e of column 32h + 16m + l16
-            const half4 v0 = ld_tr(tr_addr<SH>(sVT, 32 * p + 4 * g, 32 * h + 16 * m, l16));
-            half4 v1 = {0, 0, 0, 0};
-            if (hi) v1 = ld_tr(tr_addr<SH>(sVT, 32 * p + 16 + 4 * g, 32 * h + 16 * m, l16));
+            const half4 v0 = vt[p][m][0];
+            const half4 v1 = vt[p][m][1];
             half8 afr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -594,18 +610,23 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     const unsigned agg_bytes = (unsigned)(aggf * 4), st_bytes = (unsigned)(D * D * 4);
     unsigned* flags = P.flags + (size_t)unit * P.nseg;
     // M4: local state update S = Diag(2^{chunk total}) S + k-hat^T v
+    // (every fragment is read before the first product, so the four MFMAs
+    // do not each wait for their own LDS reads)
     auto state_update = [&]() {
+        half8 kf[2], vf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            kf[kb] = tr_frag_s<SH>(sKT, 32 * kb + 8 * g, 16 * sa, l16);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) vf[jj][kb] = tr_frag_s<SH>(sVT, 32 * kb + 8 * g, 16 * (sb0 + jj), l16);
+        }
+        float4v dec = *(const float4v*)(sDec + 16 * sa + 4 * g);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int bb = sb0 + jj;
+            S[jj] = S[jj] * dec;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[jj][e] *= sDec[16 * sa + 4 * g + e];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const half8 kf = tr_frag_s<SH>(sKT, 32 * kb + 8 * g, 16 * sa, l16);
-                const half8 vf = tr_frag_s<SH>(sVT, 32 * kb + 8 * g, 16 * bb, l16);
-                S[jj] = mma(kf, vf, S[jj]);
-            }
+            for (int kb = 0; kb < 2; ++kb) S[jj] = mma(kf[kb], vf[jj][kb], S[jj]);
         }
     };
     // the segment aggregate (local state [ch][dv] straight from the state
@@ -774,15 +795,19 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         }
         // ---- M3: O^T += S_loc^T (q (.) 2^b)^T, local state from the segment start
         if (c > 0) {
+            half8 qf[2], sfr[2][2];  // every operand read before the first product
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const half8 qf = *(const half8*)(sQH + tl * SH + 32 * kb + 8 * g);
+                qf[kb] = *(const half8*)(sQH + tl * SH + 32 * kb + 8 * g);
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const half8 sfr = *(const half8*)(sST + (32 * h + 16 * m + l16) * SH + 32 * kb + 8 * g);
-                    o[m] = mma(sfr, qf, o[m]);
-                }
+                for (int m = 0; m < 2; ++m)
+                    sfr[kb][m] = *(const half8*)(sST + (32 * h + 16 * m + l16) * SH + 32 * kb + 8 * g);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) o[m] = mma(sfr[kb][m], qf[kb], o[m]);
         }
         okeep[c][0] = o[0];
         okeep[c][1] = o[1];
