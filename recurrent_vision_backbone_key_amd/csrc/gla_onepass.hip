@@ -1135,14 +1135,19 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         if (cc >= nch) break;
         float4v o0 = okeep[cc][0], o1 = okeep[cc][1];
         if (need_in) {
+            half8 qf[2], h0[2], h1[2];  // every operand read before the first product
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int k0 = 32 * kb + 8 * g;
-                const half8 qf = *(const half8*)(sOut + (cc * C + tl) * SH + k0);
-                const half8 h0 = *(const half8*)(sST + (32 * h + l16) * SH + k0);
-                const half8 h1 = *(const half8*)(sST + (32 * h + 16 + l16) * SH + k0);
-                o0 = mma(h0, qf, o0);
-                o1 = mma(h1, qf, o1);
+                qf[kb] = *(const half8*)(sOut + (cc * C + tl) * SH + k0);
+                h0[kb] = *(const half8*)(sST + (32 * h + l16) * SH + k0);
+                h1[kb] = *(const half8*)(sST + (32 * h + 16 + l16) * SH + k0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                o0 = mma(h0[kb], qf[kb], o0);
+                o1 = mma(h1[kb], qf[kb], o1);
             }
         }
         okeep[cc][0] = o0 * P.scale;
