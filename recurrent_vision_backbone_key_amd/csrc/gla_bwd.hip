@@ -686,12 +686,26 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
     // ---- P = s dO V^T on the blocks j <= si (this half: j = h mod 2),
     //      diagonal blocks masked to u >= t
     for (int j = h; j <= si; j += 2) {
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int ks = 0; ks < KS; ++ks) {
-            const int col = 4 * ks + g;
-            acc = mma(sDO[(16 * si + l16) * SD + col], sV[(16 * j + l16) * SD + col], acc);
+        // operands of PB steps read before their products, two chains
+        constexpr int PB = KS < 8 ? KS : 8;
+        float4v acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < KS; k0 += PB) {
+            float av[PB], bv[PB];
+#pragma unroll
+            for (int u = 0; u < PB; ++u) {
+                const int col = 4 * (k0 + u) + g;
+                av[u] = sDO[(16 * si + l16) * SD + col];
+                bv[u] = sV[(16 * j + l16) * SD + col];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < PB; ++u) {
+                if (u & 1) acc1 = mma(av[u], bv[u], acc1);
+                else acc = mma(av[u], bv[u], acc);
+            }
         }
+        acc = acc + acc1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int u = 4 * g + e;
@@ -713,14 +727,19 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
                 float4v m[CT];
 #pragma unroll
                 for (int cl = 0; cl < CT; ++cl) m[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+                float av[4], bv[4][CT];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int sp = 16 * j + 4 * ks + g;
-                    const float a = sP[(16 * si + l16) * SC + sp];
+                    av[ks] = sP[(16 * si + l16) * SC + sp];
 #pragma unroll
-                    for (int cl = 0; cl < CT; ++cl)
-                        m[cl] = mma(a, sKT[sp * SD + 16 * (ct0 + cl) + l16], m[cl]);
+                    for (int cl = 0; cl < CT; ++cl) bv[ks][cl] = sKT[sp * SD + 16 * (ct0 + cl) + l16];
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int cl = 0; cl < CT; ++cl) m[cl] = mma(av[ks], bv[ks][cl], m[cl]);
 #pragma unroll
                 for (int cl = 0; cl < CT; ++cl) {
                     const float f = E(si, j, 16 * (ct0 + cl) + l16);
@@ -771,14 +790,19 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
                 float4v m[CT];
 #pragma unroll
                 for (int cl = 0; cl < CT; ++cl) m[cl] = float4v{0.f, 0.f, 0.f, 0.f};
+                float av[4], bv[4][CT];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int up = 16 * j + 4 * ks + g;
-                    const float a = sP[up * SC + 16 * si + l16];
+                    av[ks] = sP[up * SC + 16 * si + l16];
 #pragma unroll
-                    for (int cl = 0; cl < CT; ++cl)
-                        m[cl] = mma(a, sQH[up * SD + 16 * (ct0 + cl) + l16], m[cl]);
+                    for (int cl = 0; cl < CT; ++cl) bv[ks][cl] = sQH[up * SD + 16 * (ct0 + cl) + l16];
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int cl = 0; cl < CT; ++cl) m[cl] = mma(av[ks], bv[ks][cl], m[cl]);
 #pragma unroll
                 for (int cl = 0; cl < CT; ++cl) {
                     const float f = E(j, si, 16 * (ct0 + cl) + l16);
@@ -841,12 +865,15 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
                 float kb[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) kb[ks] = kh[ks] * E(j, si, 4 * ks + g);
+                float qv[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) qv[ks] = sQH[(16 * j + l16) * SD + 4 * ks + g];
+                __builtin_amdgcn_sched_barrier(0);
                 float4v a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ks += 2) {
-                    const int ch = 4 * ks + g;
-                    a = mma(sQH[(16 * j + l16) * SD + ch], kb[ks], a);
-                    a1 = mma(sQH[(16 * j + l16) * SD + ch + 4], kb[ks + 1], a1);
+                    a = mma(qv[ks], kb[ks], a);
+                    a1 = mma(qv[ks + 1], kb[ks + 1], a1);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -855,11 +882,16 @@ __global__ __launch_bounds__(NT) void gla_bwd_chunk_kernel(Params P, BwdParams Q
                 }
             }
             // dv[t][col] += sum_u A[u][t] dO[u][col], k-slot g of step e is u = 16 j + 4g + e
+            float dov[CT][4];
 #pragma unroll
             for (int cl = 0; cl < CT; ++cl)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dvacc[cl] = mma(a[e], sDO[(16 * j + 4 * g + e) * SD + 16 * (ct0 + cl) + l16], dvacc[cl]);
+                for (int e = 0; e < 4; ++e) dov[cl][e] = sDO[(16 * j + 4 * g + e) * SD + 16 * (ct0 + cl) + l16];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cl = 0; cl < CT; ++cl)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dvacc[cl] = mma(a[e], dov[cl][e], dvacc[cl]);
         }
         if (has_r) {
 #pragma unroll
@@ -1094,12 +1126,15 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     ka[ks] = sKT[(16 * j + l16) * SD + 4 * ks + g] * E(si, j, 4 * ks + g);
+                float qv[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) qv[ks] = sQH[(16 * si + l16) * SD + 4 * ks + g];
+                __builtin_amdgcn_sched_barrier(0);
                 float4v a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ks += 2) {
-                    const int ch = 4 * ks + g;
-                    a = mma(ka[ks], sQH[(16 * si + l16) * SD + ch], a);
-                    a1 = mma(ka[ks + 1], sQH[(16 * si + l16) * SD + ch + 4], a1);
+                    a = mma(ka[ks], qv[ks], a);
+                    a1 = mma(ka[ks + 1], qv[ks + 1], a1);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1108,11 +1143,16 @@ __global__ __launch_bounds__(NT) void gla_bwd_oepi_kernel(Params P, BwdParams Q,
                 }
             }
             // o[t][col] += sum_tau scores[t][tau] v[tau][col]; k-slot g of step e is tau = 16 j + 4g + e
+            float vv[CT][4];
 #pragma unroll
             for (int cl = 0; cl < CT; ++cl)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    oacc[cl] = mma(a[e], sV[(16 * j + 4 * g + e) * SD + 16 * (ct0 + cl) + l16], oacc[cl]);
+                for (int e = 0; e < 4; ++e) vv[cl][e] = sV[(16 * j + 4 * g + e) * SD + 16 * (ct0 + cl) + l16];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cl = 0; cl < CT; ++cl)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oacc[cl] = mma(a[e], vv[cl][e], oacc[cl]);
         }
         if (has_in) {
 #pragma unroll 4
