@@ -479,75 +479,121 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     //      segments after them give up their bounded wait, report and write
     //      NaN.  Beside the ticket, thread 0 reads the error word and the
     //      initialisation mark.
+    //      Direct (plans of one round): the task follows from the grid index b
+    //      with no round trip, so the first chunk's loads leave at once.
+    //      Chip-wide, task b is segment b / (B NH) of scan b mod (B NH).
+    //      LOCAL: the turn-by-turn dispatch gives the workgroups on one XCD
+    //      the indices b with b mod xcds fixed, in increasing order, so b /
+    //      xcds numbers them 0 .. xcd_tasks - 1 in dispatch order, and the XCD
+    //      comes from the XCC_ID register.  Either way a workgroup waits only
+    //      on segments of smaller grid index, which every XCD dispatches in
+    //      increasing order, so the lowest unfinished workgroup always holds
+    //      or gets a compute unit.  The counter is still taken, off the
+    //      critical path, so a dispatch that broke the turn order or a counter
+    //      left uncleared is reported as with tickets.
+    const bool direct = P.one_round != 0;
+    unsigned long long em = 0ull;
+    unsigned tk = 0u;
+    unsigned* ctr = nullptr;
     if (tid == 0) {
-        const unsigned long long em =
-            __hip_atomic_load((const unsigned long long*)P.err, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
+        em = __hip_atomic_load((const unsigned long long*)P.err, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         if (LOCAL) {
             const unsigned x = (__builtin_amdgcn_s_getreg(kXccIdReg) & 15u) % (unsigned)P.xcds;
-            unsigned* ctr = P.ticket + GLA_HDR_XCD + 32 * x;
-            const unsigned t = atomicAdd(ctr, 1u);
-            if (t == (unsigned)P.xcd_tasks - 1u) st_u(ctr, 0u);  // every ticket of this XCD is taken
-            sMisc[0] = (int)t;
-            sMisc[2] = (int)x;
+            ctr = P.ticket + GLA_HDR_XCD + 32 * x;
+            tk = atomicAdd(ctr, 1u);
+            if (!direct) {
+                if (tk == (unsigned)P.xcd_tasks - 1u) st_u(ctr, 0u);  // every ticket of this XCD is taken
+                sMisc[2] = (int)x;
+            }
         } else {
-            const unsigned t = atomicAdd(P.ticket + GLA_HDR_TICKET, 1u);
-            if (t == (unsigned)grid - 1u) st_u(P.ticket + GLA_HDR_TICKET, 0u);  // every ticket is taken
-            sMisc[0] = (int)t;
+            ctr = P.ticket + GLA_HDR_TICKET;
+            tk = atomicAdd(ctr, 1u);
+            if (!direct && tk == (unsigned)grid - 1u) st_u(ctr, 0u);  // every ticket is taken
         }
-        // (the word pair is consumed only here, after the ticket's round trip)
-        const bool mark_ok = (unsigned)(em >> 32) == GLA_WS_MARK;
-        sMisc[3] = (mark_ok ? 1 : 0) | ((unsigned)em != 0u ? 2 : 0);
+        if (!direct) {
+            sMisc[0] = (int)tk;
+            // (the word pair is consumed only here, after the ticket's round trip)
+            const bool mark_ok = (unsigned)(em >> 32) == GLA_WS_MARK;
+            sMisc[3] = (mark_ok ? 1 : 0) | ((unsigned)em != 0u ? 2 : 0);
+        }
     }
-    __syncthreads();
-    const int ticket = sMisc[0];
-    // poisoned: a failure upstream (a sticky error from an earlier call, a
-    // wait that gave up, a transfer folded from a poisoned segment): every
-    // store of this task writes NaN and every flag it publishes carries the
-    // poison bit, so no row downstream of a failure holds plausible data
-    bool poisoned = (sMisc[3] & 2) != 0;
+    // completes the direct path's counter protocol and its checks (thread 0):
+    // the last of an XCD's workgroups clears its counter; sMisc[3] takes the
+    // mark and sticky-error bits, plus 4 for a ticket beyond the XCD's tasks
+    auto direct_checks = [&]() {
+        if (tid == 0) {
+            const unsigned ntk = LOCAL ? (unsigned)P.xcd_tasks : (unsigned)grid;
+            if (tk == ntk - 1u) st_u(ctr, 0u);
+            const bool mark_ok = (unsigned)(em >> 32) == GLA_WS_MARK;
+            sMisc[3] = (mark_ok ? 1 : 0) | ((unsigned)em != 0u ? 2 : 0) | (tk >= ntk ? 4 : 0);
+        }
+    };
+    bool poisoned = false;
     int seg, unit;
-    if (!(sMisc[3] & 1)) {
-        // the workspace was not initialised by gla_workspace_init (counters and
-        // flags untrusted): report and fill the rows of this block's task (one
-        // block per task) with NaN
-        if (tid == 0) atomicOr(P.err, GLA_WS_ERR_INIT);
-        const int b = blockIdx.x;
-        if (LOCAL) {
-            const int x = b % P.xcds, t = b / P.xcds;
-            const int units_x = (nunits - x + P.xcds - 1) / P.xcds;
-            if (x >= nunits || t >= units_x * P.nseg) return;
-            seg = t / units_x;
-            unit = x + P.xcds * (t - seg * units_x);
-        } else {
-            if (b >= grid) return;
-            seg = b / nunits;
-            unit = b - seg * nunits;
-        }
-        nan_rows(P, unit, seg, tid);
-        return;
-    }
-    if (LOCAL) {
-        const int x = sMisc[2];
+    if (direct && LOCAL) {
+        const int x = (int)((__builtin_amdgcn_s_getreg(kXccIdReg) & 15u) % (unsigned)P.xcds);
+        const int t = (int)blockIdx.x / P.xcds;
         const int units_x = (nunits - x + P.xcds - 1) / P.xcds;  // scans x, x + xcds, ... run here
-        if (ticket >= P.xcd_tasks) {  // counters not cleared: report, fill the task's rows with NaN
-            if (tid == 0) atomicOr(P.err, GLA_WS_ERR_TICKET);
-            const int t = ticket % P.xcd_tasks;
-            if (t < units_x * P.nseg) nan_rows(P, x + P.xcds * (t % units_x), t / units_x, tid);
+        if (t >= units_x * P.nseg) {  // spare workgroup of this XCD
+            direct_checks();
             return;
         }
-        if (ticket >= units_x * P.nseg) return;  // spare workgroup of this XCD
-        seg = ticket / units_x;
-        unit = x + P.xcds * (ticket - seg * units_x);
+        seg = t / units_x;
+        unit = x + P.xcds * (t - seg * units_x);
+    } else if (direct) {
+        seg = (int)blockIdx.x / nunits;
+        unit = (int)blockIdx.x - seg * nunits;
     } else {
-        if (ticket >= grid) {  // counters not cleared: report, fill the task's rows with NaN
-            if (tid == 0) atomicOr(P.err, GLA_WS_ERR_TICKET);
-            const int t = ticket % grid;
-            nan_rows(P, t % nunits, t / nunits, tid);
+        __syncthreads();
+        const int ticket = sMisc[0];
+        // poisoned: a failure upstream (a sticky error from an earlier call, a
+        // wait that gave up, a transfer folded from a poisoned segment): every
+        // store of this task writes NaN and every flag it publishes carries the
+        // poison bit, so no row downstream of a failure holds plausible data
+        poisoned = (sMisc[3] & 2) != 0;
+        if (!(sMisc[3] & 1)) {
+            // the workspace was not initialised by gla_workspace_init (counters and
+            // flags untrusted): report and fill the rows of this block's task (one
+            // block per task) with NaN
+            if (tid == 0) atomicOr(P.err, GLA_WS_ERR_INIT);
+            const int b = blockIdx.x;
+            if (LOCAL) {
+                const int x = b % P.xcds, t = b / P.xcds;
+                const int units_x = (nunits - x + P.xcds - 1) / P.xcds;
+                if (x >= nunits || t >= units_x * P.nseg) return;
+                seg = t / units_x;
+                unit = x + P.xcds * (t - seg * units_x);
+            } else {
+                if (b >= grid) return;
+                seg = b / nunits;
+                unit = b - seg * nunits;
+            }
+            nan_rows(P, unit, seg, tid);
             return;
         }
-        seg = ticket / nunits;
-        unit = ticket - seg * nunits;
+        if (LOCAL) {
+            const int x = sMisc[2];
+            const int units_x = (nunits - x + P.xcds - 1) / P.xcds;  // scans x, x + xcds, ... run here
+            if (ticket >= P.xcd_tasks) {  // counters not cleared: report, fill the task's rows with NaN
+                if (tid == 0) atomicOr(P.err, GLA_WS_ERR_TICKET);
+                const int t = ticket % P.xcd_tasks;
+                if (t < units_x * P.nseg) nan_rows(P, x + P.xcds * (t % units_x), t / units_x, tid);
+                return;
+            }
+            if (ticket >= units_x * P.nseg) return;  // spare workgroup of this XCD
+            seg = ticket / units_x;
+            unit = x + P.xcds * (ticket - seg * units_x);
+        } else {
+            if (ticket >= grid) {  // counters not cleared: report, fill the task's rows with NaN
+                if (tid == 0) atomicOr(P.err, GLA_WS_ERR_TICKET);
+                const int t = ticket % grid;
+                nan_rows(P, t % nunits, t / nunits, tid);
+                return;
+            }
+            seg = ticket / nunits;
+            unit = ticket - seg * nunits;
+        }
     }
     const int c_begin = seg * P.seg_chunks;
     const int nch = min(P.nchunks, c_begin + P.seg_chunks) - c_begin;
@@ -573,7 +619,26 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 P.gb ? *(const float4v*)(P.gb + hd * D + 4 * i) : float4v{0.f, 0.f, 0.f, 0.f};
         }
     }
+    if (direct) direct_checks();
     __syncthreads();
+    if (direct) {
+        poisoned = (sMisc[3] & 2) != 0;
+        if (!(sMisc[3] & 1)) {
+            // workspace not initialised by gla_workspace_init (flags untrusted):
+            // report and fill this task's rows with NaN, once the first chunk's
+            // loads have landed
+            wait_mem();
+            if (tid == 0) atomicOr(P.err, GLA_WS_ERR_INIT);
+            nan_rows(P, unit, seg, tid);
+            return;
+        }
+        if (sMisc[3] & 4) {
+            // the XCD received more workgroups than its tasks, or its counter
+            // was not cleared: report and poison this task's outputs and flags
+            if (tid == 0) atomicOr(P.err, GLA_WS_ERR_TICKET);
+            poisoned = true;
+        }
+    }
 
     float4v okeep[NCHK][2];
     half8 qkeep[NCHK];    // this lane's 8 channels of the segment-relative query
