@@ -495,6 +495,39 @@ def test_error_word_is_sticky_until_status(torch):
     assert rel_err(y.cpu().numpy(), run_oracle(x, 0, H, W)) <= TOL["f16"]
 
 
+@pytest.mark.parametrize("shape", [(1, 6, "xcd-local"), (3, 3, "chip-wide")])
+def test_garbage_task_counters_poison_and_report(torch, shape):
+    """Task counters holding garbage (header word 0 and the per-XCD words
+    128 + 32x) on an initialised workspace: one-round plans, which take their
+    task from the grid index, still take a counter ticket and check it, so
+    every workgroup finds its ticket past the call's tasks, reports
+    GLA_WS_ERR_TICKET and poisons its outputs; the status call reports it and
+    re-initialises the workspace, after which the same call matches the
+    oracle.  (1 x 6 scans of 40x40 run XCD-local on an 8-XCD device, 3 x 3
+    chip-wide, both in one round.)"""
+    from recurrent_vision_backbone_key_amd import gla
+    B, NH, kind = shape
+    H = W = 40
+    x = make_inputs(B, NH, H, W, 64, 64, "f16", (0.0, 1.0), True, seed=813 + B)
+    t = _dev(x, torch)
+    opts = gla.make_opts(B, NH, 64, 64, gla.F16)
+    ws = gla.new_workspace(3, H, W, 64, opts, "cuda")
+    words = ws[:4096].view(torch.int32)
+    words[0] = 0x40000000
+    for xcd in range(8):
+        words[128 + 32 * xcd] = 0x40000000
+    print(f"[case] garbage task counters, {kind} plan", flush=True)
+    y = gla.fwd(t["q"], t["k"], t["v"], t["z"], 3, H, W, r=t["r"], norm_weight=t["w"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all(), "garbage task counters left non-NaN outputs"
+    bits = gla.workspace_status(ws)
+    assert bits & gla.WS_ERR_TICKET, f"error bits {bits:#x}"
+    y = gla.fwd(t["q"], t["k"], t["v"], t["z"], 3, H, W, r=t["r"], norm_weight=t["w"], workspace=ws)
+    torch.cuda.synchronize()
+    assert gla.workspace_status(ws) == 0
+    assert rel_err(y.cpu().numpy(), run_oracle(x, 3, H, W)) <= TOL["f16"]
+
+
 def test_staged_gate_projection_then_single_pass_on_one_workspace(torch):
     """A gate-projection call whose logits are staged in the workspace (three
     passes, one segment: no forward slots) and then a single-pass call on the
