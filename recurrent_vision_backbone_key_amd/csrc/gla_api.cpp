@@ -85,6 +85,7 @@ int run_fwd(gla::Params& P, const void* q, const void* k, const void* v, int dir
     P.xcd_tasks = plan.xcd_tasks;
     P.xcds = plan.xcds;
     P.one_round = plan.one_round;
+    P.group = plan.group > 0 ? plan.group : plan.nseg;
     P.agg = P.incl = nullptr;
     if (plan.onepass) {
         char* ws = (char*)opts->workspace;
@@ -312,6 +313,7 @@ void bwd_params(const void* q, const void* k, const void* v, const float* gate_l
     P.xcd_tasks = 0;
     P.xcds = 1;
     P.one_round = 0;
+    P.group = 1;
     no_proj(P);
     Q.dout = dout;
     Q.dq = dq;

@@ -40,6 +40,8 @@ struct Params {
     int xcd_tasks;      // single pass, xcd_local: workgroups per XCD (grid / xcds)
     int xcds;           // single pass: XCDs of the device
     int one_round;      // single pass: every workgroup of the call is resident at once
+    int group;          // single pass, one round: segments per group of the two-level
+                        // exchange (nseg: one level)
     float scale;        // output scale
     float inv_tau;      // 1 / tau
     float eps;          // RMSNorm epsilon

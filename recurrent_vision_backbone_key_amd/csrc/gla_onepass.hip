@@ -138,6 +138,8 @@ template <bool LOCAL> struct Pol {
     static constexpr int kStore = LOCAL ? 0 : 16;
 };
 constexpr int kStoreThrough = 16;  // sc1
+constexpr int kFoldBatch = 8;      // exchange transfers per round of loads (the plan's group
+                                   // sizes keep every fold within one round)
 constexpr unsigned kPoison = 8u;
 template <bool LOCAL>
 __device__ __forceinline__ float4v ld_x4(__amdgpu_buffer_rsrc_t r, unsigned off)
@@ -662,11 +664,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     // (11 more VGPRs) slowed its other plans by 2-3 %.
     const bool last = (seg == P.nseg - 1);
     const bool one_round = P.one_round != 0;
-    int G = P.nseg;  // one round: group size of the two-level exchange
-    if (P.nseg >= 24) {
-        G = 1;
-        while (G * G < P.nseg) ++G;
-    }
+    const int G = P.group;  // one round: group size of the two-level exchange (plan)
     const int grp = seg / G, gfirst = grp * G;
     const bool leader = !last && seg == gfirst + G - 1;
     const bool early = NCHK == 1 && one_round && P.nseg >= 8 && !last && !leader;
@@ -988,7 +986,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             // then the aggregates of segments first .. first+cnt-1, in that order;
             // m0, m1 collect the product of the multipliers
             auto fold = [&](float4v& s0, float4v& s1, float& m0, float& m1, int ng, int first, int cnt) {
-                constexpr int FW = 8;  // transfers per round of loads
+                constexpr int FW = kFoldBatch;  // transfers per round of loads
                 const int n = ng + cnt;
                 for (int t0 = 0; t0 < n; t0 += FW) {
                     float4v a0[FW], a1[FW];

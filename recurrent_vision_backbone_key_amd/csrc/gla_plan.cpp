@@ -52,7 +52,32 @@ extern "C" int gla_config_built(int dtype, int dk, int dv, int chunk)
     return gla::config_fits(dtype == GLA_F16 ? 2 : 4, dk, dv, chunk) ? 1 : 0;
 }
 
-extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o,
+extern "C" // Two-level exchange of one-round single-pass plans: segment j of a scan folds
+// j / G combined transfers (groups before its own) and j mod G aggregates
+// (its own group's segments before it), at most
+//     max((nseg-1) / G + (nseg-1) mod G,  nseg / G + G - 2)
+// transfers.  Below 24 segments one level (G = nseg) is faster: the leaders'
+// extra publish round trip costs more than it saves (5 segments: 34.1 ->
+// 35.7 us per call).  From 24 on, G = ceil(sqrt(nseg)), or one more when that
+// folds no more transfers at the worst segment and stays within one round of
+// 8 loads: with 25 segments groups of 6 instead of 5 (the last segment folds
+// 4 transfers instead of 8) measured 13.31 -> 13.16 us per call; with 28,
+// groups of 7 would fold 9 (a second round of loads cost about 1 us).
+int gla_exchange_group(int nseg)
+{
+    if (nseg < 24) return nseg;
+    int g = 1;
+    while (g * g < nseg) ++g;
+    auto most = [nseg](int gs) {
+        const int a = (nseg - 1) / gs + (nseg - 1) % gs;
+        const int b = nseg / gs + gs - 2;
+        return (nseg / gs >= 1 && b > a) ? b : a;
+    };
+    const int m0 = most(g), m1 = most(g + 1);
+    return (m1 <= m0 && m1 <= 8) ? g + 1 : g;
+}
+
+int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o,
                              int has_gate, const gla_geom* geo, gla_plan* plan)
 {
     if (!o || !plan) return GLA_EINVAL;
@@ -78,6 +103,7 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
     plan->onepass = 0;
     plan->xcds = xcds;
     plan->one_round = 0;
+    plan->group = 0;
     plan->proj_fused = 0;
     plan->off_z = 0;
     plan->off_flags = plan->off_agg = plan->off_incl = plan->off_slots = 0;
@@ -131,6 +157,7 @@ extern "C" int gla_make_plan(int dir, int H, int W, int chunk, const gla_opts* o
             plan->xcd_local = local ? 1 : 0;
             plan->xcd_tasks = local ? (int)(upx * nseg) : 0;
             plan->one_round = local ? (plan->xcd_tasks <= cus_per_xcd) : (units * nseg <= cus);
+            plan->group = gla_exchange_group(nseg);
             plan->off_flags = GLA_HEADER_BYTES;
             plan->off_agg = kReserved;
             plan->off_incl = plan->off_agg + nflag * ((size_t)64 * 64 + 64) * 4;

@@ -42,6 +42,8 @@ typedef struct gla_plan {
     int xcd_tasks;               // single pass, xcd_local: workgroups per XCD
     int xcds;                    // single pass: XCDs of the device
     int one_round;               // single pass: every workgroup of the call resident at once
+    int group;                   // single pass, one round: segments per group of the
+                                 // two-level exchange (nseg: one level)
     size_t workspace_bytes;
     size_t off_flags, off_agg, off_incl;  // single-pass workspace layout (bytes)
     size_t off_slots;                     // three-pass segment slots (bytes)
@@ -49,6 +51,11 @@ typedef struct gla_plan {
     size_t off_z;                // gate projection: x W1 (fused) or z staged here (bytes)
     float tau, scale, eps;
 } gla_plan;
+
+// Group size of the one-round exchange over nseg segments: nseg (one level)
+// below 24 segments, else ceil(sqrt(nseg)), or one more when no segment then
+// folds more transfers nor more than kFoldBatch (8) of them.
+int gla_exchange_group(int nseg);
 
 // Size-only checks and the work plan (segments, workspace bytes) for a
 // device of geometry `geo` (null: the MI355X default).

@@ -443,6 +443,22 @@ def test_dk_dv_differ(torch, dk, dv, dtype):
                    dtype, torch, segment_chunks=seg)
 
 
+@pytest.mark.parametrize("grid", [(32, 48), (40, 40), (32, 52), (36, 48), (32, 56), (36, 52)],
+                         ids=["24seg", "25seg", "26seg", "27seg", "28seg", "30seg"])
+def test_two_level_exchange_group_sizes(torch, grid):
+    """One-chunk segments of one round, 24 to 30 per scan: the two-level
+    exchange's group size is ceil(sqrt(nseg)) or one more (25 to 27
+    segments), which changes which segments lead a group and how many
+    transfers each folds; gated and ungated, every direction, against the
+    oracle."""
+    H, W = grid
+    for gated in (False, True):
+        x = make_inputs(1, 6, H, W, 64, 64, "f16", (0.0, 1.0), gated, seed=905 + H + W + gated)
+        for d in DIRS:
+            _check(f"exchange {H}x{W} {'g' if gated else 'u'}", x, d, H, W, 64, "f16", torch,
+                   segment_chunks=1)
+
+
 # ---------------------------------------------------------------- failures are loud
 
 def test_uninitialised_workspace_writes_nan_and_reports(torch):

@@ -24,7 +24,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int), ("nchunks", ctypes.c_int), ("seg_chunks", ctypes.c_int),
                 ("nseg", ctypes.c_int), ("onepass", ctypes.c_int), ("xcd_local", ctypes.c_int),
                 ("xcd_tasks", ctypes.c_int), ("xcds", ctypes.c_int), ("one_round", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t), ("off_flags", ctypes.c_size_t),
+                ("group", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t), ("off_flags", ctypes.c_size_t),
                 ("off_agg", ctypes.c_size_t), ("off_incl", ctypes.c_size_t),
                 ("off_slots", ctypes.c_size_t), ("proj_fused", ctypes.c_int),
                 ("off_z", ctypes.c_size_t), ("tau", ctypes.c_float), ("scale", ctypes.c_float),
@@ -129,3 +129,38 @@ def test_one_round_matches_the_grid(planner):
                 assert p.xcd_tasks == units_x * p.nseg
             else:
                 assert p.one_round == (B * NH * p.nseg <= capacity(p.seg_chunks, cus))
+
+
+def test_exchange_group_sizes(planner):
+    """Group size of the two-level exchange: one level below 24 segments;
+    from 24 on ceil(sqrt(nseg)), or one more when that folds no more
+    transfers at the worst segment and at most 8 (one round of loads);
+    every segment's fold (j / G combined transfers, j mod G aggregates)
+    checked by brute force against that bound."""
+    planner.gla_exchange_group.restype = ctypes.c_int
+    planner.gla_exchange_group.argtypes = [ctypes.c_int]
+    want = {1: 1, 5: 5, 23: 23, 24: 5, 25: 6, 26: 7, 27: 7, 28: 6, 29: 6, 30: 6, 36: 6, 37: 7, 65: 9}
+    for n, g in want.items():
+        assert planner.gla_exchange_group(n) == g, (n, planner.gla_exchange_group(n), g)
+
+    def most(n, g):
+        return max(j // g + j % g for j in range(n))
+    for n in range(24, 66):
+        g = planner.gla_exchange_group(n)
+        g0 = 1
+        while g0 * g0 < n:
+            g0 += 1
+        assert g in (g0, g0 + 1)
+        if g == g0 + 1:
+            assert most(n, g) <= min(most(n, g0), 8)
+        else:
+            assert most(n, g0 + 1) > min(most(n, g0), 8)
+
+
+def test_plan_carries_the_exchange_group(planner):
+    """A one-round single-pass plan of 25 one-chunk segments (a 40x40 frame,
+    6 heads) carries groups of 6; a 5-segment plan (8 frames) one level."""
+    p = plan(planner, None, 1, 6, 40, 40)
+    assert (p.onepass, p.nseg, p.one_round, p.group) == (1, 25, 1, 6)
+    p = plan(planner, None, 8, 6, 40, 40)
+    assert (p.onepass, p.nseg, p.one_round, p.group) == (1, 5, 1, 5)
