@@ -2,7 +2,9 @@
 16-byte-per-lane streaming read, a read + write copy and the kernels'
 row-gather pattern (tests/probes/gla_probes.hip), each over buffers larger
 than the 256 MB last-level cache, timed with HIP events on the launch stream
-over repeated launches.  Prints one JSON line.
+over repeated launches; and the latency of the segment exchange's flag
+handoff between two workgroups on one XCD or on two, for each store / load
+cache policy (sc1 or default).  Prints one JSON line.
 
 Usage (repo root): ``python tests/probes/ceilings.py [--reps N]``.
 """
@@ -28,9 +30,30 @@ def load():
     h.gla_probe_read.argtypes = [vp, sz, vp, ci, vp]
     h.gla_probe_copy.argtypes = [vp, vp, sz, ci, vp]
     h.gla_probe_gather.argtypes = [vp, ci, vp, ci, vp]
-    for f in (h.gla_probe_tr16, h.gla_probe_read, h.gla_probe_copy, h.gla_probe_gather):
+    h.gla_probe_handoff.argtypes = [vp, ci, ci, ci, ci, vp, vp]
+    for f in (h.gla_probe_tr16, h.gla_probe_read, h.gla_probe_copy, h.gla_probe_gather, h.gla_probe_handoff):
         f.restype = ci
     return h
+
+
+def handoff(h, consumer, store_sc1, load_sc1, iters=500):
+    """One flag handoff probe: producer workgroup 0, consumer `consumer`.
+    Returns a dict with the one-way latency in microseconds (the producer's
+    loop time over 2 iters handoffs) or the number of handoffs seen before a
+    bounded wait ran out, and the XCC_IDs of the two workgroups."""
+    import torch
+    words = torch.zeros(64, dtype=torch.int32, device="cuda")
+    out = torch.zeros(6, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert h.gla_probe_handoff(words.data_ptr(), iters, consumer, store_sc1, load_sc1, out.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    ticks, done, xp, xc, tp, tc = out.cpu().tolist()
+    rec = {"consumer": consumer, "store": "sc1" if store_sc1 else "default",
+           "load": "sc1" if load_sc1 else "default", "xcc": [xp, xc], "handoffs": done,
+           "ran_out": bool(tp or tc)}
+    if done == iters and not (tp or tc):
+        rec["one_way_us"] = round(ticks * 0.01 / (2 * iters), 3)
+    return rec
 
 
 def main():
@@ -73,6 +96,7 @@ def main():
         "row_gather_16x64B": timed(lambda: h.gla_probe_gather(gsrc.data_ptr(), args.side, sink.data_ptr(),
                                                                blocks, s), rows * 128),
         "bytes": {"read": n, "copy": 2 * n, "gather": rows * 128},
+        "flag_handoff": [handoff(h, c, ss, ls) for c in (8, 1) for ss, ls in ((1, 1), (0, 1), (1, 0), (0, 0))],
         "peak_tb_per_s": 8.0,
     }
     print(json.dumps(out), flush=True)

@@ -10,6 +10,10 @@
 //    (16-byte-per-lane reads, read + write copy, and the kernels' row-gather
 //    pattern: 16 rows x 64 bytes per wavefront instruction in a permuted row
 //    order, 512-thread workgroups).
+//  * gla_probe_handoff: latency of the exchange's flag handoff between two
+//    workgroups on one XCD or on two, for each store / load cache policy
+//    (the kernels: sc1 loads; sc1 stores across XCDs, default-policy flag
+//    stores within one), and whether a policy pair sees the handoff at all.
 //
 // Every launch is bounds-checked on the host: the byte counts must be
 // multiples of the per-thread access and the grids cover them exactly.
@@ -100,9 +104,103 @@ __global__ __launch_bounds__(512) void probe_gather_kernel(const u32x4* src, int
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Flag handoff between two single-wave workgroups (the exchange's protocol
+// reduced to one word): the producer stores i to word 0 and waits until the
+// consumer has copied it to word 32; the consumer waits for i in word 0 and
+// stores it to word 32.  Stores and polls are relaxed atomics, so every poll
+// is issued again; agent scope compiles to the sc1 policy the kernels use on
+// their buffer instructions, workgroup scope to the default policy (SC1: 1
+// for sc1 stores / loads).  Every wait is bounded (kSpin polls); a wait that
+// runs out ends both sides (the other one runs out too) and is reported.
+// Workgroup 0 produces; the consumer is workgroup `consumer` (1: the next XCD
+// under turn-by-turn dispatch, 8: the same XCD on an 8-XCD device); every
+// other workgroup returns at once.  out[0]: realtime ticks (100 MHz) of the
+// producer's loop, out[1]: handoffs completed, out[2], out[3]: XCC_ID of
+// producer and consumer, out[4], out[5]: a wait ran out (producer, consumer).
+constexpr unsigned kSpin = 1u << 20;
+constexpr int kXccId = 20 | (0 << 6) | ((4 - 1) << 11);
+
+template <bool SC1>
+__device__ __forceinline__ unsigned hload(const unsigned* p)
+{
+    return SC1 ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+template <bool SC1>
+__device__ __forceinline__ void hstore(unsigned* p, unsigned v)
+{
+    if (SC1)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <bool SS, bool LS>
+__global__ __launch_bounds__(64) void probe_handoff_kernel(unsigned* words, int iters, int consumer,
+                                                           unsigned long long* out)
+{
+    const int b = blockIdx.x;
+    if (b != 0 && b != consumer) return;
+    if (threadIdx.x != 0) return;
+    const unsigned xcc = __builtin_amdgcn_s_getreg(kXccId) & 15u;
+    bool timeout = false;
+    if (b == 0) {
+        out[2] = xcc;
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        int done = 0;
+        for (int i = 1; i <= iters; ++i) {
+            hstore<SS>(words, (unsigned)i);
+            unsigned spins = 0;
+            while (hload<LS>(words + 32) != (unsigned)i && spins <= kSpin) ++spins;
+            if (spins > kSpin) {
+                timeout = true;
+                break;
+            }
+            done = i;
+        }
+        const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+        out[0] = t1 - t0;
+        out[1] = (unsigned long long)done;
+        out[4] = timeout ? 1ull : 0ull;
+    } else {
+        out[3] = xcc;
+        for (int i = 1; i <= iters; ++i) {
+            unsigned spins = 0;
+            while (hload<LS>(words) != (unsigned)i && spins <= kSpin) ++spins;
+            if (spins > kSpin) {
+                timeout = true;
+                break;
+            }
+            hstore<SS>(words + 32, (unsigned)i);
+        }
+        out[5] = timeout ? 1ull : 0ull;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// words: 64 zeroed device words; out: 6 zeroed device 64-bit words.
+// store_sc1 / load_sc1: 1 for the sc1 policy, 0 for the default one.
+__attribute__((visibility("default"))) int gla_probe_handoff(unsigned* words, int iters, int consumer,
+                                                             int store_sc1, int load_sc1,
+                                                             unsigned long long* out, void* stream)
+{
+    if (iters <= 0 || consumer < 1 || consumer > 64) return 2;
+    const dim3 grid(consumer + 1), block(64);
+    hipStream_t st = (hipStream_t)stream;
+    if (store_sc1 && load_sc1)
+        hipLaunchKernelGGL((probe_handoff_kernel<true, true>), grid, block, 0, st, words, iters, consumer, out);
+    else if (!store_sc1 && load_sc1)
+        hipLaunchKernelGGL((probe_handoff_kernel<false, true>), grid, block, 0, st, words, iters, consumer, out);
+    else if (store_sc1 && !load_sc1)
+        hipLaunchKernelGGL((probe_handoff_kernel<true, false>), grid, block, 0, st, words, iters, consumer, out);
+    else
+        hipLaunchKernelGGL((probe_handoff_kernel<false, false>), grid, block, 0, st, words, iters, consumer, out);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 
 // out: 64 lanes x 12 binary16 values (the 4 of the single read, then the 8 of
 // the fragment), device memory.  Returns 0, or 1 on a launch error.

@@ -84,3 +84,22 @@ def test_streaming_probes_compute_what_they_read(probes):
                     acc ^= int(rows[row, 4 * h + g].astype(np.uint64).sum()) & 0xFFFFFFFF
             want[b * 512 + tid] = acc
     assert np.array_equal(sink.cpu().numpy().view(np.uint32).astype(np.uint64), want)
+
+
+def test_flag_handoff_policies_the_exchange_uses(probes):
+    """The segment exchange's cache policies see each other's flags: sc1
+    stores and sc1 loads between workgroups on one XCD and on two, and
+    default-policy stores read by sc1 loads on one XCD (the flags of
+    XCD-local plans); every handoff arrives within the bounded wait.  (On an
+    8-XCD device workgroups 0 and 8 share an XCD and 0 and 1 do not, under
+    turn-by-turn dispatch.)"""
+    import torch
+    from ceilings import handoff
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for consumer, ss, ls in ((8, 1, 1), (1, 1, 1), (8, 0, 1)):
+        rec = handoff(probes, consumer, ss, ls, iters=200)
+        print(f"[handoff] {rec}", flush=True)
+        assert rec["handoffs"] == 200 and not rec["ran_out"], rec
+        if cus == 256:
+            same = rec["xcc"][0] == rec["xcc"][1]
+            assert same == (consumer == 8), rec
