@@ -233,15 +233,16 @@ def time_steps(step, rotate, steps, warmup, args, steps_per_graph):
     each (a replay has a fixed cost of about 15 us on this platform, so several
     steps share one); graph i holds steps on input sets i*G .. i*G+G-1 (mod
     rotate), enough graphs that the sets cycle without repeating back to back.
-    Runs `warmup` untimed steps, then times `steps` steps with HIP events on
-    the replay stream.  Returns (ms per step, G, whether graphs were used)."""
+    Runs `warmup` untimed steps (whole replays, then the remainder as eager
+    steps, so that G depends on `steps` only), then times `steps` steps with
+    HIP events on the replay stream.  Returns (ms per step, G, whether graphs
+    were used)."""
     import torch
 
     G = 1
     if not args.no_graph:
         G = args.steps_per_graph or steps_per_graph
         G = math.gcd(G, steps) if steps > 0 else 1
-        G = math.gcd(G, warmup) if warmup > 0 else G
     n_graphs = rotate // math.gcd(rotate, G)
     stream = torch.cuda.current_stream()
     graphs = None
@@ -271,6 +272,8 @@ def time_steps(step, rotate, steps, warmup, args, steps_per_graph):
 
     for i in range(warmup // G):
         run(i)
+    for j in range(warmup % G):
+        step((warmup // G * G + j) % rotate)
     torch.cuda.synchronize()
     # one event before every replay (or eager step) and one after the last:
     # the whole bracket gives the mean, consecutive pairs give each replay's
