@@ -727,7 +727,19 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         }
         gate_stage<PROJ>(raw, cur, sTot, sW2, sGB, P.inv_tau, si, h, g, l16, c0);
         if (c + 1 < nch) load_raw<PROJ>(raw, src, P, sRows[(c + 1) * C + tl], c0, g);
-        __syncthreads();  // (1) sub-chunk totals
+        __syncthreads();  // (1) sub-chunk totals; every wave has left the previous chunk
+        if (LY::kMulti && c > 0) {
+            // the local state's binary16 copy for this chunk's inter-chunk term
+            // (S holds the state after the previous chunk until this chunk's
+            // state update)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int bb = sb0 + jj;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sST[(16 * bb + l16) * SH + 16 * sa + 4 * g + e] = (_Float16)S[jj][e];
+            }
+        }
         float bl[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) bl[e] = cur.bl[e];
@@ -876,17 +888,12 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
         okeep[c][1] = o[1];
 
         if (!pub_now) state_update();
-        __syncthreads();  // (4) all readers of this chunk's buffers are done
-        if (LY::kMulti && c + 1 < nch) {
-            // the local state's binary16 copy for the next chunk's inter-chunk term
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int bb = sb0 + jj;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sST[(16 * bb + l16) * SH + 16 * sa + 4 * g + e] = (_Float16)S[jj][e];
-            }
-        }
+        // No barrier between chunks: before the next chunk's barrier (1) a wave
+        // writes only its sub-chunk totals, which every wave has read before
+        // this chunk's barrier (3); every other buffer is written after (1),
+        // when all waves have left this chunk.  Waves with the short products
+        // of the first sub-chunks go on to the next gate stage meanwhile.
+        if (c + 1 >= nch) __syncthreads();  // (4) all readers of the last chunk's buffers are done
     }
 
     // r of every chunk at this lane's output positions (token tl, value
