@@ -23,8 +23,11 @@
 //           last segment then waits until every earlier one has finished
 //           its exchange and clears the scan's flags for the next call.
 //
-// Work split inside a chunk: wavefront w handles the 16-token sub-chunk
-// i = w & 3 and the half h = w >> 2 of the channels.  A lane holds 8 channels
+// Work split inside a chunk: wavefront w handles the half h = w >> 2 of the
+// channels and the 16-token sub-chunk i = w & 3 (h = 0) or 3 - (w & 3)
+// (h = 1): waves w and w + 4 share a SIMD, and sub-chunk i has i + 1 score
+// tiles, so each SIMD holds one light and one heavy sub-chunk (0 and 3, 1
+// and 2).  The two waves of a sub-chunk are w and 7 - w.  A lane holds 8 channels
 // of one token, which is both the row layout of the MFMA operands and the
 // layout the gate stage needs: the log-decay is accumulated along the 16
 // tokens of the sub-chunk with a DPP prefix scan across the lane row.  With
@@ -339,7 +342,7 @@ __device__ __forceinline__ void scores_values(const _Float16* sE, const _Float16
     for (int j = 0; j < NSUB; ++j) {
         at[j] = float4v{0.f, 0.f, 0.f, 0.f};
         if (j > SI) continue;
-        const float4v other = *(const float4v*)(sPA + (((wave ^ 4) * NSUB + j) * 64 + lane) * 4);
+        const float4v other = *(const float4v*)(sPA + (((7 - wave) * NSUB + j) * 64 + lane) * 4);
         if (j < SI) {
             at[j] = part[j] + other;
         } else {
@@ -462,8 +465,8 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
-    const int si = wave & 3;        // sub-chunk of this wave
     const int h = wave >> 2;        // channel half (phase 1) / value half (outputs)
+    const int si = h ? 3 - (wave & 3) : (wave & 3);  // sub-chunk of this wave (partner: 7 - wave)
     const int cht = lane & 31;      // table layout: channel 32*h + cht
     const int ht = lane >> 5;       //               first or second group of tables
     const int c0 = 32 * h + 8 * g;  // this lane's 8 channels (row layout)
