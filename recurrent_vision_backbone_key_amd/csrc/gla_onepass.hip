@@ -900,22 +900,29 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     }
 
     // r of every chunk at this lane's output positions (token tl, value
-    // channels 32h + 16m + 4g .. +3): loads issued now, in flight during the
-    // exchange
+    // channels 32h + 16m + 4g .. +3), in flight during the exchange: loaded
+    // now, or, by the segments of one-round plans that publish an aggregate
+    // after the loop, right after its flag (the flag waits for every
+    // outstanding access of the wave, and r comes from memory, later than
+    // the aggregate stores' acknowledgement)
     half4 rreg[NCHK][2];
+    auto load_r = [&]() {
 #pragma unroll
-    for (int cc = 0; cc < NCHK; ++cc) {
+        for (int cc = 0; cc < NCHK; ++cc) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) rreg[cc][m] = half4{0, 0, 0, 0};
-        if (gated && cc < nch) {
-            const int t = sRows[cc * C + tl];
-            if (t >= 0) {
+            for (int m = 0; m < 2; ++m) rreg[cc][m] = half4{0, 0, 0, 0};
+            if (gated && cc < nch) {
+                const int t = sRows[cc * C + tl];
+                if (t >= 0) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    rreg[cc][m] = *(const half4*)((const _Float16*)P.r + (size_t)t * D + 32 * h + 16 * m + 4 * g);
+                    for (int m = 0; m < 2; ++m)
+                        rreg[cc][m] = *(const half4*)((const _Float16*)P.r + (size_t)t * D + 32 * h + 16 * m + 4 * g);
+                }
             }
         }
-    }
+    };
+    const bool r_after_flag = NCHK <= 5 && P.nseg > 1 && one_round && !last && !leader && !early;
+    if (!r_after_flag) load_r();
 
     // ================= phase 2: segment exchange =================
     float* sL = (float*)(lds + LY::LSEG);
@@ -1037,6 +1044,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 st_x4(r, off1, l1);
                 if (tid < D / 4) st_x4(r, st_bytes + 16u * tid, *(const float4v*)(sG + 4 * tid));
                 set_flag(need_in ? 1u : 5u);  // the first segment reads nothing
+                if (r_after_flag) load_r();
             }
             if (leader) {
                 // combined transfer of this group: its earlier aggregates, then this
