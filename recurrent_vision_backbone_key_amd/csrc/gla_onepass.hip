@@ -902,9 +902,9 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     // r of every chunk at this lane's output positions (token tl, value
     // channels 32h + 16m + 4g .. +3), in flight during the exchange: loaded
     // now, or, by the segments of one-round plans that publish an aggregate
-    // after the loop, right after its flag (the flag waits for every
-    // outstanding access of the wave, and r comes from memory, later than
-    // the aggregate stores' acknowledgement)
+    // or a group's combined transfer after the loop, right after that flag
+    // (the flag waits for every outstanding access of the wave, and r comes
+    // from memory, later than the stores are acknowledged)
     half4 rreg[NCHK][2];
     auto load_r = [&]() {
 #pragma unroll
@@ -921,7 +921,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             }
         }
     };
-    const bool r_after_flag = NCHK <= 5 && P.nseg > 1 && one_round && !last && !leader && !early;
+    const bool r_after_flag = NCHK <= 5 && P.nseg > 1 && one_round && !last && !early;
     if (!r_after_flag) load_r();
 
     // ================= phase 2: segment exchange =================
@@ -1069,6 +1069,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                     st_x1_pol<LOCAL>(r, st_bytes + 4u * (ch0 + 32), m1);
                 }
                 set_flag(2u);
+                if (r_after_flag) load_r();
             }
             if (need_in) {
                 wait_for(grp, gfirst, seg - gfirst);
