@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gla.h"
 #include "gla_device.h"
 #include "gla_geometry.h"
@@ -999,47 +1001,58 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                 __syncthreads();
                 poisoned |= sMisc[14] != 0;
             };
-            // fold, from (s0, s1), the combined transfers of groups 0 .. ng-1 and
-            // then the aggregates of segments first .. first+cnt-1, in that order;
-            // m0, m1 collect the product of the multipliers
-            auto fold = [&](float4v& s0, float4v& s1, float& m0, float& m1, int ng, int first, int cnt) {
-                constexpr int FW = kFoldBatch;  // transfers per round of loads
-                const int n = ng + cnt;
-                for (int t0 = 0; t0 < n; t0 += FW) {
-                    float4v a0[FW], a1[FW];
-                    float g0[FW], g1[FW];
+            // one round of loads of up to W transfers t0 .. t0 + W - 1 (of n),
+            // then their fold steps in order
+            auto fold_round = [&](auto wc, float4v& s0, float4v& s1, float& m0, float& m1, int ng,
+                                  int first, int n, int t0) {
+                constexpr int W = decltype(wc)::value;
+                float4v a0[W], a1[W];
+                float g0[W], g1[W];
     #pragma unroll
-                    for (int b = 0; b < FW; ++b) {
-                        // The one-chunk instance issues no loads for the slots past
-                        // the last transfer (1600-token frame, folds of 4 to 8
-                        // transfers: 13.24 -> 12.69 us per call); the others load
-                        // the last transfer again there, which measured faster for
-                        // them than the branches (gated batch 31.1 against 31.7 us).
-                        if (NCHK == 1 && t0 + b >= n) {
-                            a0[b] = a1[b] = float4v{0.f, 0.f, 0.f, 0.f};
-                            g0[b] = g1[b] = 1.f;
-                            continue;
-                        }
-                        const int t = min(t0 + b, n - 1);
-                        const float* base = t < ng ? P.incl + leader_slot(t) * aggf
-                                                   : P.agg + ((size_t)unit * P.nseg + first + t - ng) * aggf;
-                        const __amdgpu_buffer_rsrc_t r = xrsrc(base, agg_bytes);
-                        a0[b] = ld_x4<LOCAL>(r, off0);
-                        a1[b] = ld_x4<LOCAL>(r, off1);
-                        g0[b] = ld_x1<LOCAL>(r, st_bytes + 4u * ch0);
-                        g1[b] = ld_x1<LOCAL>(r, st_bytes + 4u * (ch0 + 32));
+                for (int b = 0; b < W; ++b) {
+                    // The one-chunk instance issues no loads for the slots past
+                    // the last transfer (1600-token frame, folds of 4 to 8
+                    // transfers: 13.25 -> 12.77 us per call); the others load
+                    // the last transfer again there, which measured faster for
+                    // them than the branches (gated batch 31.1 against 31.7 us).
+                    if (NCHK == 1 && t0 + b >= n) {
+                        a0[b] = a1[b] = float4v{0.f, 0.f, 0.f, 0.f};
+                        g0[b] = g1[b] = 1.f;
+                        continue;
                     }
+                    const int t = min(t0 + b, n - 1);
+                    const float* base = t < ng ? P.incl + leader_slot(t) * aggf
+                                               : P.agg + ((size_t)unit * P.nseg + first + t - ng) * aggf;
+                    const __amdgpu_buffer_rsrc_t r = xrsrc(base, agg_bytes);
+                    a0[b] = ld_x4<LOCAL>(r, off0);
+                    a1[b] = ld_x4<LOCAL>(r, off1);
+                    g0[b] = ld_x1<LOCAL>(r, st_bytes + 4u * ch0);
+                    g1[b] = ld_x1<LOCAL>(r, st_bytes + 4u * (ch0 + 32));
+                }
     #pragma unroll
-                    for (int b = 0; b < FW; ++b)
-                        if (t0 + b < n) {
+                for (int b = 0; b < W; ++b)
+                    if (t0 + b < n) {
     #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                s0[e] = fold_step(g0[b], s0[e], a0[b][e]);
-                                s1[e] = fold_step(g1[b], s1[e], a1[b][e]);
-                            }
-                            m0 *= g0[b];
-                            m1 *= g1[b];
+                        for (int e = 0; e < 4; ++e) {
+                            s0[e] = fold_step(g0[b], s0[e], a0[b][e]);
+                            s1[e] = fold_step(g1[b], s1[e], a1[b][e]);
                         }
+                        m0 *= g0[b];
+                        m1 *= g1[b];
+                    }
+            };
+            // fold, from (s0, s1), the combined transfers of groups 0 .. ng-1 and
+            // then the aggregates of segments first .. first+cnt-1, in that order
+            // (m0, m1 collect the product of the multipliers); rounds of kFoldBatch
+            // transfers, and of 4 for a last round of at
+            // most 4 in the multi-chunk instances (fewer repeated loads)
+            auto fold = [&](float4v& s0, float4v& s1, float& m0, float& m1, int ng, int first, int cnt) {
+                const int n = ng + cnt;
+                for (int t0 = 0; t0 < n; t0 += kFoldBatch) {
+                    if (NCHK > 1 && n - t0 <= 4)
+                        fold_round(std::integral_constant<int, 4>{}, s0, s1, m0, m1, ng, first, n, t0);
+                    else
+                        fold_round(std::integral_constant<int, kFoldBatch>{}, s0, s1, m0, m1, ng, first, n, t0);
                 }
             };
             auto set_flag = [&](unsigned v) {
