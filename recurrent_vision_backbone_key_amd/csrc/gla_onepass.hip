@@ -1167,13 +1167,16 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                     s0 = ld_x4<LOCAL>(r, off0);
                     s1 = ld_x4<LOCAL>(r, off1);
                 }
-                constexpr int FW = 8;  // aggregates per round of loads
-                for (int sg0 = k + 1; sg0 < seg; sg0 += FW) {
-                    // issue the loads of up to FW aggregates, then fold them in order
-                    float4v a0[FW], a1[FW];
-                    float g0[FW], g1[FW];
+                // rounds of 8 aggregates, and of 4 for a last round of at most 4
+                // (a segment mostly folds the few aggregates after the latest
+                // inclusive state: fewer repeated loads)
+                auto lb_round = [&](auto wc, int sg0) {
+                    constexpr int W = decltype(wc)::value;
+                    // issue the loads of up to W aggregates, then fold them in order
+                    float4v a0[W], a1[W];
+                    float g0[W], g1[W];
     #pragma unroll
-                    for (int b = 0; b < FW; ++b) {
+                    for (int b = 0; b < W; ++b) {
                         const int sg = min(sg0 + b, seg - 1);
                         const __amdgpu_buffer_rsrc_t r = xrsrc(P.agg + ((size_t)unit * P.nseg + sg) * aggf, agg_bytes);
                         a0[b] = ld_x4<LOCAL>(r, off0);
@@ -1182,7 +1185,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                         g1[b] = ld_x1<LOCAL>(r, st_bytes + 4u * (ch0 + 32));
                     }
     #pragma unroll
-                    for (int b = 0; b < FW; ++b)
+                    for (int b = 0; b < W; ++b)
                         if (sg0 + b < seg) {
     #pragma unroll
                             for (int e = 0; e < 4; ++e) {
@@ -1190,6 +1193,12 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
                                 s1[e] = fold_step(g1[b], s1[e], a1[b][e]);
                             }
                         }
+                };
+                for (int sg0 = k + 1; sg0 < seg; sg0 += 8) {
+                    if (seg - sg0 <= 4)
+                        lb_round(std::integral_constant<int, 4>{}, sg0);
+                    else
+                        lb_round(std::integral_constant<int, 8>{}, sg0);
                 }
                 // S_in^T (binary16) for phase 3; inclusive state for successors
     #pragma unroll
