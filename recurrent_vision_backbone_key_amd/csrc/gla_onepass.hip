@@ -967,39 +967,48 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             // order makes the result independent of timing.  Flag bits: 1
             // aggregate, 2 combined transfer, 4 done reading.
             auto leader_slot = [&](int gg) { return (size_t)unit * P.nseg + (size_t)(gg * G + G - 1); };
-            // wave 0 waits until groups 0 .. ng-1 have their combined transfers and
-            // segments first .. first+cnt-1 their aggregates (ng + cnt <= 64)
-            // (a poison bit on any of those flags, or a wait that gives up,
-            // poisons this task)
-            auto wait_for = [&](int ng, int first, int cnt) {
-                if (wave == 0) {
-                    unsigned spins = 0;
-                    bool bad = false;
-                    for (;;) {
-                        bool ok = true;
-                        unsigned f = 0u;
-                        if (lane < ng) {
-                            f = ld_flag<LOCAL>(flags, P.nseg, lane * G + G - 1);
-                            ok = (f & 2u) != 0u;
-                        } else if (lane < ng + cnt) {
-                            f = ld_flag<LOCAL>(flags, P.nseg, first + lane - ng);
-                            ok = (f & 1u) != 0u;
-                        }
-                        if (__all(ok)) {
-                            bad = __any((f & kPoison) != 0u);
-                            break;
-                        }
-                        if (++spins > (1u << 22)) {
-                            if (lane == 0) atomicOr(P.err, GLA_WS_ERR_WAIT);
-                            bad = true;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
+            // the calling wave waits until groups 0 .. ng-1 have their combined
+            // transfers and segments first .. first+cnt-1 their aggregates
+            // (ng + cnt <= 64); true if a poison bit is on any of those flags or
+            // the wait gave up
+            auto poll_flags = [&](int ng, int first, int cnt) -> bool {
+                unsigned spins = 0;
+                for (;;) {
+                    bool ok = true;
+                    unsigned f = 0u;
+                    if (lane < ng) {
+                        f = ld_flag<LOCAL>(flags, P.nseg, lane * G + G - 1);
+                        ok = (f & 2u) != 0u;
+                    } else if (lane < ng + cnt) {
+                        f = ld_flag<LOCAL>(flags, P.nseg, first + lane - ng);
+                        ok = (f & 1u) != 0u;
                     }
-                    if (lane == 0) sMisc[14] = bad ? 1 : 0;
+                    if (__all(ok)) return __any((f & kPoison) != 0u);
+                    if (++spins > (1u << 22)) {
+                        if (lane == 0) atomicOr(P.err, GLA_WS_ERR_WAIT);
+                        return true;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
                 }
-                __syncthreads();
-                poisoned |= sMisc[14] != 0;
+            };
+            auto wait_for = [&](int ng, int first, int cnt) {
+                if constexpr (NCHK == 1) {
+                    // one-chunk segments: every wave polls the flags itself and
+                    // goes on to its own loads when all are set, with no barrier
+                    // (a flag's ready and poison bits are stored together, so the
+                    // waves agree on the poison)
+                    poisoned |= poll_flags(ng, first, cnt);
+                } else {
+                    // longer segments: wave 0 polls and a barrier hands its
+                    // verdict to the others (measured faster there, the other
+                    // waves' polls competing with wave 0's)
+                    if (wave == 0) {
+                        const bool bad = poll_flags(ng, first, cnt);
+                        if (lane == 0) sMisc[14] = bad ? 1 : 0;
+                    }
+                    __syncthreads();
+                    poisoned |= sMisc[14] != 0;
+                }
             };
             // one round of loads of up to W transfers t0 .. t0 + W - 1 (of n),
             // then their fold steps in order
@@ -1244,18 +1253,33 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
             if (cc < nch) *(half8*)(sOut + (cc * C + tl) * SH + c0) = qkeep[cc];
         __syncthreads();
     }
+    // the S_in^T fragments of this wave's value tiles, the same for every chunk:
+    // read once before the chunk loop when there are several chunks, with the
+    // query fragments otherwise (measured faster for one chunk)
+    constexpr bool kHoistIn = NCHK > 1;
+    half8 h0[2], h1[2];
+    if (kHoistIn && need_in) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int k0 = 32 * kb + 8 * g;
+            h0[kb] = *(const half8*)(sST + (32 * h + l16) * SH + k0);
+            h1[kb] = *(const half8*)(sST + (32 * h + 16 + l16) * SH + k0);
+        }
+    }
 #pragma unroll
     for (int cc = 0; cc < NCHK; ++cc) {
         if (cc >= nch) break;
         float4v o0 = okeep[cc][0], o1 = okeep[cc][1];
         if (need_in) {
-            half8 qf[2], h0[2], h1[2];  // every operand read before the first product
+            half8 qf[2];  // every operand read before the first product
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int k0 = 32 * kb + 8 * g;
                 qf[kb] = *(const half8*)(sOut + (cc * C + tl) * SH + k0);
-                h0[kb] = *(const half8*)(sST + (32 * h + l16) * SH + k0);
-                h1[kb] = *(const half8*)(sST + (32 * h + 16 + l16) * SH + k0);
+                if (!kHoistIn) {
+                    h0[kb] = *(const half8*)(sST + (32 * h + l16) * SH + k0);
+                    h1[kb] = *(const half8*)(sST + (32 * h + 16 + l16) * SH + k0);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
