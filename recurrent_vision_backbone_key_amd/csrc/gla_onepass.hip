@@ -108,6 +108,8 @@ template <int NCHK> struct Lay {
     static_assert(TOTAL_PROJ <= kLdsLimit, "LDS budget of one CU exceeded");
     static_assert(GSEG + D * 4 <= TOT, "segment aggregate overlaps live buffers");
     static_assert(OUT + NCHK * C * SH * 2 <= ROWS, "output staging overlaps live buffers");
+    static_assert(kMulti || (OUT >= ST + D * SH * 2 && OUT + C * SH * 2 <= LSEG),
+                  "one-chunk query staging overlaps the exchange's buffers");
 };
 static_assert(kFusedProjRank == 16, "the fused gate expansion is built for rank 16");
 
@@ -930,6 +932,12 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     float* sL = (float*)(lds + LY::LSEG);
     float* sG = (float*)(lds + LY::GSEG);
     const bool need_in = (seg > 0);
+    _Float16* sOut = (_Float16*)(lds + LY::OUT);
+    // one chunk: the query staging area (the k-hat buffer, free since the
+    // chunk's last barrier) is apart from everything the exchange uses, so the
+    // query-operand halves are exchanged now and the barrier that ends the
+    // exchange orders them before phase 3
+    if (!LY::kMulti && need_in && nch > 0) *(half8*)(sOut + tl * SH + c0) = qkeep[0];
     if (P.nseg > 1) {
         // local state and total decay into LDS, row-major [ch][dv]
 #pragma unroll
@@ -1245,8 +1253,7 @@ __global__ __launch_bounds__(NT) void gla_onepass_kernel(Params P)
     __syncthreads();
 
     // ================= phase 3: incoming state, epilogue, stores =================
-    _Float16* sOut = (_Float16*)(lds + LY::OUT);
-    if (need_in) {
+    if (LY::kMulti && need_in) {
         // exchange the query-operand halves through the staging area
 #pragma unroll
         for (int cc = 0; cc < NCHK; ++cc)
